@@ -1,0 +1,313 @@
+#!/usr/bin/env python3
+"""Benchmark of the latent-KV hot path on one MI355X.
+
+A step is one pass of the whole path for one layer: evict the 3 oldest frames
+of that layer's 21-frame window, fused cache write of the new 3-frame chunk
+(4680 tokens), absorbed attention of the chunk's 4680 queries over the 32760
+resident keys.  Steps cycle over the windows of 30 layers (440 MB of latent
+cache, more than the 256 MB last-level cache).  Printed metric: attended query
+tokens/s per layer = batch * 4680 / step time, plus MFMA utilisation.
+
+Also reported: the main attention kernel alone (HIP events recorded by the
+library on its stream) against the bf16 MFMA roofline, the dense per-head MHA
+comparison on the same shape, a cache-bound small-query case against HBM
+bandwidth, and the fp64 CPU oracle timed on a bounded sample.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attended query tokens/s per layer (21-frame window, 4680-q chunk) + MFMA util %"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_core_wan_window_traffic.json")
+CORE_SOURCES = ["rank_latent_kv_absorbed_amd/csrc/mla_attn_core.h",
+                "rank_latent_kv_absorbed_amd/csrc/mla_attend.hip",
+                "rank_latent_kv_absorbed_amd/csrc/mla_device.h"]
+
+
+def core_source_sha():
+    h = hashlib.sha256()
+    for p in CORE_SOURCES:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()[:16]
+
+
+class HipEvents:
+    """Raw hipEvent_t handles from the HIP runtime (for the library's profiling hook)."""
+
+    def __init__(self):
+        self.rt = ctypes.CDLL("libamdhip64.so")
+        self.rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                ctypes.c_void_p]
+        self.rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.made = []
+
+    def create(self):
+        e = ctypes.c_void_p()
+        assert self.rt.hipEventCreate(ctypes.byref(e)) == 0
+        self.made.append(e.value)
+        return e.value
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        assert self.rt.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return ms.value
+
+    def close(self):
+        for e in self.made:
+            self.rt.hipEventDestroy(e)
+        self.made = []
+
+
+def cpu_baseline(cfg, x_chunk, w, q, n1=16, n2=64):
+    """The fp64 oracle, untuned, on a bounded sample of one step: the cache
+    write of a 3-frame chunk into a 21-frame window and the attention of n1 and
+    n2 query tokens; attention time is extrapolated linearly to the chunk."""
+    import numpy as np
+    from oracle import mla as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    T = cfg.T
+    rng = np.random.default_rng(0)
+    store = O.round_to_bf16(rng.standard_normal((1, cfg.window_frames * T, cfg.width)))
+    ring = O.RingModel(cfg.window_frames, T)
+    ring.write(0, cfg.window_frames)
+    xs = x_chunk[:1].double().numpy()
+    wd = {k: v.double().numpy() for k, v in w.items()}
+    qs = q[:1].double().numpy()
+    t0 = time.perf_counter()
+    O.cache_evict(ring, cfg.chunk_frames)
+    O.cache_write(store, ring, xs, wd["w_dkr"], cfg.window_frames, cfg.chunk_frames, cfg)
+    t_write = time.perf_counter() - t0
+    q0 = cfg.window_frames * T
+    times = []
+    for n in (n1, n2):
+        t0 = time.perf_counter()
+        O.attend(store, ring, qs, q0, wd["w_uk"], wd["w_uv"], cfg, rows=np.arange(n))
+        times.append(time.perf_counter() - t0)
+    slope = max((times[1] - times[0]) / (n2 - n1), 0.0)
+    icpt = max(times[0] - slope * n1, 0.0)
+    t_step = t_write + icpt + slope * cfg.Lq
+    return {
+        "value": cfg.Lq / t_step, "unit": "query tokens/s per layer", "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"fp64 NumPy oracle, batch 1: cache write of one {cfg.chunk_frames}-frame chunk "
+                   f"({cfg.Lq} tokens, {t_write:.2f} s) into a {cfg.window_frames}-frame window, "
+                   f"attention of {n1} and {n2} query tokens x {cfg.n_heads} heads over "
+                   f"{cfg.window_frames * T} keys ({times[0]:.2f} s, {times[1]:.2f} s), "
+                   f"attention extrapolated linearly to {cfg.Lq} queries"),
+        "seconds_measured": round(t_write + sum(times), 2),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=60)
+    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--batch", type=int, default=1)
+    ap.add_argument("--layers", type=int, default=30)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip dense and small-query cases")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus_requested": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    from rank_latent_kv_absorbed_amd import LatentCache, DenseCache, attend_flops, attend_bytes
+    from rank_latent_kv_absorbed_amd.mla import mha_attend_flops
+    from synthetic import chunk_q, chunk_x, config, dense_weights, layer_weights
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    cfg = config("wan_window").with_(batch=args.batch)
+    B, T, Lq, W = cfg.batch, cfg.T, cfg.Lq, cfg.window_frames
+    Lk = W * T
+    L = args.layers
+
+    # inputs resident in HBM before timing
+    x_chunk_cpu = chunk_x(cfg, cfg.chunk_frames, chunk=1)
+    q_cpu = chunk_q(cfg, Lq, chunk=1)
+    x_chunk = x_chunk_cpu.to(dev)
+    q = q_cpu.to(dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+    x_pre = torch.randn((B, W * T, cfg.hidden), generator=gen, device=dev).to(torch.bfloat16)
+    weights_cpu = [layer_weights(cfg, layer=l) for l in range(L)]
+    weights = [{k: v.to(dev) for k, v in w.items()} for w in weights_cpu]
+    caches = []
+    for l in range(L):
+        c = LatentCache(cfg, device=dev)
+        c.write(x_pre, weights[l]["w_dkr"], 0, W)
+        caches.append(c)
+    newest = [W - 1] * L
+    out = torch.empty((B, Lq, cfg.n_heads, cfg.d_v), dtype=torch.float32, device=dev)
+    ws = torch.empty(caches[0].workspace_bytes(Lq), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    ev = HipEvents()
+    state = {"i": 0}
+
+    def step(core_events=None):
+        l = state["i"] % L
+        state["i"] += 1
+        c, w = caches[l], weights[l]
+        c.evict(cfg.chunk_frames)
+        f0 = newest[l] + 1
+        c.write(x_chunk, w["w_dkr"], f0, cfg.chunk_frames)
+        newest[l] = f0 + cfg.chunk_frames - 1
+        if core_events is not None:
+            c.set_profile_events(*core_events)
+        c.attend(q, f0 * T, w["w_uk"], w["w_uv"], out=out, workspace=ws)
+        if core_events is not None:
+            c.set_profile_events(None, None)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    core_ev = [(ev.create(), ev.create()) for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for k in range(args.steps):
+        step(core_ev[k])
+    t_stop.record()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_stop)
+    core_ms = [ev.elapsed_ms(a, b) for a, b in core_ev]
+    ms_step = total_ms / args.steps
+    core_avg = sum(core_ms) / len(core_ms)
+
+    # algorithmic work
+    core_flop = B * cfg.n_heads * Lq * Lk * (2 * (cfg.d_c + cfg.d_rope) + 2 * cfg.d_c)
+    att_flop = attend_flops(cfg.n_heads, Lq, Lk, cfg.d_c, cfg.d_rope, cfg.d_nope, cfg.d_v, B)
+    write_flop = 2 * B * Lq * cfg.hidden * cfg.width
+    step_flop = att_flop + write_flop
+    value = B * Lq / (ms_step / 1e3)
+    mfma_pct = 100.0 * step_flop / (ms_step / 1e3) / (PEAK_BF16_TFLOPS * 1e12)
+    achieved = core_flop / (core_avg / 1e3) / 1e12
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        tr = json.load(open(TRAFFIC_FILE))
+        if tr.get("kernel_source_sha") == core_source_sha() and tr.get("batch") == B:
+            traffic = tr.get("hbm_bytes_per_launch")
+
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "query tokens/s per layer",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "wan_window: per layer, evict 3 frames + fused cache write of a "
+                               "3-frame chunk + absorbed attention of its queries over a 21-frame "
+                               "window; 30 layer windows cycled",
+                   "global_batch": B, "query_tokens": Lq, "resident_keys": Lk, "n_heads": cfg.n_heads,
+                   "d_c": cfg.d_c, "d_rope": cfg.d_rope, "d_nope": cfg.d_nope, "d_v": cfg.d_v,
+                   "hidden": cfg.hidden, "grid": [cfg.grid_h, cfg.grid_w], "layers_cycled": L,
+                   "parallelism": "none (1 GPU)"},
+        "mfma_util_pct": round(mfma_pct, 2),
+        "roofline": {"bound": "mfma", "kernel": "attn_core_kernel<224,192> (latent attention)",
+                     "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "avg_launch_ms": round(core_avg, 4),
+                     "algorithmic_flop_per_launch": core_flop},
+        "breakdown_ms": {"step": round(ms_step, 4), "attend_core": round(core_avg, 4)},
+        "cache_bytes": {"latent_per_layer": caches[0].nbytes, "latent_30_layers": caches[0].nbytes * 30,
+                        "dense_per_layer": None},
+    }
+
+    if not args.no_extras:
+        # dense per-head MHA on the same shape (one layer), for time and cache bytes
+        dcache = DenseCache(cfg, device=dev)
+        dw = {k: v.to(dev) for k, v in dense_weights(cfg).items()}
+        dcache.write(x_pre, dw["w_k"], dw["w_v"], 0, W)
+        dcache.evict(cfg.chunk_frames)
+        dcache.write(x_chunk, dw["w_k"], dw["w_v"], W, cfg.chunk_frames)
+        dout = torch.empty((B, Lq, cfg.n_heads, cfg.d_qk), dtype=torch.float32, device=dev)
+        dws = torch.empty(dcache.workspace_bytes(Lq), dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            dcache.attend(q, W * T, out=dout, workspace=dws)
+        dev_ev = [(ev.create(), ev.create()) for _ in range(10)]
+        torch.cuda.synchronize()
+        for a_, b_ in dev_ev:
+            dcache.set_profile_events(a_, b_)
+            dcache.attend(q, W * T, out=dout, workspace=dws)
+        torch.cuda.synchronize()
+        d_ms = sum(ev.elapsed_ms(a_, b_) for a_, b_ in dev_ev) / len(dev_ev)
+        d_flop = mha_attend_flops(cfg.n_heads, Lq, Lk, cfg.d_qk, B)
+        result["dense_mha"] = {"attend_core_ms": round(d_ms, 4),
+                               "tflops": round(d_flop / (d_ms / 1e3) / 1e12, 2),
+                               "cache_bytes_per_layer": dcache.nbytes,
+                               "latent_vs_dense_attend_time": round(core_avg / d_ms, 3),
+                               "cache_capacity_ratio": round(dcache.nbytes / caches[0].nbytes, 3)}
+        result["cache_bytes"]["dense_per_layer"] = dcache.nbytes
+        del dcache, dws, dout
+
+        # cache-bound small-query case: Lq queries per sequence, batch 8, 30 layers cycled
+        sq = {}
+        Bs = 8
+        scfg = cfg.with_(batch=Bs)
+        scaches = []
+        for l in range(L):
+            c = LatentCache(scfg, device=dev)
+            c.ring().copy_(torch.randn(c.ring().shape, generator=gen, device=dev).to(torch.bfloat16))
+            c.set_state(0, W - 1)
+            scaches.append(c)
+        for Lqs in (1, 8):
+            qs = torch.randn((Bs, Lqs, cfg.n_heads, cfg.d_qk), generator=gen, device=dev).to(torch.bfloat16)
+            so = torch.empty((Bs, Lqs, cfg.n_heads, cfg.d_v), dtype=torch.float32, device=dev)
+            sws = torch.empty(scaches[0].workspace_bytes(Lqs), dtype=torch.uint8, device=dev)
+            for l in range(L):
+                scaches[l].attend(qs, Lk - Lqs, weights[l]["w_uk"], weights[l]["w_uv"], out=so, workspace=sws)
+            sev = [(ev.create(), ev.create()) for _ in range(2 * L)]
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for i, (a_, b_) in enumerate(sev):
+                c = scaches[i % L]
+                c.set_profile_events(a_, b_)
+                c.attend(qs, Lk - Lqs, weights[i % L]["w_uk"], weights[i % L]["w_uv"], out=so, workspace=sws)
+                c.set_profile_events(None, None)
+            e1.record()
+            torch.cuda.synchronize()
+            call_ms = e0.elapsed_time(e1) / len(sev)
+            kms = sum(ev.elapsed_ms(a_, b_) for a_, b_ in sev) / len(sev)
+            nbytes = attend_bytes(cfg.n_heads, Lqs, Lk, cfg.d_c, cfg.d_rope, cfg.d_nope, cfg.d_v, Bs)
+            sq[f"Lq{Lqs}_B{Bs}"] = {"attend_ms": round(call_ms, 4), "core_kernel_ms": round(kms, 4),
+                                   "algorithmic_bytes": nbytes,
+                                   "core_GBps": round(Bs * Lk * cfg.width * 2 / (kms / 1e3) / 1e9, 1),
+                                   "call_GBps": round(nbytes / (call_ms / 1e3) / 1e9, 1),
+                                   "hbm_frac_core": round(Bs * Lk * cfg.width * 2 / (kms / 1e3) / 1e9 / PEAK_HBM_GBS, 4)}
+        result["small_query_cache_bound"] = sq
+        del scaches
+
+    ev.close()
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, x_chunk_cpu, weights_cpu[0], q_cpu)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,210 @@
+/*
+ * mla.h -- C ABI of libmla: a latent KV cache with absorbed multi-head latent
+ * attention for chunked video-token rollouts, on AMD MI355X (gfx950).
+ *
+ * The operations follow the VideoMLA pages ("VideoMLA: Low-Rank Latent KV Cache
+ * for Minute-Scale Autoregressive Video Diffusion"; abstract, and the technical
+ * summary's sections "problem definition" and "method", items 1-4):
+ *   - per cached layer and per token, only the pair (c^KV_t, k^R_t) is stored:
+ *     a content latent shared by all heads, c = W^KV_down x  (method item 1),
+ *     and one positional key shared by all heads, rotated by 3D-RoPE over
+ *     (latent frame, grid row, grid column)                   (method item 3);
+ *   - the cache is a fixed-size sliding window of whole latent frames
+ *     (problem definition: a 21-latent-frame window);
+ *   - attention rebuilds each head's content key and value from the latent
+ *     with per-head up-projections W^K_up, W^V_up            (method item 2).
+ *     This library computes that result in absorbed form: W^K_up is folded into
+ *     each head's query, softmax(.)·C is accumulated in latent space, and
+ *     W^V_up is applied afterwards (equal by associativity).
+ * A dense per-head K/V cache (problem definition: every cached token stores
+ * full keys and values for every head) is provided with the same conventions
+ * as the in-run comparison.
+ *
+ * Conventions
+ *   - All matrices are row-major; weights map column vectors, y = W x:
+ *       w_dkr [d_c + d_rope][hidden]  rows < d_c: W^KV_down, rows >= d_c: W^KR
+ *       w_uk  [n_h][d_nope][d_c]      k^nope_h = w_uk[h] c
+ *       w_uv  [n_h][d_v][d_c]         v_h      = w_uv[h] c
+ *       w_k, w_v (dense) [n_h*d_h][hidden], d_h = d_nope + d_rope
+ *   - Tokens of a latent frame are row-major over the grid (row, column);
+ *     token tau of frame f has global index f*T + tau, T = grid_h*grid_w, and
+ *     position (f, tau / grid_w, tau % grid_w).
+ *   - 3D-RoPE rotates adjacent element pairs (2p, 2p+1); the first
+ *     rope_pairs_t pairs follow the frame axis, the next rope_pairs_h the row
+ *     axis, the last rope_pairs_w the column axis; pair i of an axis group with
+ *     P_a pairs turns by pos_axis * rope_base^(-i / P_a) radians.
+ *   - Score scale is 1/sqrt(d_nope + d_rope); every resident token is a key
+ *     (no mask inside the window).
+ *   - Ring slot of token tau of frame f: (f mod window_frames)*T + tau; batch
+ *     element b's rows start at b*window_frames*T.  Latent rows hold
+ *     [c (d_c) | k^R rotated (d_rope)]; dense rows hold [K: n_h x d_h | V: n_h x d_h].
+ *   - x, q and weights have the config's dtype (bf16 or fp32); the ring stores
+ *     cache_dtype (fp32 with fp32 inputs; bf16 or fp16 with bf16 inputs: two
+ *     bytes per stored scalar either way).  Prepared queries and softmax
+ *     weights enter the matrix units in the cache type; every sum is fp32 and
+ *     the attention output is always fp32.
+ *
+ * Ownership: the caller owns every device buffer (ring storage, weights,
+ * activations, outputs, workspace).  The library owns only the small host
+ * handle and never allocates device memory.
+ *
+ * Errors: every check runs before anything is enqueued; on error the handle's
+ * state and all memory are unchanged.  A failed kernel launch returns
+ * MLA_ERR_HIP; faults inside kernels surface at the caller's next
+ * synchronisation.  No C++ exception crosses this interface.
+ *
+ * Concurrency: a handle is not thread-safe.  Calls on one stream are ordered;
+ * ordering across streams is the caller's job.  Device pointers must be
+ * 16-byte aligned.  `stream` is a hipStream_t (NULL = the null stream).
+ */
+#ifndef MLA_H
+#define MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = 1,       /* bad config, null/misaligned pointer, bad size */
+  MLA_ERR_STORAGE_TOO_SMALL = 2, /* storage_bytes < mla_cache_bytes(cfg)           */
+  MLA_ERR_FULL = 3,              /* write would exceed the window's free frames    */
+  MLA_ERR_NOT_CONTIGUOUS = 4,    /* write does not continue the newest frame       */
+  MLA_ERR_EVICT_RANGE = 5,       /* evicting more frames than are resident         */
+  MLA_ERR_EMPTY = 6,             /* attend on an empty window                      */
+  MLA_ERR_WORKSPACE = 7,         /* workspace missing or smaller than required     */
+  MLA_ERR_UNSUPPORTED = 8,       /* shape valid but not built for this dtype       */
+  MLA_ERR_WRONG_KIND = 9,        /* latent call on a dense handle or vice versa    */
+  MLA_ERR_HIP = 10               /* kernel launch failed                           */
+} mla_status;
+
+typedef enum { MLA_F32 = 0, MLA_BF16 = 1, MLA_F16 = 2 } mla_dtype;
+
+typedef struct {
+  int32_t hidden;         /* layer input width                                  */
+  int32_t n_heads;        /* n_h                                                */
+  int32_t d_nope;         /* per-head content part of q.k                       */
+  int32_t d_rope;         /* shared positional key width (even)                 */
+  int32_t d_v;            /* per-head value width                               */
+  int32_t d_c;            /* shared content latent width                        */
+  int32_t grid_h, grid_w; /* tokens per latent frame T = grid_h*grid_w          */
+  int32_t window_frames;  /* ring capacity W in whole latent frames             */
+  int32_t batch;          /* B independent sequences on one schedule            */
+  int32_t rope_pairs_t, rope_pairs_h, rope_pairs_w; /* sum = d_rope/2 (latent) */
+  float rope_base;        /* frequency base, e.g. 10000                         */
+  int32_t dtype;          /* inputs (x, q, weights): MLA_BF16 or MLA_F32         */
+  int32_t cache_dtype;    /* ring storage: MLA_F32 with fp32 inputs; MLA_BF16 or
+                             MLA_F16 with bf16 inputs (2 bytes per scalar)      */
+} mla_layer_config;
+
+typedef struct {
+  int64_t oldest_frame;   /* first resident frame (== newest+1 when empty)      */
+  int64_t newest_frame;   /* last resident frame                                */
+  int32_t n_resident_frames;
+  int32_t capacity_frames;
+} mla_cache_info;
+
+typedef struct mla_cache mla_cache; /* opaque host handle, one per cached layer */
+
+/* Bytes of ring storage for one latent layer:
+ * batch * window_frames * T * (d_c + d_rope) * sizeof(cache_dtype).  0 on a bad config. */
+size_t mla_cache_bytes(const mla_layer_config* cfg);
+
+/* Bytes of ring storage for one dense layer:
+ * batch * window_frames * T * 2 * n_heads * (d_nope + d_rope) * sizeof(cache_dtype). */
+size_t mha_cache_bytes(const mla_layer_config* cfg);
+
+/* Create a latent-cache handle over caller-owned `storage` (device memory of at
+ * least mla_cache_bytes(cfg)).  The window starts empty.  The storage content
+ * is not touched. */
+mla_status mla_cache_create(const mla_layer_config* cfg, void* storage, size_t storage_bytes,
+                            mla_cache** out);
+
+/* Same for a dense per-head K/V cache (the comparison path). */
+mla_status mha_cache_create(const mla_layer_config* cfg, void* storage, size_t storage_bytes,
+                            mla_cache** out);
+
+/* Free the host handle only; the storage stays the caller's. NULL is ignored. */
+void mla_cache_destroy(mla_cache* cache);
+
+/* Fused cache write (method items 1 and 3): for n_frames whole latent frames
+ * starting at global frame `frame0`, per token computes
+ *   c = W^KV_down x,  k^R = RoPE3D(W^KR x, position),
+ * rounds both to cache_dtype (nearest even) and stores [c | k^R] at the
+ * token's ring slot.  x: [batch][n_frames*T][hidden]; w_dkr as above.
+ * Needs frame0 == newest+1 unless the window is empty (MLA_ERR_NOT_CONTIGUOUS),
+ * and n_frames <= capacity - resident (MLA_ERR_FULL): nothing is overwritten
+ * silently.  The new frames become resident when the call returns. */
+mla_status mla_cache_write(mla_cache* cache, const void* x, const void* w_dkr, int64_t frame0,
+                           int32_t n_frames, void* stream);
+
+/* Dense comparison write: per head k_h = RoPE3D((w_k x)_h) over all d_h dims
+ * (pairs split t/h/w as P - 2*floor(P/3), floor(P/3), floor(P/3), P = d_h/2),
+ * v_h = (w_v x)_h, rounded to cache_dtype. Same window rules. */
+mla_status mha_cache_write(mla_cache* cache, const void* x, const void* w_k, const void* w_v,
+                           int64_t frame0, int32_t n_frames, void* stream);
+
+/* Slide the window: drop the n_frames oldest resident frames (host-side
+ * bookkeeping only; launches nothing).  MLA_ERR_EVICT_RANGE if n_frames is
+ * negative or larger than the resident count. Works on both handle kinds. */
+mla_status mla_cache_evict(mla_cache* cache, int32_t n_frames);
+
+/* Read the window state. */
+mla_status mla_cache_query(const mla_cache* cache, mla_cache_info* info);
+
+/* Restore a saved window state (resume from a snapshot of the storage).
+ * Requires 0 <= oldest, newest >= oldest-1, newest-oldest+1 <= capacity. */
+mla_status mla_cache_set_state(mla_cache* cache, int64_t oldest_frame, int64_t newest_frame);
+
+/* Ring slot of token tau of frame `frame` (independent of residency), or -1 on
+ * bad arguments.  Same for every batch element. */
+int64_t mla_cache_slot(const mla_cache* cache, int64_t frame, int32_t tau);
+
+/* Device workspace mla_attend needs for Lq queries with `key_splits` key
+ * ranges (0 = the library's choice for this shape). */
+size_t mla_attend_workspace_bytes(const mla_cache* cache, int32_t Lq, int32_t key_splits);
+
+/* Absorbed latent attention (method item 2 in absorbed form) of a query chunk
+ * over every resident token of the window:
+ *   q     [batch][Lq][n_h][d_nope + d_rope], per head [q^nope | q^R], q^R not yet
+ *         rotated; query row i sits at global token q_token0 + i;
+ *   out   [batch][Lq][n_h][d_v] fp32, out_h = W^V_up,h (sum_j p_j c_j),
+ *         p = softmax_j((q^nope.W^K_up,h c_j + RoPE3D(q^R).k^R_j) / sqrt(d_nope+d_rope)).
+ * key_splits = 0 lets the library choose; > 0 forces that many key ranges
+ * (merged exactly by log-sum-exp).  workspace: device memory of at least
+ * mla_attend_workspace_bytes(cache, Lq, key_splits).  MLA_ERR_EMPTY if no frame
+ * is resident. */
+mla_status mla_attend(mla_cache* cache, const void* q, int64_t q_token0, int32_t Lq,
+                      const void* w_uk, const void* w_uv, float* out, int32_t key_splits,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace for mha_attend (rotated, pre-scaled queries). */
+size_t mha_attend_workspace_bytes(const mla_cache* cache, int32_t Lq);
+
+/* Dense comparison attention: per head, q rotated over all d_h dims,
+ * softmax(q.k / sqrt(d_h)) . v over every resident token.
+ * q [batch][Lq][n_h][d_h]; out [batch][Lq][n_h][d_h] fp32. */
+mla_status mha_attend(mla_cache* cache, const void* q, int64_t q_token0, int32_t Lq, float* out,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Profiling hook: when `start`/`stop` are hipEvent_t handles (not NULL), each
+ * later mla_attend / mha_attend on this handle records `start` on its stream
+ * right before its main attention kernel and `stop` right after it, so a
+ * caller can time that kernel alone with hipEventElapsedTime.  NULL, NULL
+ * switches it off.  The events stay owned by the caller. */
+mla_status mla_cache_set_profile_events(mla_cache* cache, void* start, void* stop);
+
+/* Human-readable name of a status code (static string). */
+const char* mla_status_str(mla_status status);
+
+/* Library version string. */
+const char* mla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H */

@@ -75,12 +75,20 @@ def round_to_f32(a):
     return np.asarray(a, dtype=np.float64).astype(np.float32).astype(np.float64)
 
 
+def round_to_f16(a):
+    """Round float64 values to IEEE binary16 (NumPy's cast: nearest even,
+    with binary16 subnormals and overflow to inf)."""
+    return np.asarray(a, dtype=np.float64).astype(np.float16).astype(np.float64)
+
+
 def round_storage(a, dtype):
-    """Round to the cache storage dtype: 'bf16', 'f32', or None (keep fp64)."""
+    """Round to the cache storage dtype: 'bf16', 'f16', 'f32', or None (keep fp64)."""
     if dtype is None:
         return np.asarray(a, dtype=np.float64)
     if dtype == "bf16":
         return round_to_bf16(a)
+    if dtype == "f16":
+        return round_to_f16(a)
     if dtype == "f32":
         return round_to_f32(a)
     raise ValueError(f"unknown storage dtype {dtype!r}")

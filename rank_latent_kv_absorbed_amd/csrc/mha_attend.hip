@@ -1,0 +1,212 @@
+// Dense per-head attention over a dense K/V window (the comparison path: in
+// the VideoMLA problem definition every cached token stores full keys and
+// values for every head).  Queries are rotated over the whole head width and
+// pre-scaled, then the shared flash-style core runs per head with K and V as
+// separate slices of the cached row, and a merge kernel normalises into fp32.
+#include "mla_attn_core.h"
+
+namespace mla {
+
+namespace {
+
+constexpr int kDenseRB = 1;
+
+// q [B][Lq][n_h][d_h] -> qrot [B][n_h * Lq_pad][d_h] bf16 (head-major rows).
+template <typename E>
+__global__ __launch_bounds__(256) void mha_qprep_bf16_kernel(MhaAttendArgs a, int lq_pad) {
+  const int P = a.d_h / 2;
+  const int64_t n = (int64_t)a.B * a.Lq * a.n_h * P;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= n) return;
+  const int p = (int)(idx % P);
+  int64_t r = idx / P;
+  const int h = (int)(r % a.n_h);
+  r /= a.n_h;
+  const int tok = (int)(r % a.Lq);
+  const int b = (int)(r / a.Lq);
+  const bf16_t* qs = (const bf16_t*)a.q + (((size_t)b * a.Lq + tok) * a.n_h + h) * a.d_h + 2 * p;
+  float x0 = (float)qs[0], x1 = (float)qs[1];
+  rope_pair(a.rope, p, token_pos(a.q_token0 + tok, a.T, a.grid_w), x0, x1);
+  E* o = (E*)a.qrot + ((size_t)b * a.n_h * lq_pad + (size_t)h * lq_pad + tok) * a.d_h + 2 * p;
+  o[0] = Elem<E>::from(x0 * a.qscale);
+  o[1] = Elem<E>::from(x1 * a.qscale);
+}
+
+// Merge key ranges and normalise: one thread per (row, 4 output dims).
+__global__ __launch_bounds__(256) void mha_merge_kernel(MhaAttendArgs a, const float* opart,
+                                                        const float* ml, int n_split, int lq_pad) {
+  const int C4 = a.d_h / 4;
+  const int64_t n = (int64_t)a.B * a.n_h * a.Lq * C4;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= n) return;
+  const int c4 = (int)(idx % C4);
+  int64_t r = idx / C4;
+  const int tok = (int)(r % a.Lq);
+  r /= a.Lq;
+  const int h = (int)(r % a.n_h);
+  const int b = (int)(r / a.n_h);
+  const int64_t R = (int64_t)a.n_h * lq_pad;
+  const int64_t row = (int64_t)h * lq_pad + tok;
+  float M = -INFINITY;
+  for (int sp = 0; sp < n_split; ++sp) M = fmaxf(M, ml[(((int64_t)sp * a.B + b) * R + row) * 2]);
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  float L = 0.0f;
+  for (int sp = 0; sp < n_split; ++sp) {
+    const int64_t prow = ((int64_t)sp * a.B + b) * R + row;
+    const float ms = ml[prow * 2];
+    if (ms == -INFINITY) continue;
+    const float wgt = exp2f(ms - M);
+    L += wgt * ml[prow * 2 + 1];
+    const f32x4 x = *reinterpret_cast<const f32x4*>(opart + prow * a.d_h + 4 * c4);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[t] += wgt * x[t];
+  }
+  const float inv = 1.0f / L;
+  f32x4 o = {acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+  *reinterpret_cast<f32x4*>(a.out + (((size_t)b * a.Lq + tok) * a.n_h + h) * a.d_h + 4 * c4) = o;
+}
+
+// fp32 dense path (small shapes): one block per (token, head), exact two-pass softmax.
+__global__ __launch_bounds__(256) void mha_attend_f32_kernel(MhaAttendArgs a) {
+  extern __shared__ float sm[];
+  float* qr = sm;            // [d_h]
+  float* part = qr + a.d_h;  // [256]
+  float* pk = part + 256;    // [256]
+  float* acc = pk + 256;     // [d_h]
+  const int tid = threadIdx.x;
+  const int row = blockIdx.x, b = blockIdx.y;
+  const int tok = row / a.n_h, h = row % a.n_h;
+  const int stride = 2 * a.n_h * a.d_h;
+  const float* q = (const float*)a.q + (((size_t)b * a.Lq + tok) * a.n_h + h) * a.d_h;
+  const float* ring = (const float*)a.ring + (size_t)b * a.ring_rows * stride;
+  for (int p = tid; p < a.d_h / 2; p += 256) {
+    float x0 = q[2 * p], x1 = q[2 * p + 1];
+    rope_pair(a.rope, p, token_pos(a.q_token0 + tok, a.T, a.grid_w), x0, x1);
+    qr[2 * p] = x0 * a.qscale;
+    qr[2 * p + 1] = x1 * a.qscale;
+  }
+  for (int d = tid; d < a.d_h; d += 256) acc[d] = 0.0f;
+  __syncthreads();
+  auto krow = [&](int j) {
+    int64_t slot = a.key_slot0 + j;
+    if (slot >= a.ring_rows) slot -= a.ring_rows;
+    return ring + slot * stride + (size_t)h * a.d_h;
+  };
+  auto score = [&](int j) {
+    const float* k = krow(j);
+    float s = 0.0f;
+    for (int d = 0; d < a.d_h; ++d) s = fmaf(qr[d], k[d], s);
+    return s;
+  };
+  float mx = -INFINITY;
+  for (int j = tid; j < a.Lk; j += 256) mx = fmaxf(mx, score(j));
+  part[tid] = mx;
+  __syncthreads();
+  for (int st = 128; st > 0; st >>= 1) {
+    if (tid < st) part[tid] = fmaxf(part[tid], part[tid + st]);
+    __syncthreads();
+  }
+  const float M = part[0];
+  __syncthreads();
+  float lacc = 0.0f;
+  for (int j0 = 0; j0 < a.Lk; j0 += 256) {
+    const int j = j0 + tid;
+    float p = 0.0f;
+    if (j < a.Lk) p = exp2f(score(j) - M);
+    pk[tid] = p;
+    lacc += p;
+    __syncthreads();
+    const int n = min(256, a.Lk - j0);
+    for (int d = tid; d < a.d_h; d += 256) {
+      float s = acc[d];
+      for (int jj = 0; jj < n; ++jj) s = fmaf(pk[jj], krow(j0 + jj)[a.n_h * a.d_h + d], s);
+      acc[d] = s;
+    }
+    __syncthreads();
+  }
+  part[tid] = lacc;
+  __syncthreads();
+  for (int st = 128; st > 0; st >>= 1) {
+    if (tid < st) part[tid] += part[tid + st];
+    __syncthreads();
+  }
+  const float inv = 1.0f / part[0];
+  float* out = a.out + (((size_t)b * a.Lq + tok) * a.n_h + h) * a.d_h;
+  for (int d = tid; d < a.d_h; d += 256) out[d] = acc[d] * inv;
+}
+
+}  // namespace
+
+int mha_lq_pad(int Lq) { return (Lq + core_block_rows<kDenseRB>() - 1) / core_block_rows<kDenseRB>() * core_block_rows<kDenseRB>(); }
+
+bool mha_attend_bf16_supported(int d_h) { return d_h == 128; }
+
+namespace {
+template <typename E>
+hipError_t launch_mha_typed(const MhaAttendArgs& a, float* opart, float* ml, int n_split,
+                            int keys_per_split, hipStream_t s) {
+  const int lq_pad = mha_lq_pad(a.Lq);
+  {
+    const int64_t n = (int64_t)a.B * a.Lq * a.n_h * (a.d_h / 2);
+    hipLaunchKernelGGL(mha_qprep_bf16_kernel<E>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       a, lq_pad);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
+    AttnCore c;
+    c.qrows = a.qrot;
+    c.ring = a.ring;
+    c.opart = opart;
+    c.ml = ml;
+    c.ring_rows = a.ring_rows;
+    c.ring_stride = 2 * a.n_h * a.d_h;
+    c.k_off = 0;
+    c.v_off = a.n_h * a.d_h;
+    c.head_stride = a.d_h;
+    c.R = a.n_h * lq_pad;
+    c.rows_per_head = lq_pad;
+    c.valid_per_head = a.Lq;
+    c.B = a.B;
+    c.Lk = a.Lk;
+    c.n_split = n_split;
+    c.keys_per_split = keys_per_split;
+    c.key_slot0 = a.key_slot0;
+    dim3 grid((unsigned)(c.R / core_block_rows<kDenseRB>()), (unsigned)n_split, (unsigned)a.B);
+    if (a.ev_start != nullptr) {
+      hipError_t e = hipEventRecord(a.ev_start, s);
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((attn_core_kernel<E, 128, 128, kDenseRB, false>), grid, dim3(256), 0, s, c);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (a.ev_stop != nullptr) {
+      e = hipEventRecord(a.ev_stop, s);
+      if (e != hipSuccess) return e;
+    }
+  }
+  {
+    const int64_t n = (int64_t)a.B * a.n_h * a.Lq * (a.d_h / 4);
+    hipLaunchKernelGGL(mha_merge_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a,
+                       (const float*)opart, (const float*)ml, n_split, lq_pad);
+    return hipGetLastError();
+  }
+}
+}  // namespace
+
+// The host carves the workspace into rotated queries (a.qrot), partial value
+// sums (opart) and per-row max/sum (ml).
+hipError_t launch_mha_attend_bf16_ws(const MhaAttendArgs& a, float* opart, float* ml, int n_split,
+                                     int keys_per_split, hipStream_t s) {
+  return a.cache_type == 2 ? launch_mha_typed<f16_t>(a, opart, ml, n_split, keys_per_split, s)
+                           : launch_mha_typed<bf16_t>(a, opart, ml, n_split, keys_per_split, s);
+}
+
+hipError_t launch_mha_attend_f32(const MhaAttendArgs& a, hipStream_t s) {
+  const size_t lds = (size_t)(2 * a.d_h + 512) * sizeof(float);
+  hipLaunchKernelGGL(mha_attend_f32_kernel, dim3((unsigned)(a.Lq * a.n_h), (unsigned)a.B),
+                     dim3(256), lds, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace mla

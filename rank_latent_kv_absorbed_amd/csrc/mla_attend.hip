@@ -1,0 +1,328 @@
+// Absorbed latent attention for gfx950 (VideoMLA technical summary, method
+// item 2, computed in absorbed form).
+//
+// Three kernels run back to back on the caller's stream:
+//  1. qprep:    q_lat,h = W^K_up,h^T q^nope_h and q^R rotated at the query's
+//               position, both scaled by log2(e)/sqrt(d_nope + d_rope), written
+//               as one bf16 row [q_lat | q^R_rot] per (token, head) pair.
+//  2. attend:   the shared flash-style core (mla_attn_core.h).  Rows are
+//               (token, head) pairs; every row scores against the same cached
+//               rows [c | k^R], so a key tile staged once in LDS serves all heads
+//               and tokens of a block, and V = c is read from the same tile.
+//               Each block covers one key range and writes un-normalised
+//               partials (O_lat, max, sum).
+//  3. epilogue: merges the key ranges by log-sum-exp, normalises, and applies
+//               W^V_up,h with bf16 MFMA on a hi/lo split of O_lat (keeps fp32
+//               accuracy), writing fp32 output.
+#include "mla_attn_core.h"
+
+namespace mla {
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// 1. query prologue
+// ---------------------------------------------------------------------------
+template <typename E, int DC>
+__global__ __launch_bounds__(256) void qprep_bf16_kernel(AttendArgs a) {
+  constexpr int NT = DC / 32;
+  extern __shared__ bf16_t wt[];  // W^K_up,h transposed: [DC][d_nope + 8]
+  const int wts = a.d_nope + 8;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, l = tid & 63, lo = l & 31, hi = l >> 5;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int d_qk = a.d_nope + a.d_rope;
+  const int width = DC + a.d_rope;
+  const int R = a.Lq * a.n_h;
+
+  const bf16_t* wuk = (const bf16_t*)a.w_uk + (size_t)h * a.d_nope * DC;
+  for (int c = tid; c < a.d_nope * (DC / 8); c += 256) {
+    const int n = c / (DC / 8), i0 = (c % (DC / 8)) * 8;
+    bf16x8 v = ld_bf16x8(wuk + (size_t)n * DC + i0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) wt[(i0 + j) * wts + n] = v[j];
+  }
+  __syncthreads();
+
+  const int tok = blockIdx.x * 128 + w * 32 + lo;
+  const bool valid = tok < a.Lq;
+  const bf16_t* qrow =
+      (const bf16_t*)a.q + (((size_t)b * a.Lq + (valid ? tok : 0)) * a.n_h + h) * d_qk;
+  f32x16 acc[NT];
+#pragma unroll
+  for (int it = 0; it < NT; ++it)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[it][r] = 0.0f;
+  for (int k0 = 0; k0 < a.d_nope; k0 += 16) {
+    bf16x8 bq = valid ? ld_bf16x8(qrow + k0 + 8 * hi) : zero_bf16x8();
+#pragma unroll
+    for (int it = 0; it < NT; ++it)
+      acc[it] = mfma32(ld_bf16x8(wt + (it * 32 + lo) * wts + k0 + 8 * hi), bq, acc[it]);
+  }
+  E* out = (E*)a.qcat + ((size_t)b * R + (size_t)tok * a.n_h + h) * width;
+  if (valid) {
+#pragma unroll
+    for (int it = 0; it < NT; ++it)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        typename Elem<E>::v4 o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[j] = Elem<E>::from(acc[it][4 * g + j] * a.qscale);
+        *reinterpret_cast<typename Elem<E>::v4*>(out + it * 32 + 8 * g + 4 * hi) = o;
+      }
+  }
+  // rotary part: lanes walk (token, pair) of this wave's 32 tokens
+  const int P = a.d_rope / 2;
+  for (int e = l; e < 32 * P; e += 64) {
+    const int tt = blockIdx.x * 128 + w * 32 + e / P;
+    const int p = e % P;
+    if (tt >= a.Lq) continue;
+    const bf16_t* qr =
+        (const bf16_t*)a.q + (((size_t)b * a.Lq + tt) * a.n_h + h) * d_qk + a.d_nope + 2 * p;
+    float x0 = (float)qr[0], x1 = (float)qr[1];
+    rope_pair(a.rope, p, token_pos(a.q_token0 + tt, a.T, a.grid_w), x0, x1);
+    E* o = (E*)a.qcat + ((size_t)b * R + (size_t)tt * a.n_h + h) * width + DC + 2 * p;
+    o[0] = Elem<E>::from(x0 * a.qscale);
+    o[1] = Elem<E>::from(x1 * a.qscale);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 3. merge of key ranges + W^V_up epilogue
+// ---------------------------------------------------------------------------
+template <int DC>
+__global__ __launch_bounds__(64) void epilogue_bf16_kernel(AttendArgs a) {
+  constexpr int NKS = DC / 16;
+  const int l = threadIdx.x, lo = l & 31, hi = l >> 5;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int tok = blockIdx.x * 32 + lo;
+  const bool valid = tok < a.Lq;
+  const int R = a.Lq * a.n_h;
+  const size_t row = (size_t)(valid ? tok : 0) * a.n_h + h;
+
+  float M = -INFINITY;
+  for (int sp = 0; sp < a.n_split; ++sp) M = fmaxf(M, a.ml[(((size_t)sp * a.B + b) * R + row) * 2]);
+  float v[NKS][8];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) v[ks][t] = 0.0f;
+  float L = 0.0f;
+  for (int sp = 0; sp < a.n_split; ++sp) {
+    const size_t prow = ((size_t)sp * a.B + b) * R + row;
+    const float ms = a.ml[prow * 2];
+    if (ms == -INFINITY) continue;
+    const float wgt = exp2f(ms - M);
+    L += wgt * a.ml[prow * 2 + 1];
+    const float* op = a.opart + prow * DC + 8 * hi;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const f32x4 x0 = *reinterpret_cast<const f32x4*>(op + 16 * ks);
+      const f32x4 x1 = *reinterpret_cast<const f32x4*>(op + 16 * ks + 4);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        v[ks][t] += wgt * x0[t];
+        v[ks][4 + t] += wgt * x1[t];
+      }
+    }
+  }
+  const float inv = valid ? 1.0f / L : 0.0f;
+  bf16x8 vh[NKS], vl[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const float x = v[ks][t] * inv;
+      const bf16_t xh = to_bf16(x);
+      vh[ks][t] = xh;
+      vl[ks][t] = to_bf16(x - (float)xh);
+    }
+
+  const bf16_t* wuv = (const bf16_t*)a.w_uv + (size_t)h * a.d_v * DC + 8 * hi;
+  float* out = a.out + (((size_t)b * a.Lq + tok) * a.n_h + h) * a.d_v;
+  for (int vt = 0; vt < a.d_v / 32; ++vt) {
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+    const bf16_t* wr = wuv + (size_t)(vt * 32 + lo) * DC;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const bf16x8 wa = ld_bf16x8(wr + 16 * ks);
+      acc = mfma32(wa, vh[ks], acc);
+      acc = mfma32(wa, vl[ks], acc);
+    }
+    if (valid) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4 o4 = {acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
+        *reinterpret_cast<f32x4*>(out + vt * 32 + 8 * g + 4 * hi) = o4;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 path (small shapes): one block per (token, head) row, exact two-pass
+// softmax in the absorbed form, plain fp32 arithmetic.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void attend_f32_kernel(AttendArgs a) {
+  extern __shared__ float sm[];
+  const int d_qk = a.d_nope + a.d_rope;
+  const int width = a.d_c + a.d_rope;
+  float* qlat = sm;                  // [d_c + d_rope]
+  float* part = qlat + width;        // [256] reduction scratch
+  float* pk = part + 256;            // [256] probabilities of one key chunk
+  float* olat = pk + 256;            // [d_c]
+  const int tid = threadIdx.x;
+  const int row = blockIdx.x, b = blockIdx.y;
+  const int tok = row / a.n_h, h = row % a.n_h;
+  const float* q = (const float*)a.q + (((size_t)b * a.Lq + tok) * a.n_h + h) * d_qk;
+  const float* wuk = (const float*)a.w_uk + (size_t)h * a.d_nope * a.d_c;
+  const float* ring = (const float*)a.ring + (size_t)b * a.ring_rows * width;
+  const float scale = a.qscale;  // log2(e)/sqrt(d_qk)
+
+  for (int i = tid; i < a.d_c; i += 256) {
+    float acc = 0.0f;
+    for (int n = 0; n < a.d_nope; ++n) acc = fmaf(q[n], wuk[(size_t)n * a.d_c + i], acc);
+    qlat[i] = acc * scale;
+    olat[i] = 0.0f;
+  }
+  for (int p = tid; p < a.d_rope / 2; p += 256) {
+    float x0 = q[a.d_nope + 2 * p], x1 = q[a.d_nope + 2 * p + 1];
+    rope_pair(a.rope, p, token_pos(a.q_token0 + tok, a.T, a.grid_w), x0, x1);
+    qlat[a.d_c + 2 * p] = x0 * scale;
+    qlat[a.d_c + 2 * p + 1] = x1 * scale;
+  }
+  __syncthreads();
+  auto key_row = [&](int j) {
+    int64_t slot = a.key_slot0 + j;
+    if (slot >= a.ring_rows) slot -= a.ring_rows;
+    return ring + slot * width;
+  };
+  auto score = [&](int j) {
+    const float* k = key_row(j);
+    float s = 0.0f;
+    for (int i = 0; i < width; ++i) s = fmaf(qlat[i], k[i], s);
+    return s;
+  };
+  float mx = -INFINITY;
+  for (int j = tid; j < a.Lk; j += 256) mx = fmaxf(mx, score(j));
+  part[tid] = mx;
+  __syncthreads();
+  for (int st = 128; st > 0; st >>= 1) {
+    if (tid < st) part[tid] = fmaxf(part[tid], part[tid + st]);
+    __syncthreads();
+  }
+  const float M = part[0];
+  __syncthreads();
+  float lacc = 0.0f;
+  for (int j0 = 0; j0 < a.Lk; j0 += 256) {
+    const int j = j0 + tid;
+    float p = 0.0f;
+    if (j < a.Lk) p = exp2f(score(j) - M);
+    pk[tid] = p;
+    lacc += p;
+    __syncthreads();
+    const int n = min(256, a.Lk - j0);
+    for (int i = tid; i < a.d_c; i += 256) {
+      float acc = olat[i];
+      for (int jj = 0; jj < n; ++jj) acc = fmaf(pk[jj], key_row(j0 + jj)[i], acc);
+      olat[i] = acc;
+    }
+    __syncthreads();
+  }
+  part[tid] = lacc;
+  __syncthreads();
+  for (int st = 128; st > 0; st >>= 1) {
+    if (tid < st) part[tid] += part[tid + st];
+    __syncthreads();
+  }
+  const float inv = 1.0f / part[0];
+  const float* wuv = (const float*)a.w_uv + (size_t)h * a.d_v * a.d_c;
+  float* out = a.out + (((size_t)b * a.Lq + tok) * a.n_h + h) * a.d_v;
+  for (int vv = tid; vv < a.d_v; vv += 256) {
+    float acc = 0.0f;
+    for (int i = 0; i < a.d_c; ++i) acc = fmaf(wuv[(size_t)vv * a.d_c + i], olat[i], acc);
+    out[vv] = acc * inv;
+  }
+}
+
+template <typename E, int DC>
+hipError_t launch_dc(const AttendArgs& a, hipStream_t s) {
+  {
+    const size_t lds = (size_t)DC * (a.d_nope + 8) * sizeof(bf16_t);
+    dim3 grid((unsigned)((a.Lq + 127) / 128), (unsigned)a.n_h, (unsigned)a.B);
+    hipLaunchKernelGGL((qprep_bf16_kernel<E, DC>), grid, dim3(256), lds, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
+    constexpr int RB = 1;
+    AttnCore c;
+    c.qrows = a.qcat;
+    c.ring = a.ring;
+    c.opart = a.opart;
+    c.ml = a.ml;
+    c.ring_rows = a.ring_rows;
+    c.ring_stride = DC + 32;
+    c.k_off = 0;
+    c.v_off = 0;
+    c.head_stride = 0;
+    c.R = a.Lq * a.n_h;
+    c.rows_per_head = c.R;
+    c.valid_per_head = c.R;
+    c.B = a.B;
+    c.Lk = a.Lk;
+    c.n_split = a.n_split;
+    c.keys_per_split = a.keys_per_split;
+    c.key_slot0 = a.key_slot0;
+    dim3 grid((unsigned)((c.R + core_block_rows<RB>() - 1) / core_block_rows<RB>()),
+              (unsigned)a.n_split, (unsigned)a.B);
+    if (a.ev_start != nullptr) {
+      hipError_t e = hipEventRecord(a.ev_start, s);
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((attn_core_kernel<E, DC + 32, DC, RB, true>), grid, dim3(256), 0, s, c);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (a.ev_stop != nullptr) {
+      e = hipEventRecord(a.ev_stop, s);
+      if (e != hipSuccess) return e;
+    }
+  }
+  {
+    dim3 grid((unsigned)((a.Lq + 31) / 32), (unsigned)a.n_h, (unsigned)a.B);
+    hipLaunchKernelGGL(epilogue_bf16_kernel<DC>, grid, dim3(64), 0, s, a);
+    return hipGetLastError();
+  }
+}
+
+}  // namespace
+
+bool attend_bf16_supported(int d_c, int d_rope, int d_nope, int d_v) {
+  return (d_c == 64 || d_c == 128 || d_c == 192) && d_rope == 32 && d_nope > 0 &&
+         d_nope % 16 == 0 && d_v > 0 && d_v % 32 == 0;
+}
+
+template <typename E>
+hipError_t launch_typed(const AttendArgs& a, hipStream_t s) {
+  switch (a.d_c) {
+    case 64: return launch_dc<E, 64>(a, s);
+    case 128: return launch_dc<E, 128>(a, s);
+    case 192: return launch_dc<E, 192>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_attend_bf16(const AttendArgs& a, hipStream_t s) {
+  return a.cache_type == 2 ? launch_typed<f16_t>(a, s) : launch_typed<bf16_t>(a, s);
+}
+
+hipError_t launch_attend_f32(const AttendArgs& a, hipStream_t s) {
+  const size_t lds = (size_t)(a.d_c + a.d_rope + 512 + a.d_c) * sizeof(float);
+  dim3 grid((unsigned)(a.Lq * a.n_h), (unsigned)a.B);
+  hipLaunchKernelGGL(attend_f32_kernel, grid, dim3(256), lds, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,120 @@
+// Device-side helpers for the gfx950 kernels: vector types, the bf16 MFMA
+// wrapper and its lane layout, RNE conversion, 3D-RoPE positions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mla_launch.h"
+
+namespace mla {
+
+typedef __bf16 bf16_t;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16_t;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// v_mfma_f32_32x32x16_bf16, D = A * B + C, lane l of a 64-wide wave holds
+//   A[m = l % 32][k = 8 * (l / 32) + t]      (t = 0..7)
+//   B[k = 8 * (l / 32) + t][n = l % 32]
+//   D[m = 8 * (r / 4) + 4 * (l / 32) + r % 4][n = l % 32]   (r = 0..15)
+// (checked on gfx950 hardware against a host matmul).
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Row of the 32x32 accumulator held in register r by lane half `hi`.
+__device__ __forceinline__ int acc_row(int r, int hi) { return 8 * (r >> 2) + 4 * hi + (r & 3); }
+
+__device__ __forceinline__ bf16x8 ld_bf16x8(const bf16_t* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+__device__ __forceinline__ void st_bf16x8(bf16_t* p, bf16x8 v) { *reinterpret_cast<bf16x8*>(p) = v; }
+__device__ __forceinline__ void st_bf16x4(bf16_t* p, bf16x4 v) { *reinterpret_cast<bf16x4*>(p) = v; }
+
+__device__ __forceinline__ bf16x8 zero_bf16x8() {
+  bf16x8 z;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) z[t] = (bf16_t)0.0f;
+  return z;
+}
+
+// float -> bf16, round to nearest even (the compiler's fptrunc lowers to the
+// hardware RNE conversion on gfx950).
+__device__ __forceinline__ bf16_t to_bf16(float f) { return (bf16_t)f; }
+
+// Element types of the cache, prepared queries and probabilities.  Both are
+// 2-byte types fed to 32x32x16 MFMA with fp32 accumulation; the operand lane
+// layout is the same for both.
+template <typename E>
+struct Elem;
+
+template <>
+struct Elem<bf16_t> {
+  typedef bf16x8 v8;
+  typedef bf16x4 v4;
+  static __device__ __forceinline__ f32x16 mfma(v8 a, v8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ bf16_t from(float f) { return (bf16_t)f; }
+};
+
+template <>
+struct Elem<f16_t> {
+  typedef f16x8 v8;
+  typedef f16x4 v4;
+  static __device__ __forceinline__ f32x16 mfma(v8 a, v8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f16_t from(float f) { return (f16_t)f; }
+};
+
+template <typename E>
+__device__ __forceinline__ typename Elem<E>::v8 ld8(const E* p) {
+  return *reinterpret_cast<const typename Elem<E>::v8*>(p);
+}
+template <typename E>
+__device__ __forceinline__ typename Elem<E>::v8 zero8() {
+  typename Elem<E>::v8 z;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) z[t] = (E)0.0f;
+  return z;
+}
+
+// Position (frame, row, column) of global token g.
+struct TokPos {
+  int64_t f;
+  int y, x;
+};
+__device__ __forceinline__ TokPos token_pos(int64_t g, int T, int grid_w) {
+  TokPos p;
+  p.f = g / T;
+  int tau = (int)(g - p.f * T);
+  p.y = tau / grid_w;
+  p.x = tau - p.y * grid_w;
+  return p;
+}
+
+__device__ __forceinline__ double pos_axis(const TokPos& p, int axis) {
+  return axis == 0 ? (double)p.f : (axis == 1 ? (double)p.y : (double)p.x);
+}
+
+// Rotate the pair (a, b) of rotary pair `pair` at position p; the angle is
+// formed in double so that large frame indices keep full accuracy.
+__device__ __forceinline__ void rope_pair(const RopeTable& rt, int pair, const TokPos& p, float& a,
+                                          float& b) {
+  double ang = pos_axis(p, rt.axis[pair]) * rt.inv_freq[pair];
+  double s, c;
+  sincos(ang, &s, &c);
+  double ra = (double)a * c - (double)b * s;
+  double rb = (double)a * s + (double)b * c;
+  a = (float)ra;
+  b = (float)rb;
+}
+
+}  // namespace mla

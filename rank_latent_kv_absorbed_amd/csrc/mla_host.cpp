@@ -1,0 +1,465 @@
+// Host side of libmla: argument validation, sliding-window bookkeeping,
+// workspace carving and kernel launches.  Implements include/mla.h.
+//
+// Window semantics (VideoMLA abstract: a fixed-size sliding-window KV cache;
+// technical summary, problem definition: a window of latent frames): whole
+// frames enter at the newest end and leave from the oldest end; token tau of
+// frame f always lives at ring slot (f mod W)*T + tau.  Every check runs
+// before anything is enqueued, so a failed call changes nothing.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <new>
+
+#include "../../include/mla.h"
+#include "mla_launch.h"
+
+struct mla_cache {
+  mla_layer_config cfg;
+  bool dense;
+  void* storage;
+  size_t storage_bytes;
+  int64_t oldest;  // first resident frame
+  int64_t newest;  // last resident frame; empty when newest < oldest
+  hipEvent_t prof_start;
+  hipEvent_t prof_stop;
+};
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t elem_size(int32_t dtype) {
+  return (dtype == MLA_BF16 || dtype == MLA_F16) ? 2 : (dtype == MLA_F32 ? 4 : 0);
+}
+
+// Input / storage combinations with kernels: fp32 everywhere, or bf16 inputs
+// with a 2-byte (bf16 or fp16) ring.
+bool valid_types(const mla_layer_config* c) {
+  if (c->dtype == MLA_F32) return c->cache_dtype == MLA_F32;
+  if (c->dtype == MLA_BF16) return c->cache_dtype == MLA_BF16 || c->cache_dtype == MLA_F16;
+  return false;
+}
+
+bool aligned16(const void* p) { return p != nullptr && ((uintptr_t)p & 15u) == 0; }
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int64_t tokens_per_frame(const mla_layer_config& c) { return (int64_t)c.grid_h * c.grid_w; }
+
+int64_t dense_width(const mla_layer_config& c) {
+  return 2LL * c.n_heads * (c.d_nope + c.d_rope);
+}
+
+bool valid_config(const mla_layer_config* c, bool dense) {
+  if (c == nullptr) return false;
+  if (c->hidden <= 0 || c->n_heads <= 0 || c->d_nope < 0 || c->d_rope < 0 || c->d_v <= 0 ||
+      c->d_c <= 0 || c->grid_h <= 0 || c->grid_w <= 0 || c->window_frames <= 0 || c->batch <= 0)
+    return false;
+  if (c->d_rope % 2 != 0 || c->d_nope + c->d_rope <= 0) return false;
+  if (c->rope_pairs_t < 0 || c->rope_pairs_h < 0 || c->rope_pairs_w < 0) return false;
+  if (!dense && c->rope_pairs_t + c->rope_pairs_h + c->rope_pairs_w != c->d_rope / 2) return false;
+  if (dense && (c->d_nope + c->d_rope) % 2 != 0) return false;
+  if (!(c->rope_base > 0.0f) || !isfinite(c->rope_base)) return false;
+  if (!valid_types(c)) return false;
+  if (c->d_rope / 2 > mla::kMaxRopePairs) return false;
+  if (dense && (c->d_nope + c->d_rope) / 2 > mla::kMaxRopePairs) return false;
+  // ring rows and key counts are kept in 32-bit integers inside the kernels
+  const int64_t ring_rows = (int64_t)c->window_frames * tokens_per_frame(*c);
+  if (ring_rows >= (1LL << 30)) return false;
+  return true;
+}
+
+mla::RopeTable make_rope(int pt, int ph, int pw, double base) {
+  mla::RopeTable t;
+  memset(&t, 0, sizeof(t));
+  const int counts[3] = {pt, ph, pw};
+  int p = 0;
+  for (int axis = 0; axis < 3; ++axis)
+    for (int i = 0; i < counts[axis]; ++i, ++p) {
+      t.axis[p] = axis;
+      t.inv_freq[p] = pow(base, -(double)i / (double)counts[axis]);
+    }
+  t.n_pairs = p;
+  return t;
+}
+
+mla::RopeTable latent_rope(const mla_layer_config& c) {
+  return make_rope(c.rope_pairs_t, c.rope_pairs_h, c.rope_pairs_w, (double)c.rope_base);
+}
+
+mla::RopeTable dense_rope(const mla_layer_config& c) {
+  const int P = (c.d_nope + c.d_rope) / 2;
+  return make_rope(P - 2 * (P / 3), P / 3, P / 3, (double)c.rope_base);
+}
+
+int64_t n_resident(const mla_cache* h) { return h->newest - h->oldest + 1; }
+
+mla_status check_write(const mla_cache* h, int64_t frame0, int32_t n_frames) {
+  if (n_frames <= 0 || frame0 < 0) return MLA_ERR_INVALID_ARG;
+  const int64_t res = n_resident(h);
+  if (res > 0 && frame0 != h->newest + 1) return MLA_ERR_NOT_CONTIGUOUS;
+  if (res + n_frames > h->cfg.window_frames) return MLA_ERR_FULL;
+  return MLA_OK;
+}
+
+void commit_write(mla_cache* h, int64_t frame0, int32_t n_frames) {
+  if (n_resident(h) <= 0) h->oldest = frame0;
+  h->newest = frame0 + n_frames - 1;
+}
+
+// Key ranges per call: one range when the row blocks already cover the chip;
+// otherwise enough ranges for about two blocks per compute unit, keeping at
+// least four key tiles per range.
+int choose_splits(int64_t row_blocks, int64_t Lk) {
+  constexpr int64_t kCUs = 256;
+  if (row_blocks >= kCUs / 2) return 1;
+  int64_t s = (2 * kCUs + row_blocks - 1) / row_blocks;
+  const int64_t cap = Lk / (4 * mla::kKeyTile);
+  if (s > cap) s = cap;
+  return (int)(s < 1 ? 1 : s);
+}
+
+struct LatentLayout {
+  int splits;
+  int keys_per_split;
+  size_t qcat_off, opart_off, ml_off, total;
+};
+
+LatentLayout latent_layout(const mla_cache* h, int32_t Lq, int32_t key_splits) {
+  const mla_layer_config& c = h->cfg;
+  const int64_t R = (int64_t)Lq * c.n_heads;
+  const int64_t Lk = n_resident(h) > 0 ? n_resident(h) * tokens_per_frame(c)
+                                       : (int64_t)c.window_frames * tokens_per_frame(c);
+  LatentLayout L;
+  const int64_t row_blocks = ((R + 255) / 256) * c.batch;
+  L.splits = key_splits > 0 ? key_splits : choose_splits(row_blocks, Lk);
+  int64_t kps = (Lk + L.splits - 1) / L.splits;
+  kps = (kps + mla::kKeyTile - 1) / mla::kKeyTile * mla::kKeyTile;
+  L.keys_per_split = (int)kps;
+  const size_t width = (size_t)(c.d_c + c.d_rope);
+  L.qcat_off = 0;
+  L.opart_off = round_up((size_t)c.batch * R * width * 2, kAlign);
+  L.ml_off = L.opart_off + round_up((size_t)L.splits * c.batch * R * c.d_c * 4, kAlign);
+  L.total = L.ml_off + round_up((size_t)L.splits * c.batch * R * 2 * 4, kAlign);
+  return L;
+}
+
+struct DenseLayout {
+  int splits;
+  int keys_per_split;
+  int lq_pad;
+  size_t qrot_off, opart_off, ml_off, total;
+};
+
+DenseLayout dense_layout(const mla_cache* h, int32_t Lq) {
+  const mla_layer_config& c = h->cfg;
+  const int d_h = c.d_nope + c.d_rope;
+  DenseLayout L;
+  L.lq_pad = mla::mha_lq_pad(Lq);
+  const int64_t R = (int64_t)c.n_heads * L.lq_pad;
+  const int64_t Lk = n_resident(h) > 0 ? n_resident(h) * tokens_per_frame(c)
+                                       : (int64_t)c.window_frames * tokens_per_frame(c);
+  L.splits = choose_splits((R / 256) * c.batch, Lk);
+  int64_t kps = (Lk + L.splits - 1) / L.splits;
+  kps = (kps + mla::kKeyTile - 1) / mla::kKeyTile * mla::kKeyTile;
+  L.keys_per_split = (int)kps;
+  L.qrot_off = 0;
+  L.opart_off = round_up((size_t)c.batch * R * d_h * 2, kAlign);
+  L.ml_off = L.opart_off + round_up((size_t)L.splits * c.batch * R * d_h * 4, kAlign);
+  L.total = L.ml_off + round_up((size_t)L.splits * c.batch * R * 2 * 4, kAlign);
+  return L;
+}
+
+mla_status launch_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
+
+mla_status create(const mla_layer_config* cfg, void* storage, size_t storage_bytes, bool dense,
+                  mla_cache** out) {
+  if (out == nullptr) return MLA_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (!valid_config(cfg, dense) || !aligned16(storage)) return MLA_ERR_INVALID_ARG;
+  const size_t need = dense ? mha_cache_bytes(cfg) : mla_cache_bytes(cfg);
+  if (storage_bytes < need) return MLA_ERR_STORAGE_TOO_SMALL;
+  mla_cache* h = new (std::nothrow) mla_cache;
+  if (h == nullptr) return MLA_ERR_INVALID_ARG;
+  h->cfg = *cfg;
+  h->dense = dense;
+  h->storage = storage;
+  h->storage_bytes = storage_bytes;
+  h->oldest = 0;
+  h->newest = -1;
+  h->prof_start = nullptr;
+  h->prof_stop = nullptr;
+  *out = h;
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mla_cache_bytes(const mla_layer_config* cfg) {
+  if (!valid_config(cfg, false)) return 0;
+  return (size_t)cfg->batch * cfg->window_frames * tokens_per_frame(*cfg) *
+         (cfg->d_c + cfg->d_rope) * elem_size(cfg->cache_dtype);
+}
+
+size_t mha_cache_bytes(const mla_layer_config* cfg) {
+  if (!valid_config(cfg, true)) return 0;
+  return (size_t)cfg->batch * cfg->window_frames * tokens_per_frame(*cfg) * dense_width(*cfg) *
+         elem_size(cfg->cache_dtype);
+}
+
+mla_status mla_cache_create(const mla_layer_config* cfg, void* storage, size_t storage_bytes,
+                            mla_cache** out) {
+  return create(cfg, storage, storage_bytes, false, out);
+}
+
+mla_status mha_cache_create(const mla_layer_config* cfg, void* storage, size_t storage_bytes,
+                            mla_cache** out) {
+  return create(cfg, storage, storage_bytes, true, out);
+}
+
+void mla_cache_destroy(mla_cache* cache) { delete cache; }
+
+mla_status mla_cache_write(mla_cache* h, const void* x, const void* w_dkr, int64_t frame0,
+                           int32_t n_frames, void* stream) {
+  if (h == nullptr || !aligned16(x) || !aligned16(w_dkr)) return MLA_ERR_INVALID_ARG;
+  if (h->dense) return MLA_ERR_WRONG_KIND;
+  mla_status st = check_write(h, frame0, n_frames);
+  if (st != MLA_OK) return st;
+  const mla_layer_config& c = h->cfg;
+  const int width = c.d_c + c.d_rope;
+  if (c.dtype == MLA_BF16 && !mla::cache_write_bf16_supported(width, c.hidden))
+    return MLA_ERR_UNSUPPORTED;
+  mla::CacheWriteArgs a;
+  a.x = x;
+  a.w = w_dkr;
+  a.w2 = w_dkr;
+  a.w_split = width;
+  a.ring = h->storage;
+  a.tokens_per_batch = (int)(n_frames * tokens_per_frame(c));
+  a.M = (int64_t)c.batch * a.tokens_per_batch;
+  a.hidden = c.hidden;
+  a.width = width;
+  a.rot_begin = c.d_c;
+  a.rot_end = width;
+  a.rot_group = c.d_rope > 0 ? c.d_rope : 1;
+  a.T = (int)tokens_per_frame(c);
+  a.grid_w = c.grid_w;
+  a.W = c.window_frames;
+  a.ring_rows = (int64_t)c.window_frames * a.T;
+  a.frame0 = frame0;
+  a.out_type = c.cache_dtype;
+  a.rope = latent_rope(c);
+  hipStream_t s = (hipStream_t)stream;
+  st = launch_status(c.dtype == MLA_BF16 ? mla::launch_cache_write_bf16(a, s)
+                                         : mla::launch_cache_write_f32(a, s));
+  if (st == MLA_OK) commit_write(h, frame0, n_frames);
+  return st;
+}
+
+mla_status mha_cache_write(mla_cache* h, const void* x, const void* w_k, const void* w_v,
+                           int64_t frame0, int32_t n_frames, void* stream) {
+  if (h == nullptr || !aligned16(x) || !aligned16(w_k) || !aligned16(w_v))
+    return MLA_ERR_INVALID_ARG;
+  if (!h->dense) return MLA_ERR_WRONG_KIND;
+  mla_status st = check_write(h, frame0, n_frames);
+  if (st != MLA_OK) return st;
+  const mla_layer_config& c = h->cfg;
+  const int d_h = c.d_nope + c.d_rope;
+  const int width = (int)dense_width(c);
+  if (c.dtype == MLA_BF16 && !mla::cache_write_bf16_supported(width, c.hidden))
+    return MLA_ERR_UNSUPPORTED;
+  mla::CacheWriteArgs a;
+  a.x = x;
+  a.w = w_k;
+  a.w2 = w_v;
+  a.w_split = c.n_heads * d_h;
+  a.ring = h->storage;
+  a.tokens_per_batch = (int)(n_frames * tokens_per_frame(c));
+  a.M = (int64_t)c.batch * a.tokens_per_batch;
+  a.hidden = c.hidden;
+  a.width = width;
+  a.rot_begin = 0;
+  a.rot_end = c.n_heads * d_h;
+  a.rot_group = d_h;
+  a.T = (int)tokens_per_frame(c);
+  a.grid_w = c.grid_w;
+  a.W = c.window_frames;
+  a.ring_rows = (int64_t)c.window_frames * a.T;
+  a.frame0 = frame0;
+  a.out_type = c.cache_dtype;
+  a.rope = dense_rope(c);
+  hipStream_t s = (hipStream_t)stream;
+  st = launch_status(c.dtype == MLA_BF16 ? mla::launch_cache_write_bf16(a, s)
+                                         : mla::launch_cache_write_f32(a, s));
+  if (st == MLA_OK) commit_write(h, frame0, n_frames);
+  return st;
+}
+
+mla_status mla_cache_evict(mla_cache* h, int32_t n_frames) {
+  if (h == nullptr) return MLA_ERR_INVALID_ARG;
+  if (n_frames < 0 || n_frames > n_resident(h)) return MLA_ERR_EVICT_RANGE;
+  h->oldest += n_frames;
+  return MLA_OK;
+}
+
+mla_status mla_cache_query(const mla_cache* h, mla_cache_info* info) {
+  if (h == nullptr || info == nullptr) return MLA_ERR_INVALID_ARG;
+  info->oldest_frame = h->oldest;
+  info->newest_frame = h->newest;
+  info->n_resident_frames = (int32_t)n_resident(h);
+  info->capacity_frames = h->cfg.window_frames;
+  return MLA_OK;
+}
+
+mla_status mla_cache_set_state(mla_cache* h, int64_t oldest, int64_t newest) {
+  if (h == nullptr || oldest < 0 || newest < oldest - 1 ||
+      newest - oldest + 1 > h->cfg.window_frames)
+    return MLA_ERR_INVALID_ARG;
+  h->oldest = oldest;
+  h->newest = newest;
+  return MLA_OK;
+}
+
+int64_t mla_cache_slot(const mla_cache* h, int64_t frame, int32_t tau) {
+  if (h == nullptr || frame < 0 || tau < 0 || tau >= tokens_per_frame(h->cfg)) return -1;
+  return (frame % h->cfg.window_frames) * tokens_per_frame(h->cfg) + tau;
+}
+
+size_t mla_attend_workspace_bytes(const mla_cache* h, int32_t Lq, int32_t key_splits) {
+  if (h == nullptr || h->dense || Lq <= 0 || key_splits < 0) return 0;
+  if (h->cfg.dtype == MLA_F32) return 0;
+  return latent_layout(h, Lq, key_splits).total;
+}
+
+mla_status mla_attend(mla_cache* h, const void* q, int64_t q_token0, int32_t Lq, const void* w_uk,
+                      const void* w_uv, float* out, int32_t key_splits, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  if (h == nullptr || !aligned16(q) || !aligned16(w_uk) || !aligned16(w_uv) || !aligned16(out) ||
+      Lq <= 0 || key_splits < 0 || q_token0 < 0)
+    return MLA_ERR_INVALID_ARG;
+  if (h->dense) return MLA_ERR_WRONG_KIND;
+  if (n_resident(h) <= 0) return MLA_ERR_EMPTY;
+  const mla_layer_config& c = h->cfg;
+  if ((int64_t)Lq * c.n_heads >= (1LL << 30)) return MLA_ERR_INVALID_ARG;
+  const bool bf16 = c.dtype == MLA_BF16;
+  if (bf16 && !mla::attend_bf16_supported(c.d_c, c.d_rope, c.d_nope, c.d_v))
+    return MLA_ERR_UNSUPPORTED;
+  mla::AttendArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.ring = h->storage;
+  a.w_uk = w_uk;
+  a.w_uv = w_uv;
+  a.out = out;
+  a.B = c.batch;
+  a.Lq = Lq;
+  a.n_h = c.n_heads;
+  a.d_nope = c.d_nope;
+  a.d_rope = c.d_rope;
+  a.d_v = c.d_v;
+  a.d_c = c.d_c;
+  a.q_token0 = q_token0;
+  a.T = (int)tokens_per_frame(c);
+  a.grid_w = c.grid_w;
+  a.ring_rows = (int64_t)c.window_frames * a.T;
+  a.key_slot0 = (h->oldest % c.window_frames) * a.T;
+  a.Lk = (int)(n_resident(h) * a.T);
+  a.cache_type = c.cache_dtype;
+  a.qscale = (float)(1.4426950408889634 / sqrt((double)(c.d_nope + c.d_rope)));
+  a.ev_start = h->prof_start;
+  a.ev_stop = h->prof_stop;
+  a.rope = latent_rope(c);
+  hipStream_t s = (hipStream_t)stream;
+  if (!bf16) return launch_status(mla::launch_attend_f32(a, s));
+  const LatentLayout L = latent_layout(h, Lq, key_splits);
+  if (workspace == nullptr || ((uintptr_t)workspace % kAlign) != 0 || workspace_bytes < L.total)
+    return MLA_ERR_WORKSPACE;
+  char* ws = (char*)workspace;
+  a.qcat = ws + L.qcat_off;
+  a.opart = (float*)(ws + L.opart_off);
+  a.ml = (float*)(ws + L.ml_off);
+  a.n_split = L.splits;
+  a.keys_per_split = L.keys_per_split;
+  return launch_status(mla::launch_attend_bf16(a, s));
+}
+
+size_t mha_attend_workspace_bytes(const mla_cache* h, int32_t Lq) {
+  if (h == nullptr || !h->dense || Lq <= 0) return 0;
+  if (h->cfg.dtype == MLA_F32) return 0;
+  return dense_layout(h, Lq).total;
+}
+
+mla_status mha_attend(mla_cache* h, const void* q, int64_t q_token0, int32_t Lq, float* out,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (h == nullptr || !aligned16(q) || !aligned16(out) || Lq <= 0 || q_token0 < 0)
+    return MLA_ERR_INVALID_ARG;
+  if (!h->dense) return MLA_ERR_WRONG_KIND;
+  if (n_resident(h) <= 0) return MLA_ERR_EMPTY;
+  const mla_layer_config& c = h->cfg;
+  const int d_h = c.d_nope + c.d_rope;
+  if ((int64_t)Lq * c.n_heads >= (1LL << 30)) return MLA_ERR_INVALID_ARG;
+  const bool bf16 = c.dtype == MLA_BF16;
+  if (bf16 && !mla::mha_attend_bf16_supported(d_h)) return MLA_ERR_UNSUPPORTED;
+  mla::MhaAttendArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.ring = h->storage;
+  a.out = out;
+  a.B = c.batch;
+  a.Lq = Lq;
+  a.n_h = c.n_heads;
+  a.d_h = d_h;
+  a.q_token0 = q_token0;
+  a.T = (int)tokens_per_frame(c);
+  a.grid_w = c.grid_w;
+  a.ring_rows = (int64_t)c.window_frames * a.T;
+  a.key_slot0 = (h->oldest % c.window_frames) * a.T;
+  a.Lk = (int)(n_resident(h) * a.T);
+  a.cache_type = c.cache_dtype;
+  a.qscale = (float)(1.4426950408889634 / sqrt((double)d_h));
+  a.ev_start = h->prof_start;
+  a.ev_stop = h->prof_stop;
+  a.rope = dense_rope(c);
+  hipStream_t s = (hipStream_t)stream;
+  if (!bf16) return launch_status(mla::launch_mha_attend_f32(a, s));
+  const DenseLayout L = dense_layout(h, Lq);
+  if (workspace == nullptr || ((uintptr_t)workspace % kAlign) != 0 || workspace_bytes < L.total)
+    return MLA_ERR_WORKSPACE;
+  char* ws = (char*)workspace;
+  a.qrot = ws + L.qrot_off;
+  return launch_status(mla::launch_mha_attend_bf16_ws(a, (float*)(ws + L.opart_off),
+                                                      (float*)(ws + L.ml_off), L.splits,
+                                                      L.keys_per_split, s));
+}
+
+mla_status mla_cache_set_profile_events(mla_cache* h, void* start, void* stop) {
+  if (h == nullptr || ((start == nullptr) != (stop == nullptr))) return MLA_ERR_INVALID_ARG;
+  h->prof_start = (hipEvent_t)start;
+  h->prof_stop = (hipEvent_t)stop;
+  return MLA_OK;
+}
+
+const char* mla_status_str(mla_status st) {
+  switch (st) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_INVALID_ARG: return "invalid argument";
+    case MLA_ERR_STORAGE_TOO_SMALL: return "storage too small";
+    case MLA_ERR_FULL: return "window full";
+    case MLA_ERR_NOT_CONTIGUOUS: return "frames do not continue the newest resident frame";
+    case MLA_ERR_EVICT_RANGE: return "evicting more frames than are resident";
+    case MLA_ERR_EMPTY: return "window empty";
+    case MLA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case MLA_ERR_UNSUPPORTED: return "shape not supported for this dtype";
+    case MLA_ERR_WRONG_KIND: return "latent call on a dense handle or vice versa";
+    case MLA_ERR_HIP: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+const char* mla_version(void) { return "libmla 0.1 (gfx950)"; }
+
+}  // extern "C"

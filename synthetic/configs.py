@@ -26,13 +26,16 @@ class LayerConfig:
     batch: int = 1
     rope_split: tuple = None          # pairs per axis (t, h, w); None -> default
     rope_base: float = 10000.0
-    dtype: str = "bf16"               # storage / activation dtype; accumulation is fp32
+    dtype: str = "bf16"               # inputs (x, q, weights); accumulation is fp32
+    cache_dtype: str = None           # ring storage; None -> fp16 for bf16 inputs, fp32 for fp32
     prefill_frames: int = 0           # frames written before the measured chunk
     evict_frames: int = 0             # frames evicted before the chunk is written
     chunk_frames: int = 3             # frames in the query chunk (written, then attended)
     seed: int = 0
 
     def __post_init__(self):
+        if self.cache_dtype is None:
+            object.__setattr__(self, "cache_dtype", "f32" if self.dtype == "f32" else "f16")
         if self.rope_split is None:
             p = self.d_rope // 2
             object.__setattr__(self, "rope_split", (p - 2 * (p // 3), p // 3, p // 3))

@@ -1,0 +1,84 @@
+// Recording launcher for CPU tests of the host library: the kernels are
+// replaced by functions that store their arguments (and can be told to fail),
+// so window bookkeeping, validation and launch arguments run on any machine.
+#include <string.h>
+
+#include "mla_launch.h"
+
+namespace {
+mla::CacheWriteArgs g_write;
+mla::AttendArgs g_attend;
+mla::MhaAttendArgs g_mha;
+int g_mha_splits = 0, g_mha_kps = 0;
+int g_kind = 0;  // 1 write bf16, 2 write f32, 3 attend bf16, 4 attend f32, 5 mha bf16, 6 mha f32
+int g_count = 0;
+int g_fail = 0;
+hipError_t rec(int kind) {
+  g_kind = kind;
+  ++g_count;
+  if (g_fail) {
+    g_fail = 0;
+    return hipErrorLaunchFailure;
+  }
+  return hipSuccess;
+}
+}  // namespace
+
+namespace mla {
+bool cache_write_bf16_supported(int width, int hidden) {
+  return width > 0 && width % 32 == 0 && hidden > 0 && hidden % 64 == 0;
+}
+bool attend_bf16_supported(int d_c, int d_rope, int d_nope, int d_v) {
+  return (d_c == 64 || d_c == 128 || d_c == 192) && d_rope == 32 && d_nope % 16 == 0 && d_nope > 0 &&
+         d_v % 32 == 0 && d_v > 0;
+}
+bool mha_attend_bf16_supported(int d_h) { return d_h == 128; }
+int mha_lq_pad(int Lq) { return (Lq + 127) / 128 * 128; }
+hipError_t launch_cache_write_bf16(const CacheWriteArgs& a, hipStream_t) { g_write = a; return rec(1); }
+hipError_t launch_cache_write_f32(const CacheWriteArgs& a, hipStream_t) { g_write = a; return rec(2); }
+hipError_t launch_attend_bf16(const AttendArgs& a, hipStream_t) { g_attend = a; return rec(3); }
+hipError_t launch_attend_f32(const AttendArgs& a, hipStream_t) { g_attend = a; return rec(4); }
+hipError_t launch_mha_attend_bf16_ws(const MhaAttendArgs& a, float*, float*, int n_split,
+                                     int kps, hipStream_t) {
+  g_mha = a;
+  g_mha_splits = n_split;
+  g_mha_kps = kps;
+  return rec(5);
+}
+hipError_t launch_mha_attend_f32(const MhaAttendArgs& a, hipStream_t) { g_mha = a; return rec(6); }
+}  // namespace mla
+
+extern "C" {
+int fake_kind() { return g_kind; }
+int fake_count() { return g_count; }
+void fake_fail_next() { g_fail = 1; }
+// frame0, M, tokens_per_batch, width, ring_rows, rot_begin, rot_end, rot_group, w_split, hidden
+void fake_write_info(long long* o) {
+  const mla::CacheWriteArgs& a = g_write;
+  long long v[10] = {a.frame0, a.M, a.tokens_per_batch, a.width, a.ring_rows, a.rot_begin,
+                     a.rot_end, a.rot_group, a.w_split, a.hidden};
+  memcpy(o, v, sizeof(v));
+}
+// key_slot0, Lk, n_split, keys_per_split, B, Lq, q_token0, ring_rows, n_h, d_c
+void fake_attend_info(long long* o) {
+  const mla::AttendArgs& a = g_attend;
+  long long v[10] = {a.key_slot0, a.Lk, a.n_split, a.keys_per_split, a.B, a.Lq, a.q_token0,
+                     a.ring_rows, a.n_h, a.d_c};
+  memcpy(o, v, sizeof(v));
+}
+float fake_attend_qscale() { return g_attend.qscale; }
+// key_slot0, Lk, n_split, keys_per_split, Lq, q_token0
+void fake_mha_info(long long* o) {
+  long long v[6] = {g_mha.key_slot0, g_mha.Lk, g_mha_splits, g_mha_kps, g_mha.Lq, g_mha.q_token0};
+  memcpy(o, v, sizeof(v));
+}
+// which: 0 = last write, 1 = last attend, 2 = last dense attend
+int fake_rope(int which, int* axis, double* inv_freq) {
+  const mla::RopeTable& t = which == 0 ? g_write.rope : (which == 1 ? g_attend.rope : g_mha.rope);
+  for (int p = 0; p < t.n_pairs; ++p) {
+    axis[p] = t.axis[p];
+    inv_freq[p] = t.inv_freq[p];
+  }
+  return t.n_pairs;
+}
+}

@@ -1,0 +1,283 @@
+"""CPU tests of the C ABI: the built library loads and exports every function
+include/mla.h declares, and the host logic (validation, window bookkeeping,
+launch arguments, workspace sizes, error codes) is checked against the
+oracle's ring model.  Host logic runs from the same mla_host.cpp compiled with
+g++ against a recording launcher (tests/hostsim/fake_launch.cpp), so no GPU
+and no kernel is involved.
+"""
+
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from oracle import mla as O
+from synthetic import config
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla.h")
+CSRC = os.path.join(ROOT, "rank_latent_kv_absorbed_amd", "csrc")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b((?:mla|mha)_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def real_lib():
+    from rank_latent_kv_absorbed_amd import mla as binding
+    if not os.path.exists(binding.LIB_PATH):
+        from rank_latent_kv_absorbed_amd import build
+        build.build()
+    return ctypes.CDLL(binding.LIB_PATH)
+
+
+def test_library_exports_every_declared_function(real_lib):
+    names = header_functions()
+    assert len(names) >= 17
+    for n in names:
+        assert hasattr(real_lib, n), n
+    from rank_latent_kv_absorbed_amd.mla import SIGNATURES
+    assert sorted(SIGNATURES) == names
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    from rank_latent_kv_absorbed_amd import mla as binding
+    monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(binding, "_lib", None)
+    with pytest.raises(binding.LibraryMissing):
+        binding.lib()
+
+
+# --------------------------------------------------------------------------
+# host logic against the recording launcher
+# --------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def sim(tmp_path_factory):
+    out = str(tmp_path_factory.mktemp("hostsim") / "libmla_hostsim.so")
+    cmd = ["g++", "-O1", "-std=c++17", "-fPIC", "-shared", "-D__HIP_PLATFORM_AMD__",
+           "-I", "/opt/rocm/include", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+           os.path.join(CSRC, "mla_host.cpp"), os.path.join(ROOT, "tests", "hostsim", "fake_launch.cpp"),
+           "-o", out]
+    subprocess.run(cmd, check=True, capture_output=True)
+    L = ctypes.CDLL(out)
+    from rank_latent_kv_absorbed_amd.mla import SIGNATURES
+    for name, (res, args) in SIGNATURES.items():
+        f = getattr(L, name)
+        f.restype, f.argtypes = res, args
+    L.fake_attend_qscale.restype = ctypes.c_float
+    return L
+
+
+FAKE_STORAGE = 1 << 40          # host never dereferences storage; any aligned address works
+FAKE_PTR = 1 << 41
+
+
+def _cfg(name="wan_window", **kw):
+    from rank_latent_kv_absorbed_amd.mla import make_config
+    return make_config(config(name, **kw))
+
+
+def _create(L, c, dense=False, nbytes=None):
+    from rank_latent_kv_absorbed_amd.mla import _HANDLE
+    h = _HANDLE()
+    size = (L.mha_cache_bytes if dense else L.mla_cache_bytes)(ctypes.byref(c))
+    st = (L.mha_cache_create if dense else L.mla_cache_create)(
+        ctypes.byref(c), ctypes.c_void_p(FAKE_STORAGE), size if nbytes is None else nbytes,
+        ctypes.byref(h))
+    return st, h
+
+
+def _info(L, h):
+    from rank_latent_kv_absorbed_amd.mla import CacheInfoC
+    i = CacheInfoC()
+    assert L.mla_cache_query(h, ctypes.byref(i)) == 0
+    return i.oldest_frame, i.newest_frame, i.n_resident_frames, i.capacity_frames
+
+
+def _write_info(L):
+    a = (ctypes.c_longlong * 10)()
+    L.fake_write_info(a)
+    return list(a)
+
+
+def _attend_info(L):
+    a = (ctypes.c_longlong * 10)()
+    L.fake_attend_info(a)
+    return list(a)
+
+
+P = ctypes.c_void_p
+
+
+def test_cache_bytes_closed_forms(sim):
+    c = _cfg()
+    assert sim.mla_cache_bytes(ctypes.byref(c)) == 14_676_480
+    assert sim.mha_cache_bytes(ctypes.byref(c)) == 201_277_440
+    c.batch = 8
+    assert sim.mla_cache_bytes(ctypes.byref(c)) == 8 * 14_676_480
+    c.batch, c.d_c = 1, 64
+    assert sim.mla_cache_bytes(ctypes.byref(c)) == 6_289_920
+    t = _cfg("tiny")
+    assert sim.mla_cache_bytes(ctypes.byref(t)) == 3 * 16 * 24 * 4
+
+
+def test_invalid_configs_rejected(sim):
+    for field, val in (("d_rope", 7), ("rope_pairs_t", 5), ("hidden", 0), ("window_frames", 0),
+                       ("dtype", 3), ("batch", -1), ("grid_w", 0)):
+        c = _cfg()
+        setattr(c, field, val)
+        assert sim.mla_cache_bytes(ctypes.byref(c)) == 0, field
+        st, _ = _create(sim, c, nbytes=1 << 30)
+        assert st == 1, field
+    c = _cfg()
+    st, _ = _create(sim, c, nbytes=14_676_480 - 1)
+    assert st == 2
+
+
+def test_rollout_schedule_matches_ring_model(sim):
+    """80 chunks of 3 frames through a 21-frame window: window state, write
+    launch arguments, attend key range and slot map agree with the oracle."""
+    c = _cfg()
+    st, h = _create(sim, c)
+    assert st == 0
+    ring = O.RingModel(21, 1560)
+    for k in range(80):
+        n_ev = max(0, ring.n_resident + 3 - 21)
+        assert sim.mla_cache_evict(h, n_ev) == 0
+        ring.evict(n_ev)
+        assert sim.mla_cache_write(h, P(FAKE_PTR), P(FAKE_PTR), 3 * k, 3, None) == 0
+        ring.write(3 * k, 3)
+        w = _write_info(sim)
+        assert w[:8] == [3 * k, 3 * 1560, 3 * 1560, 224, 21 * 1560, 192, 224, 32]
+        assert _info(sim, h) == (ring.oldest, ring.newest, ring.n_resident, 21)
+        assert sim.mla_attend(h, P(FAKE_PTR), 3 * k * 1560, 4680, P(FAKE_PTR), P(FAKE_PTR),
+                              P(FAKE_PTR), 0, P(FAKE_PTR), 1 << 40, None) == 0
+        a = _attend_info(sim)
+        slots = ring.resident_slots()
+        assert a[0] == slots[0] and a[1] == len(slots)
+        # keys are the contiguous (mod ring) run of slots starting at key_slot0
+        np.testing.assert_array_equal((a[0] + np.arange(a[1])) % (21 * 1560), slots)
+        for f in (ring.oldest, ring.newest):
+            for tau in (0, 777, 1559):
+                assert sim.mla_cache_slot(h, f, tau) == ring.slot(f, tau)
+    sim.mla_cache_destroy(h)
+
+
+def test_write_errors_leave_state_unchanged(sim):
+    c = _cfg()
+    st, h = _create(sim, c)
+    assert sim.mla_cache_write(h, P(FAKE_PTR), P(FAKE_PTR), 10, 18, None) == 0
+    before = _info(sim, h)
+    n = sim.fake_count()
+    assert sim.mla_cache_write(h, P(FAKE_PTR), P(FAKE_PTR), 28, 4, None) == 3     # full
+    assert sim.mla_cache_write(h, P(FAKE_PTR), P(FAKE_PTR), 29, 1, None) == 4     # gap
+    assert sim.mla_cache_write(h, P(FAKE_PTR), P(FAKE_PTR), 27, 1, None) == 4     # overlap
+    assert sim.mla_cache_write(h, P(FAKE_PTR), P(FAKE_PTR), 28, 0, None) == 1
+    assert sim.mla_cache_write(h, P(FAKE_PTR + 2), P(FAKE_PTR), 28, 1, None) == 1  # misaligned
+    assert sim.mla_cache_write(h, None, P(FAKE_PTR), 28, 1, None) == 1
+    assert sim.mla_cache_evict(h, 19) == 5
+    assert sim.mla_cache_evict(h, -1) == 5
+    assert _info(sim, h) == before and sim.fake_count() == n
+    # a launch failure is reported and does not commit the frames
+    sim.fake_fail_next()
+    assert sim.mla_cache_write(h, P(FAKE_PTR), P(FAKE_PTR), 28, 3, None) == 10
+    assert _info(sim, h) == before
+    assert sim.mla_cache_write(h, P(FAKE_PTR), P(FAKE_PTR), 28, 3, None) == 0
+    assert _info(sim, h) == (10, 30, 21, 21)
+    # empty window: attend refuses, a write may start anywhere
+    assert sim.mla_cache_evict(h, 21) == 0
+    assert sim.mla_attend(h, P(FAKE_PTR), 0, 16, P(FAKE_PTR), P(FAKE_PTR), P(FAKE_PTR), 0,
+                          P(FAKE_PTR), 1 << 40, None) == 6
+    assert sim.mla_cache_write(h, P(FAKE_PTR), P(FAKE_PTR), 500, 2, None) == 0
+    assert _info(sim, h)[:3] == (500, 501, 2)
+
+
+def test_attend_arguments_and_workspace(sim):
+    c = _cfg()
+    st, h = _create(sim, c)
+    assert sim.mla_cache_set_state(h, 3, 23) == 0
+    need = sim.mla_attend_workspace_bytes(h, 4680, 0)
+    R = 4680 * 12
+    assert need >= R * 224 * 2 + R * 192 * 4 + R * 8
+    ws = 1 << 40
+    assert sim.mla_attend(h, P(FAKE_PTR), 21 * 1560, 4680, P(FAKE_PTR), P(FAKE_PTR), P(FAKE_PTR),
+                          0, P(ws), need - 1, None) == 7
+    assert sim.mla_attend(h, P(FAKE_PTR), 21 * 1560, 4680, P(FAKE_PTR), P(FAKE_PTR), P(FAKE_PTR),
+                          0, P(ws + 64), need, None) == 7                      # misaligned
+    assert sim.mla_attend(h, P(FAKE_PTR), 21 * 1560, 4680, P(FAKE_PTR), P(FAKE_PTR), P(FAKE_PTR),
+                          0, P(ws), need, None) == 0
+    a = _attend_info(sim)
+    assert a[0] == (3 % 21) * 1560 and a[1] == 21 * 1560 and a[5] == 4680 and a[6] == 21 * 1560
+    assert a[2] >= 1 and a[2] * a[3] >= a[1] and a[3] % 64 == 0
+    assert sim.fake_attend_qscale() == np.float32(math.log2(math.e) / math.sqrt(128))
+    # forced key splits: ranges are key-tile multiples covering the window
+    for s in (1, 2, 7, 64):
+        need = sim.mla_attend_workspace_bytes(h, 8, s)
+        assert sim.mla_attend(h, P(FAKE_PTR), 0, 8, P(FAKE_PTR), P(FAKE_PTR), P(FAKE_PTR), s,
+                              P(ws), need, None) == 0
+        a = _attend_info(sim)
+        assert a[2] == s and a[3] % 64 == 0 and a[2] * a[3] >= a[1] > (a[2] - 1) * a[3] - 64
+    # small queries get several key ranges by default; a large chunk gets one
+    sim.mla_attend(h, P(FAKE_PTR), 0, 1, P(FAKE_PTR), P(FAKE_PTR), P(FAKE_PTR), 0, P(ws), 1 << 40, None)
+    assert _attend_info(sim)[2] > 1
+    sim.mla_attend(h, P(FAKE_PTR), 0, 4680, P(FAKE_PTR), P(FAKE_PTR), P(FAKE_PTR), 0, P(ws), 1 << 40, None)
+    assert _attend_info(sim)[2] == 1
+
+
+def test_wrong_kind_and_unsupported(sim):
+    c = _cfg()
+    st, dense = _create(sim, c, dense=True)
+    assert st == 0
+    assert sim.mla_cache_write(dense, P(FAKE_PTR), P(FAKE_PTR), 0, 1, None) == 9
+    st, lat = _create(sim, c)
+    assert sim.mha_cache_write(lat, P(FAKE_PTR), P(FAKE_PTR), P(FAKE_PTR), 0, 1, None) == 9
+    c2 = _cfg(d_c=96)
+    st, h = _create(sim, c2)
+    assert st == 0
+    assert sim.mla_cache_write(h, P(FAKE_PTR), P(FAKE_PTR), 0, 1, None) == 0
+    assert sim.mla_attend(h, P(FAKE_PTR), 0, 8, P(FAKE_PTR), P(FAKE_PTR), P(FAKE_PTR), 0,
+                          P(1 << 40), 1 << 40, None) == 8
+
+
+def test_rope_tables_match_oracle(sim):
+    c = _cfg()
+    st, h = _create(sim, c)
+    sim.mla_cache_write(h, P(FAKE_PTR), P(FAKE_PTR), 0, 3, None)
+    axis = (ctypes.c_int * 64)()
+    inv = (ctypes.c_double * 64)()
+    n = sim.fake_rope(0, axis, inv)
+    want = O.rope_pair_table((6, 5, 5), 10000.0)
+    assert n == len(want) == 16
+    for p, (ax, f) in enumerate(want):
+        assert axis[p] == ax and inv[p] == f
+    st, d = _create(sim, c, dense=True)
+    sim.mha_cache_write(d, P(FAKE_PTR), P(FAKE_PTR), P(FAKE_PTR), 0, 3, None)
+    n = sim.fake_rope(0, axis, inv)
+    want = O.rope_pair_table(O.default_rope_split(128), 10000.0)
+    assert n == 64 and [axis[p] for p in range(64)] == [a for a, _ in want]
+    assert [inv[p] for p in range(64)] == [f for _, f in want]
+    w = _write_info(sim)
+    assert w[3] == 3072 and w[5:9] == [0, 1536, 128, 1536]
+
+
+def test_set_state_and_slot_validation(sim):
+    c = _cfg()
+    st, h = _create(sim, c)
+    assert sim.mla_cache_set_state(h, 5, 3) == 1
+    assert sim.mla_cache_set_state(h, 5, 26) == 1
+    assert sim.mla_cache_set_state(h, -1, 3) == 1
+    assert sim.mla_cache_set_state(h, 5, 25) == 0
+    assert _info(sim, h) == (5, 25, 21, 21)
+    assert sim.mla_cache_set_state(h, 7, 6) == 0       # empty
+    assert _info(sim, h)[2] == 0
+    assert sim.mla_cache_slot(h, 22, 1560) == -1
+    assert sim.mla_cache_slot(h, -1, 0) == -1
+    assert sim.mla_cache_slot(h, 43, 5) == (43 % 21) * 1560 + 5

@@ -1,0 +1,287 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs.  Small and mid sizes compare every output element; the
+Wan-sized window compares sampled query rows at full size.
+
+Bars: bf16 inputs with fp32 accumulation -> max|err| <= 1e-2 max|ref| and
+sum|err| <= 2e-3 sum|ref| (for both 2-byte ring types); fp32 path -> 1e-5 /
+1e-6; cache placement and the window's slot map are bit-exact.
+
+The ring is fp16 by default; bf16 storage is exercised at the Wan-sized
+windows (>= 4680 keys), where its query-rounding error still meets the bar.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import mla as O
+from synthetic import config, chunk_q, chunk_x
+from tests.parity_util import (NAN_BITS, DenseRun, LatentRun, assert_parity, dev, nan_fill_,
+                               parity_stats, sample_rows)
+
+TORCH_T = {"bf16": torch.bfloat16, "f16": torch.float16}
+SIG_BITS = {"bf16": 8, "f16": 11}
+
+pytestmark = pytest.mark.gpu
+
+WAN_HEADS = dict(hidden=1536, n_heads=12, d_nope=96, d_rope=32, d_v=128, d_c=192)
+
+
+def mid_cfg(**kw):
+    base = dict(hidden=256, n_heads=4, d_nope=32, d_rope=32, d_v=64, d_c=64, grid_h=6, grid_w=10,
+                window_frames=5, batch=2, rope_split=None, dtype="bf16")
+    base.update(kw)
+    return config("wan_layer").with_(**base)
+
+
+def wan_small(**kw):
+    base = dict(WAN_HEADS, grid_h=5, grid_w=13, window_frames=6, batch=2, rope_split=None,
+                dtype="bf16")
+    base.update(kw)
+    return config("wan_layer").with_(**base)
+
+
+def setup_module(module):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.manual_seed(0)
+
+
+def _ring_bits(run):
+    return run.gpu.ring().view(torch.int16).cpu().numpy()
+
+
+def _oracle_bits(store, cache_dtype):
+    t = torch.from_numpy(store).to(TORCH_T[cache_dtype])
+    return t.view(torch.int16).numpy()
+
+
+def _onehot_x(cfg, n_frames, seed):
+    """Rows 2^e * onehot(k) with distinct (k, e) per token: every product of
+    the cache-write GEMM is exact, so the stored rows are known exactly."""
+    rng = np.random.default_rng(seed)
+    n = n_frames * cfg.T
+    x = np.zeros((cfg.batch, n, cfg.hidden))
+    for b in range(cfg.batch):
+        ks = rng.integers(0, cfg.hidden, n)
+        es = rng.integers(-4, 5, n)
+        x[b, np.arange(n), ks] = 2.0 ** es
+    return torch.from_numpy(x).to(torch.bfloat16)
+
+
+# --------------------------------------------------------------------------
+# cache write
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cache_dtype", ["f16", "bf16"])
+def test_cache_write_exact_placement_and_untouched_slots(cache_dtype):
+    cfg = mid_cfg(cache_dtype=cache_dtype)
+    run = LatentRun(cfg, poison=True)
+    run.w["w_dkr"][cfg.d_c:] = 0          # k^R rows zero: every stored value is exact
+    run.wd["w_dkr"] = dev(run.w["w_dkr"])
+    run.write(7, 2, x=_onehot_x(cfg, 2, 1))   # frames 7, 8 -> ring frames 2, 3
+    torch.cuda.synchronize()
+    got = _ring_bits(run)
+    want = _oracle_bits(run.store, cache_dtype)
+    written = np.zeros(cfg.window_frames * cfg.T, bool)
+    written[2 * cfg.T:4 * cfg.T] = True
+    np.testing.assert_array_equal(got[:, written], want[:, written])
+    assert (got[:, ~written] == NAN_BITS[cache_dtype]).all(), "kernel wrote outside the chunk's slots"
+
+
+@pytest.mark.parametrize("cache_dtype", ["f16", "bf16"])
+def test_cache_write_values_within_one_ulp(cache_dtype):
+    """Stored rows are the oracle's rounded values or a neighbour: the GPU sums
+    in fp32, so a value may round the other way when the fp64 sum lies within
+    the fp32 summation error of a rounding boundary."""
+    cfg = wan_small(batch=1, cache_dtype=cache_dtype)
+    run = LatentRun(cfg)
+    x = run.write(0, 4)
+    torch.cuda.synchronize()
+    got = run.gpu.ring().double().cpu().numpy()
+    ref = run.store
+    written = np.zeros(cfg.window_frames * cfg.T, bool)
+    written[:4 * cfg.T] = True
+    g, r = got[:, written], ref[:, written]
+    ulp = np.ldexp(1.0, np.frexp(np.abs(r))[1] - SIG_BITS[cache_dtype])
+    # fp32 accumulation bound of the 1536-term products (rotation adds a few ulp of fp32)
+    mag = np.abs(x.double().numpy()[0]) @ np.abs(run.w["w_dkr"].double().numpy()).T
+    acc = 1536 * 2.0 ** -24 * np.concatenate([mag[:, :cfg.d_c], np.repeat(
+        mag[:, cfg.d_c:].reshape(-1, cfg.d_rope // 2, 2).sum(-1), 2, axis=-1)], -1)
+    assert (np.abs(g - r)[0] <= ulp[0] + acc).all()
+    assert np.mean(g == r) > 0.97
+
+
+@pytest.mark.parametrize("cache_dtype", ["f16", "bf16"])
+def test_rollout_ring_bit_exact_through_wraps(cache_dtype):
+    """A 12-chunk rollout through a 5-frame window (the ring wraps four times):
+    after every chunk the resident rows match the oracle bit for bit."""
+    cfg = mid_cfg(batch=1, cache_dtype=cache_dtype)
+    run = LatentRun(cfg, poison=True)
+    run.w["w_dkr"][cfg.d_c:] = 0
+    run.wd["w_dkr"] = dev(run.w["w_dkr"])
+    for k in range(12):
+        n_ev = max(0, run.ring.n_resident + 2 - cfg.window_frames)
+        run.evict(n_ev)
+        run.write(2 * k, 2, x=_onehot_x(cfg, 2, 100 + k))
+        torch.cuda.synchronize()
+        info = run.gpu.info()
+        assert (info["oldest_frame"], info["newest_frame"]) == (run.ring.oldest, run.ring.newest)
+        slots = run.ring.resident_slots()
+        np.testing.assert_array_equal(_ring_bits(run)[:, slots],
+                                      _oracle_bits(run.store, cache_dtype)[:, slots])
+        for f in (run.ring.oldest, run.ring.newest):
+            assert run.gpu.slot(f, 7) == run.ring.slot(f, 7)
+
+
+# --------------------------------------------------------------------------
+# attention, every element
+# --------------------------------------------------------------------------
+
+def test_attend_tiny_fp32_path():
+    cfg = config("tiny")
+    run = LatentRun(cfg)
+    run.write(0, 2)
+    run.write(2, 1)
+    q = run.query(cfg.T)
+    got, ref, _ = run.attend(q, 2 * cfg.T)
+    assert_parity(got, ref, "f32", "tiny fp32")
+
+
+@pytest.mark.parametrize("key_splits", [0, 1, 3])
+def test_attend_mid_ragged_with_wrap(key_splits):
+    cfg = mid_cfg()
+    run = LatentRun(cfg)
+    run.write(0, 4)
+    run.evict(2)
+    run.write(4, 2)       # frames 2..5 resident, ring wrapped (frame 5 -> slot 0)
+    run.evict(1)
+    run.write(6, 2)       # frames 3..7, Lk = 300 keys: 4 full key tiles + a ragged one
+    q = run.query(2 * cfg.T)
+    got, ref, _ = run.attend(q, 6 * cfg.T, key_splits=key_splits)
+    assert_parity(got, ref, "bf16", f"mid splits={key_splits}")
+
+
+@pytest.mark.parametrize("d_c", [64, 128, 192])
+def test_attend_wan_heads_latent_widths(d_c):
+    cfg = wan_small(d_c=d_c)
+    run = LatentRun(cfg)
+    run.write(0, 4)
+    run.evict(1)
+    run.write(4, 2)
+    q = run.query(2 * cfg.T)
+    got, ref, _ = run.attend(q, 4 * cfg.T)
+    assert_parity(got, ref, "bf16", f"wan heads d_c={d_c}")
+
+
+@pytest.mark.parametrize("cache_dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("Lq", [1, 4, 8])
+def test_attend_small_queries_cache_bound_shapes(Lq, cache_dtype):
+    cfg = config("wan_layer").with_(window_frames=3, batch=3, cache_dtype=cache_dtype)
+    run = LatentRun(cfg)
+    run.write(0, 3)       # Lk = 4680
+    q = run.query(Lq)
+    got, ref, _ = run.attend(q, 3 * cfg.T - Lq)
+    assert_parity(got, ref, "bf16", f"small query Lq={Lq} {cache_dtype}")
+
+
+def test_nan_poison_determinism_and_split_agreement():
+    cfg = wan_small()
+    runs = [LatentRun(cfg, poison=p) for p in (False, True)]
+    for r in runs:
+        r.write(0, 4)
+        r.evict(2)
+        r.write(4, 2)
+    q = runs[0].query(2 * cfg.T)
+    outs = []
+    for r in runs:
+        for _ in range(2):
+            outs.append(r.gpu.attend(dev(q), 4 * cfg.T, r.wd["w_uk"], r.wd["w_uv"]).cpu())
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0]), "results differ between runs or with NaN-filled free slots"
+    got, ref, _ = runs[1].attend(q, 4 * cfg.T, key_splits=5)
+    assert_parity(got, ref, "bf16", "5 key ranges")
+    mx, mean = parity_stats(got, outs[0].numpy())
+    assert mx < 2e-3 and mean < 5e-4
+
+
+def test_frame_shift_changes_nothing_beyond_rounding():
+    cfg = wan_small(batch=1)
+    outs = []
+    for off in (0, 100):
+        run = LatentRun(cfg)
+        run.write(off, 3, x=chunk_x(cfg, 3, chunk=0))
+        q = run.query(cfg.T)
+        got, ref, _ = run.attend(q, (off + 2) * cfg.T)
+        assert_parity(got, ref, "bf16", f"frame offset {off}")
+        outs.append(got)
+    mx, mean = parity_stats(outs[1], outs[0])
+    assert mx < 1e-2 and mean < 4e-3
+
+
+# --------------------------------------------------------------------------
+# attention at Wan sizes, sampled rows
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cache_dtype", ["f16", "bf16"])
+def test_wan_layer_sampled_rows(cache_dtype):
+    cfg = config("wan_layer").with_(cache_dtype=cache_dtype)
+    run = LatentRun(cfg)
+    run.write(0, cfg.prefill_frames)
+    run.write(cfg.chunk_frame0, cfg.chunk_frames)
+    q = run.query(cfg.Lq)
+    rows = sample_rows(cfg.Lq, 96)
+    got, ref, _ = run.attend(q, cfg.chunk_frame0 * cfg.T, rows=rows)
+    assert_parity(got, ref, "bf16", f"wan layer (6+3 frames) sampled {cache_dtype}")
+
+
+@pytest.mark.parametrize("batch,cache_dtype", [(1, "f16"), (2, "f16"), (1, "bf16")])
+def test_full_window_sampled_rows(batch, cache_dtype):
+    cfg = config("wan_window").with_(batch=batch, cache_dtype=cache_dtype)
+    run = LatentRun(cfg)
+    run.write(0, cfg.prefill_frames)
+    run.evict(cfg.evict_frames)
+    run.write(cfg.chunk_frame0, cfg.chunk_frames)
+    assert run.gpu.info()["n_resident_frames"] == 21
+    q = run.query(cfg.Lq)
+    rows = sample_rows(cfg.Lq, 48 if batch == 1 else 24)
+    got, ref, _ = run.attend(q, cfg.chunk_frame0 * cfg.T, rows=rows)
+    assert_parity(got, ref, "bf16", f"21-frame window B={batch} {cache_dtype} sampled")
+
+
+# --------------------------------------------------------------------------
+# dense comparison path
+# --------------------------------------------------------------------------
+
+def test_dense_mha_full_small():
+    cfg = wan_small()
+    run = DenseRun(cfg)
+    run.write(0, 4)
+    run.evict(1)
+    run.write(4, 2)
+    q = chunk_q(cfg, 2 * cfg.T, chunk=7)
+    got, ref = run.attend(q, 4 * cfg.T)
+    assert_parity(got, ref, "bf16", "dense small")
+
+
+def test_dense_mha_tiny_fp32():
+    cfg = config("tiny").with_(batch=2)
+    run = DenseRun(cfg)
+    run.write(0, 3)
+    q = chunk_q(cfg, cfg.T, chunk=3)
+    got, ref = run.attend(q, 2 * cfg.T)
+    assert_parity(got, ref, "f32", "dense tiny fp32")
+
+
+def test_dense_mha_window_sampled():
+    cfg = config("wan_window")
+    run = DenseRun(cfg)
+    run.write(0, cfg.prefill_frames)
+    run.evict(cfg.evict_frames)
+    run.write(cfg.chunk_frame0, cfg.chunk_frames)
+    q = chunk_q(cfg, cfg.Lq, chunk=9)
+    rows = sample_rows(cfg.Lq, 32)
+    got, ref = run.attend(q, cfg.chunk_frame0 * cfg.T, rows=rows)
+    assert_parity(got, ref, "bf16", "dense 21-frame window sampled")

@@ -77,6 +77,13 @@ def test_bf16_rounding_matches_torch():
     np.testing.assert_array_equal(got, want)
 
 
+def test_f16_rounding_matches_torch():
+    rng = np.random.default_rng(9)
+    v = (rng.standard_normal(20000) * np.exp2(rng.integers(-30, 18, 20000))).astype(np.float32)
+    want = torch.from_numpy(v).to(torch.float16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(O.round_to_f16(v.astype(np.float64)), want)
+
+
 def test_f32_rounding_matches_torch():
     v = np.random.default_rng(2).standard_normal(1000) * 1e3
     want = torch.from_numpy(v).to(torch.float32).to(torch.float64).numpy()
