@@ -72,10 +72,10 @@ class HipEvents:
         self.made = []
 
 
-def cpu_baseline(cfg, x_chunk, w, q, n1=16, n2=64):
-    """The fp64 oracle, untuned, on a bounded sample of one step: the cache
-    write of a 3-frame chunk into a 21-frame window and the attention of n1 and
-    n2 query tokens; attention time is extrapolated linearly to the chunk."""
+def cpu_baseline(cfg, x_chunk, w, q, repeats=3):
+    """The fp64 oracle, untuned, on one full step of the workload at batch 1:
+    evict 3 frames, cache write of the 3-frame chunk into the 21-frame window,
+    attention of all of the chunk's queries; median of `repeats` runs."""
     import numpy as np
     from oracle import mla as O
     try:
@@ -85,34 +85,29 @@ def cpu_baseline(cfg, x_chunk, w, q, n1=16, n2=64):
         threads = len(os.sched_getaffinity(0))
     T = cfg.T
     rng = np.random.default_rng(0)
-    store = O.round_to_bf16(rng.standard_normal((1, cfg.window_frames * T, cfg.width)))
-    ring = O.RingModel(cfg.window_frames, T)
-    ring.write(0, cfg.window_frames)
     xs = x_chunk[:1].double().numpy()
     wd = {k: v.double().numpy() for k, v in w.items()}
     qs = q[:1].double().numpy()
-    t0 = time.perf_counter()
-    O.cache_evict(ring, cfg.chunk_frames)
-    O.cache_write(store, ring, xs, wd["w_dkr"], cfg.window_frames, cfg.chunk_frames, cfg)
-    t_write = time.perf_counter() - t0
-    q0 = cfg.window_frames * T
     times = []
-    for n in (n1, n2):
+    for _ in range(repeats):
+        store = O.round_storage(rng.standard_normal((1, cfg.window_frames * T, cfg.width)),
+                                cfg.cache_dtype)
+        ring = O.RingModel(cfg.window_frames, T)
+        ring.write(0, cfg.window_frames)
         t0 = time.perf_counter()
-        O.attend(store, ring, qs, q0, wd["w_uk"], wd["w_uv"], cfg, rows=np.arange(n))
+        O.cache_evict(ring, cfg.chunk_frames)
+        O.cache_write(store, ring, xs, wd["w_dkr"], cfg.window_frames, cfg.chunk_frames, cfg,
+                      storage=cfg.cache_dtype)
+        O.attend(store, ring, qs, cfg.window_frames * T, wd["w_uk"], wd["w_uv"], cfg)
         times.append(time.perf_counter() - t0)
-    slope = max((times[1] - times[0]) / (n2 - n1), 0.0)
-    icpt = max(times[0] - slope * n1, 0.0)
-    t_step = t_write + icpt + slope * cfg.Lq
+    t_step = sorted(times)[len(times) // 2]
     return {
         "value": cfg.Lq / t_step, "unit": "query tokens/s per layer", "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"fp64 NumPy oracle, batch 1: cache write of one {cfg.chunk_frames}-frame chunk "
-                   f"({cfg.Lq} tokens, {t_write:.2f} s) into a {cfg.window_frames}-frame window, "
-                   f"attention of {n1} and {n2} query tokens x {cfg.n_heads} heads over "
-                   f"{cfg.window_frames * T} keys ({times[0]:.2f} s, {times[1]:.2f} s), "
-                   f"attention extrapolated linearly to {cfg.Lq} queries"),
-        "seconds_measured": round(t_write + sum(times), 2),
+        "sample": (f"one full step at batch 1 (evict {cfg.chunk_frames} frames, cache write of "
+                   f"{cfg.Lq} tokens, attention of {cfg.Lq} queries x {cfg.n_heads} heads over "
+                   f"{cfg.window_frames * T} keys), fp64 NumPy oracle, median of {repeats} runs"),
+        "seconds_measured": round(sum(times), 2),
     }
 
 

@@ -9,7 +9,8 @@ namespace mla {
 
 namespace {
 
-constexpr int kDenseRB = 1;
+constexpr int kDenseRB = 1, kDenseNW = 8;
+constexpr int kDenseBlockRows = core_block_rows<kDenseRB, kDenseNW>();
 
 // q [B][Lq][n_h][d_h] -> qrot [B][n_h * Lq_pad][d_h] bf16 (head-major rows).
 template <typename E>
@@ -137,7 +138,7 @@ __global__ __launch_bounds__(256) void mha_attend_f32_kernel(MhaAttendArgs a) {
 
 }  // namespace
 
-int mha_lq_pad(int Lq) { return (Lq + core_block_rows<kDenseRB>() - 1) / core_block_rows<kDenseRB>() * core_block_rows<kDenseRB>(); }
+int mha_lq_pad(int Lq) { return (Lq + kDenseBlockRows - 1) / kDenseBlockRows * kDenseBlockRows; }
 
 bool mha_attend_bf16_supported(int d_h) { return d_h == 128; }
 
@@ -172,12 +173,13 @@ hipError_t launch_mha_typed(const MhaAttendArgs& a, float* opart, float* ml, int
     c.n_split = n_split;
     c.keys_per_split = keys_per_split;
     c.key_slot0 = a.key_slot0;
-    dim3 grid((unsigned)(c.R / core_block_rows<kDenseRB>()), (unsigned)n_split, (unsigned)a.B);
+    dim3 grid((unsigned)(c.R / kDenseBlockRows), (unsigned)n_split, (unsigned)a.B);
     if (a.ev_start != nullptr) {
       hipError_t e = hipEventRecord(a.ev_start, s);
       if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((attn_core_kernel<E, 128, 128, kDenseRB, false>), grid, dim3(256), 0, s, c);
+    hipLaunchKernelGGL((attn_core_kernel<E, 128, 128, kDenseRB, kDenseNW, false>), grid,
+                       dim3(kDenseNW * 64), 0, s, c);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.ev_stop != nullptr) {

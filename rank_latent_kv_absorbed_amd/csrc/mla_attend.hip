@@ -257,7 +257,7 @@ hipError_t launch_dc(const AttendArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   {
-    constexpr int RB = 1;
+    constexpr int RB = 1, NW = 8;
     AttnCore c;
     c.qrows = a.qcat;
     c.ring = a.ring;
@@ -276,13 +276,14 @@ hipError_t launch_dc(const AttendArgs& a, hipStream_t s) {
     c.n_split = a.n_split;
     c.keys_per_split = a.keys_per_split;
     c.key_slot0 = a.key_slot0;
-    dim3 grid((unsigned)((c.R + core_block_rows<RB>() - 1) / core_block_rows<RB>()),
-              (unsigned)a.n_split, (unsigned)a.B);
+    constexpr int BR = core_block_rows<RB, NW>();
+    dim3 grid((unsigned)((c.R + BR - 1) / BR), (unsigned)a.n_split, (unsigned)a.B);
     if (a.ev_start != nullptr) {
       hipError_t e = hipEventRecord(a.ev_start, s);
       if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((attn_core_kernel<E, DC + 32, DC, RB, true>), grid, dim3(256), 0, s, c);
+    hipLaunchKernelGGL((attn_core_kernel<E, DC + 32, DC, RB, NW, true>), grid, dim3(NW * 64), 0, s,
+                       c);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.ev_stop != nullptr) {
