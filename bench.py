@@ -120,6 +120,9 @@ def main():
     ap.add_argument("--layers", type=int, default=30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip dense and small-query cases")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one plain device-to-device copy of this size first (a known-byte "
+                         "kernel for scaling hardware traffic counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -158,6 +161,15 @@ def main():
     out = torch.empty((B, Lq, cfg.n_heads, cfg.d_v), dtype=torch.float32, device=dev)
     ws = torch.empty(caches[0].workspace_bytes(Lq), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
+
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     ev = HipEvents()
     state = {"i": 0}
