@@ -173,8 +173,10 @@ size_t mla_attend_workspace_bytes(const mla_cache* cache, int32_t Lq, int32_t ke
  *         rotated; query row i sits at global token q_token0 + i;
  *   out   [batch][Lq][n_h][d_v] fp32, out_h = W^V_up,h (sum_j p_j c_j),
  *         p = softmax_j((q^nope.W^K_up,h c_j + RoPE3D(q^R).k^R_j) / sqrt(d_nope+d_rope)).
- * key_splits = 0 lets the library choose; > 0 forces that many key ranges
- * (merged exactly by log-sum-exp).  workspace: device memory of at least
+ * The work is spread evenly over the compute units (stream-K); row groups
+ * whose keys end up on several units are merged exactly by log-sum-exp.
+ * key_splits = 0 lets the library choose; > 0 cuts every row group's key
+ * range into about that many pieces.  workspace: device memory of at least
  * mla_attend_workspace_bytes(cache, Lq, key_splits).  MLA_ERR_EMPTY if no frame
  * is resident. */
 mla_status mla_attend(mla_cache* cache, const void* q, int64_t q_token0, int32_t Lq,

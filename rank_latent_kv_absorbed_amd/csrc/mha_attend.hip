@@ -9,8 +9,8 @@ namespace mla {
 
 namespace {
 
-constexpr int kDenseRB = 1, kDenseNW = 8;
-constexpr int kDenseBlockRows = core_block_rows<kDenseRB, kDenseNW>();
+constexpr int kDenseNW = kCoreBlockRows / 32;
+constexpr int kDenseBlockRows = kCoreBlockRows;
 
 // q [B][Lq][n_h][d_h] -> qrot [B][n_h * Lq_pad][d_h] bf16 (head-major rows).
 template <typename E>
@@ -33,9 +33,8 @@ __global__ __launch_bounds__(256) void mha_qprep_bf16_kernel(MhaAttendArgs a, in
   o[1] = Elem<E>::from(x1 * a.qscale);
 }
 
-// Merge key ranges and normalise: one thread per (row, 4 output dims).
-__global__ __launch_bounds__(256) void mha_merge_kernel(MhaAttendArgs a, const float* opart,
-                                                        const float* ml, int n_split, int lq_pad) {
+// Merge a row group's partials and normalise: one thread per (row, 4 dims).
+__global__ __launch_bounds__(256) void mha_merge_kernel(MhaAttendArgs a, AttnCore c) {
   const int C4 = a.d_h / 4;
   const int64_t n = (int64_t)a.B * a.n_h * a.Lq * C4;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -46,24 +45,10 @@ __global__ __launch_bounds__(256) void mha_merge_kernel(MhaAttendArgs a, const f
   r /= a.Lq;
   const int h = (int)(r % a.n_h);
   const int b = (int)(r / a.n_h);
-  const int64_t R = (int64_t)a.n_h * lq_pad;
-  const int64_t row = (int64_t)h * lq_pad + tok;
-  float M = -INFINITY;
-  for (int sp = 0; sp < n_split; ++sp) M = fmaxf(M, ml[(((int64_t)sp * a.B + b) * R + row) * 2]);
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  float L = 0.0f;
-  for (int sp = 0; sp < n_split; ++sp) {
-    const int64_t prow = ((int64_t)sp * a.B + b) * R + row;
-    const float ms = ml[prow * 2];
-    if (ms == -INFINITY) continue;
-    const float wgt = exp2f(ms - M);
-    L += wgt * ml[prow * 2 + 1];
-    const f32x4 x = *reinterpret_cast<const f32x4*>(opart + prow * a.d_h + 4 * c4);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) acc[t] += wgt * x[t];
-  }
-  const float inv = 1.0f / L;
-  f32x4 o = {acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+  const int row = h * c.rows_per_head + tok;
+  float acc[4];
+  merge_row_partials(c, a.d_h, b, row, 4 * c4, 4, acc);
+  f32x4 o = {acc[0], acc[1], acc[2], acc[3]};
   *reinterpret_cast<f32x4*>(a.out + (((size_t)b * a.Lq + tok) * a.n_h + h) * a.d_h + 4 * c4) = o;
 }
 
@@ -144,8 +129,8 @@ bool mha_attend_bf16_supported(int d_h) { return d_h == 128; }
 
 namespace {
 template <typename E>
-hipError_t launch_mha_typed(const MhaAttendArgs& a, float* opart, float* ml, int n_split,
-                            int keys_per_split, hipStream_t s) {
+hipError_t launch_mha_typed(const MhaAttendArgs& a, float* opart, float* ml, const Schedule& sched,
+                            hipStream_t s) {
   const int lq_pad = mha_lq_pad(a.Lq);
   {
     const int64_t n = (int64_t)a.B * a.Lq * a.n_h * (a.d_h / 2);
@@ -154,31 +139,29 @@ hipError_t launch_mha_typed(const MhaAttendArgs& a, float* opart, float* ml, int
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  AttnCore c;
+  c.qrows = a.qrot;
+  c.ring = a.ring;
+  c.opart = opart;
+  c.ml = ml;
+  c.ring_rows = a.ring_rows;
+  c.ring_stride = 2 * a.n_h * a.d_h;
+  c.k_off = 0;
+  c.v_off = a.n_h * a.d_h;
+  c.head_stride = a.d_h;
+  c.R = a.n_h * lq_pad;
+  c.rows_per_head = lq_pad;
+  c.valid_per_head = a.Lq;
+  c.B = a.B;
+  c.Lk = a.Lk;
+  c.sched = sched;
+  c.key_slot0 = a.key_slot0;
   {
-    AttnCore c;
-    c.qrows = a.qrot;
-    c.ring = a.ring;
-    c.opart = opart;
-    c.ml = ml;
-    c.ring_rows = a.ring_rows;
-    c.ring_stride = 2 * a.n_h * a.d_h;
-    c.k_off = 0;
-    c.v_off = a.n_h * a.d_h;
-    c.head_stride = a.d_h;
-    c.R = a.n_h * lq_pad;
-    c.rows_per_head = lq_pad;
-    c.valid_per_head = a.Lq;
-    c.B = a.B;
-    c.Lk = a.Lk;
-    c.n_split = n_split;
-    c.keys_per_split = keys_per_split;
-    c.key_slot0 = a.key_slot0;
-    dim3 grid((unsigned)(c.R / kDenseBlockRows), (unsigned)n_split, (unsigned)a.B);
     if (a.ev_start != nullptr) {
       hipError_t e = hipEventRecord(a.ev_start, s);
       if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((attn_core_kernel<E, 128, 128, kDenseRB, kDenseNW, false>), grid,
+    hipLaunchKernelGGL((attn_core_kernel<E, 128, 128, kDenseNW, false>), dim3(sched.n_blocks),
                        dim3(kDenseNW * 64), 0, s, c);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -189,8 +172,7 @@ hipError_t launch_mha_typed(const MhaAttendArgs& a, float* opart, float* ml, int
   }
   {
     const int64_t n = (int64_t)a.B * a.n_h * a.Lq * (a.d_h / 4);
-    hipLaunchKernelGGL(mha_merge_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a,
-                       (const float*)opart, (const float*)ml, n_split, lq_pad);
+    hipLaunchKernelGGL(mha_merge_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a, c);
     return hipGetLastError();
   }
 }
@@ -198,10 +180,23 @@ hipError_t launch_mha_typed(const MhaAttendArgs& a, float* opart, float* ml, int
 
 // The host carves the workspace into rotated queries (a.qrot), partial value
 // sums (opart) and per-row max/sum (ml).
-hipError_t launch_mha_attend_bf16_ws(const MhaAttendArgs& a, float* opart, float* ml, int n_split,
-                                     int keys_per_split, hipStream_t s) {
-  return a.cache_type == 2 ? launch_mha_typed<f16_t>(a, opart, ml, n_split, keys_per_split, s)
-                           : launch_mha_typed<bf16_t>(a, opart, ml, n_split, keys_per_split, s);
+hipError_t launch_mha_attend_bf16_ws(const MhaAttendArgs& a, float* opart, float* ml,
+                                     const Schedule& sched, hipStream_t s) {
+  return a.cache_type == 2 ? launch_mha_typed<f16_t>(a, opart, ml, sched, s)
+                           : launch_mha_typed<bf16_t>(a, opart, ml, sched, s);
+}
+
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
 }
 
 hipError_t launch_mha_attend_f32(const MhaAttendArgs& a, hipStream_t s) {

@@ -20,6 +20,8 @@ namespace mla {
 
 namespace {
 
+constexpr int kCoreWaves = kCoreBlockRows / 32;
+
 // ---------------------------------------------------------------------------
 // 1. query prologue
 // ---------------------------------------------------------------------------
@@ -98,21 +100,21 @@ __global__ __launch_bounds__(64) void epilogue_bf16_kernel(AttendArgs a) {
   const int tok = blockIdx.x * 32 + lo;
   const bool valid = tok < a.Lq;
   const int R = a.Lq * a.n_h;
-  const size_t row = (size_t)(valid ? tok : 0) * a.n_h + h;
+  const int row = (valid ? tok : 0) * a.n_h + h;
 
+  // log-sum-exp merge of the partials this row's row group left behind
+  const int n_part = sched_group_slots(a.sched, b * a.sched.n_rg + row / kCoreBlockRows);
   float M = -INFINITY;
-  for (int sp = 0; sp < a.n_split; ++sp) M = fmaxf(M, a.ml[(((size_t)sp * a.B + b) * R + row) * 2]);
+  for (int k = 0; k < n_part; ++k) M = fmaxf(M, a.ml[(((size_t)k * a.B + b) * R + row) * 2]);
   float v[NKS][8];
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
     for (int t = 0; t < 8; ++t) v[ks][t] = 0.0f;
   float L = 0.0f;
-  for (int sp = 0; sp < a.n_split; ++sp) {
-    const size_t prow = ((size_t)sp * a.B + b) * R + row;
-    const float ms = a.ml[prow * 2];
-    if (ms == -INFINITY) continue;
-    const float wgt = exp2f(ms - M);
+  for (int k = 0; k < n_part; ++k) {
+    const size_t prow = ((size_t)k * a.B + b) * R + row;
+    const float wgt = exp2_fast(a.ml[prow * 2] - M);
     L += wgt * a.ml[prow * 2 + 1];
     const float* op = a.opart + prow * DC + 8 * hi;
 #pragma unroll
@@ -257,7 +259,6 @@ hipError_t launch_dc(const AttendArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   {
-    constexpr int RB = 1, NW = 8;
     AttnCore c;
     c.qrows = a.qcat;
     c.ring = a.ring;
@@ -273,17 +274,14 @@ hipError_t launch_dc(const AttendArgs& a, hipStream_t s) {
     c.valid_per_head = c.R;
     c.B = a.B;
     c.Lk = a.Lk;
-    c.n_split = a.n_split;
-    c.keys_per_split = a.keys_per_split;
+    c.sched = a.sched;
     c.key_slot0 = a.key_slot0;
-    constexpr int BR = core_block_rows<RB, NW>();
-    dim3 grid((unsigned)((c.R + BR - 1) / BR), (unsigned)a.n_split, (unsigned)a.B);
     if (a.ev_start != nullptr) {
       hipError_t e = hipEventRecord(a.ev_start, s);
       if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((attn_core_kernel<E, DC + 32, DC, RB, NW, true>), grid, dim3(NW * 64), 0, s,
-                       c);
+    hipLaunchKernelGGL((attn_core_kernel<E, DC + 32, DC, kCoreWaves, true>), dim3(a.sched.n_blocks),
+                       dim3(kCoreWaves * 64), 0, s, c);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.ev_stop != nullptr) {

@@ -2,26 +2,33 @@
 // dense comparison path, for gfx950 MFMA (fp16 or bf16 operands, fp32 sums).
 //
 // Rows are prepared query rows (cache type, pre-scaled by log2(e)/sqrt(d));
-// keys are ring rows of the window.  A block of NW waves owns NW*32*RB rows
-// and one key range, which it walks in tiles of kKeyTile keys:
+// keys are ring rows of the window.  A block of NW = 8 waves owns row groups
+// of kCoreBlockRows rows (32 per wave) and walks key tiles of kKeyTile keys:
 //
+//  * Schedule (Schedule in mla_launch.h): whole row groups data-parallel
+//    while they last, the remainder balanced stream-K style with main blocks
+//    in key-tile lockstep and a short, L2-resident tail range shared by the
+//    spare blocks, so every compute unit gets the same work however the row
+//    count divides.  A block writes one partial (un-normalised value sums,
+//    running max, running sum) per row-group segment; the merge kernels
+//    combine a group's partials by log-sum-exp.
 //  * Key tiles move HBM -> LDS with gfx950's direct 16-byte loads
 //    (global_load_lds_dwordx4): each wave instruction fills one contiguous
 //    KiB of LDS, lane l writing bytes [16l, 16l+16).  Rows are padded by one
-//    16-byte chunk (no bank conflicts on the score reads); padding lanes are
-//    switched off.  Two tile buffers: the next tile streams in while the
-//    current one is consumed, with one barrier per tile.
-//  * Scores S^T[key][row] = sum_d K[key][d] Q[row][d] on 32x32x16 MFMA; the
-//    query fragments stay in registers for the whole key range.  In this
-//    orientation a lane owns one row (MFMA column): the row's running max and
-//    sum live in the lane, and one exchange with the other half-wave combines
-//    the two halves of the key tile.
+//    16-byte chunk; padding lanes are switched off.  Two tile buffers (two
+//    distinct LDS arrays, used alternately by an unrolled step pair so that
+//    every access names its buffer): the next tile streams in while the
+//    current one is consumed, one barrier per tile.
+//  * Scores S^T[key][row] = sum_d K[key][d] Q[row][d] on 32x32x16 MFMA; a
+//    segment's query fragments stay in registers.  In this orientation a lane
+//    owns one row (MFMA column): the row's running max and sum live in the
+//    lane, and one exchange with the other half-wave covers the whole tile.
 //  * Values O^T[dim][row] += sum_key V^T[dim][key] P[row][key]: the V^T
 //    operand is read straight from the key-major tile with the LDS transpose
-//    read (ds_read_b64_tr_b16), so no transposed copy of V is ever stored.
+//    read (ds_read_b64_tr_b16), so no transposed copy of V is stored.
 //  * Online softmax in the exp2 domain with a lazy rescale: the running max
-//    is only raised (and O, l rescaled) when a new score exceeds it by more
-//    than 2^8, so most tiles skip the rescale; probabilities stay <= 256.
+//    is raised (and O, l rescaled) only when a score exceeds it by more than
+//    2^8, so most tiles skip the rescale; probabilities stay <= 256.
 //
 // Latent rows (SHARED_KV): K = [c | k^R] and V = c are one cached row, so the
 // value operand reads the first DV columns of the key tile.  Dense rows: K and
@@ -35,16 +42,18 @@ namespace mla {
 struct AttnCore {
   const void* qrows;     // [B][R][DQK] elements of the cache type
   const void* ring;      // [B][ring_rows][ring_stride]
-  float* opart;          // [n_split][B][R][DV]   un-normalised value sums
-  float* ml;             // [n_split][B][R][2]    running max (log2 units), sum
+  float* opart;          // [n_slots][B][R][DV]  un-normalised value sums
+  float* ml;             // [n_slots][B][R][2]   running max (log2 units), sum
   int64_t ring_rows;
   int ring_stride;       // elements per cached token row
   int k_off, v_off;      // offsets of K and V of head 0 inside a cached row
   int head_stride;       // offset step per head (0 for the shared latent row)
-  int R;                 // rows per batch element
+  int R;                 // rows per batch element (dense: a multiple of
+                         // kCoreBlockRows per head; latent: ragged)
   int rows_per_head;     // rows of one head (latent: R)
   int valid_per_head;    // rows of a head that are real (rest is padding)
-  int B, Lk, n_split, keys_per_split;
+  int B, Lk;
+  Schedule sched;
   int64_t key_slot0;     // ring slot of resident key 0
 };
 
@@ -68,7 +77,7 @@ __device__ __forceinline__ void global_to_lds16(const void* g, void* lds) {
 // Raise-the-max threshold of the lazy rescale (log2 units).
 constexpr float kRescaleThreshold = 8.0f;
 
-template <typename E, int DQK, int DV, int RB, int NW, bool SHARED_KV>
+template <typename E, int DQK, int DV, int NW, bool SHARED_KV>
 __global__ __launch_bounds__(NW * 64) void attn_core_kernel(AttnCore a) {
   typedef typename Elem<E>::v8 V8;
   constexpr int NKS = DQK / 16;               // MFMA depth steps of the score product
@@ -82,180 +91,199 @@ __global__ __launch_bounds__(NW * 64) void attn_core_kernel(AttnCore a) {
   constexpr int SPANS = KT * RCH / 64;        // 1-KiB direct-load spans per tile
   constexpr int TILE = KT * KSTR;             // elements per tile buffer
   static_assert(KT == 64, "one span per padded chunk column needs 64-key tiles");
+  static_assert(NW * 32 == kCoreBlockRows, "block rows are fixed by the schedule");
   static_assert(!SHARED_KV || DV <= DQK, "shared rows hold V inside K");
 
-  __shared__ __attribute__((aligned(1024))) E kt[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) E kt0[TILE];
+  __shared__ __attribute__((aligned(1024))) E kt1[TILE];
 
+  const Schedule& sc = a.sched;
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63, lo = l & 31, hi = l >> 5;
-  const int b = blockIdx.z, split = blockIdx.y;
-  const int blk_row0 = blockIdx.x * (NW * 32 * RB);
-  const int row0 = blk_row0 + w * (32 * RB);
-  const int head = blk_row0 / a.rows_per_head;
-  const int k_begin = split * a.keys_per_split;
-  const int k_end = min(a.Lk, k_begin + a.keys_per_split);
+  const int g = blockIdx.x;
+  const int n_steps = sched_block_steps(sc, g);
 
-  V8 qf[RB][NKS];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int row = row0 + rb * 32 + lo;
-    const bool ok = row < a.R && (row % a.rows_per_head) < a.valid_per_head;
-    const E* src = (const E*)a.qrows + ((size_t)b * a.R + (ok ? row : 0)) * DQK + 8 * hi;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) qf[rb][ks] = ok ? ld8<E>(src + 16 * ks) : zero8<E>();
-  }
-
-  f32x16 o[RB][NDT];
-  float m[RB], lsum[RB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    m[rb] = -INFINITY;
-    lsum[rb] = 0.0f;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[rb][dt][r] = 0.0f;
-  }
-
-  const E* ring = (const E*)a.ring + (size_t)b * a.ring_rows * a.ring_stride;
-  const int koff = a.k_off + head * a.head_stride;
-  const int voff = a.v_off + head * a.head_stride;
-
-  // Issue the direct loads of tile t0 into buffer `buf`.  Keys past the range
-  // re-load the last valid key (their scores are masked), so every LDS row a
-  // wave reads holds finite cache data.
-  auto load_tile = [&](int t0, int buf) {
+  // Issue the direct loads of key tile kt of batch element b into `dst`.  Keys
+  // past the window re-load the last key (their scores are masked), so every
+  // LDS row a wave reads holds finite cache data.
+  auto load_tile = [&](int b, int rg, int kt, E* dst) {
+    const E* ring = (const E*)a.ring + (size_t)b * a.ring_rows * a.ring_stride;
+    const int head = (rg * kCoreBlockRows) / a.rows_per_head;
+    const int koff = a.k_off + head * a.head_stride;
+    const int voff = a.v_off + head * a.head_stride;
 #pragma unroll
     for (int sp = w; sp < SPANS; sp += NW) {
       const int c = sp * 64 + l;
       const int key = c / RCH, q = c - (c / RCH) * RCH;
       if (q < CPK) {
-        int kg = min(t0 + key, k_end - 1);
+        const int kg = min(kt * KT + key, a.Lk - 1);
         int64_t slot = a.key_slot0 + kg;
         if (slot >= a.ring_rows) slot -= a.ring_rows;
         const E* src = ring + slot * a.ring_stride + (q < KCH ? koff + q * 8 : voff + (q - KCH) * 8);
-        global_to_lds16(src, kt + buf * TILE + sp * 512);
+        global_to_lds16(src, dst + sp * 512);
       }
     }
   };
 
-  if (k_begin < k_end) load_tile(k_begin, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
-  // lane-constant parts of the LDS addresses
+  // lane-constant parts of the transpose-read addresses
   const int tr_key = 4 * hi + ((l & 15) >> 2);           // key offset of this lane's row
   const int tr_col = 16 * ((l & 31) >> 4) + 4 * (l & 3);  // column offset in a 32-wide tile
 
-  int buf = 0;
-  for (int t0 = k_begin; t0 < k_end; t0 += KT, buf ^= 1) {
-    const bool more = t0 + KT < k_end;
-    if (more) load_tile(t0 + KT, buf ^ 1);
-    const E* tile = kt + buf * TILE;
+  V8 qf[NKS];
+  f32x16 o[NDT];
+  float m = -INFINITY, lsum = 0.0f;
+  int row = 0;
 
-    f32x16 s[RB][2];
+  // One step: `cur` holds the key tile of step i; prefetch step i+1 into `nxt`.
+  auto step = [&](int i, const E* cur, E* nxt) {
+    const StepInfo si = sched_decode(sc, g, i);
+    const int b = si.grp / sc.n_rg;
+    const int rg = si.grp - b * sc.n_rg;
+    const int kt = si.kt;
+
+    if (si.first) {  // new row-group segment: queries in, state reset
+      row = rg * kCoreBlockRows + w * 32 + lo;
+      const bool ok = row < a.R && (row % a.rows_per_head) < a.valid_per_head;
+      const E* src = (const E*)a.qrows + ((size_t)b * a.R + (ok ? row : 0)) * DQK + 8 * hi;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) qf[ks] = ok ? ld8<E>(src + 16 * ks) : zero8<E>();
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[dt][r] = 0.0f;
+      m = -INFINITY;
+      lsum = 0.0f;
+    }
+    if (i + 1 < n_steps) {
+      const StepInfo sn = sched_decode(sc, g, i + 1);
+      const int b1 = sn.grp / sc.n_rg;
+      load_tile(b1, sn.grp - b1 * sc.n_rg, sn.kt, nxt);
+    }
+
+    f32x16 sv[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
+      for (int r = 0; r < 16; ++r) sv[kb][r] = 0.0f;
+      const E* krow = cur + (kb * 32 + lo) * KSTR + 8 * hi;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[rb][kb][r] = 0.0f;
-      const E* krow = tile + (kb * 32 + lo) * KSTR + 8 * hi;
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const V8 ka = ld8<E>(krow + 16 * ks);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) s[rb][kb] = Elem<E>::mfma(ka, qf[rb][ks], s[rb][kb]);
-      }
+      for (int ks = 0; ks < NKS; ++ks) sv[kb] = Elem<E>::mfma(ld8<E>(krow + 16 * ks), qf[ks], sv[kb]);
     }
-    if (t0 + KT > k_end) {
+    const int t0 = kt * KT;
+    if (t0 + KT > a.Lk) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          if (t0 + kb * 32 + acc_row(r, hi) >= k_end) {
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb) s[rb][kb][r] = -INFINITY;
-          }
-        }
+        for (int r = 0; r < 16; ++r)
+          if (t0 + kb * 32 + acc_row(r, hi) >= a.Lk) sv[kb][r] = -INFINITY;
     }
 
-    V8 pf[RB][2][2];
+    float mx = -INFINITY;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      float mx = -INFINITY;
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sv[kb][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    // lazy rescale: raise the max only when a score passes it by > 2^8
+    if (__ballot(mx > m + kRescaleThreshold)) {
+      const float mnew = fmaxf(m, mx);
+      const float alpha = exp2_fast(m - mnew);
+      m = mnew;
+      lsum *= alpha;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[rb][kb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      // lazy rescale: raise the max only when a score passes it by > 2^8
-      if (__ballot(mx > m[rb] + kRescaleThreshold)) {
-        const float mnew = fmaxf(m[rb], mx);
-        const float alpha = exp2f(m[rb] - mnew);
-        m[rb] = mnew;
-        lsum[rb] *= alpha;
+      for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[rb][dt][r] *= alpha;
-      }
-      const float mc = m[rb];
-      float ps = 0.0f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = exp2f(s[rb][kb][r] - mc);
-          ps += p;
-          pf[rb][kb][r >> 3][r & 7] = Elem<E>::from(p);
-        }
-      lsum[rb] += ps;
+        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
     }
+    V8 pf[2][2];
+    float ps = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = exp2_fast(sv[kb][r] - m);
+        ps += p;
+        pf[kb][r >> 3][r & 7] = Elem<E>::from(p);
+      }
+    lsum += ps;
 
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        const E* vrow = tile + (kb * 32 + 16 * st + tr_key) * KSTR + VOFF + tr_col;
+        const E* vrow = cur + (kb * 32 + 16 * st + tr_key) * KSTR + VOFF + tr_col;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
           const i16x4 lo4 = lds_read_tr16(vrow + dt * 32);
           const i16x4 hi4 = lds_read_tr16(vrow + 8 * KSTR + dt * 32);
           const V8 va = __builtin_bit_cast(V8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) o[rb][dt] = Elem<E>::mfma(va, pf[rb][kb][st], o[rb][dt]);
+          o[dt] = Elem<E>::mfma(va, pf[kb][st], o[dt]);
         }
       }
 
+    if (si.last) {  // segment ends: write this block's partial
+      const int slot = si.slot;
+      const float ltot = lsum + __shfl_xor(lsum, 32);
+      if (row < a.R) {
+        const size_t prow = ((size_t)slot * a.B + b) * a.R + row;
+        float* op = a.opart + prow * DV;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int gg = 0; gg < 4; ++gg) {
+            f32x4 v = {o[dt][4 * gg], o[dt][4 * gg + 1], o[dt][4 * gg + 2], o[dt][4 * gg + 3]};
+            *reinterpret_cast<f32x4*>(op + dt * 32 + 8 * gg + 4 * hi) = v;
+          }
+        if (hi == 0) {
+          a.ml[prow * 2] = m;
+          a.ml[prow * 2 + 1] = ltot;
+        }
+      }
+    }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-  }
+  };
 
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int row = row0 + rb * 32 + lo;
-    if (row >= a.R) continue;
-    const float ltot = lsum[rb] + __shfl_xor(lsum[rb], 32);
-    const size_t prow = ((size_t)split * a.B + b) * a.R + row;
-    float* op = a.opart + prow * DV;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        f32x4 v = {o[rb][dt][4 * g], o[rb][dt][4 * g + 1], o[rb][dt][4 * g + 2],
-                   o[rb][dt][4 * g + 3]};
-        *reinterpret_cast<f32x4*>(op + dt * 32 + 8 * g + 4 * hi) = v;
-      }
-    if (hi == 0) {
-      a.ml[prow * 2] = m[rb];
-      a.ml[prow * 2 + 1] = ltot;
-    }
+  if (n_steps <= 0) return;
+  {
+    const StepInfo s0 = sched_decode(sc, g, 0);
+    const int b = s0.grp / sc.n_rg;
+    load_tile(b, s0.grp - b * sc.n_rg, s0.kt, kt0);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int i = 0; i < n_steps; i += 2) {
+    step(i, kt0, kt1);
+    if (i + 1 < n_steps) step(i + 1, kt1, kt0);
   }
 }
 
-// Rows per block of the core kernel.
-template <int RB, int NW>
-constexpr int core_block_rows() { return NW * 32 * RB; }
+// Log-sum-exp merge of one row's partials into `acc` (n values from column
+// c0, n a multiple of 4): acc = sum_k w_k O_k / sum_k w_k l_k with
+// w_k = 2^(m_k - max_k m_k).
+__device__ __forceinline__ void merge_row_partials(const AttnCore& a, int DV, int b, int row,
+                                                   int c0, int n, float* acc) {
+  const Schedule& sc = a.sched;
+  const int n_part = sched_group_slots(sc, b * sc.n_rg + row / kCoreBlockRows);
+  float M = -INFINITY;
+  for (int k = 0; k < n_part; ++k) M = fmaxf(M, a.ml[(((size_t)k * a.B + b) * a.R + row) * 2]);
+  for (int i = 0; i < n; ++i) acc[i] = 0.0f;
+  float L = 0.0f;
+  for (int k = 0; k < n_part; ++k) {
+    const size_t prow = ((size_t)k * a.B + b) * a.R + row;
+    const float wgt = exp2_fast(a.ml[prow * 2] - M);
+    L += wgt * a.ml[prow * 2 + 1];
+    const float* op = a.opart + prow * DV + c0;
+    for (int i = 0; i < n; i += 4) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(op + i);
+      acc[i] += wgt * x[0];
+      acc[i + 1] += wgt * x[1];
+      acc[i + 2] += wgt * x[2];
+      acc[i + 3] += wgt * x[3];
+    }
+  }
+  const float inv = 1.0f / L;
+  for (int i = 0; i < n; ++i) acc[i] *= inv;
+}
 
 }  // namespace mla

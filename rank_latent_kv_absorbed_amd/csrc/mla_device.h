@@ -86,6 +86,11 @@ __device__ __forceinline__ typename Elem<E>::v8 zero8() {
   return z;
 }
 
+// 2^x on the hardware exponential unit (v_exp_f32) without the library's
+// denormal-range fix-up: results below 2^-126 flush to zero, which softmax
+// weights tolerate (they are summed against a maximum weight of at least 1).
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Position (frame, row, column) of global token g.
 struct TokPos {
   int64_t f;

@@ -109,46 +109,75 @@ void commit_write(mla_cache* h, int64_t frame0, int32_t n_frames) {
   h->newest = frame0 + n_frames - 1;
 }
 
-// Key ranges per call: one range when the row blocks already cover the chip;
-// otherwise enough ranges for about two blocks per compute unit, keeping at
-// least four key tiles per range.
-int choose_splits(int64_t row_blocks, int64_t Lk) {
-  constexpr int64_t kCUs = 256;
-  if (row_blocks >= kCUs / 2) return 1;
-  int64_t s = (2 * kCUs + row_blocks - 1) / row_blocks;
-  const int64_t cap = Lk / (4 * mla::kKeyTile);
-  if (s > cap) s = cap;
-  return (int)(s < 1 ? 1 : s);
+// Schedule of the attention core (see mla::Schedule).  Default: one block per
+// compute unit, but no more blocks than leave each at least kMinStepsPerBlock
+// key tiles, so that partial writes stay small next to the work.  key_splits
+// > 0 instead gives every row group key_splits blocks' worth of work, cutting
+// its key range into about that many pieces.
+constexpr int64_t kMinStepsPerBlock = 8;
+
+mla::Schedule make_schedule(int64_t B, int64_t R, int64_t Lk, int32_t key_splits, int64_t cus) {
+  mla::Schedule s;
+  const int64_t n_rg = (R + mla::kCoreBlockRows - 1) / mla::kCoreBlockRows;
+  const int64_t n_kt = (Lk + mla::kKeyTile - 1) / mla::kKeyTile;
+  const int64_t groups = B * n_rg;
+  const int64_t total = groups * n_kt;
+  int64_t nb;
+  if (key_splits > 0) {
+    nb = groups * key_splits;
+  } else {
+    const int64_t by_work = (total + kMinStepsPerBlock - 1) / kMinStepsPerBlock;
+    nb = cus < by_work ? cus : by_work;
+  }
+  if (nb < 1) nb = 1;
+  const int64_t full = groups / nb;
+  const int64_t rem = groups - full * nb;
+  int64_t main_len = n_kt, tpb = 1;
+  if (rem > 0) {
+    main_len = (rem * n_kt + nb - 1) / nb;
+    if (main_len > n_kt) main_len = n_kt;
+    const int64_t tail = rem * (n_kt - main_len);
+    if (tail > 0) tpb = (tail + (nb - rem) - 1) / (nb - rem);
+  }
+  s.n_rg = (int)n_rg;
+  s.n_kt = (int)n_kt;
+  s.n_groups = (int)groups;
+  s.n_blocks = (int)nb;
+  s.full_rounds = (int)full;
+  s.rem = (int)rem;
+  s.main_len = (int)main_len;
+  s.tail_per_block = (int)tpb;
+  s.n_slots = (int)(main_len < n_kt ? 1 + (n_kt - main_len + tpb - 1) / tpb + 1 : 1);
+  return s;
+}
+
+int64_t window_keys(const mla_cache* h) {
+  const mla_layer_config& c = h->cfg;
+  return n_resident(h) > 0 ? n_resident(h) * tokens_per_frame(c)
+                           : (int64_t)c.window_frames * tokens_per_frame(c);
 }
 
 struct LatentLayout {
-  int splits;
-  int keys_per_split;
+  mla::Schedule sched;
   size_t qcat_off, opart_off, ml_off, total;
 };
 
 LatentLayout latent_layout(const mla_cache* h, int32_t Lq, int32_t key_splits) {
   const mla_layer_config& c = h->cfg;
   const int64_t R = (int64_t)Lq * c.n_heads;
-  const int64_t Lk = n_resident(h) > 0 ? n_resident(h) * tokens_per_frame(c)
-                                       : (int64_t)c.window_frames * tokens_per_frame(c);
   LatentLayout L;
-  const int64_t row_blocks = ((R + 255) / 256) * c.batch;
-  L.splits = key_splits > 0 ? key_splits : choose_splits(row_blocks, Lk);
-  int64_t kps = (Lk + L.splits - 1) / L.splits;
-  kps = (kps + mla::kKeyTile - 1) / mla::kKeyTile * mla::kKeyTile;
-  L.keys_per_split = (int)kps;
+  L.sched = make_schedule(c.batch, R, window_keys(h), key_splits, mla::device_cu_count());
   const size_t width = (size_t)(c.d_c + c.d_rope);
+  const size_t slots = (size_t)L.sched.n_slots;
   L.qcat_off = 0;
   L.opart_off = round_up((size_t)c.batch * R * width * 2, kAlign);
-  L.ml_off = L.opart_off + round_up((size_t)L.splits * c.batch * R * c.d_c * 4, kAlign);
-  L.total = L.ml_off + round_up((size_t)L.splits * c.batch * R * 2 * 4, kAlign);
+  L.ml_off = L.opart_off + round_up(slots * c.batch * R * c.d_c * 4, kAlign);
+  L.total = L.ml_off + round_up(slots * c.batch * R * 2 * 4, kAlign);
   return L;
 }
 
 struct DenseLayout {
-  int splits;
-  int keys_per_split;
+  mla::Schedule sched;
   int lq_pad;
   size_t qrot_off, opart_off, ml_off, total;
 };
@@ -159,16 +188,12 @@ DenseLayout dense_layout(const mla_cache* h, int32_t Lq) {
   DenseLayout L;
   L.lq_pad = mla::mha_lq_pad(Lq);
   const int64_t R = (int64_t)c.n_heads * L.lq_pad;
-  const int64_t Lk = n_resident(h) > 0 ? n_resident(h) * tokens_per_frame(c)
-                                       : (int64_t)c.window_frames * tokens_per_frame(c);
-  L.splits = choose_splits((R / 256) * c.batch, Lk);
-  int64_t kps = (Lk + L.splits - 1) / L.splits;
-  kps = (kps + mla::kKeyTile - 1) / mla::kKeyTile * mla::kKeyTile;
-  L.keys_per_split = (int)kps;
+  L.sched = make_schedule(c.batch, R, window_keys(h), 0, mla::device_cu_count());
+  const size_t slots = (size_t)L.sched.n_slots;
   L.qrot_off = 0;
   L.opart_off = round_up((size_t)c.batch * R * d_h * 2, kAlign);
-  L.ml_off = L.opart_off + round_up((size_t)L.splits * c.batch * R * d_h * 4, kAlign);
-  L.total = L.ml_off + round_up((size_t)L.splits * c.batch * R * 2 * 4, kAlign);
+  L.ml_off = L.opart_off + round_up(slots * c.batch * R * d_h * 4, kAlign);
+  L.total = L.ml_off + round_up(slots * c.batch * R * 2 * 4, kAlign);
   return L;
 }
 
@@ -382,8 +407,7 @@ mla_status mla_attend(mla_cache* h, const void* q, int64_t q_token0, int32_t Lq,
   a.qcat = ws + L.qcat_off;
   a.opart = (float*)(ws + L.opart_off);
   a.ml = (float*)(ws + L.ml_off);
-  a.n_split = L.splits;
-  a.keys_per_split = L.keys_per_split;
+  a.sched = L.sched;
   return launch_status(mla::launch_attend_bf16(a, s));
 }
 
@@ -432,8 +456,7 @@ mla_status mha_attend(mla_cache* h, const void* q, int64_t q_token0, int32_t Lq,
   char* ws = (char*)workspace;
   a.qrot = ws + L.qrot_off;
   return launch_status(mla::launch_mha_attend_bf16_ws(a, (float*)(ws + L.opart_off),
-                                                      (float*)(ws + L.ml_off), L.splits,
-                                                      L.keys_per_split, s));
+                                                      (float*)(ws + L.ml_off), L.sched, s));
 }
 
 mla_status mla_cache_set_profile_events(mla_cache* h, void* start, void* stop) {

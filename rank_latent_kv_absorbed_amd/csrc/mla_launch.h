@@ -40,6 +40,109 @@ struct CacheWriteArgs {
   RopeTable rope;
 };
 
+// Rows per block of the attention core (8 waves x 32 rows).
+constexpr int kCoreBlockRows = 256;
+
+#if defined(__HIPCC__)
+#define MLA_HD __host__ __device__
+#else
+#define MLA_HD
+#endif
+
+// Work schedule of the attention core over (row group, key tile) steps, where a
+// group is one batch element's block of kCoreBlockRows rows:
+//  * data-parallel rounds: while there are at least n_blocks groups left, each
+//    block takes whole groups (all key tiles), all blocks in key-tile lockstep;
+//  * the remaining `rem` groups (rem < n_blocks) are balanced stream-K style:
+//    group j's "main" block (block j) walks key tiles [0, main_len) in lockstep
+//    with the other main blocks, and the tail tiles [main_len, n_kt) of all
+//    remaining groups - a short key range that stays L2-resident - are cut into
+//    contiguous runs of tail_per_block steps for blocks rem .. n_blocks-1.
+// A group whose tiles span several blocks leaves one partial (value sums, max,
+// sum) per block, merged exactly by log-sum-exp: slot 0 = main block, slots
+// 1.. = tail blocks in order.
+struct Schedule {
+  int n_rg;             // row groups per batch element
+  int n_kt;             // key tiles in the window
+  int n_groups;         // batch * n_rg
+  int n_blocks;
+  int full_rounds;      // data-parallel rounds of whole groups
+  int rem;              // groups left for the balanced part
+  int main_len;         // key tiles a remaining group's main block walks
+  int tail_per_block;   // tail steps per tail block (>= 1)
+  int n_slots;          // partial slots to provide per group (upper bound)
+};
+
+struct StepInfo {
+  int grp, kt, slot;
+  bool first, last;     // first / last step of this block's segment of grp
+};
+
+// Tail blocks (index into rem..n_blocks-1) touching remaining group j.
+MLA_HD inline int sched_tail_first(const Schedule& s, int j) {
+  return j * (s.n_kt - s.main_len) / s.tail_per_block;
+}
+MLA_HD inline int sched_tail_last(const Schedule& s, int j) {
+  return ((j + 1) * (s.n_kt - s.main_len) - 1) / s.tail_per_block;
+}
+
+// Steps block g executes.
+MLA_HD inline int sched_block_steps(const Schedule& s, int g) {
+  int n = s.full_rounds * s.n_kt;
+  if (s.rem > 0) {
+    if (g < s.rem) {
+      n += s.main_len;
+    } else {
+      const int tail = s.rem * (s.n_kt - s.main_len);
+      const int t0 = (g - s.rem) * s.tail_per_block;
+      const int t1 = t0 + s.tail_per_block < tail ? t0 + s.tail_per_block : tail;
+      n += t1 > t0 ? t1 - t0 : 0;
+    }
+  }
+  return n;
+}
+
+// Step i (0 <= i < sched_block_steps(s, g)) of block g.
+MLA_HD inline StepInfo sched_decode(const Schedule& s, int g, int i) {
+  StepInfo r;
+  const int dp = s.full_rounds * s.n_kt;
+  if (i < dp) {
+    r.grp = g + (i / s.n_kt) * s.n_blocks;
+    r.kt = i % s.n_kt;
+    r.slot = 0;
+    r.first = r.kt == 0;
+    r.last = r.kt == s.n_kt - 1;
+    return r;
+  }
+  const int i2 = i - dp;
+  const int base = s.full_rounds * s.n_blocks;
+  if (g < s.rem) {
+    r.grp = base + g;
+    r.kt = i2;
+    r.slot = 0;
+    r.first = i2 == 0;
+    r.last = i2 == s.main_len - 1;
+    return r;
+  }
+  const int tl = s.n_kt - s.main_len;
+  const int t = (g - s.rem) * s.tail_per_block + i2;
+  const int j = t / tl;
+  r.grp = base + j;
+  r.kt = s.main_len + (t - j * tl);
+  r.slot = 1 + (g - s.rem) - sched_tail_first(s, j);
+  r.first = i2 == 0 || r.kt == s.main_len;
+  r.last = i2 == sched_block_steps(s, g) - dp - 1 || r.kt == s.n_kt - 1;
+  return r;
+}
+
+// Partials left for group grp (its slots are 0 .. count-1).
+MLA_HD inline int sched_group_slots(const Schedule& s, int grp) {
+  const int base = s.full_rounds * s.n_blocks;
+  if (grp < base || s.main_len >= s.n_kt) return 1;
+  const int j = grp - base;
+  return 1 + sched_tail_last(s, j) - sched_tail_first(s, j) + 1;
+}
+
 // Absorbed latent attention.
 struct AttendArgs {
   const void* q;          // [B][Lq][n_h][d_nope + d_rope]
@@ -56,8 +159,7 @@ struct AttendArgs {
   int64_t ring_rows;
   int64_t key_slot0;      // ring slot of resident key 0
   int Lk;                 // resident keys
-  int n_split;
-  int keys_per_split;     // multiple of the key tile
+  Schedule sched;
   int cache_type;         // 1 = bf16, 2 = fp16 (2-byte path); inputs are bf16
   float qscale;           // log2(e) / sqrt(d_nope + d_rope)
   hipEvent_t ev_start;    // optional: recorded right before / after the core kernel
@@ -95,11 +197,14 @@ hipError_t launch_attend_bf16(const AttendArgs& a, hipStream_t s);
 hipError_t launch_attend_f32(const AttendArgs& a, hipStream_t s);
 bool attend_bf16_supported(int d_c, int d_rope, int d_nope, int d_v);
 
-// Dense path: rotated queries go to a.qrot ([B][n_h * mha_lq_pad(Lq)][d_h]
-// bf16); opart/ml hold per-key-range partials as in the latent path.
+// Dense path: rotated queries go to a.qrot ([B][n_h * mha_lq_pad(Lq)][d_h]);
+// opart/ml hold per-slot partials as in the latent path.
 int mha_lq_pad(int Lq);
-hipError_t launch_mha_attend_bf16_ws(const MhaAttendArgs& a, float* opart, float* ml, int n_split,
-                                     int keys_per_split, hipStream_t s);
+hipError_t launch_mha_attend_bf16_ws(const MhaAttendArgs& a, float* opart, float* ml,
+                                     const Schedule& sched, hipStream_t s);
+
+// Compute units of the current device (queried once per device).
+int device_cu_count();
 hipError_t launch_mha_attend_f32(const MhaAttendArgs& a, hipStream_t s);
 bool mha_attend_bf16_supported(int d_h);
 

@@ -9,7 +9,7 @@ namespace {
 mla::CacheWriteArgs g_write;
 mla::AttendArgs g_attend;
 mla::MhaAttendArgs g_mha;
-int g_mha_splits = 0, g_mha_kps = 0;
+mla::Schedule g_mha_sched;
 int g_kind = 0;  // 1 write bf16, 2 write f32, 3 attend bf16, 4 attend f32, 5 mha bf16, 6 mha f32
 int g_count = 0;
 int g_fail = 0;
@@ -33,16 +33,16 @@ bool attend_bf16_supported(int d_c, int d_rope, int d_nope, int d_v) {
          d_v % 32 == 0 && d_v > 0;
 }
 bool mha_attend_bf16_supported(int d_h) { return d_h == 128; }
-int mha_lq_pad(int Lq) { return (Lq + 127) / 128 * 128; }
+int mha_lq_pad(int Lq) { return (Lq + kCoreBlockRows - 1) / kCoreBlockRows * kCoreBlockRows; }
+int device_cu_count() { return 256; }
 hipError_t launch_cache_write_bf16(const CacheWriteArgs& a, hipStream_t) { g_write = a; return rec(1); }
 hipError_t launch_cache_write_f32(const CacheWriteArgs& a, hipStream_t) { g_write = a; return rec(2); }
 hipError_t launch_attend_bf16(const AttendArgs& a, hipStream_t) { g_attend = a; return rec(3); }
 hipError_t launch_attend_f32(const AttendArgs& a, hipStream_t) { g_attend = a; return rec(4); }
-hipError_t launch_mha_attend_bf16_ws(const MhaAttendArgs& a, float*, float*, int n_split,
-                                     int kps, hipStream_t) {
+hipError_t launch_mha_attend_bf16_ws(const MhaAttendArgs& a, float*, float*, const Schedule& sc,
+                                     hipStream_t) {
   g_mha = a;
-  g_mha_splits = n_split;
-  g_mha_kps = kps;
+  g_mha_sched = sc;
   return rec(5);
 }
 hipError_t launch_mha_attend_f32(const MhaAttendArgs& a, hipStream_t) { g_mha = a; return rec(6); }
@@ -59,17 +59,33 @@ void fake_write_info(long long* o) {
                      a.rot_end, a.rot_group, a.w_split, a.hidden};
   memcpy(o, v, sizeof(v));
 }
-// key_slot0, Lk, n_split, keys_per_split, B, Lq, q_token0, ring_rows, n_h, d_c
+// key_slot0, Lk, B, Lq, q_token0, ring_rows, n_h, d_c, then the schedule:
+// n_rg, n_kt, n_groups, n_blocks, full_rounds, rem, main_len, tail_per_block, n_slots
 void fake_attend_info(long long* o) {
   const mla::AttendArgs& a = g_attend;
-  long long v[10] = {a.key_slot0, a.Lk, a.n_split, a.keys_per_split, a.B, a.Lq, a.q_token0,
-                     a.ring_rows, a.n_h, a.d_c};
+  const mla::Schedule& s = a.sched;
+  long long v[17] = {a.key_slot0, a.Lk, a.B, a.Lq, a.q_token0, a.ring_rows, a.n_h, a.d_c,
+                     s.n_rg, s.n_kt, s.n_groups, s.n_blocks, s.full_rounds, s.rem, s.main_len,
+                     s.tail_per_block, s.n_slots};
   memcpy(o, v, sizeof(v));
 }
+// The last attend's schedule as the kernels decode it.
+int fake_sched_steps(int g) { return mla::sched_block_steps(g_attend.sched, g); }
+void fake_sched_decode(int g, int i, int* o) {
+  const mla::StepInfo si = mla::sched_decode(g_attend.sched, g, i);
+  o[0] = si.grp;
+  o[1] = si.kt;
+  o[2] = si.slot;
+  o[3] = si.first;
+  o[4] = si.last;
+}
+int fake_sched_group_slots(int grp) { return mla::sched_group_slots(g_attend.sched, grp); }
 float fake_attend_qscale() { return g_attend.qscale; }
-// key_slot0, Lk, n_split, keys_per_split, Lq, q_token0
+// key_slot0, Lk, Lq, q_token0, n_rg, n_kt, n_blocks, n_slots
 void fake_mha_info(long long* o) {
-  long long v[6] = {g_mha.key_slot0, g_mha.Lk, g_mha_splits, g_mha_kps, g_mha.Lq, g_mha.q_token0};
+  const mla::Schedule& s = g_mha_sched;
+  long long v[8] = {g_mha.key_slot0, g_mha.Lk, g_mha.Lq, g_mha.q_token0, s.n_rg, s.n_kt,
+                    s.n_blocks, s.n_slots};
   memcpy(o, v, sizeof(v));
 }
 // which: 0 = last write, 1 = last attend, 2 = last dense attend

@@ -109,9 +109,44 @@ def _write_info(L):
 
 
 def _attend_info(L):
-    a = (ctypes.c_longlong * 10)()
+    a = (ctypes.c_longlong * 17)()
     L.fake_attend_info(a)
-    return list(a)
+    keys = ["key_slot0", "Lk", "B", "Lq", "q_token0", "ring_rows", "n_h", "d_c", "n_rg", "n_kt",
+            "n_groups", "n_blocks", "full_rounds", "rem", "main_len", "tpb", "n_slots"]
+    return dict(zip(keys, list(a)))
+
+
+def check_schedule(L, info, R):
+    """Walk the last attend's schedule exactly as the kernel decodes it: every
+    (row group, key tile) step runs once; each block's steps form segments
+    flagged first/last; a group's segments use slots 0..k-1 with k the count
+    the merge reads, k <= the workspace's slot count; block work is balanced."""
+    n_rg, n_kt, nb = info["n_rg"], info["n_kt"], info["n_blocks"]
+    assert n_rg == -(-R // 256) and n_kt == -(-info["Lk"] // 64)
+    groups = info["B"] * n_rg
+    seen = np.zeros((groups, n_kt), np.int32)
+    slots = {}
+    out = (ctypes.c_int * 5)()
+    steps = [L.fake_sched_steps(g) for g in range(nb)]
+    for g in range(nb):
+        prev = None
+        for i in range(steps[g]):
+            L.fake_sched_decode(g, i, out)
+            grp, kt, slot, first, last = list(out)
+            seen[grp, kt] += 1
+            if prev is None or prev[4]:
+                assert first, (g, i)
+                slots.setdefault(grp, set()).add(slot)
+            else:
+                assert not first and grp == prev[0] and kt == prev[1] + 1 and slot == prev[2]
+            prev = (grp, kt, slot, first, last)
+        assert prev is None or prev[4]
+    assert (seen == 1).all()
+    for grp in range(groups):
+        k = L.fake_sched_group_slots(grp)
+        assert slots[grp] == set(range(k)) and k <= info["n_slots"]
+    busy = [s for s in steps if s > 0]
+    assert max(busy) <= -(-groups * n_kt // nb) + 1
 
 
 P = ctypes.c_void_p
@@ -162,9 +197,9 @@ def test_rollout_schedule_matches_ring_model(sim):
                               P(FAKE_PTR), 0, P(FAKE_PTR), 1 << 40, None) == 0
         a = _attend_info(sim)
         slots = ring.resident_slots()
-        assert a[0] == slots[0] and a[1] == len(slots)
+        assert a["key_slot0"] == slots[0] and a["Lk"] == len(slots)
         # keys are the contiguous (mod ring) run of slots starting at key_slot0
-        np.testing.assert_array_equal((a[0] + np.arange(a[1])) % (21 * 1560), slots)
+        np.testing.assert_array_equal((a["key_slot0"] + np.arange(a["Lk"])) % (21 * 1560), slots)
         for f in (ring.oldest, ring.newest):
             for tau in (0, 777, 1559):
                 assert sim.mla_cache_slot(h, f, tau) == ring.slot(f, tau)
@@ -215,21 +250,29 @@ def test_attend_arguments_and_workspace(sim):
     assert sim.mla_attend(h, P(FAKE_PTR), 21 * 1560, 4680, P(FAKE_PTR), P(FAKE_PTR), P(FAKE_PTR),
                           0, P(ws), need, None) == 0
     a = _attend_info(sim)
-    assert a[0] == (3 % 21) * 1560 and a[1] == 21 * 1560 and a[5] == 4680 and a[6] == 21 * 1560
-    assert a[2] >= 1 and a[2] * a[3] >= a[1] and a[3] % 64 == 0
+    assert a["key_slot0"] == (3 % 21) * 1560 and a["Lk"] == 21 * 1560 and a["Lq"] == 4680
+    assert a["q_token0"] == 21 * 1560
     assert sim.fake_attend_qscale() == np.float32(math.log2(math.e) / math.sqrt(128))
-    # forced key splits: ranges are key-tile multiples covering the window
+    # full window, one sequence: 220 main blocks walk key tiles 0..439 in
+    # lockstep, 36 tail blocks share tiles 440..511 of every group, 440 each
+    assert (a["n_blocks"], a["n_rg"], a["n_kt"], a["rem"], a["main_len"], a["tpb"]) == \
+        (256, 220, 512, 220, 440, 440)
+    check_schedule(sim, a, R)
+    # forced key splits: every row group gets about that many pieces
     for s in (1, 2, 7, 64):
         need = sim.mla_attend_workspace_bytes(h, 8, s)
         assert sim.mla_attend(h, P(FAKE_PTR), 0, 8, P(FAKE_PTR), P(FAKE_PTR), P(FAKE_PTR), s,
                               P(ws), need, None) == 0
         a = _attend_info(sim)
-        assert a[2] == s and a[3] % 64 == 0 and a[2] * a[3] >= a[1] > (a[2] - 1) * a[3] - 64
-    # small queries get several key ranges by default; a large chunk gets one
-    sim.mla_attend(h, P(FAKE_PTR), 0, 1, P(FAKE_PTR), P(FAKE_PTR), P(FAKE_PTR), 0, P(ws), 1 << 40, None)
-    assert _attend_info(sim)[2] > 1
-    sim.mla_attend(h, P(FAKE_PTR), 0, 4680, P(FAKE_PTR), P(FAKE_PTR), P(FAKE_PTR), 0, P(ws), 1 << 40, None)
-    assert _attend_info(sim)[2] == 1
+        assert a["n_blocks"] == a["n_groups"] * s
+        check_schedule(sim, a, 8 * 12)
+    # small and large query counts spread over the compute units
+    for Lq in (1, 8, 100, 4680):
+        sim.mla_attend(h, P(FAKE_PTR), 0, Lq, P(FAKE_PTR), P(FAKE_PTR), P(FAKE_PTR), 0, P(ws),
+                       1 << 40, None)
+        a = _attend_info(sim)
+        check_schedule(sim, a, Lq * 12)
+        assert a["n_blocks"] == min(256, -(-a["n_groups"] * a["n_kt"] // 8))
 
 
 def test_wrong_kind_and_unsupported(sim):
