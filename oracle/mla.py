@@ -78,7 +78,8 @@ def round_to_f32(a):
 def round_to_f16(a):
     """Round float64 values to IEEE binary16 (NumPy's cast: nearest even,
     with binary16 subnormals and overflow to inf)."""
-    return np.asarray(a, dtype=np.float64).astype(np.float16).astype(np.float64)
+    with np.errstate(over="ignore"):  # overflow to inf is the intended result
+        return np.asarray(a, dtype=np.float64).astype(np.float16).astype(np.float64)
 
 
 def round_storage(a, dtype):

@@ -9,9 +9,6 @@ namespace mla {
 
 namespace {
 
-constexpr int kDenseNW = kCoreBlockRows / 32;
-constexpr int kDenseBlockRows = kCoreBlockRows;
-
 // q [B][Lq][n_h][d_h] -> qrot [B][n_h * Lq_pad][d_h] bf16 (head-major rows).
 template <typename E>
 __global__ __launch_bounds__(256) void mha_qprep_bf16_kernel(MhaAttendArgs a, int lq_pad) {
@@ -123,15 +120,14 @@ __global__ __launch_bounds__(256) void mha_attend_f32_kernel(MhaAttendArgs a) {
 
 }  // namespace
 
-int mha_lq_pad(int Lq) { return (Lq + kDenseBlockRows - 1) / kDenseBlockRows * kDenseBlockRows; }
-
 bool mha_attend_bf16_supported(int d_h) { return d_h == 128; }
 
 namespace {
 template <typename E>
 hipError_t launch_mha_typed(const MhaAttendArgs& a, float* opart, float* ml, const Schedule& sched,
                             hipStream_t s) {
-  const int lq_pad = mha_lq_pad(a.Lq);
+  const int br = sched.block_rows;
+  const int lq_pad = (a.Lq + br - 1) / br * br;
   {
     const int64_t n = (int64_t)a.B * a.Lq * a.n_h * (a.d_h / 2);
     hipLaunchKernelGGL(mha_qprep_bf16_kernel<E>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
@@ -161,8 +157,15 @@ hipError_t launch_mha_typed(const MhaAttendArgs& a, float* opart, float* ml, con
       hipError_t e = hipEventRecord(a.ev_start, s);
       if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((attn_core_kernel<E, 128, 128, kDenseNW, false>), dim3(sched.n_blocks),
-                       dim3(kDenseNW * 64), 0, s, c);
+    const dim3 grid((unsigned)sched.n_blocks);
+    if (br == 256 && sched.key_tile == 64)
+      hipLaunchKernelGGL((attn_core_kernel<E, 128, 128, 8, 64, false>), grid, dim3(512), 0, s, c);
+    else if (br == 128 && sched.key_tile == 32)
+      hipLaunchKernelGGL((attn_core_kernel<E, 128, 128, 4, 32, false>), grid, dim3(256), 0, s, c);
+    else if (br == 32 && sched.key_tile == 32)
+      hipLaunchKernelGGL((attn_core_kernel<E, 128, 128, 1, 32, false>), grid, dim3(64), 0, s, c);
+    else
+      return hipErrorInvalidValue;
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.ev_stop != nullptr) {

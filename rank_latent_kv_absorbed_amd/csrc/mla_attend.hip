@@ -12,24 +12,29 @@
 //               Each block covers one key range and writes un-normalised
 //               partials (O_lat, max, sum).
 //  3. epilogue: merges the key ranges by log-sum-exp, normalises, and applies
-//               W^V_up,h with bf16 MFMA on a hi/lo split of O_lat (keeps fp32
-//               accuracy), writing fp32 output.
+//               W^V_up,h, writing fp32 output.  Many rows: one lane per row,
+//               bf16 MFMA on a hi/lo split of O_lat (keeps fp32 accuracy).  A
+//               few rows with many key ranges each (small query chunks): one
+//               block per row, partials spread over the block, plain fp32.
 #include "mla_attn_core.h"
 
 namespace mla {
 
 namespace {
 
-constexpr int kCoreWaves = kCoreBlockRows / 32;
-
 // ---------------------------------------------------------------------------
 // 1. query prologue
 // ---------------------------------------------------------------------------
+// W^K_up,h is staged in LDS in its natural [d_nope][DC] layout; the MFMA
+// operand A[m = latent dim i][k = n] = W[n][i] comes out of it with the LDS
+// transpose read, which hands lane (i, half hi) the k-slots t = 0..7 as
+// n = 16 ks + 8 (t / 4) + 4 hi + t % 4.  The query operand uses the same
+// k-slot order: two 8-byte loads per step.
 template <typename E, int DC>
 __global__ __launch_bounds__(256) void qprep_bf16_kernel(AttendArgs a) {
   constexpr int NT = DC / 32;
-  extern __shared__ bf16_t wt[];  // W^K_up,h transposed: [DC][d_nope + 8]
-  const int wts = a.d_nope + 8;
+  constexpr int WSTR = DC + 8;                 // padded LDS row (elements)
+  extern __shared__ bf16_t wlds[];             // [d_nope][WSTR]
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63, lo = l & 31, hi = l >> 5;
   const int h = blockIdx.y, b = blockIdx.z;
@@ -40,26 +45,36 @@ __global__ __launch_bounds__(256) void qprep_bf16_kernel(AttendArgs a) {
   const bf16_t* wuk = (const bf16_t*)a.w_uk + (size_t)h * a.d_nope * DC;
   for (int c = tid; c < a.d_nope * (DC / 8); c += 256) {
     const int n = c / (DC / 8), i0 = (c % (DC / 8)) * 8;
-    bf16x8 v = ld_bf16x8(wuk + (size_t)n * DC + i0);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) wt[(i0 + j) * wts + n] = v[j];
+    *reinterpret_cast<bf16x8*>(wlds + n * WSTR + i0) = ld_bf16x8(wuk + (size_t)n * DC + i0);
   }
   __syncthreads();
 
   const int tok = blockIdx.x * 128 + w * 32 + lo;
   const bool valid = tok < a.Lq;
   const bf16_t* qrow =
-      (const bf16_t*)a.q + (((size_t)b * a.Lq + (valid ? tok : 0)) * a.n_h + h) * d_qk;
+      (const bf16_t*)a.q + (((size_t)b * a.Lq + (valid ? tok : 0)) * a.n_h + h) * d_qk + 4 * hi;
+  const int tr_key = 4 * hi + ((l & 15) >> 2);
+  const int tr_col = 16 * ((l & 31) >> 4) + 4 * (l & 3);
   f32x16 acc[NT];
 #pragma unroll
   for (int it = 0; it < NT; ++it)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[it][r] = 0.0f;
   for (int k0 = 0; k0 < a.d_nope; k0 += 16) {
-    bf16x8 bq = valid ? ld_bf16x8(qrow + k0 + 8 * hi) : zero_bf16x8();
+    bf16x8 bq = zero_bf16x8();
+    if (valid) {
+      const bf16x4 q0 = *reinterpret_cast<const bf16x4*>(qrow + k0);
+      const bf16x4 q1 = *reinterpret_cast<const bf16x4*>(qrow + k0 + 8);
+      bq = __builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    const bf16_t* wrow = wlds + (k0 + tr_key) * WSTR + tr_col;
 #pragma unroll
-    for (int it = 0; it < NT; ++it)
-      acc[it] = mfma32(ld_bf16x8(wt + (it * 32 + lo) * wts + k0 + 8 * hi), bq, acc[it]);
+    for (int it = 0; it < NT; ++it) {
+      const i16x4 lo4 = lds_read_tr16(wrow + it * 32);
+      const i16x4 hi4 = lds_read_tr16(wrow + 8 * WSTR + it * 32);
+      const bf16x8 wa = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+      acc[it] = mfma32(wa, bq, acc[it]);
+    }
   }
   E* out = (E*)a.qcat + ((size_t)b * R + (size_t)tok * a.n_h + h) * width;
   if (valid) {
@@ -103,7 +118,7 @@ __global__ __launch_bounds__(64) void epilogue_bf16_kernel(AttendArgs a) {
   const int row = (valid ? tok : 0) * a.n_h + h;
 
   // log-sum-exp merge of the partials this row's row group left behind
-  const int n_part = sched_group_slots(a.sched, b * a.sched.n_rg + row / kCoreBlockRows);
+  const int n_part = sched_group_slots(a.sched, b * a.sched.n_rg + row / a.sched.block_rows);
   float M = -INFINITY;
   for (int k = 0; k < n_part; ++k) M = fmaxf(M, a.ml[(((size_t)k * a.B + b) * R + row) * 2]);
   float v[NKS][8];
@@ -160,6 +175,84 @@ __global__ __launch_bounds__(64) void epilogue_bf16_kernel(AttendArgs a) {
         *reinterpret_cast<f32x4*>(out + vt * 32 + 8 * g + 4 * hi) = o4;
       }
     }
+  }
+}
+
+// Few-row variant: one 256-thread block per (token, head) row.  Thread
+// (column chunk c, slot lane j) sums the partials j, j + LANES, ... of four
+// columns; the lanes are added through LDS, normalised, and the W^V_up,h
+// product runs in plain fp32 with one output dimension per thread.
+template <int DC>
+__global__ __launch_bounds__(256) void epilogue_rows_kernel(AttendArgs a) {
+  constexpr int C4 = DC / 4;       // 4-column chunks of a partial row
+  constexpr int LANES = 256 / C4;  // slot lanes
+  __shared__ float red[256];
+  __shared__ float part[LANES][DC];
+  __shared__ float olat[DC];
+  const int tid = threadIdx.x;
+  const int row = blockIdx.x, b = blockIdx.y;  // row = tok * n_h + h
+  const int R = a.Lq * a.n_h;
+  const int tok = row / a.n_h, h = row - tok * a.n_h;
+  const int n_part = sched_group_slots(a.sched, b * a.sched.n_rg + row / a.sched.block_rows);
+  auto prow_of = [&](int k) { return ((size_t)k * a.B + b) * R + row; };
+
+  float mx = -INFINITY;
+  for (int k = tid; k < n_part; k += 256) mx = fmaxf(mx, a.ml[prow_of(k) * 2]);
+  red[tid] = mx;
+  __syncthreads();
+  for (int st = 128; st > 0; st >>= 1) {
+    if (tid < st) red[tid] = fmaxf(red[tid], red[tid + st]);
+    __syncthreads();
+  }
+  const float M = red[0];
+  __syncthreads();
+  float ls = 0.0f;
+  for (int k = tid; k < n_part; k += 256) {
+    const size_t pr = prow_of(k);
+    ls += exp2_fast(a.ml[pr * 2] - M) * a.ml[pr * 2 + 1];
+  }
+  red[tid] = ls;
+  __syncthreads();
+  for (int st = 128; st > 0; st >>= 1) {
+    if (tid < st) red[tid] += red[tid + st];
+    __syncthreads();
+  }
+  const float inv = 1.0f / red[0];
+
+  const int c4 = tid % C4, j = tid / C4;
+  if (j < LANES) {
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int k = j; k < n_part; k += LANES) {
+      const size_t pr = prow_of(k);
+      const float wgt = exp2_fast(a.ml[pr * 2] - M);
+      const f32x4 x = *reinterpret_cast<const f32x4*>(a.opart + pr * DC + 4 * c4);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[t] += wgt * x[t];
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) part[j][4 * c4 + t] = acc[t];
+  }
+  __syncthreads();
+  for (int i = tid; i < DC; i += 256) {
+    float sum = 0.0f;
+#pragma unroll
+    for (int jj = 0; jj < LANES; ++jj) sum += part[jj][i];
+    olat[i] = sum * inv;
+  }
+  __syncthreads();
+
+  const bf16_t* wuv = (const bf16_t*)a.w_uv + (size_t)h * a.d_v * DC;
+  float* out = a.out + (((size_t)b * a.Lq + tok) * a.n_h + h) * a.d_v;
+  for (int v = tid; v < a.d_v; v += 256) {
+    const bf16_t* wr = wuv + (size_t)v * DC;
+    float sum = 0.0f;
+#pragma unroll 4
+    for (int i = 0; i < DC; i += 8) {
+      const bf16x8 w8 = ld_bf16x8(wr + i);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) sum = fmaf((float)w8[t], olat[i + t], sum);
+    }
+    out[v] = sum;
   }
 }
 
@@ -249,10 +342,25 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(AttendArgs a) {
   }
 }
 
+// Core launch for the schedule's shape (block rows, key tile).
+template <typename E, int DC>
+hipError_t launch_core(const AttnCore& c, hipStream_t s) {
+  const dim3 grid((unsigned)c.sched.n_blocks);
+  if (c.sched.block_rows == 256 && c.sched.key_tile == 64)
+    hipLaunchKernelGGL((attn_core_kernel<E, DC + 32, DC, 8, 64, true>), grid, dim3(512), 0, s, c);
+  else if (c.sched.block_rows == 128 && c.sched.key_tile == 32)
+    hipLaunchKernelGGL((attn_core_kernel<E, DC + 32, DC, 4, 32, true>), grid, dim3(256), 0, s, c);
+  else if (c.sched.block_rows == 32 && c.sched.key_tile == 32)
+    hipLaunchKernelGGL((attn_core_kernel<E, DC + 32, DC, 1, 32, true>), grid, dim3(64), 0, s, c);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
 template <typename E, int DC>
 hipError_t launch_dc(const AttendArgs& a, hipStream_t s) {
   {
-    const size_t lds = (size_t)DC * (a.d_nope + 8) * sizeof(bf16_t);
+    const size_t lds = (size_t)a.d_nope * (DC + 8) * sizeof(bf16_t);
     dim3 grid((unsigned)((a.Lq + 127) / 128), (unsigned)a.n_h, (unsigned)a.B);
     hipLaunchKernelGGL((qprep_bf16_kernel<E, DC>), grid, dim3(256), lds, s, a);
     hipError_t e = hipGetLastError();
@@ -280,14 +388,17 @@ hipError_t launch_dc(const AttendArgs& a, hipStream_t s) {
       hipError_t e = hipEventRecord(a.ev_start, s);
       if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((attn_core_kernel<E, DC + 32, DC, kCoreWaves, true>), dim3(a.sched.n_blocks),
-                       dim3(kCoreWaves * 64), 0, s, c);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_core<E, DC>(c, s);
     if (e != hipSuccess) return e;
     if (a.ev_stop != nullptr) {
       e = hipEventRecord(a.ev_stop, s);
       if (e != hipSuccess) return e;
     }
+  }
+  if (a.sched.block_rows < kCoreMaxBlockRows) {
+    hipLaunchKernelGGL(epilogue_rows_kernel<DC>, dim3((unsigned)(a.Lq * a.n_h), (unsigned)a.B),
+                       dim3(256), 0, s, a);
+    return hipGetLastError();
   }
   {
     dim3 grid((unsigned)((a.Lq + 31) / 32), (unsigned)a.n_h, (unsigned)a.B);

@@ -2,8 +2,11 @@
 // dense comparison path, for gfx950 MFMA (fp16 or bf16 operands, fp32 sums).
 //
 // Rows are prepared query rows (cache type, pre-scaled by log2(e)/sqrt(d));
-// keys are ring rows of the window.  A block of NW = 8 waves owns row groups
-// of kCoreBlockRows rows (32 per wave) and walks key tiles of kKeyTile keys:
+// keys are ring rows of the window.  A block of NW waves owns row groups of
+// 32 * NW rows (32 per wave) and walks key tiles of KT keys (CoreShape: 8 x 64
+// for many rows, narrower blocks on 32-key tiles for a few rows).  A wave whose
+// 32 rows are all padding still loads its share of each tile but skips the
+// arithmetic:
 //
 //  * Schedule (Schedule in mla_launch.h): whole row groups data-parallel
 //    while they last, the remainder balanced stream-K style with main blocks
@@ -48,8 +51,8 @@ struct AttnCore {
   int ring_stride;       // elements per cached token row
   int k_off, v_off;      // offsets of K and V of head 0 inside a cached row
   int head_stride;       // offset step per head (0 for the shared latent row)
-  int R;                 // rows per batch element (dense: a multiple of
-                         // kCoreBlockRows per head; latent: ragged)
+  int R;                 // rows per batch element (dense: a multiple of the
+                         // block rows per head; latent: ragged)
   int rows_per_head;     // rows of one head (latent: R)
   int valid_per_head;    // rows of a head that are real (rest is padding)
   int B, Lk;
@@ -77,21 +80,25 @@ __device__ __forceinline__ void global_to_lds16(const void* g, void* lds) {
 // Raise-the-max threshold of the lazy rescale (log2 units).
 constexpr float kRescaleThreshold = 8.0f;
 
-template <typename E, int DQK, int DV, int NW, bool SHARED_KV>
-__global__ __launch_bounds__(NW * 64) void attn_core_kernel(AttnCore a) {
+// Register budget: two waves per SIMD whatever the block size, so that narrow
+// blocks can share a compute unit.
+template <typename E, int DQK, int DV, int NW, int KT, bool SHARED_KV>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_core_kernel(AttnCore a) {
   typedef typename Elem<E>::v8 V8;
   constexpr int NKS = DQK / 16;               // MFMA depth steps of the score product
   constexpr int NDT = DV / 32;                // 32-wide tiles of the value product
-  constexpr int KT = kKeyTile;                // keys per LDS tile
+  constexpr int BR = NW * 32;                 // rows per row group
+  constexpr int NKB = KT / 32;                // 32-key blocks per tile
   constexpr int KCH = DQK / 8;                // 16-byte chunks of K per key
   constexpr int CPK = SHARED_KV ? KCH : KCH + DV / 8;  // chunks staged per key
   constexpr int RCH = CPK + 1;                // chunks per padded LDS row
   constexpr int KSTR = RCH * 8;               // padded LDS row stride (elements)
   constexpr int VOFF = SHARED_KV ? 0 : DQK;   // V columns inside an LDS row
-  constexpr int SPANS = KT * RCH / 64;        // 1-KiB direct-load spans per tile
+  constexpr int CHUNKS = KT * RCH;            // 16-byte chunks per tile
+  constexpr int SPANS = (CHUNKS + 63) / 64;   // 1-KiB direct-load spans per tile
   constexpr int TILE = KT * KSTR;             // elements per tile buffer
-  static_assert(KT == 64, "one span per padded chunk column needs 64-key tiles");
-  static_assert(NW * 32 == kCoreBlockRows, "block rows are fixed by the schedule");
+  static_assert(KT == 32 || KT == 64, "key tiles are one or two 32-key MFMA blocks");
   static_assert(!SHARED_KV || DV <= DQK, "shared rows hold V inside K");
 
   __shared__ __attribute__((aligned(1024))) E kt0[TILE];
@@ -108,14 +115,14 @@ __global__ __launch_bounds__(NW * 64) void attn_core_kernel(AttnCore a) {
   // LDS row a wave reads holds finite cache data.
   auto load_tile = [&](int b, int rg, int kt, E* dst) {
     const E* ring = (const E*)a.ring + (size_t)b * a.ring_rows * a.ring_stride;
-    const int head = (rg * kCoreBlockRows) / a.rows_per_head;
+    const int head = (rg * BR) / a.rows_per_head;
     const int koff = a.k_off + head * a.head_stride;
     const int voff = a.v_off + head * a.head_stride;
 #pragma unroll
     for (int sp = w; sp < SPANS; sp += NW) {
       const int c = sp * 64 + l;
       const int key = c / RCH, q = c - (c / RCH) * RCH;
-      if (q < CPK) {
+      if (c < CHUNKS && q < CPK) {
         const int kg = min(kt * KT + key, a.Lk - 1);
         int64_t slot = a.key_slot0 + kg;
         if (slot >= a.ring_rows) slot -= a.ring_rows;
@@ -133,6 +140,7 @@ __global__ __launch_bounds__(NW * 64) void attn_core_kernel(AttnCore a) {
   f32x16 o[NDT];
   float m = -INFINITY, lsum = 0.0f;
   int row = 0;
+  bool live = false;  // this wave's rows include a real one (wave-uniform)
 
   // One step: `cur` holds the key tile of step i; prefetch step i+1 into `nxt`.
   auto step = [&](int i, const E* cur, E* nxt) {
@@ -142,7 +150,9 @@ __global__ __launch_bounds__(NW * 64) void attn_core_kernel(AttnCore a) {
     const int kt = si.kt;
 
     if (si.first) {  // new row-group segment: queries in, state reset
-      row = rg * kCoreBlockRows + w * 32 + lo;
+      row = rg * BR + w * 32 + lo;
+      const int row0 = rg * BR + w * 32;  // rows of a wave never straddle a head
+      live = row0 < a.R && (row0 % a.rows_per_head) < a.valid_per_head;
       const bool ok = row < a.R && (row % a.rows_per_head) < a.valid_per_head;
       const E* src = (const E*)a.qrows + ((size_t)b * a.R + (ok ? row : 0)) * DQK + 8 * hi;
 #pragma unroll
@@ -160,86 +170,88 @@ __global__ __launch_bounds__(NW * 64) void attn_core_kernel(AttnCore a) {
       load_tile(b1, sn.grp - b1 * sc.n_rg, sn.kt, nxt);
     }
 
-    f32x16 sv[2];
+    if (live) {
+      f32x16 sv[NKB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sv[kb][r] = 0.0f;
-      const E* krow = cur + (kb * 32 + lo) * KSTR + 8 * hi;
+        for (int r = 0; r < 16; ++r) sv[kb][r] = 0.0f;
+        const E* krow = cur + (kb * 32 + lo) * KSTR + 8 * hi;
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) sv[kb] = Elem<E>::mfma(ld8<E>(krow + 16 * ks), qf[ks], sv[kb]);
-    }
-    const int t0 = kt * KT;
-    if (t0 + KT > a.Lk) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (t0 + kb * 32 + acc_row(r, hi) >= a.Lk) sv[kb][r] = -INFINITY;
-    }
-
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sv[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    // lazy rescale: raise the max only when a score passes it by > 2^8
-    if (__ballot(mx > m + kRescaleThreshold)) {
-      const float mnew = fmaxf(m, mx);
-      const float alpha = exp2_fast(m - mnew);
-      m = mnew;
-      lsum *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-    }
-    V8 pf[2][2];
-    float ps = 0.0f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = exp2_fast(sv[kb][r] - m);
-        ps += p;
-        pf[kb][r >> 3][r & 7] = Elem<E>::from(p);
+        for (int ks = 0; ks < NKS; ++ks) sv[kb] = Elem<E>::mfma(ld8<E>(krow + 16 * ks), qf[ks], sv[kb]);
       }
-    lsum += ps;
-
+      const int t0 = kt * KT;
+      if (t0 + KT > a.Lk) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const E* vrow = cur + (kb * 32 + 16 * st + tr_key) * KSTR + VOFF + tr_col;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          const i16x4 lo4 = lds_read_tr16(vrow + dt * 32);
-          const i16x4 hi4 = lds_read_tr16(vrow + 8 * KSTR + dt * 32);
-          const V8 va = __builtin_bit_cast(V8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-          o[dt] = Elem<E>::mfma(va, pf[kb][st], o[dt]);
-        }
+          for (int r = 0; r < 16; ++r)
+            if (t0 + kb * 32 + acc_row(r, hi) >= a.Lk) sv[kb][r] = -INFINITY;
       }
 
-    if (si.last) {  // segment ends: write this block's partial
-      const int slot = si.slot;
-      const float ltot = lsum + __shfl_xor(lsum, 32);
-      if (row < a.R) {
-        const size_t prow = ((size_t)slot * a.B + b) * a.R + row;
-        float* op = a.opart + prow * DV;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sv[kb][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      // lazy rescale: raise the max only when a score passes it by > 2^8
+      if (__ballot(mx > m + kRescaleThreshold)) {
+        const float mnew = fmaxf(m, mx);
+        const float alpha = exp2_fast(m - mnew);
+        m = mnew;
+        lsum *= alpha;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-          for (int gg = 0; gg < 4; ++gg) {
-            f32x4 v = {o[dt][4 * gg], o[dt][4 * gg + 1], o[dt][4 * gg + 2], o[dt][4 * gg + 3]};
-            *reinterpret_cast<f32x4*>(op + dt * 32 + 8 * gg + 4 * hi) = v;
+          for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+      }
+      V8 pf[NKB][2];
+      float ps = 0.0f;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = exp2_fast(sv[kb][r] - m);
+          ps += p;
+          pf[kb][r >> 3][r & 7] = Elem<E>::from(p);
+        }
+      lsum += ps;
+
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const E* vrow = cur + (kb * 32 + 16 * st + tr_key) * KSTR + VOFF + tr_col;
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) {
+            const i16x4 lo4 = lds_read_tr16(vrow + dt * 32);
+            const i16x4 hi4 = lds_read_tr16(vrow + 8 * KSTR + dt * 32);
+            const V8 va = __builtin_bit_cast(V8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+            o[dt] = Elem<E>::mfma(va, pf[kb][st], o[dt]);
           }
-        if (hi == 0) {
-          a.ml[prow * 2] = m;
-          a.ml[prow * 2 + 1] = ltot;
+        }
+
+      if (si.last) {  // segment ends: write this block's partial
+        const int slot = si.slot;
+        const float ltot = lsum + __shfl_xor(lsum, 32);
+        if (row < a.R) {
+          const size_t prow = ((size_t)slot * a.B + b) * a.R + row;
+          float* op = a.opart + prow * DV;
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int gg = 0; gg < 4; ++gg) {
+              f32x4 v = {o[dt][4 * gg], o[dt][4 * gg + 1], o[dt][4 * gg + 2], o[dt][4 * gg + 3]};
+              *reinterpret_cast<f32x4*>(op + dt * 32 + 8 * gg + 4 * hi) = v;
+            }
+          if (hi == 0) {
+            a.ml[prow * 2] = m;
+            a.ml[prow * 2 + 1] = ltot;
+          }
         }
       }
-    }
+    }  // live
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
@@ -264,7 +276,7 @@ __global__ __launch_bounds__(NW * 64) void attn_core_kernel(AttnCore a) {
 __device__ __forceinline__ void merge_row_partials(const AttnCore& a, int DV, int b, int row,
                                                    int c0, int n, float* acc) {
   const Schedule& sc = a.sched;
-  const int n_part = sched_group_slots(sc, b * sc.n_rg + row / kCoreBlockRows);
+  const int n_part = sched_group_slots(sc, b * sc.n_rg + row / sc.block_rows);
   float M = -INFINITY;
   for (int k = 0; k < n_part; ++k) M = fmaxf(M, a.ml[(((size_t)k * a.B + b) * a.R + row) * 2]);
   for (int i = 0; i < n; ++i) acc[i] = 0.0f;

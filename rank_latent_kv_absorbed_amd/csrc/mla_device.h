@@ -109,17 +109,24 @@ __device__ __forceinline__ double pos_axis(const TokPos& p, int axis) {
   return axis == 0 ? (double)p.f : (axis == 1 ? (double)p.y : (double)p.x);
 }
 
-// Rotate the pair (a, b) of rotary pair `pair` at position p; the angle is
-// formed in double so that large frame indices keep full accuracy.
+// cos and sin of an angle given in double: the angle is reduced to [-pi, pi]
+// in double (exact to ~1e-16 for any frame index), then evaluated in fp32.
+__device__ __forceinline__ void rope_cos_sin(double ang, float& c, float& s) {
+  const double two_pi = 6.283185307179586476925286766559;
+  const double k = rint(ang * (1.0 / two_pi));
+  const float r = (float)fma(-k, two_pi, ang);
+  sincosf(r, &s, &c);
+}
+
+// Rotate the pair (a, b) of rotary pair `pair` at position p.
 __device__ __forceinline__ void rope_pair(const RopeTable& rt, int pair, const TokPos& p, float& a,
                                           float& b) {
-  double ang = pos_axis(p, rt.axis[pair]) * rt.inv_freq[pair];
-  double s, c;
-  sincos(ang, &s, &c);
-  double ra = (double)a * c - (double)b * s;
-  double rb = (double)a * s + (double)b * c;
-  a = (float)ra;
-  b = (float)rb;
+  float c, s;
+  rope_cos_sin(pos_axis(p, rt.axis[pair]) * rt.inv_freq[pair], c, s);
+  const float ra = a * c - b * s;
+  const float rb = a * s + b * c;
+  a = ra;
+  b = rb;
 }
 
 }  // namespace mla

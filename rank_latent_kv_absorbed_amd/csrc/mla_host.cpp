@@ -109,17 +109,21 @@ void commit_write(mla_cache* h, int64_t frame0, int32_t n_frames) {
   h->newest = frame0 + n_frames - 1;
 }
 
-// Schedule of the attention core (see mla::Schedule).  Default: one block per
-// compute unit, but no more blocks than leave each at least kMinStepsPerBlock
-// key tiles, so that partial writes stay small next to the work.  key_splits
-// > 0 instead gives every row group key_splits blocks' worth of work, cutting
-// its key range into about that many pieces.
+// Schedule of the attention core (see mla::Schedule) for core shape `sh`
+// whose key rows take `chunks_per_key` 16-byte LDS chunks.  Default: as many
+// blocks as fit the device at once (one per compute unit for the widest shape),
+// but no more than leave each at least kMinStepsPerBlock key tiles, so that
+// partial writes stay small next to the work.  key_splits > 0 instead gives
+// every row group key_splits blocks' worth of work, cutting its key range into
+// about that many pieces.
 constexpr int64_t kMinStepsPerBlock = 8;
 
-mla::Schedule make_schedule(int64_t B, int64_t R, int64_t Lk, int32_t key_splits, int64_t cus) {
+mla::Schedule make_schedule(int64_t B, int64_t R, int64_t Lk, int32_t key_splits, int64_t cus,
+                            mla::CoreShape sh, int chunks_per_key) {
   mla::Schedule s;
-  const int64_t n_rg = (R + mla::kCoreBlockRows - 1) / mla::kCoreBlockRows;
-  const int64_t n_kt = (Lk + mla::kKeyTile - 1) / mla::kKeyTile;
+  const int64_t br = 32 * sh.waves;
+  const int64_t n_rg = (R + br - 1) / br;
+  const int64_t n_kt = (Lk + sh.key_tile - 1) / sh.key_tile;
   const int64_t groups = B * n_rg;
   const int64_t total = groups * n_kt;
   int64_t nb;
@@ -127,7 +131,8 @@ mla::Schedule make_schedule(int64_t B, int64_t R, int64_t Lk, int32_t key_splits
     nb = groups * key_splits;
   } else {
     const int64_t by_work = (total + kMinStepsPerBlock - 1) / kMinStepsPerBlock;
-    nb = cus < by_work ? cus : by_work;
+    const int64_t resident = cus * mla::core_blocks_per_cu(sh, chunks_per_key);
+    nb = resident < by_work ? resident : by_work;
   }
   if (nb < 1) nb = 1;
   const int64_t full = groups / nb;
@@ -139,6 +144,8 @@ mla::Schedule make_schedule(int64_t B, int64_t R, int64_t Lk, int32_t key_splits
     const int64_t tail = rem * (n_kt - main_len);
     if (tail > 0) tpb = (tail + (nb - rem) - 1) / (nb - rem);
   }
+  s.block_rows = (int)br;
+  s.key_tile = sh.key_tile;
   s.n_rg = (int)n_rg;
   s.n_kt = (int)n_kt;
   s.n_groups = (int)groups;
@@ -166,7 +173,8 @@ LatentLayout latent_layout(const mla_cache* h, int32_t Lq, int32_t key_splits) {
   const mla_layer_config& c = h->cfg;
   const int64_t R = (int64_t)Lq * c.n_heads;
   LatentLayout L;
-  L.sched = make_schedule(c.batch, R, window_keys(h), key_splits, mla::device_cu_count());
+  L.sched = make_schedule(c.batch, R, window_keys(h), key_splits, mla::device_cu_count(),
+                          mla::core_shape_for_rows(R), (c.d_c + c.d_rope) / 8 + 1);
   const size_t width = (size_t)(c.d_c + c.d_rope);
   const size_t slots = (size_t)L.sched.n_slots;
   L.qcat_off = 0;
@@ -186,9 +194,11 @@ DenseLayout dense_layout(const mla_cache* h, int32_t Lq) {
   const mla_layer_config& c = h->cfg;
   const int d_h = c.d_nope + c.d_rope;
   DenseLayout L;
-  L.lq_pad = mla::mha_lq_pad(Lq);
+  const mla::CoreShape sh = mla::core_shape_for_rows(Lq);
+  L.lq_pad = (Lq + 32 * sh.waves - 1) / (32 * sh.waves) * (32 * sh.waves);
   const int64_t R = (int64_t)c.n_heads * L.lq_pad;
-  L.sched = make_schedule(c.batch, R, window_keys(h), 0, mla::device_cu_count());
+  L.sched = make_schedule(c.batch, R, window_keys(h), 0, mla::device_cu_count(), sh,
+                          2 * d_h / 8 + 1);
   const size_t slots = (size_t)L.sched.n_slots;
   L.qrot_off = 0;
   L.opart_off = round_up((size_t)c.batch * R * d_h * 2, kAlign);

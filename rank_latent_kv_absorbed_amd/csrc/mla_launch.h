@@ -40,17 +40,44 @@ struct CacheWriteArgs {
   RopeTable rope;
 };
 
-// Rows per block of the attention core (8 waves x 32 rows).
-constexpr int kCoreBlockRows = 256;
-
 #if defined(__HIPCC__)
 #define MLA_HD __host__ __device__
 #else
 #define MLA_HD
 #endif
 
+// Shapes of the attention core: a block of `waves` waves owns 32 * waves rows
+// and stages `key_tile` keys per LDS tile.  Many query rows (the chunk case)
+// take the widest block, which reuses each staged key tile most; a few rows
+// (cache-bound small-query shapes) take narrow blocks on short tiles so that
+// several blocks share a compute unit and keep more key bytes in flight.
+struct CoreShape {
+  int waves;
+  int key_tile;
+};
+constexpr CoreShape kCoreShapes[] = {{8, 64}, {4, 32}, {1, 32}};
+constexpr int kCoreMaxBlockRows = 256;
+
+// Shape for `rows` query rows of one row unit (latent: Lq * n_h rows of a
+// batch element; dense: Lq rows of one head).
+inline CoreShape core_shape_for_rows(int64_t rows) {
+  if (rows <= 32) return kCoreShapes[2];
+  if (rows <= 128) return kCoreShapes[1];
+  return kCoreShapes[0];
+}
+
+// Blocks of a shape that fit one compute unit at once: LDS (160 KiB per CU)
+// holds two key tiles of `chunks_per_key` 16-byte chunks per key, and the
+// core's register use allows two waves per SIMD (eight per CU).
+inline int core_blocks_per_cu(CoreShape sh, int chunks_per_key) {
+  const int lds = 2 * sh.key_tile * chunks_per_key * 16;
+  const int by_lds = (160 * 1024) / lds;
+  const int by_waves = 8 / sh.waves;
+  return by_lds < by_waves ? by_lds : by_waves;
+}
+
 // Work schedule of the attention core over (row group, key tile) steps, where a
-// group is one batch element's block of kCoreBlockRows rows:
+// group is one batch element's block of block_rows rows:
 //  * data-parallel rounds: while there are at least n_blocks groups left, each
 //    block takes whole groups (all key tiles), all blocks in key-tile lockstep;
 //  * the remaining `rem` groups (rem < n_blocks) are balanced stream-K style:
@@ -62,6 +89,8 @@ constexpr int kCoreBlockRows = 256;
 // sum) per block, merged exactly by log-sum-exp: slot 0 = main block, slots
 // 1.. = tail blocks in order.
 struct Schedule {
+  int block_rows;       // rows per group (32 * waves of the core shape)
+  int key_tile;         // keys per step
   int n_rg;             // row groups per batch element
   int n_kt;             // key tiles in the window
   int n_groups;         // batch * n_rg
@@ -186,9 +215,6 @@ struct MhaAttendArgs {
   RopeTable rope;
 };
 
-// Key tile of the attention kernels (keys staged in LDS per step).
-constexpr int kKeyTile = 64;
-
 hipError_t launch_cache_write_bf16(const CacheWriteArgs& a, hipStream_t s);
 hipError_t launch_cache_write_f32(const CacheWriteArgs& a, hipStream_t s);
 bool cache_write_bf16_supported(int width, int hidden);
@@ -197,9 +223,9 @@ hipError_t launch_attend_bf16(const AttendArgs& a, hipStream_t s);
 hipError_t launch_attend_f32(const AttendArgs& a, hipStream_t s);
 bool attend_bf16_supported(int d_c, int d_rope, int d_nope, int d_v);
 
-// Dense path: rotated queries go to a.qrot ([B][n_h * mha_lq_pad(Lq)][d_h]);
-// opart/ml hold per-slot partials as in the latent path.
-int mha_lq_pad(int Lq);
+// Dense path: rotated queries go to a.qrot ([B][n_h * Lq_pad][d_h], Lq_pad =
+// Lq rounded up to the schedule's block_rows); opart/ml hold per-slot partials
+// as in the latent path.
 hipError_t launch_mha_attend_bf16_ws(const MhaAttendArgs& a, float* opart, float* ml,
                                      const Schedule& sched, hipStream_t s);
 

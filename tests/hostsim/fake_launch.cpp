@@ -33,7 +33,6 @@ bool attend_bf16_supported(int d_c, int d_rope, int d_nope, int d_v) {
          d_v % 32 == 0 && d_v > 0;
 }
 bool mha_attend_bf16_supported(int d_h) { return d_h == 128; }
-int mha_lq_pad(int Lq) { return (Lq + kCoreBlockRows - 1) / kCoreBlockRows * kCoreBlockRows; }
 int device_cu_count() { return 256; }
 hipError_t launch_cache_write_bf16(const CacheWriteArgs& a, hipStream_t) { g_write = a; return rec(1); }
 hipError_t launch_cache_write_f32(const CacheWriteArgs& a, hipStream_t) { g_write = a; return rec(2); }
@@ -60,32 +59,38 @@ void fake_write_info(long long* o) {
   memcpy(o, v, sizeof(v));
 }
 // key_slot0, Lk, B, Lq, q_token0, ring_rows, n_h, d_c, then the schedule:
-// n_rg, n_kt, n_groups, n_blocks, full_rounds, rem, main_len, tail_per_block, n_slots
+// n_rg, n_kt, n_groups, n_blocks, full_rounds, rem, main_len, tail_per_block, n_slots,
+// block_rows, key_tile
 void fake_attend_info(long long* o) {
   const mla::AttendArgs& a = g_attend;
   const mla::Schedule& s = a.sched;
-  long long v[17] = {a.key_slot0, a.Lk, a.B, a.Lq, a.q_token0, a.ring_rows, a.n_h, a.d_c,
+  long long v[19] = {a.key_slot0, a.Lk, a.B, a.Lq, a.q_token0, a.ring_rows, a.n_h, a.d_c,
                      s.n_rg, s.n_kt, s.n_groups, s.n_blocks, s.full_rounds, s.rem, s.main_len,
-                     s.tail_per_block, s.n_slots};
+                     s.tail_per_block, s.n_slots, s.block_rows, s.key_tile};
   memcpy(o, v, sizeof(v));
 }
-// The last attend's schedule as the kernels decode it.
-int fake_sched_steps(int g) { return mla::sched_block_steps(g_attend.sched, g); }
-void fake_sched_decode(int g, int i, int* o) {
-  const mla::StepInfo si = mla::sched_decode(g_attend.sched, g, i);
+// The last (which = 0: latent, 1: dense) attend's schedule as the kernels decode it.
+static const mla::Schedule& sched_of(int which) { return which ? g_mha_sched : g_attend.sched; }
+int fake_sched_steps(int which, int g) { return mla::sched_block_steps(sched_of(which), g); }
+void fake_sched_decode(int which, int g, int i, int* o) {
+  const mla::StepInfo si = mla::sched_decode(sched_of(which), g, i);
   o[0] = si.grp;
   o[1] = si.kt;
   o[2] = si.slot;
   o[3] = si.first;
   o[4] = si.last;
 }
-int fake_sched_group_slots(int grp) { return mla::sched_group_slots(g_attend.sched, grp); }
+int fake_sched_group_slots(int which, int grp) {
+  return mla::sched_group_slots(sched_of(which), grp);
+}
 float fake_attend_qscale() { return g_attend.qscale; }
-// key_slot0, Lk, Lq, q_token0, n_rg, n_kt, n_blocks, n_slots
+// key_slot0, Lk, B, Lq, q_token0, n_rg, n_kt, n_groups, n_blocks, full_rounds, rem,
+// main_len, tail_per_block, n_slots, block_rows, key_tile
 void fake_mha_info(long long* o) {
   const mla::Schedule& s = g_mha_sched;
-  long long v[8] = {g_mha.key_slot0, g_mha.Lk, g_mha.Lq, g_mha.q_token0, s.n_rg, s.n_kt,
-                    s.n_blocks, s.n_slots};
+  long long v[16] = {g_mha.key_slot0, g_mha.Lk, g_mha.B, g_mha.Lq, g_mha.q_token0, s.n_rg,
+                     s.n_kt, s.n_groups, s.n_blocks, s.full_rounds, s.rem, s.main_len,
+                     s.tail_per_block, s.n_slots, s.block_rows, s.key_tile};
   memcpy(o, v, sizeof(v));
 }
 // which: 0 = last write, 1 = last attend, 2 = last dense attend

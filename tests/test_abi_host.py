@@ -109,29 +109,51 @@ def _write_info(L):
 
 
 def _attend_info(L):
-    a = (ctypes.c_longlong * 17)()
+    a = (ctypes.c_longlong * 19)()
     L.fake_attend_info(a)
     keys = ["key_slot0", "Lk", "B", "Lq", "q_token0", "ring_rows", "n_h", "d_c", "n_rg", "n_kt",
-            "n_groups", "n_blocks", "full_rounds", "rem", "main_len", "tpb", "n_slots"]
+            "n_groups", "n_blocks", "full_rounds", "rem", "main_len", "tpb", "n_slots",
+            "block_rows", "key_tile"]
     return dict(zip(keys, list(a)))
 
 
-def check_schedule(L, info, R):
+def _mha_info(L):
+    a = (ctypes.c_longlong * 16)()
+    L.fake_mha_info(a)
+    keys = ["key_slot0", "Lk", "B", "Lq", "q_token0", "n_rg", "n_kt", "n_groups", "n_blocks",
+            "full_rounds", "rem", "main_len", "tpb", "n_slots", "block_rows", "key_tile"]
+    return dict(zip(keys, list(a)))
+
+
+# Core shapes (block rows, key tile) by rows per row unit, and how many blocks
+# of each fit one compute unit (two LDS tiles of key_tile * chunks * 16 bytes in
+# 160 KiB; at most eight waves).
+def expected_shape(rows):
+    return (32, 32) if rows <= 32 else ((128, 32) if rows <= 128 else (256, 64))
+
+
+def blocks_per_cu(shape, chunks_per_key):
+    br, kt = shape
+    return min(160 * 1024 // (2 * kt * chunks_per_key * 16), 8 // (br // 32))
+
+
+def check_schedule(L, info, R, which=0):
     """Walk the last attend's schedule exactly as the kernel decodes it: every
     (row group, key tile) step runs once; each block's steps form segments
     flagged first/last; a group's segments use slots 0..k-1 with k the count
     the merge reads, k <= the workspace's slot count; block work is balanced."""
     n_rg, n_kt, nb = info["n_rg"], info["n_kt"], info["n_blocks"]
-    assert n_rg == -(-R // 256) and n_kt == -(-info["Lk"] // 64)
+    br, kt = info["block_rows"], info["key_tile"]
+    assert n_rg == -(-R // br) and n_kt == -(-info["Lk"] // kt)
     groups = info["B"] * n_rg
     seen = np.zeros((groups, n_kt), np.int32)
     slots = {}
     out = (ctypes.c_int * 5)()
-    steps = [L.fake_sched_steps(g) for g in range(nb)]
+    steps = [L.fake_sched_steps(which, g) for g in range(nb)]
     for g in range(nb):
         prev = None
         for i in range(steps[g]):
-            L.fake_sched_decode(g, i, out)
+            L.fake_sched_decode(which, g, i, out)
             grp, kt, slot, first, last = list(out)
             seen[grp, kt] += 1
             if prev is None or prev[4]:
@@ -143,7 +165,7 @@ def check_schedule(L, info, R):
         assert prev is None or prev[4]
     assert (seen == 1).all()
     for grp in range(groups):
-        k = L.fake_sched_group_slots(grp)
+        k = L.fake_sched_group_slots(which, grp)
         assert slots[grp] == set(range(k)) and k <= info["n_slots"]
     busy = [s for s in steps if s > 0]
     assert max(busy) <= -(-groups * n_kt // nb) + 1
@@ -255,6 +277,7 @@ def test_attend_arguments_and_workspace(sim):
     assert sim.fake_attend_qscale() == np.float32(math.log2(math.e) / math.sqrt(128))
     # full window, one sequence: 220 main blocks walk key tiles 0..439 in
     # lockstep, 36 tail blocks share tiles 440..511 of every group, 440 each
+    assert (a["block_rows"], a["key_tile"]) == (256, 64)
     assert (a["n_blocks"], a["n_rg"], a["n_kt"], a["rem"], a["main_len"], a["tpb"]) == \
         (256, 220, 512, 220, 440, 440)
     check_schedule(sim, a, R)
@@ -266,13 +289,38 @@ def test_attend_arguments_and_workspace(sim):
         a = _attend_info(sim)
         assert a["n_blocks"] == a["n_groups"] * s
         check_schedule(sim, a, 8 * 12)
-    # small and large query counts spread over the compute units
-    for Lq in (1, 8, 100, 4680):
-        sim.mla_attend(h, P(FAKE_PTR), 0, Lq, P(FAKE_PTR), P(FAKE_PTR), P(FAKE_PTR), 0, P(ws),
-                       1 << 40, None)
+    # small and large query counts: narrow blocks on short key tiles for a few
+    # rows, several per compute unit; at least 8 key tiles per block
+    for Lq in (1, 2, 3, 8, 10, 11, 100, 4680):
+        assert sim.mla_attend(h, P(FAKE_PTR), 0, Lq, P(FAKE_PTR), P(FAKE_PTR), P(FAKE_PTR), 0,
+                              P(ws), 1 << 40, None) == 0
         a = _attend_info(sim)
+        shape = expected_shape(Lq * 12)
+        assert (a["block_rows"], a["key_tile"]) == shape
         check_schedule(sim, a, Lq * 12)
-        assert a["n_blocks"] == min(256, -(-a["n_groups"] * a["n_kt"] // 8))
+        resident = 256 * blocks_per_cu(shape, 224 // 8 + 1)
+        assert a["n_blocks"] == min(resident, -(-a["n_groups"] * a["n_kt"] // 8))
+
+
+def test_dense_attend_schedule(sim):
+    c = _cfg()
+    st, h = _create(sim, c, dense=True)
+    assert st == 0 and sim.mla_cache_set_state(h, 0, 20) == 0
+    ws = 1 << 40
+    for Lq in (1, 31, 32, 33, 128, 129, 4680):
+        need = sim.mha_attend_workspace_bytes(h, Lq)
+        shape = expected_shape(Lq)
+        lq_pad = -(-Lq // shape[0]) * shape[0]
+        R = 12 * lq_pad
+        assert need >= R * 128 * 2 + R * 128 * 4 + R * 8
+        assert sim.mha_attend(h, P(FAKE_PTR), 0, Lq, P(FAKE_PTR), P(ws), need - 1, None) == 7
+        assert sim.mha_attend(h, P(FAKE_PTR), 21 * 1560, Lq, P(FAKE_PTR), P(ws), need, None) == 0
+        a = _mha_info(sim)
+        assert (a["block_rows"], a["key_tile"]) == shape
+        assert a["Lk"] == 21 * 1560 and a["Lq"] == Lq and a["q_token0"] == 21 * 1560
+        check_schedule(sim, a, R, which=1)
+        resident = 256 * blocks_per_cu(shape, 2 * 128 // 8 + 1)
+        assert a["n_blocks"] == min(resident, -(-a["n_groups"] * a["n_kt"] // 8))
 
 
 def test_wrong_kind_and_unsupported(sim):

@@ -164,6 +164,24 @@ def test_attend_mid_ragged_with_wrap(key_splits):
     assert_parity(got, ref, "bf16", f"mid splits={key_splits}")
 
 
+# Lq * n_heads = 12 rows: one-wave blocks on 32-key tiles; 80 rows: four-wave
+# blocks with a wave of padding; 132 rows: eight-wave blocks with three padding
+# waves.  300 keys leave a ragged last tile; forced splits put several blocks
+# on each row group.
+@pytest.mark.parametrize("Lq,key_splits", [(3, 0), (3, 4), (20, 0), (20, 2), (33, 0), (33, 3)])
+def test_attend_narrow_blocks_ragged_with_wrap(Lq, key_splits):
+    cfg = mid_cfg()
+    run = LatentRun(cfg)
+    run.write(0, 4)
+    run.evict(2)
+    run.write(4, 2)
+    run.evict(1)
+    run.write(6, 2)       # frames 3..7 resident through a ring wrap, Lk = 300
+    q = run.query(Lq)
+    got, ref, _ = run.attend(q, 8 * cfg.T - Lq, key_splits=key_splits)
+    assert_parity(got, ref, "bf16", f"narrow blocks Lq={Lq} splits={key_splits}")
+
+
 @pytest.mark.parametrize("d_c", [64, 128, 192])
 def test_attend_wan_heads_latent_widths(d_c):
     cfg = wan_small(d_c=d_c)
@@ -251,6 +269,20 @@ def test_full_window_sampled_rows(batch, cache_dtype):
     assert_parity(got, ref, "bf16", f"21-frame window B={batch} {cache_dtype} sampled")
 
 
+@pytest.mark.parametrize("Lq", [1, 8])
+def test_small_queries_full_window(Lq):
+    """Decode-like shapes on the full 21-frame window: each sequence's few rows
+    spread over many key ranges (about a hundred partials per row)."""
+    cfg = config("wan_window").with_(batch=2)
+    run = LatentRun(cfg)
+    run.write(0, cfg.prefill_frames)
+    run.evict(cfg.evict_frames)
+    run.write(cfg.chunk_frame0, cfg.chunk_frames)
+    q = run.query(Lq)
+    got, ref, _ = run.attend(q, (cfg.chunk_frame0 + cfg.chunk_frames) * cfg.T - Lq)
+    assert_parity(got, ref, "bf16", f"21-frame window small query Lq={Lq}")
+
+
 # --------------------------------------------------------------------------
 # dense comparison path
 # --------------------------------------------------------------------------
@@ -264,6 +296,20 @@ def test_dense_mha_full_small():
     q = chunk_q(cfg, 2 * cfg.T, chunk=7)
     got, ref = run.attend(q, 4 * cfg.T)
     assert_parity(got, ref, "bf16", "dense small")
+
+
+# one-wave blocks (1 row per head), four-wave blocks with padding (40),
+# eight-wave blocks with padding waves (129)
+@pytest.mark.parametrize("Lq", [1, 40, 129])
+def test_dense_mha_small_queries(Lq):
+    cfg = wan_small()
+    run = DenseRun(cfg)
+    run.write(0, 4)
+    run.evict(1)
+    run.write(4, 2)
+    q = chunk_q(cfg, Lq, chunk=5)
+    got, ref = run.attend(q, 6 * cfg.T - Lq)
+    assert_parity(got, ref, "bf16", f"dense small query Lq={Lq}")
 
 
 def test_dense_mha_tiny_fp32():
