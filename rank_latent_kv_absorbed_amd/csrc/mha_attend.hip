@@ -158,14 +158,18 @@ hipError_t launch_mha_typed(const MhaAttendArgs& a, float* opart, float* ml, con
       if (e != hipSuccess) return e;
     }
     const dim3 grid((unsigned)sched.n_blocks);
-    if (br == 256 && sched.key_tile == 64)
-      hipLaunchKernelGGL((attn_core_kernel<E, 128, 128, 8, 64, false>), grid, dim3(512), 0, s, c);
-    else if (br == 128 && sched.key_tile == 32)
-      hipLaunchKernelGGL((attn_core_kernel<E, 128, 128, 4, 32, false>), grid, dim3(256), 0, s, c);
-    else if (br == 32 && sched.key_tile == 32)
-      hipLaunchKernelGGL((attn_core_kernel<E, 128, 128, 1, 32, false>), grid, dim3(64), 0, s, c);
-    else
-      return hipErrorInvalidValue;
+    bool launched = false;
+#define MLA_SHAPE(NW, KT, NS)                                                                  \
+  if (!launched && br == 32 * NW && sched.key_tile == KT && sched.stages == NS) {             \
+    hipLaunchKernelGGL((attn_core_kernel<E, 128, 128, NW, KT, NS, false>), grid, dim3(NW * 64), \
+                       0, s, c);                                                              \
+    launched = true;                                                                          \
+  }
+    MLA_SHAPE(8, 64, 2)
+    MLA_SHAPE(4, 32, 4)
+    MLA_SHAPE(1, 32, 2)
+#undef MLA_SHAPE
+    if (!launched) return hipErrorInvalidValue;
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.ev_stop != nullptr) {

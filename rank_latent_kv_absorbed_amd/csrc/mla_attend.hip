@@ -342,19 +342,22 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(AttendArgs a) {
   }
 }
 
-// Core launch for the schedule's shape (block rows, key tile).
+// Core launch for the schedule's shape (block rows, key tile, stages).
 template <typename E, int DC>
 hipError_t launch_core(const AttnCore& c, hipStream_t s) {
-  const dim3 grid((unsigned)c.sched.n_blocks);
-  if (c.sched.block_rows == 256 && c.sched.key_tile == 64)
-    hipLaunchKernelGGL((attn_core_kernel<E, DC + 32, DC, 8, 64, true>), grid, dim3(512), 0, s, c);
-  else if (c.sched.block_rows == 128 && c.sched.key_tile == 32)
-    hipLaunchKernelGGL((attn_core_kernel<E, DC + 32, DC, 4, 32, true>), grid, dim3(256), 0, s, c);
-  else if (c.sched.block_rows == 32 && c.sched.key_tile == 32)
-    hipLaunchKernelGGL((attn_core_kernel<E, DC + 32, DC, 1, 32, true>), grid, dim3(64), 0, s, c);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+  const Schedule& sc = c.sched;
+  const dim3 grid((unsigned)sc.n_blocks);
+#define MLA_SHAPE(NW, KT, NS)                                                                   \
+  if (sc.block_rows == 32 * NW && sc.key_tile == KT && sc.stages == NS) {                      \
+    hipLaunchKernelGGL((attn_core_kernel<E, DC + 32, DC, NW, KT, NS, true>), grid, dim3(NW * 64), \
+                       0, s, c);                                                               \
+    return hipGetLastError();                                                                  \
+  }
+  MLA_SHAPE(8, 64, 2)
+  MLA_SHAPE(4, 32, 4)
+  MLA_SHAPE(1, 32, 2)
+#undef MLA_SHAPE
+  return hipErrorInvalidValue;
 }
 
 template <typename E, int DC>

@@ -17,11 +17,21 @@
 //    combine a group's partials by log-sum-exp.
 //  * Key tiles move HBM -> LDS with gfx950's direct 16-byte loads
 //    (global_load_lds_dwordx4): each wave instruction fills one contiguous
-//    KiB of LDS, lane l writing bytes [16l, 16l+16).  Rows are padded by one
-//    16-byte chunk; padding lanes are switched off.  Two tile buffers (two
-//    distinct LDS arrays, used alternately by an unrolled step pair so that
-//    every access names its buffer): the next tile streams in while the
-//    current one is consumed, one barrier per tile.
+//    KiB of LDS, lane l writing bytes [16l, 16l+16).  LDS rows are not padded;
+//    instead the 16-byte chunks of a key row are XOR-permuted by the key index
+//    (chunk q of key r sits at position q ^ swz(r), inside its aligned group of
+//    4 chunks for latent rows, 16 for dense rows), so that the score and
+//    transpose reads of 16 consecutive keys hit distinct LDS banks.  Every lane
+//    of a load instruction is active and the lanes of each aligned 64-byte
+//    group read one 64-byte piece of the ring (in permuted order), which the
+//    memory pipeline coalesces like a straight copy.  NS tile buffers (distinct
+//    LDS arrays, cycled by an NS-fold unrolled step loop so that every access
+//    names its buffer) form a ring: NS - 1 tiles stream in while one is
+//    consumed, one barrier per tile.  Each wave waits for its own loads of the
+//    next tile with an exact vector-memory count (loads retire in order), then
+//    the barrier publishes the tile to the block.  The chunk shape uses two
+//    buffers (it is MFMA-bound); the narrow shapes use deeper rings, since a
+//    few query rows leave them bound by the key bytes in flight.
 //  * Scores S^T[key][row] = sum_d K[key][d] Q[row][d] on 32x32x16 MFMA; a
 //    segment's query fragments stay in registers.  In this orientation a lane
 //    owns one row (MFMA column): the row's running max and sum live in the
@@ -80,9 +90,48 @@ __device__ __forceinline__ void global_to_lds16(const void* g, void* lds) {
 // Raise-the-max threshold of the lazy rescale (log2 units).
 constexpr float kRescaleThreshold = 8.0f;
 
+// s_waitcnt immediate that waits until at most n vector memory operations of
+// this wave are outstanding (vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt
+// left at their maxima, i.e. not waited on).
+#define MLA_VMCNT(n) ((((n)&15) | (((n) >> 4) << 14)) | (7 << 4) | (15 << 8))
+#define MLA_VMCASE(n) \
+  case n:             \
+    __builtin_amdgcn_s_waitcnt(MLA_VMCNT(n)); \
+    break;
+
+__device__ __forceinline__ void wait_vmem(int n) {
+  switch (n) {
+    MLA_VMCASE(0) MLA_VMCASE(1) MLA_VMCASE(2) MLA_VMCASE(3) MLA_VMCASE(4) MLA_VMCASE(5)
+    MLA_VMCASE(6) MLA_VMCASE(7) MLA_VMCASE(8) MLA_VMCASE(9) MLA_VMCASE(10) MLA_VMCASE(11)
+    MLA_VMCASE(12) MLA_VMCASE(13) MLA_VMCASE(14) MLA_VMCASE(15) MLA_VMCASE(16) MLA_VMCASE(17)
+    MLA_VMCASE(18) MLA_VMCASE(19) MLA_VMCASE(20) MLA_VMCASE(21) MLA_VMCASE(22) MLA_VMCASE(23)
+    MLA_VMCASE(24) MLA_VMCASE(25) MLA_VMCASE(26) MLA_VMCASE(27) MLA_VMCASE(28) MLA_VMCASE(29)
+    MLA_VMCASE(30) MLA_VMCASE(31) MLA_VMCASE(32) MLA_VMCASE(33) MLA_VMCASE(34) MLA_VMCASE(35)
+    MLA_VMCASE(36) MLA_VMCASE(37) MLA_VMCASE(38) MLA_VMCASE(39) MLA_VMCASE(40) MLA_VMCASE(41)
+    MLA_VMCASE(42) MLA_VMCASE(43) MLA_VMCASE(44) MLA_VMCASE(45) MLA_VMCASE(46) MLA_VMCASE(47)
+    MLA_VMCASE(48) MLA_VMCASE(49) MLA_VMCASE(50) MLA_VMCASE(51) MLA_VMCASE(52) MLA_VMCASE(53)
+    MLA_VMCASE(54) MLA_VMCASE(55) MLA_VMCASE(56) MLA_VMCASE(57) MLA_VMCASE(58) MLA_VMCASE(59)
+    MLA_VMCASE(60) MLA_VMCASE(61) MLA_VMCASE(62)
+    default: __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0)); break;
+  }
+}
+#undef MLA_VMCASE
+
+// Block barrier that waits only for this wave's LDS instructions: tile loads
+// in flight stay in flight (the steps wait for the ones they need with
+// wait_vmem first).  A memory fence here would also wait for every direct
+// global->LDS load, since those write LDS.  The empty asm statements keep the
+// compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt not waited on
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Register budget: two waves per SIMD whatever the block size, so that narrow
 // blocks can share a compute unit.
-template <typename E, int DQK, int DV, int NW, int KT, bool SHARED_KV>
+template <typename E, int DQK, int DV, int NW, int KT, int NS, bool SHARED_KV>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_core_kernel(AttnCore a) {
   typedef typename Elem<E>::v8 V8;
@@ -92,49 +141,98 @@ void attn_core_kernel(AttnCore a) {
   constexpr int NKB = KT / 32;                // 32-key blocks per tile
   constexpr int KCH = DQK / 8;                // 16-byte chunks of K per key
   constexpr int CPK = SHARED_KV ? KCH : KCH + DV / 8;  // chunks staged per key
-  constexpr int RCH = CPK + 1;                // chunks per padded LDS row
-  constexpr int KSTR = RCH * 8;               // padded LDS row stride (elements)
+  constexpr int KSTR = CPK * 8;               // LDS row stride (elements)
   constexpr int VOFF = SHARED_KV ? 0 : DQK;   // V columns inside an LDS row
-  constexpr int CHUNKS = KT * RCH;            // 16-byte chunks per tile
-  constexpr int SPANS = (CHUNKS + 63) / 64;   // 1-KiB direct-load spans per tile
+  constexpr int CHUNKS = KT * CPK;            // 16-byte chunks per tile
+  constexpr int SPANS = CHUNKS / 64;          // 1-KiB direct-load spans per tile
   constexpr int TILE = KT * KSTR;             // elements per tile buffer
   static_assert(KT == 32 || KT == 64, "key tiles are one or two 32-key MFMA blocks");
   static_assert(!SHARED_KV || DV <= DQK, "shared rows hold V inside K");
+  static_assert(NS >= 2 && NS <= 5, "two to five tile buffers");
+  static_assert(SPANS * (NS - 1) <= 63, "tile loads in flight fit the vmcnt counter");
+  // Whole spans with every lane active (exact load counts per wave); the chunk
+  // permutation stays inside aligned groups of a row.
+  static_assert(CHUNKS % 64 == 0, "tiles are whole 1-KiB spans");
+  static_assert(SHARED_KV ? (CPK % 4 == 0 && (CPK * 4) % 32 == 16)
+                          : (CPK % 16 == 0 && KCH % 16 == 0),
+                "row strides the swizzle was laid out for");
 
   __shared__ __attribute__((aligned(1024))) E kt0[TILE];
   __shared__ __attribute__((aligned(1024))) E kt1[TILE];
+  __shared__ __attribute__((aligned(1024))) E kt2[NS > 2 ? TILE : 8];
+  __shared__ __attribute__((aligned(1024))) E kt3[NS > 3 ? TILE : 8];
+  __shared__ __attribute__((aligned(1024))) E kt4[NS > 4 ? TILE : 8];
 
   const Schedule& sc = a.sched;
   const int tid = threadIdx.x;
+  // The tile loads sit under per-wave span tests (sp < SPANS below) that the
+  // compiler does not fold, even for one-wave blocks.  All waits for tile
+  // loads are explicit (exact per-wave counts, then a barrier); loads the
+  // compiler cannot count are ones it does not try to wait for itself.
   const int w = tid >> 6, l = tid & 63, lo = l & 31, hi = l >> 5;
   const int g = blockIdx.x;
   const int n_steps = sched_block_steps(sc, g);
+  const int n_ld = (SPANS - w + NW - 1) / NW;  // direct loads this wave issues per tile
+
+  // Chunk permutation of key row r (it depends on r mod 16 only).  Latent
+  // rows are 4 * CPK dwords long, an odd multiple of 16 dwords (mod 64), so
+  // four consecutive keys start in four different 16-bank windows and the
+  // XOR has to separate keys r, r + 4, r + 8, r + 12; this one also separates
+  // the even (odd) keys among 8 consecutive ones.  Dense rows are a multiple
+  // of 64 dwords: the permutation spreads 16 keys over 16 chunk slots and
+  // puts keys 4j .. 4j + 3 in different 4-chunk groups.  With 64 banks of
+  // 4 bytes, the 16 lanes of a score read and the 32 lanes of a transpose
+  // read then touch every bank once.
+  auto swz = [](int r) {
+    return SHARED_KV ? (((r >> 2) ^ (r >> 1)) & 3) : (((r & 3) << 2) | ((r >> 2) & 3));
+  };
 
   // Issue the direct loads of key tile kt of batch element b into `dst`.  Keys
   // past the window re-load the last key (their scores are masked), so every
-  // LDS row a wave reads holds finite cache data.
+  // LDS row a wave reads holds finite cache data.  Wave w issues spans w,
+  // w + NW, ...; lane l of span sp fills LDS chunk c = 64 sp + l: key
+  // c / CPK, position p = c % CPK, which holds chunk p ^ swz(key) of the key's
+  // row.  Offsets within one sequence's ring fit 32 bits (checked when the
+  // cache is created).
+  constexpr int LPW = (SPANS + NW - 1) / NW;  // span slots per wave
   auto load_tile = [&](int b, int rg, int kt, E* dst) {
     const E* ring = (const E*)a.ring + (size_t)b * a.ring_rows * a.ring_stride;
     const int head = (rg * BR) / a.rows_per_head;
     const int koff = a.k_off + head * a.head_stride;
     const int voff = a.v_off + head * a.head_stride;
+    const int t0 = kt * KT;
+    const int rows = (int)a.ring_rows;
 #pragma unroll
-    for (int sp = w; sp < SPANS; sp += NW) {
-      const int c = sp * 64 + l;
-      const int key = c / RCH, q = c - (c / RCH) * RCH;
-      if (c < CHUNKS && q < CPK) {
-        const int kg = min(kt * KT + key, a.Lk - 1);
-        int64_t slot = a.key_slot0 + kg;
-        if (slot >= a.ring_rows) slot -= a.ring_rows;
-        const E* src = ring + slot * a.ring_stride + (q < KCH ? koff + q * 8 : voff + (q - KCH) * 8);
-        global_to_lds16(src, dst + sp * 512);
+    for (int j = 0; j < LPW; ++j) {
+      const int sp = w + j * NW;
+      if (sp < SPANS) {
+        const int c = sp * 64 + l;
+        const int key = c / CPK, q = (c - key * CPK) ^ swz(key);
+        const int kg = min(t0 + key, a.Lk - 1);
+        int slot = (int)a.key_slot0 + kg;
+        slot = slot >= rows ? slot - rows : slot;
+        const int col = q < KCH ? koff + q * 8 : voff + (q - KCH) * 8;
+        global_to_lds16(ring + (slot * a.ring_stride + col), dst + sp * 512);
       }
     }
   };
 
-  // lane-constant parts of the transpose-read addresses
-  const int tr_key = 4 * hi + ((l & 15) >> 2);           // key offset of this lane's row
-  const int tr_col = 16 * ((l & 31) >> 4) + 4 * (l & 3);  // column offset in a 32-wide tile
+  // Lane-constant parts of the LDS read addresses.  Score reads: lane (lo, hi)
+  // reads chunk 2 ks + hi of key kb * 32 + lo.  Transpose reads: the lane
+  // addresses key row tr_key (+ 8 for the second half) of a 16-key step and
+  // the 8 bytes at chunk 4 dt + tr_c, half tr_h, of a 32-column tile.
+  // (2 ks + hi) ^ s = 2 (ks ^ (s >> 1)) + (hi ^ (s & 1)); for latent rows
+  // s < 4, so even and odd ks each need one lane offset.  Likewise
+  // (4 dt + c) ^ s = 4 (dt ^ (s >> 2)) + (c ^ (s & 3)).
+  const int k_sw = swz(lo);
+  const int k_off0 = 8 * (hi ^ (k_sw & 1)) + 16 * (k_sw >> 1);        // even ks (latent)
+  const int k_off1 = 8 * (hi ^ (k_sw & 1)) + 16 * ((k_sw >> 1) ^ 1);  // odd ks (latent)
+  const int tr_key = 4 * hi + ((l & 15) >> 2);
+  const int tr_c = 2 * ((l & 31) >> 4) + ((l & 3) >> 1);
+  const int tr_h = 4 * (l & 1);
+  const int tr_sw0 = swz(tr_key), tr_sw1 = swz(tr_key + 8);
+  const int tr_off0 = tr_h + 8 * (tr_c ^ (tr_sw0 & 3)), tr_off1 = tr_h + 8 * (tr_c ^ (tr_sw1 & 3));
+  const int tr_dt0 = tr_sw0 >> 2, tr_dt1 = tr_sw1 >> 2;  // 0 for latent rows
 
   V8 qf[NKS];
   f32x16 o[NDT];
@@ -142,32 +240,53 @@ void attn_core_kernel(AttnCore a) {
   int row = 0;
   bool live = false;  // this wave's rows include a real one (wave-uniform)
 
-  // One step: `cur` holds the key tile of step i; prefetch step i+1 into `nxt`.
-  auto step = [&](int i, const E* cur, E* nxt) {
+  // Tiles issued after tile i + 1 by the end of step i, counting the refill
+  // of step i itself (the ring is short near the end of the block's steps).
+  auto ahead = [&](int i) {
+    const int a2 = n_steps - i - 2;
+    return a2 < 0 ? 0 : (a2 < NS - 1 ? a2 : NS - 1);
+  };
+  auto issue = [&](int i, E* dst) {
+    const StepInfo sn = sched_decode(sc, g, i);
+    const int b1 = sn.grp / sc.n_rg;
+    load_tile(b1, sn.grp - b1 * sc.n_rg, sn.kt, dst);
+  };
+
+  // New row-group segment: query fragments in (global loads, not waited on
+  // here), running state reset.
+  auto begin_segment = [&](int b, int rg) {
+    row = rg * BR + w * 32 + lo;
+    const int row0 = rg * BR + w * 32;  // rows of a wave never straddle a head
+    live = row0 < a.R && (row0 % a.rows_per_head) < a.valid_per_head;
+    const bool ok = row < a.R && (row % a.rows_per_head) < a.valid_per_head;
+    const E* src = (const E*)a.qrows + ((size_t)b * a.R + (ok ? row : 0)) * DQK + 8 * hi;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) qf[ks] = ok ? ld8<E>(src + 16 * ks) : zero8<E>();
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[dt][r] = 0.0f;
+    m = -INFINITY;
+    lsum = 0.0f;
+  };
+
+  // One step: `cur` holds the key tile of step i.  Once every wave is done
+  // with it, tile i + NS is issued into the same buffer.  (Issuing at the end
+  // of a step keeps each buffer's write after its read within one unrolled
+  // loop pass; the compiler then adds no wait of its own for the tile loads.)
+  auto step = [&](int i, E* cur) {
     const StepInfo si = sched_decode(sc, g, i);
     const int b = si.grp / sc.n_rg;
     const int rg = si.grp - b * sc.n_rg;
     const int kt = si.kt;
 
-    if (si.first) {  // new row-group segment: queries in, state reset
-      row = rg * BR + w * 32 + lo;
-      const int row0 = rg * BR + w * 32;  // rows of a wave never straddle a head
-      live = row0 < a.R && (row0 % a.rows_per_head) < a.valid_per_head;
-      const bool ok = row < a.R && (row % a.rows_per_head) < a.valid_per_head;
-      const E* src = (const E*)a.qrows + ((size_t)b * a.R + (ok ? row : 0)) * DQK + 8 * hi;
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) qf[ks] = ok ? ld8<E>(src + 16 * ks) : zero8<E>();
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[dt][r] = 0.0f;
-      m = -INFINITY;
-      lsum = 0.0f;
-    }
-    if (i + 1 < n_steps) {
-      const StepInfo sn = sched_decode(sc, g, i + 1);
-      const int b1 = sn.grp / sc.n_rg;
-      load_tile(b1, sn.grp - b1 * sc.n_rg, sn.kt, nxt);
+    if (si.first && i > 0) {
+      // A segment starting mid-block: its query loads retire in order behind
+      // the tiles in flight, so wait for all of them here (rare: only blocks
+      // that cross from one row group to the next).
+      begin_segment(b, rg);
+      asm volatile("" ::: "memory");  // keep the loads above the wait
+      __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
     }
 
     if (live) {
@@ -176,9 +295,13 @@ void attn_core_kernel(AttnCore a) {
       for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) sv[kb][r] = 0.0f;
-        const E* krow = cur + (kb * 32 + lo) * KSTR + 8 * hi;
+        const E* krow = cur + (kb * 32 + lo) * KSTR;
+        auto kptr = [&](int ks) {
+          return SHARED_KV ? krow + 32 * (ks >> 1) + ((ks & 1) ? k_off1 : k_off0)
+                           : krow + 8 * ((2 * ks + hi) ^ k_sw);
+        };
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) sv[kb] = Elem<E>::mfma(ld8<E>(krow + 16 * ks), qf[ks], sv[kb]);
+        for (int ks = 0; ks < NKS; ++ks) sv[kb] = Elem<E>::mfma(ld8<E>(kptr(ks)), qf[ks], sv[kb]);
       }
       const int t0 = kt * KT;
       if (t0 + KT > a.Lk) {
@@ -222,11 +345,12 @@ void attn_core_kernel(AttnCore a) {
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
-          const E* vrow = cur + (kb * 32 + 16 * st + tr_key) * KSTR + VOFF + tr_col;
+          const E* vrow = cur + (kb * 32 + 16 * st + tr_key) * KSTR + VOFF;
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt) {
-            const i16x4 lo4 = lds_read_tr16(vrow + dt * 32);
-            const i16x4 hi4 = lds_read_tr16(vrow + 8 * KSTR + dt * 32);
+            const int d0 = SHARED_KV ? dt : (dt ^ tr_dt0), d1 = SHARED_KV ? dt : (dt ^ tr_dt1);
+            const i16x4 lo4 = lds_read_tr16(vrow + 32 * d0 + tr_off0);
+            const i16x4 hi4 = lds_read_tr16(vrow + 8 * KSTR + 32 * d1 + tr_off1);
             const V8 va = __builtin_bit_cast(V8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
             o[dt] = Elem<E>::mfma(va, pf[kb][st], o[dt]);
           }
@@ -252,21 +376,66 @@ void attn_core_kernel(AttnCore a) {
         }
       }
     }  // live
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    // After the last step nothing is read any more: no wait (the partial
+    // stores above retire on their own; every tile load was waited for at
+    // the end of the step before).
+    if (i + 1 < n_steps) {
+      if constexpr (NW == 1) {
+        // one wave: refill `cur` before waiting for tile i + 1, so NS tiles
+        // are in flight during the wait
+        lds_barrier();
+        if (i + NS < n_steps) issue(i + NS, cur);
+        wait_vmem(n_ld * ahead(i));
+        lds_barrier();
+      } else {
+        // several waves: one barrier per step; the refill follows it
+        wait_vmem(n_ld * (ahead(i) < NS - 2 ? ahead(i) : NS - 2));
+        lds_barrier();
+        if (i + NS < n_steps) issue(i + NS, cur);
+      }
+    }
   };
 
   if (n_steps <= 0) return;
-  {
-    const StepInfo s0 = sched_decode(sc, g, 0);
-    const int b = s0.grp / sc.n_rg;
-    load_tile(b, s0.grp - b * sc.n_rg, s0.kt, kt0);
+  // Prologue: the block's first segment (queries) and one tile per buffer.
+  // Every buffer access below names its LDS array directly, so that the
+  // compiler can tell the tile being read from the tiles still being written.
+  const StepInfo s0 = sched_decode(sc, g, 0);
+  const int b0 = s0.grp / sc.n_rg;
+  if constexpr (NW == 1) {
+    // Tiles 0 .. NS - 2, then the queries; one full wait covers them all (the
+    // compiler sees the query registers ready), and tile NS - 1 streams in
+    // during step 0.
+    issue(0, kt0);
+    if (NS > 2 && n_steps > 1) issue(1, kt1);
+    if (NS > 3 && n_steps > 2) issue(2, kt2);
+    if (NS > 4 && n_steps > 3) issue(3, kt3);
+    begin_segment(b0, s0.grp - b0 * sc.n_rg);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
+    if (n_steps > NS - 1) {
+      if constexpr (NS == 2) issue(1, kt1);
+      if constexpr (NS == 3) issue(2, kt2);
+      if constexpr (NS == 4) issue(3, kt3);
+      if constexpr (NS == 5) issue(4, kt4);
+    }
+  } else {
+    begin_segment(b0, s0.grp - b0 * sc.n_rg);
+    issue(0, kt0);
+    if (n_steps > 1) issue(1, kt1);
+    if (NS > 2 && n_steps > 2) issue(2, kt2);
+    if (NS > 3 && n_steps > 3) issue(3, kt3);
+    if (NS > 4 && n_steps > 4) issue(4, kt4);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
   }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (int i = 0; i < n_steps; i += 2) {
-    step(i, kt0, kt1);
-    if (i + 1 < n_steps) step(i + 1, kt1, kt0);
+  lds_barrier();
+  for (int i = 0; i < n_steps; i += NS) {
+    step(i, kt0);
+    if (i + 1 < n_steps) step(i + 1, kt1);
+    if constexpr (NS > 2) if (i + 2 < n_steps) step(i + 2, kt2);
+    if constexpr (NS > 3) if (i + 3 < n_steps) step(i + 3, kt3);
+    if constexpr (NS > 4) if (i + 4 < n_steps) step(i + 4, kt4);
   }
 }
 

@@ -65,9 +65,13 @@ bool valid_config(const mla_layer_config* c, bool dense) {
   if (!valid_types(c)) return false;
   if (c->d_rope / 2 > mla::kMaxRopePairs) return false;
   if (dense && (c->d_nope + c->d_rope) / 2 > mla::kMaxRopePairs) return false;
-  // ring rows and key counts are kept in 32-bit integers inside the kernels
+  // ring rows, key counts and element offsets inside one sequence's ring are
+  // kept in 32-bit integers inside the kernels
   const int64_t ring_rows = (int64_t)c->window_frames * tokens_per_frame(*c);
   if (ring_rows >= (1LL << 30)) return false;
+  const int64_t row_elems = dense ? 2LL * c->n_heads * (c->d_nope + c->d_rope)
+                                  : (int64_t)c->d_c + c->d_rope;
+  if (ring_rows * row_elems >= (1LL << 31)) return false;
   return true;
 }
 
@@ -121,6 +125,7 @@ constexpr int64_t kMinStepsPerBlock = 8;
 mla::Schedule make_schedule(int64_t B, int64_t R, int64_t Lk, int32_t key_splits, int64_t cus,
                             mla::CoreShape sh, int chunks_per_key) {
   mla::Schedule s;
+  sh = mla::core_shape_for_keys(sh, chunks_per_key);
   const int64_t br = 32 * sh.waves;
   const int64_t n_rg = (R + br - 1) / br;
   const int64_t n_kt = (Lk + sh.key_tile - 1) / sh.key_tile;
@@ -146,6 +151,7 @@ mla::Schedule make_schedule(int64_t B, int64_t R, int64_t Lk, int32_t key_splits
   }
   s.block_rows = (int)br;
   s.key_tile = sh.key_tile;
+  s.stages = sh.stages;
   s.n_rg = (int)n_rg;
   s.n_kt = (int)n_kt;
   s.n_groups = (int)groups;
@@ -174,7 +180,7 @@ LatentLayout latent_layout(const mla_cache* h, int32_t Lq, int32_t key_splits) {
   const int64_t R = (int64_t)Lq * c.n_heads;
   LatentLayout L;
   L.sched = make_schedule(c.batch, R, window_keys(h), key_splits, mla::device_cu_count(),
-                          mla::core_shape_for_rows(R), (c.d_c + c.d_rope) / 8 + 1);
+                          mla::core_shape_for_rows(R), (c.d_c + c.d_rope) / 8);
   const size_t width = (size_t)(c.d_c + c.d_rope);
   const size_t slots = (size_t)L.sched.n_slots;
   L.qcat_off = 0;
@@ -198,7 +204,7 @@ DenseLayout dense_layout(const mla_cache* h, int32_t Lq) {
   L.lq_pad = (Lq + 32 * sh.waves - 1) / (32 * sh.waves) * (32 * sh.waves);
   const int64_t R = (int64_t)c.n_heads * L.lq_pad;
   L.sched = make_schedule(c.batch, R, window_keys(h), 0, mla::device_cu_count(), sh,
-                          2 * d_h / 8 + 1);
+                          2 * d_h / 8);
   const size_t slots = (size_t)L.sched.n_slots;
   L.qrot_off = 0;
   L.opart_off = round_up((size_t)c.batch * R * d_h * 2, kAlign);

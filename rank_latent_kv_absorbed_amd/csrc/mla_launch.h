@@ -47,15 +47,16 @@ struct CacheWriteArgs {
 #endif
 
 // Shapes of the attention core: a block of `waves` waves owns 32 * waves rows
-// and stages `key_tile` keys per LDS tile.  Many query rows (the chunk case)
-// take the widest block, which reuses each staged key tile most; a few rows
-// (cache-bound small-query shapes) take narrow blocks on short tiles so that
-// several blocks share a compute unit and keep more key bytes in flight.
+// and cycles `stages` LDS buffers of `key_tile` keys.  Many query rows (the
+// chunk case) take the widest block, which reuses each staged key tile most;
+// a few rows (cache-bound small-query shapes) take narrow blocks on short
+// tiles with deeper buffer rings, to keep more key bytes in flight per CU.
 struct CoreShape {
   int waves;
   int key_tile;
+  int stages;
 };
-constexpr CoreShape kCoreShapes[] = {{8, 64}, {4, 32}, {1, 32}};
+constexpr CoreShape kCoreShapes[] = {{8, 64, 2}, {4, 32, 4}, {1, 32, 2}};
 constexpr int kCoreMaxBlockRows = 256;
 
 // Shape for `rows` query rows of one row unit (latent: Lq * n_h rows of a
@@ -66,11 +67,22 @@ inline CoreShape core_shape_for_rows(int64_t rows) {
   return kCoreShapes[0];
 }
 
+// Stages of a shape for key rows of `chunks_per_key` 16-byte chunks: the
+// tile loads a wave keeps in flight behind the next tile (stages - 1 tiles of
+// key_tile * chunks_per_key / 64 loads for a one-wave block) must fit the
+// 63-count vector-memory counter.
+inline CoreShape core_shape_for_keys(CoreShape sh, int chunks_per_key) {
+  const int spans = sh.key_tile * chunks_per_key / 64 / sh.waves;
+  const int max_stages = 1 + 63 / (spans > 0 ? spans : 1);
+  if (sh.stages > max_stages) sh.stages = max_stages;
+  return sh;
+}
+
 // Blocks of a shape that fit one compute unit at once: LDS (160 KiB per CU)
-// holds two key tiles of `chunks_per_key` 16-byte chunks per key, and the
-// core's register use allows two waves per SIMD (eight per CU).
+// holds `stages` key tiles of `chunks_per_key` 16-byte chunks per key, and
+// the core's register use allows two waves per SIMD (eight per CU).
 inline int core_blocks_per_cu(CoreShape sh, int chunks_per_key) {
-  const int lds = 2 * sh.key_tile * chunks_per_key * 16;
+  const int lds = sh.stages * sh.key_tile * chunks_per_key * 16;
   const int by_lds = (160 * 1024) / lds;
   const int by_waves = 8 / sh.waves;
   return by_lds < by_waves ? by_lds : by_waves;
@@ -91,6 +103,7 @@ inline int core_blocks_per_cu(CoreShape sh, int chunks_per_key) {
 struct Schedule {
   int block_rows;       // rows per group (32 * waves of the core shape)
   int key_tile;         // keys per step
+  int stages;           // LDS tile buffers of the core shape
   int n_rg;             // row groups per batch element
   int n_kt;             // key tiles in the window
   int n_groups;         // batch * n_rg

@@ -60,13 +60,13 @@ void fake_write_info(long long* o) {
 }
 // key_slot0, Lk, B, Lq, q_token0, ring_rows, n_h, d_c, then the schedule:
 // n_rg, n_kt, n_groups, n_blocks, full_rounds, rem, main_len, tail_per_block, n_slots,
-// block_rows, key_tile
+// block_rows, key_tile, stages
 void fake_attend_info(long long* o) {
   const mla::AttendArgs& a = g_attend;
   const mla::Schedule& s = a.sched;
-  long long v[19] = {a.key_slot0, a.Lk, a.B, a.Lq, a.q_token0, a.ring_rows, a.n_h, a.d_c,
+  long long v[20] = {a.key_slot0, a.Lk, a.B, a.Lq, a.q_token0, a.ring_rows, a.n_h, a.d_c,
                      s.n_rg, s.n_kt, s.n_groups, s.n_blocks, s.full_rounds, s.rem, s.main_len,
-                     s.tail_per_block, s.n_slots, s.block_rows, s.key_tile};
+                     s.tail_per_block, s.n_slots, s.block_rows, s.key_tile, s.stages};
   memcpy(o, v, sizeof(v));
 }
 // The last (which = 0: latent, 1: dense) attend's schedule as the kernels decode it.
@@ -85,12 +85,12 @@ int fake_sched_group_slots(int which, int grp) {
 }
 float fake_attend_qscale() { return g_attend.qscale; }
 // key_slot0, Lk, B, Lq, q_token0, n_rg, n_kt, n_groups, n_blocks, full_rounds, rem,
-// main_len, tail_per_block, n_slots, block_rows, key_tile
+// main_len, tail_per_block, n_slots, block_rows, key_tile, stages
 void fake_mha_info(long long* o) {
   const mla::Schedule& s = g_mha_sched;
-  long long v[16] = {g_mha.key_slot0, g_mha.Lk, g_mha.B, g_mha.Lq, g_mha.q_token0, s.n_rg,
+  long long v[17] = {g_mha.key_slot0, g_mha.Lk, g_mha.B, g_mha.Lq, g_mha.q_token0, s.n_rg,
                      s.n_kt, s.n_groups, s.n_blocks, s.full_rounds, s.rem, s.main_len,
-                     s.tail_per_block, s.n_slots, s.block_rows, s.key_tile};
+                     s.tail_per_block, s.n_slots, s.block_rows, s.key_tile, s.stages};
   memcpy(o, v, sizeof(v));
 }
 // which: 0 = last write, 1 = last attend, 2 = last dense attend

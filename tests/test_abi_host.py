@@ -109,32 +109,35 @@ def _write_info(L):
 
 
 def _attend_info(L):
-    a = (ctypes.c_longlong * 19)()
+    a = (ctypes.c_longlong * 20)()
     L.fake_attend_info(a)
     keys = ["key_slot0", "Lk", "B", "Lq", "q_token0", "ring_rows", "n_h", "d_c", "n_rg", "n_kt",
             "n_groups", "n_blocks", "full_rounds", "rem", "main_len", "tpb", "n_slots",
-            "block_rows", "key_tile"]
+            "block_rows", "key_tile", "stages"]
     return dict(zip(keys, list(a)))
 
 
 def _mha_info(L):
-    a = (ctypes.c_longlong * 16)()
+    a = (ctypes.c_longlong * 17)()
     L.fake_mha_info(a)
     keys = ["key_slot0", "Lk", "B", "Lq", "q_token0", "n_rg", "n_kt", "n_groups", "n_blocks",
-            "full_rounds", "rem", "main_len", "tpb", "n_slots", "block_rows", "key_tile"]
+            "full_rounds", "rem", "main_len", "tpb", "n_slots", "block_rows", "key_tile",
+            "stages"]
     return dict(zip(keys, list(a)))
 
 
-# Core shapes (block rows, key tile) by rows per row unit, and how many blocks
-# of each fit one compute unit (two LDS tiles of key_tile * chunks * 16 bytes in
-# 160 KiB; at most eight waves).
-def expected_shape(rows):
-    return (32, 32) if rows <= 32 else ((128, 32) if rows <= 128 else (256, 64))
+# Core shapes (block rows, key tile, LDS stages) by rows per row unit, and how
+# many blocks of each fit one compute unit (stages LDS tiles of
+# key_tile * chunks * 16 bytes in 160 KiB; at most eight waves).
+def expected_shape(rows, chunks_per_key=28):
+    br, kt, ns = (32, 32, 2) if rows <= 32 else ((128, 32, 4) if rows <= 128 else (256, 64, 2))
+    spans = kt * chunks_per_key // 64 // (br // 32)   # tile loads per wave
+    return br, kt, min(ns, 1 + 63 // spans)           # in-flight loads fit a 6-bit counter
 
 
 def blocks_per_cu(shape, chunks_per_key):
-    br, kt = shape
-    return min(160 * 1024 // (2 * kt * chunks_per_key * 16), 8 // (br // 32))
+    br, kt, ns = shape
+    return min(160 * 1024 // (ns * kt * chunks_per_key * 16), 8 // (br // 32))
 
 
 def check_schedule(L, info, R, which=0):
@@ -197,6 +200,15 @@ def test_invalid_configs_rejected(sim):
     c = _cfg()
     st, _ = _create(sim, c, nbytes=14_676_480 - 1)
     assert st == 2
+    # one sequence's ring must stay below 2^31 elements (32-bit offsets in the kernels)
+    c = _cfg(window_frames=6146)                   # 9 587 760 rows x 224 >= 2^31
+    assert sim.mla_cache_bytes(ctypes.byref(c)) == 0
+    c = _cfg(window_frames=6145)                   # 9 586 200 rows x 224 < 2^31
+    assert sim.mla_cache_bytes(ctypes.byref(c)) == 9_586_200 * 224 * 2
+    c = _cfg(window_frames=449)                    # dense: 700 440 rows x 3072 > 2^31
+    assert sim.mha_cache_bytes(ctypes.byref(c)) == 0
+    c = _cfg(window_frames=448)
+    assert sim.mha_cache_bytes(ctypes.byref(c)) == 448 * 1560 * 3072 * 2
 
 
 def test_rollout_schedule_matches_ring_model(sim):
@@ -296,9 +308,9 @@ def test_attend_arguments_and_workspace(sim):
                               P(ws), 1 << 40, None) == 0
         a = _attend_info(sim)
         shape = expected_shape(Lq * 12)
-        assert (a["block_rows"], a["key_tile"]) == shape
+        assert (a["block_rows"], a["key_tile"], a["stages"]) == shape
         check_schedule(sim, a, Lq * 12)
-        resident = 256 * blocks_per_cu(shape, 224 // 8 + 1)
+        resident = 256 * blocks_per_cu(shape, 224 // 8)
         assert a["n_blocks"] == min(resident, -(-a["n_groups"] * a["n_kt"] // 8))
 
 
@@ -309,17 +321,17 @@ def test_dense_attend_schedule(sim):
     ws = 1 << 40
     for Lq in (1, 31, 32, 33, 128, 129, 4680):
         need = sim.mha_attend_workspace_bytes(h, Lq)
-        shape = expected_shape(Lq)
+        shape = expected_shape(Lq, 32)
         lq_pad = -(-Lq // shape[0]) * shape[0]
         R = 12 * lq_pad
         assert need >= R * 128 * 2 + R * 128 * 4 + R * 8
         assert sim.mha_attend(h, P(FAKE_PTR), 0, Lq, P(FAKE_PTR), P(ws), need - 1, None) == 7
         assert sim.mha_attend(h, P(FAKE_PTR), 21 * 1560, Lq, P(FAKE_PTR), P(ws), need, None) == 0
         a = _mha_info(sim)
-        assert (a["block_rows"], a["key_tile"]) == shape
+        assert (a["block_rows"], a["key_tile"], a["stages"]) == shape
         assert a["Lk"] == 21 * 1560 and a["Lq"] == Lq and a["q_token0"] == 21 * 1560
         check_schedule(sim, a, R, which=1)
-        resident = 256 * blocks_per_cu(shape, 2 * 128 // 8 + 1)
+        resident = 256 * blocks_per_cu(shape, 2 * 128 // 8)
         assert a["n_blocks"] == min(resident, -(-a["n_groups"] * a["n_kt"] // 8))
 
 
