@@ -87,6 +87,10 @@ __device__ __forceinline__ void global_to_lds16(const void* g, void* lds) {
 #endif
 }
 
+// Lambdas of the kernel body are always inlined: one left out of line would
+// turn its reference captures into loads through a stack frame.
+#define MLA_INLINE __attribute__((always_inline))
+
 // Raise-the-max threshold of the lazy rescale (log2 units).
 constexpr float kRescaleThreshold = 8.0f;
 
@@ -183,7 +187,7 @@ void attn_core_kernel(AttnCore a) {
   // puts keys 4j .. 4j + 3 in different 4-chunk groups.  With 64 banks of
   // 4 bytes, the 16 lanes of a score read and the 32 lanes of a transpose
   // read then touch every bank once.
-  auto swz = [](int r) {
+  auto swz = [](int r) MLA_INLINE {
     return SHARED_KV ? (((r >> 2) ^ (r >> 1)) & 3) : (((r & 3) << 2) | ((r >> 2) & 3));
   };
 
@@ -195,26 +199,54 @@ void attn_core_kernel(AttnCore a) {
   // row.  Offsets within one sequence's ring fit 32 bits (checked when the
   // cache is created).
   constexpr int LPW = (SPANS + NW - 1) / NW;  // span slots per wave
-  auto load_tile = [&](int b, int rg, int kt, E* dst) {
+  // Lane offset (elements) of span sp relative to the first key row of a
+  // tile and the head's K columns (V columns sit at v_off - k_off from K).
+  // 16 keys fill CPK / 4 spans exactly and the chunk permutation repeats
+  // every 16 keys, so span sp + CPK / 4 is span sp shifted by 16 key rows: a
+  // one-wave block keeps the CPK / 4 distinct lane offsets, a wider block the
+  // offsets of its own (at most four) spans.
+  constexpr int PER = CPK / 4;
+  static_assert((64 * PER) % CPK == 0 && 64 * PER / CPK == 16, "16 keys per span period");
+  auto lane_offset = [&](int sp) MLA_INLINE {
+    const int c = sp * 64 + l;
+    const int key = c / CPK, q = (c - key * CPK) ^ swz(key);
+    return key * a.ring_stride + (q < KCH ? q * 8 : a.v_off - a.k_off + (q - KCH) * 8);
+  };
+  constexpr int LKEEP = NW == 1 ? (PER < SPANS ? PER : SPANS) : LPW;
+  int lane_off[LKEEP];
+#pragma unroll
+  for (int j = 0; j < LKEEP; ++j) lane_off[j] = lane_offset(NW == 1 ? j : w + j * NW);
+  auto load_tile = [&](int b, int rg, int kt, E* dst) MLA_INLINE {
     const E* ring = (const E*)a.ring + (size_t)b * a.ring_rows * a.ring_stride;
     const int head = (rg * BR) / a.rows_per_head;
-    const int koff = a.k_off + head * a.head_stride;
-    const int voff = a.v_off + head * a.head_stride;
-    const int t0 = kt * KT;
     const int rows = (int)a.ring_rows;
+    int s0 = (int)a.key_slot0 + kt * KT;
+    s0 = s0 >= rows ? s0 - rows : s0;
+    const E* base = ring + ((size_t)s0 * a.ring_stride + a.k_off + head * a.head_stride);
+    // Keys of a tile that crosses the ring's end continue at its start: the
+    // lane offsets at or past the crossing move back by the ring size.
+    // (Keys past the window still read ring rows - allocated, possibly stale
+    // memory; the step that uses the tile clears them in LDS.)
+    const bool wraps = s0 + KT > rows;
+    const int split = (rows - s0) * a.ring_stride, back = rows * a.ring_stride;
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
       const int sp = w + j * NW;
       if (sp < SPANS) {
-        const int c = sp * 64 + l;
-        const int key = c / CPK, q = (c - key * CPK) ^ swz(key);
-        const int kg = min(t0 + key, a.Lk - 1);
-        int slot = (int)a.key_slot0 + kg;
-        slot = slot >= rows ? slot - rows : slot;
-        const int col = q < KCH ? koff + q * 8 : voff + (q - KCH) * 8;
-        global_to_lds16(ring + (slot * a.ring_stride + col), dst + sp * 512);
+        int off = NW == 1 ? (j / PER) * 16 * a.ring_stride + lane_off[j % PER] : lane_off[j];
+        if (wraps) off = off >= split ? off - back : off;
+        global_to_lds16(base + off, dst + sp * 512);
       }
     }
+  };
+
+  // Zero the rows of keys past the window in a ragged last tile: their
+  // scores are masked, and zero values keep the value product finite.
+  auto scrub = [&](int kt, E* buf) MLA_INLINE {
+    const int nk = a.Lk - kt * KT;  // keys of the tile inside the window (0 < nk < KT)
+    f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int c = nk * CPK + w * 64 + l; c < KT * CPK; c += NW * 64)
+      *reinterpret_cast<f32x4*>(buf + c * 8) = zero;
   };
 
   // Lane-constant parts of the LDS read addresses.  Score reads: lane (lo, hi)
@@ -242,11 +274,11 @@ void attn_core_kernel(AttnCore a) {
 
   // Tiles issued after tile i + 1 by the end of step i, counting the refill
   // of step i itself (the ring is short near the end of the block's steps).
-  auto ahead = [&](int i) {
+  auto ahead = [&](int i) MLA_INLINE {
     const int a2 = n_steps - i - 2;
     return a2 < 0 ? 0 : (a2 < NS - 1 ? a2 : NS - 1);
   };
-  auto issue = [&](int i, E* dst) {
+  auto issue = [&](int i, E* dst) MLA_INLINE {
     const StepInfo sn = sched_decode(sc, g, i);
     const int b1 = sn.grp / sc.n_rg;
     load_tile(b1, sn.grp - b1 * sc.n_rg, sn.kt, dst);
@@ -254,7 +286,7 @@ void attn_core_kernel(AttnCore a) {
 
   // New row-group segment: query fragments in (global loads, not waited on
   // here), running state reset.
-  auto begin_segment = [&](int b, int rg) {
+  auto begin_segment = [&](int b, int rg) MLA_INLINE {
     row = rg * BR + w * 32 + lo;
     const int row0 = rg * BR + w * 32;  // rows of a wave never straddle a head
     live = row0 < a.R && (row0 % a.rows_per_head) < a.valid_per_head;
@@ -274,12 +306,16 @@ void attn_core_kernel(AttnCore a) {
   // with it, tile i + NS is issued into the same buffer.  (Issuing at the end
   // of a step keeps each buffer's write after its read within one unrolled
   // loop pass; the compiler then adds no wait of its own for the tile loads.)
-  auto step = [&](int i, E* cur) {
+  auto step = [&](int i, E* cur) MLA_INLINE {
     const StepInfo si = sched_decode(sc, g, i);
     const int b = si.grp / sc.n_rg;
     const int rg = si.grp - b * sc.n_rg;
     const int kt = si.kt;
 
+    if (kt * KT + KT > a.Lk) {  // ragged last tile: clear the keys past the window
+      scrub(kt, cur);
+      lds_barrier();
+    }
     if (si.first && i > 0) {
       // A segment starting mid-block: its query loads retire in order behind
       // the tiles in flight, so wait for all of them here (rare: only blocks
@@ -296,7 +332,7 @@ void attn_core_kernel(AttnCore a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) sv[kb][r] = 0.0f;
         const E* krow = cur + (kb * 32 + lo) * KSTR;
-        auto kptr = [&](int ks) {
+        auto kptr = [&](int ks) MLA_INLINE {
           return SHARED_KV ? krow + 32 * (ks >> 1) + ((ks & 1) ? k_off1 : k_off0)
                            : krow + 8 * ((2 * ks + hi) ^ k_sw);
         };
