@@ -133,15 +133,16 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Register budget: two waves per SIMD whatever the block size, so that narrow
-// blocks can share a compute unit.
-template <typename E, int DQK, int DV, int NW, int KT, int NS, bool SHARED_KV>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+// Register budget: two waves per SIMD for one 32-row block per wave, so that
+// narrow blocks can share a compute unit; one wave per SIMD (the whole
+// register file, accumulators in AGPRs) when each wave owns RB > 1 row blocks.
+template <typename E, int DQK, int DV, int NW, int KT, int NS, bool SHARED_KV, int RB = 1>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 2 : 1, RB == 1 ? 2 : 1)))
 void attn_core_kernel(AttnCore a) {
   typedef typename Elem<E>::v8 V8;
   constexpr int NKS = DQK / 16;               // MFMA depth steps of the score product
   constexpr int NDT = DV / 32;                // 32-wide tiles of the value product
-  constexpr int BR = NW * 32;                 // rows per row group
+  constexpr int BR = NW * 32 * RB;            // rows per row group (32 * RB per wave)
   constexpr int NKB = KT / 32;                // 32-key blocks per tile
   constexpr int KCH = DQK / 8;                // 16-byte chunks of K per key
   constexpr int CPK = SHARED_KV ? KCH : KCH + DV / 8;  // chunks staged per key
@@ -153,7 +154,7 @@ void attn_core_kernel(AttnCore a) {
   static_assert(KT == 32 || KT == 64, "key tiles are one or two 32-key MFMA blocks");
   static_assert(!SHARED_KV || DV <= DQK, "shared rows hold V inside K");
   static_assert(NS >= 2 && NS <= 5, "two to five tile buffers");
-  static_assert(SPANS * (NS - 1) <= 63, "tile loads in flight fit the vmcnt counter");
+  static_assert((SPANS + NW - 1) / NW * (NS - 1) <= 63, "tile loads in flight fit the vmcnt counter");
   // Whole spans with every lane active (exact load counts per wave); the chunk
   // permutation stays inside aligned groups of a row.
   static_assert(CHUNKS % 64 == 0, "tiles are whole 1-KiB spans");
@@ -266,10 +267,19 @@ void attn_core_kernel(AttnCore a) {
   const int tr_off0 = tr_h + 8 * (tr_c ^ (tr_sw0 & 3)), tr_off1 = tr_h + 8 * (tr_c ^ (tr_sw1 & 3));
   const int tr_dt0 = tr_sw0 >> 2, tr_dt1 = tr_sw1 >> 2;  // 0 for latent rows
 
-  V8 qf[NKS];
-  f32x16 o[NDT];
-  float m = -INFINITY, lsum = 0.0f;
-  int row = 0;
+  // Per row block rb of the wave: query fragments, value sums, running max
+  // and sum, the lane's row.  Each key fragment read from LDS feeds RB
+  // products, so LDS traffic per product falls as 1 / RB.
+  V8 qf[RB][NKS];
+  f32x16 o[RB][NDT];
+  float m[RB], lsum[RB];
+  int row[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    m[rb] = -INFINITY;
+    lsum[rb] = 0.0f;
+    row[rb] = 0;
+  }
   bool live = false;  // this wave's rows include a real one (wave-uniform)
 
   // Tiles issued after tile i + 1 by the end of step i, counting the refill
@@ -287,19 +297,23 @@ void attn_core_kernel(AttnCore a) {
   // New row-group segment: query fragments in (global loads, not waited on
   // here), running state reset.
   auto begin_segment = [&](int b, int rg) MLA_INLINE {
-    row = rg * BR + w * 32 + lo;
-    const int row0 = rg * BR + w * 32;  // rows of a wave never straddle a head
+    const int row0 = rg * BR + w * 32 * RB;  // rows of a wave never straddle a head
     live = row0 < a.R && (row0 % a.rows_per_head) < a.valid_per_head;
-    const bool ok = row < a.R && (row % a.rows_per_head) < a.valid_per_head;
-    const E* src = (const E*)a.qrows + ((size_t)b * a.R + (ok ? row : 0)) * DQK + 8 * hi;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) qf[ks] = ok ? ld8<E>(src + 16 * ks) : zero8<E>();
+    for (int rb = 0; rb < RB; ++rb) {
+      row[rb] = row0 + 32 * rb + lo;
+      const int r = row[rb];
+      const bool ok = r < a.R && (r % a.rows_per_head) < a.valid_per_head;
+      const E* src = (const E*)a.qrows + ((size_t)b * a.R + (ok ? r : 0)) * DQK + 8 * hi;
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
+      for (int ks = 0; ks < NKS; ++ks) qf[rb][ks] = ok ? ld8<E>(src + 16 * ks) : zero8<E>();
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[dt][r] = 0.0f;
-    m = -INFINITY;
-    lsum = 0.0f;
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) o[rb][dt][q] = 0.0f;
+      m[rb] = -INFINITY;
+      lsum[rb] = 0.0f;
+    }
   };
 
   // One step: `cur` holds the key tile of step i.  Once every wave is done
@@ -326,56 +340,64 @@ void attn_core_kernel(AttnCore a) {
     }
 
     if (live) {
-      f32x16 sv[NKB];
+      f32x16 sv[RB][NKB];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sv[kb][r] = 0.0f;
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sv[rb][kb][r] = 0.0f;
         const E* krow = cur + (kb * 32 + lo) * KSTR;
         auto kptr = [&](int ks) MLA_INLINE {
           return SHARED_KV ? krow + 32 * (ks >> 1) + ((ks & 1) ? k_off1 : k_off0)
                            : krow + 8 * ((2 * ks + hi) ^ k_sw);
         };
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) sv[kb] = Elem<E>::mfma(ld8<E>(kptr(ks)), qf[ks], sv[kb]);
+        for (int ks = 0; ks < NKS; ++ks) {
+          const V8 kf = ld8<E>(kptr(ks));
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) sv[rb][kb] = Elem<E>::mfma(kf, qf[rb][ks], sv[rb][kb]);
+        }
       }
       const int t0 = kt * KT;
-      if (t0 + KT > a.Lk) {
+      V8 pf[RB][NKB][2];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        if (t0 + KT > a.Lk) {
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (t0 + kb * 32 + acc_row(r, hi) >= a.Lk) sv[rb][kb][r] = -INFINITY;
+        }
+        float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (t0 + kb * 32 + acc_row(r, hi) >= a.Lk) sv[kb][r] = -INFINITY;
-      }
-
-      float mx = -INFINITY;
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sv[rb][kb][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        // lazy rescale: raise the max only when a score passes it by > 2^8
+        if (__ballot(mx > m[rb] + kRescaleThreshold)) {
+          const float mnew = fmaxf(m[rb], mx);
+          const float alpha = exp2_fast(m[rb] - mnew);
+          m[rb] = mnew;
+          lsum[rb] *= alpha;
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+          for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sv[kb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      // lazy rescale: raise the max only when a score passes it by > 2^8
-      if (__ballot(mx > m + kRescaleThreshold)) {
-        const float mnew = fmaxf(m, mx);
-        const float alpha = exp2_fast(m - mnew);
-        m = mnew;
-        lsum *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-      }
-      V8 pf[NKB][2];
-      float ps = 0.0f;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = exp2_fast(sv[kb][r] - m);
-          ps += p;
-          pf[kb][r >> 3][r & 7] = Elem<E>::from(p);
+            for (int r = 0; r < 16; ++r) o[rb][dt][r] *= alpha;
         }
-      lsum += ps;
+        float ps = 0.0f;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float p = exp2_fast(sv[rb][kb][r] - m[rb]);
+            ps += p;
+            pf[rb][kb][r >> 3][r & 7] = Elem<E>::from(p);
+          }
+        lsum[rb] += ps;
+      }
 
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
@@ -388,26 +410,31 @@ void attn_core_kernel(AttnCore a) {
             const i16x4 lo4 = lds_read_tr16(vrow + 32 * d0 + tr_off0);
             const i16x4 hi4 = lds_read_tr16(vrow + 8 * KSTR + 32 * d1 + tr_off1);
             const V8 va = __builtin_bit_cast(V8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-            o[dt] = Elem<E>::mfma(va, pf[kb][st], o[dt]);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) o[rb][dt] = Elem<E>::mfma(va, pf[rb][kb][st], o[rb][dt]);
           }
         }
 
       if (si.last) {  // segment ends: write this block's partial
         const int slot = si.slot;
-        const float ltot = lsum + __shfl_xor(lsum, 32);
-        if (row < a.R) {
-          const size_t prow = ((size_t)slot * a.B + b) * a.R + row;
-          float* op = a.opart + prow * DV;
 #pragma unroll
-          for (int dt = 0; dt < NDT; ++dt)
+        for (int rb = 0; rb < RB; ++rb) {
+          const float ltot = lsum[rb] + __shfl_xor(lsum[rb], 32);
+          if (row[rb] < a.R) {
+            const size_t prow = ((size_t)slot * a.B + b) * a.R + row[rb];
+            float* op = a.opart + prow * DV;
 #pragma unroll
-            for (int gg = 0; gg < 4; ++gg) {
-              f32x4 v = {o[dt][4 * gg], o[dt][4 * gg + 1], o[dt][4 * gg + 2], o[dt][4 * gg + 3]};
-              *reinterpret_cast<f32x4*>(op + dt * 32 + 8 * gg + 4 * hi) = v;
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+              for (int gg = 0; gg < 4; ++gg) {
+                f32x4 v = {o[rb][dt][4 * gg], o[rb][dt][4 * gg + 1], o[rb][dt][4 * gg + 2],
+                           o[rb][dt][4 * gg + 3]};
+                *reinterpret_cast<f32x4*>(op + dt * 32 + 8 * gg + 4 * hi) = v;
+              }
+            if (hi == 0) {
+              a.ml[prow * 2] = m[rb];
+              a.ml[prow * 2 + 1] = ltot;
             }
-          if (hi == 0) {
-            a.ml[prow * 2] = m;
-            a.ml[prow * 2 + 1] = ltot;
           }
         }
       }
