@@ -183,6 +183,32 @@ mla_status mla_attend(mla_cache* cache, const void* q, int64_t q_token0, int32_t
                       const void* w_uk, const void* w_uv, float* out, int32_t key_splits,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* How mla_attend computes (mla_cache_set_attend_path / mla_attend_path).
+ * MLA_PATH_ABSORBED: scores and value sums in the d_c-wide latent space with
+ *   W^K_up folded into the queries and W^V_up applied after the softmax sum.
+ * MLA_PATH_EXPAND: per-head keys [W^K_up,h c_j | k^R_j] and values W^V_up,h c_j
+ *   of the whole window rebuilt once per call into the workspace, then plain
+ *   per-head attention over them (method item 2 taken literally: the per-head
+ *   keys and values are reconstructed from the latent on demand).  Needs fewer
+ *   products per query than the absorbed form; the rebuild is a fixed cost per
+ *   call, paid back from a few hundred queries on.
+ * MLA_PATH_AUTO: the library picks by chunk length (expand from 512 queries,
+ *   when the handle supports it and key_splits is 0).  Both paths compute the
+ * same function; they differ in rounding (the expanded keys and values are
+ * rounded to the cache's element type). */
+typedef enum { MLA_PATH_AUTO = 0, MLA_PATH_ABSORBED = 1, MLA_PATH_EXPAND = 2 } mla_attend_path_kind;
+
+/* Selects the path of later mla_attend calls on this latent handle.
+ * MLA_ERR_UNSUPPORTED for MLA_PATH_EXPAND when the handle is not a 16-bit
+ * storage handle with d_nope + d_rope == d_v == 128, d_c in {64, 128, 192},
+ * d_nope a multiple of 32; MLA_ERR_WRONG_KIND on a dense handle. */
+mla_status mla_cache_set_attend_path(mla_cache* cache, int32_t path);
+
+/* The path mla_attend takes for Lq queries and `key_splits` (MLA_PATH_ABSORBED
+ * or MLA_PATH_EXPAND; -1 for bad arguments).  key_splits > 0 and fp32 handles
+ * always take the absorbed path. */
+int32_t mla_attend_path(const mla_cache* cache, int32_t Lq, int32_t key_splits);
+
 /* Workspace for mha_attend (rotated, pre-scaled queries). */
 size_t mha_attend_workspace_bytes(const mla_cache* cache, int32_t Lq);
 

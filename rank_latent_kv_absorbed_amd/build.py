@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libmla.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["mla_host.cpp", "mla_cache_write.hip", "mla_attend.hip", "mha_attend.hip"]
+SOURCES = ["mla_host.cpp", "mla_cache_write.hip", "mla_attend.hip", "mha_attend.hip", "mla_expand.hip"]
 ARCH = "gfx950"
 
 

@@ -228,6 +228,21 @@ struct MhaAttendArgs {
   RopeTable rope;
 };
 
+// Expand-then-attend: per-head keys and values of the resident window rebuilt
+// from the latent ring into the dense cache's layout.
+struct ExpandArgs {
+  const void* ring;       // [B][ring_rows][d_c + d_rope] cache type
+  const void* w_uk;       // [n_h][d_nope][d_c] bf16
+  const void* w_uv;       // [n_h][d_v][d_c] bf16
+  void* wx;               // workspace [n_h][d_nope + d_v][d_c] cache type
+  void* kv;               // workspace [B][Lk][2][n_h][d_nope + d_rope] cache type
+  int B, n_h, d_nope, d_rope, d_c, d_v;
+  int64_t ring_rows;
+  int64_t key_slot0;      // ring slot of resident key 0
+  int Lk;
+  int cache_type;         // 1 = bf16, 2 = fp16
+};
+
 hipError_t launch_cache_write_bf16(const CacheWriteArgs& a, hipStream_t s);
 hipError_t launch_cache_write_f32(const CacheWriteArgs& a, hipStream_t s);
 bool cache_write_bf16_supported(int width, int hidden);
@@ -246,5 +261,10 @@ hipError_t launch_mha_attend_bf16_ws(const MhaAttendArgs& a, float* opart, float
 int device_cu_count();
 hipError_t launch_mha_attend_f32(const MhaAttendArgs& a, hipStream_t s);
 bool mha_attend_bf16_supported(int d_h);
+
+// Expand-then-attend: the rebuild kernels (then launch_mha_attend_bf16_ws on
+// the expanded buffer).
+bool expand_supported(int d_c, int d_rope, int d_nope, int d_v);
+hipError_t launch_expand_kv(const ExpandArgs& a, hipStream_t s);
 
 }  // namespace mla

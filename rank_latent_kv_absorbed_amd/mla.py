@@ -74,6 +74,8 @@ SIGNATURES = {
     "mha_attend_workspace_bytes": (_SZ, [_HANDLE, _I32]),
     "mha_attend": (_I32, [_HANDLE, _VP, _I64, _I32, _VP, _VP, _SZ, _VP]),
     "mla_cache_set_profile_events": (_I32, [_HANDLE, _VP, _VP]),
+    "mla_cache_set_attend_path": (_I32, [_HANDLE, _I32]),
+    "mla_attend_path": (_I32, [_HANDLE, _I32, _I32]),
     "mla_status_str": (ctypes.c_char_p, [_I32]),
     "mla_version": (ctypes.c_char_p, []),
 }
@@ -211,6 +213,10 @@ class _CacheBase:
                                                   ctypes.c_void_p(stop)), "set_profile_events")
 
 
+# mla_attend_path_kind
+ATTEND_PATHS = {"auto": 0, "absorbed": 1, "expand": 2}
+
+
 class LatentCache(_CacheBase):
     """One cached layer's sliding window of (c^KV, k^R) rows."""
 
@@ -233,6 +239,17 @@ class LatentCache(_CacheBase):
 
     def workspace_bytes(self, Lq, key_splits=0):
         return lib().mla_attend_workspace_bytes(self._h, int(Lq), int(key_splits))
+
+    def set_attend_path(self, path):
+        """'auto', 'absorbed' or 'expand' (see ATTEND_PATHS)."""
+        _check(lib().mla_cache_set_attend_path(self._h, ATTEND_PATHS[path]), "set_attend_path")
+
+    def attend_path(self, Lq, key_splits=0):
+        """Name of the path an attend of Lq queries takes on this handle."""
+        k = lib().mla_attend_path(self._h, int(Lq), int(key_splits))
+        if k < 0:
+            raise ValueError(f"attend_path: bad arguments Lq={Lq} key_splits={key_splits}")
+        return {v: n for n, v in ATTEND_PATHS.items()}[k]
 
     def attend(self, q, q_token0, w_uk, w_uv, out=None, key_splits=0, workspace=None, stream=None):
         cfg = self.cfg
@@ -311,6 +328,14 @@ def attend_bytes(n_heads, Lq, Lk, d_c, d_rope, d_nope, d_v, batch=1, elem=2):
     in, fp32 output out, and the up-projection weights."""
     return batch * (Lk * (d_c + d_rope) * elem + Lq * n_heads * (d_nope + d_rope) * elem
                     + Lq * n_heads * d_v * 4) + n_heads * (d_nope + d_v) * d_c * elem
+
+
+def expand_attend_flops(n_heads, Lq, Lk, d_c, d_rope, d_nope, d_v, batch=1):
+    """Algorithmic FLOP of one expand-then-attend call: the window's per-head
+    keys and values rebuilt once, then per-head scores (d_nope + d_rope) and
+    value sums (d_v)."""
+    rebuild = batch * Lk * n_heads * 2 * d_c * (d_nope + d_v)
+    return rebuild + batch * n_heads * Lq * Lk * 2 * (d_nope + d_rope + d_v)
 
 
 def mha_attend_flops(n_heads, Lq, Lk, d_h, batch=1):

@@ -1,6 +1,8 @@
 // Recording launcher for CPU tests of the host library: the kernels are
 // replaced by functions that store their arguments (and can be told to fail),
 // so window bookkeeping, validation and launch arguments run on any machine.
+#include <math.h>
+#include <stdint.h>
 #include <string.h>
 
 #include "mla_launch.h"
@@ -10,7 +12,11 @@ mla::CacheWriteArgs g_write;
 mla::AttendArgs g_attend;
 mla::MhaAttendArgs g_mha;
 mla::Schedule g_mha_sched;
-int g_kind = 0;  // 1 write bf16, 2 write f32, 3 attend bf16, 4 attend f32, 5 mha bf16, 6 mha f32
+mla::ExpandArgs g_expand;
+float* g_mha_opart = nullptr;
+float* g_mha_ml = nullptr;
+// 1 write bf16, 2 write f32, 3 attend bf16, 4 attend f32, 5 mha bf16, 6 mha f32, 7 expand
+int g_kind = 0;
 int g_count = 0;
 int g_fail = 0;
 hipError_t rec(int kind) {
@@ -38,12 +44,19 @@ hipError_t launch_cache_write_bf16(const CacheWriteArgs& a, hipStream_t) { g_wri
 hipError_t launch_cache_write_f32(const CacheWriteArgs& a, hipStream_t) { g_write = a; return rec(2); }
 hipError_t launch_attend_bf16(const AttendArgs& a, hipStream_t) { g_attend = a; return rec(3); }
 hipError_t launch_attend_f32(const AttendArgs& a, hipStream_t) { g_attend = a; return rec(4); }
-hipError_t launch_mha_attend_bf16_ws(const MhaAttendArgs& a, float*, float*, const Schedule& sc,
-                                     hipStream_t) {
+hipError_t launch_mha_attend_bf16_ws(const MhaAttendArgs& a, float* opart, float* ml,
+                                     const Schedule& sc, hipStream_t) {
   g_mha = a;
   g_mha_sched = sc;
+  g_mha_opart = opart;
+  g_mha_ml = ml;
   return rec(5);
 }
+bool expand_supported(int d_c, int d_rope, int d_nope, int d_v) {
+  return (d_c == 64 || d_c == 128 || d_c == 192) && d_nope + d_rope == 128 && d_v == 128 &&
+         d_nope % 32 == 0 && d_rope % 8 == 0;
+}
+hipError_t launch_expand_kv(const ExpandArgs& a, hipStream_t) { g_expand = a; return rec(7); }
 hipError_t launch_mha_attend_f32(const MhaAttendArgs& a, hipStream_t) { g_mha = a; return rec(6); }
 }  // namespace mla
 
@@ -91,6 +104,24 @@ void fake_mha_info(long long* o) {
   long long v[17] = {g_mha.key_slot0, g_mha.Lk, g_mha.B, g_mha.Lq, g_mha.q_token0, s.n_rg,
                      s.n_kt, s.n_groups, s.n_blocks, s.full_rounds, s.rem, s.main_len,
                      s.tail_per_block, s.n_slots, s.block_rows, s.key_tile, s.stages};
+  memcpy(o, v, sizeof(v));
+}
+// The last expand: B, ring_rows, key_slot0, Lk, n_h, d_nope, d_rope, d_c, d_v,
+// cache_type, then the wx, kv, ring and w_uk pointers as integers.
+void fake_expand_info(long long* o) {
+  const mla::ExpandArgs& a = g_expand;
+  long long v[14] = {a.B, a.ring_rows, a.key_slot0, a.Lk, a.n_h, a.d_nope, a.d_rope, a.d_c, a.d_v,
+                     a.cache_type, (long long)(intptr_t)a.wx, (long long)(intptr_t)a.kv,
+                     (long long)(intptr_t)a.ring, (long long)(intptr_t)a.w_uk};
+  memcpy(o, v, sizeof(v));
+}
+// The last dense attend's ring_rows, d_h, ring, qrot, opart, ml, q, out pointers and qscale*1e6.
+void fake_mha_ptrs(long long* o) {
+  const mla::MhaAttendArgs& a = g_mha;
+  long long v[9] = {a.ring_rows, a.d_h, (long long)(intptr_t)a.ring, (long long)(intptr_t)a.qrot,
+                    (long long)(intptr_t)g_mha_opart, (long long)(intptr_t)g_mha_ml,
+                    (long long)(intptr_t)a.q, (long long)(intptr_t)a.out,
+                    (long long)llround((double)a.qscale * 1e6)};
   memcpy(o, v, sizeof(v));
 }
 // which: 0 = last write, 1 = last attend, 2 = last dense attend

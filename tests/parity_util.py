@@ -54,13 +54,15 @@ def nan_fill_(storage, dtype):
 class LatentRun:
     """A latent cache driven in lock step on the GPU and in the oracle."""
 
-    def __init__(self, cfg, poison=False, layer=0, storage_round=None):
+    def __init__(self, cfg, poison=False, layer=0, storage_round=None, path=None):
         from rank_latent_kv_absorbed_amd import LatentCache
         self.cfg = cfg
         self.layer = layer
         self.w = layer_weights(cfg, layer=layer)
         self.wd = {k: dev(v) for k, v in self.w.items()}
         self.gpu = LatentCache(cfg)
+        if path is not None:
+            self.gpu.set_attend_path(path)
         if poison:
             nan_fill_(self.gpu.storage, cfg.cache_dtype)
         self.ring = O.RingModel(cfg.window_frames, cfg.T)

@@ -216,7 +216,7 @@ def test_rollout_schedule_matches_ring_model(sim):
     launch arguments, attend key range and slot map agree with the oracle."""
     c = _cfg()
     st, h = _create(sim, c)
-    assert st == 0
+    assert st == 0 and sim.mla_cache_set_attend_path(h, 1) == 0
     ring = O.RingModel(21, 1560)
     for k in range(80):
         n_ev = max(0, ring.n_resident + 3 - 21)
@@ -273,6 +273,7 @@ def test_attend_arguments_and_workspace(sim):
     c = _cfg()
     st, h = _create(sim, c)
     assert sim.mla_cache_set_state(h, 3, 23) == 0
+    assert sim.mla_cache_set_attend_path(h, 1) == 0
     need = sim.mla_attend_workspace_bytes(h, 4680, 0)
     R = 4680 * 12
     assert need >= R * 224 * 2 + R * 192 * 4 + R * 8
@@ -312,6 +313,111 @@ def test_attend_arguments_and_workspace(sim):
         check_schedule(sim, a, Lq * 12)
         resident = 256 * blocks_per_cu(shape, 224 // 8)
         assert a["n_blocks"] == min(resident, -(-a["n_groups"] * a["n_kt"] // 8))
+
+
+def _expand_info(L):
+    a = (ctypes.c_longlong * 14)()
+    L.fake_expand_info(a)
+    keys = ["B", "ring_rows", "key_slot0", "Lk", "n_h", "d_nope", "d_rope", "d_c", "d_v",
+            "cache_type", "wx", "kv", "ring", "w_uk"]
+    return dict(zip(keys, list(a)))
+
+
+def _mha_ptrs(L):
+    a = (ctypes.c_longlong * 9)()
+    L.fake_mha_ptrs(a)
+    return dict(zip(["ring_rows", "d_h", "ring", "qrot", "opart", "ml", "q", "out", "qscale_u"],
+                    list(a)))
+
+
+def test_attend_path_choice(sim):
+    c = _cfg()
+    st, h = _create(sim, c)
+    assert st == 0 and sim.mla_cache_set_state(h, 0, 20) == 0
+    # automatic: long chunks expand, short ones and forced key splits stay absorbed
+    assert sim.mla_attend_path(h, 4680, 0) == 2
+    assert sim.mla_attend_path(h, 511, 0) == 1 and sim.mla_attend_path(h, 512, 0) == 2
+    assert sim.mla_attend_path(h, 4680, 3) == 1
+    assert sim.mla_attend_path(h, 0, 0) == -1 and sim.mla_attend_path(h, 8, -1) == -1
+    assert sim.mla_cache_set_attend_path(h, 2) == 0
+    assert sim.mla_attend_path(h, 1, 0) == 2 and sim.mla_attend_path(h, 1, 2) == 1
+    assert sim.mla_cache_set_attend_path(h, 1) == 0
+    assert sim.mla_attend_path(h, 4680, 0) == 1
+    assert sim.mla_cache_set_attend_path(h, 3) == 1 and sim.mla_cache_set_attend_path(h, -1) == 1
+    assert sim.mla_cache_set_attend_path(h, 0) == 0
+    # handles the expansion cannot serve: fp32, other head widths, dense handles
+    # (449 frames: the expanded window would pass 2^31 elements per sequence)
+    for kw in ({"dtype": "f32", "cache_dtype": "f32"}, {"d_nope": 64}, {"d_v": 64},
+               {"d_nope": 112, "d_rope": 16, "rope_split": (4, 2, 2)}, {"window_frames": 449}):
+        st, g = _create(sim, _cfg(**kw))
+        assert st == 0, kw
+        assert sim.mla_cache_set_attend_path(g, 2) == 8, kw
+        assert sim.mla_attend_path(g, 4680, 0) == 1, kw
+    st, g = _create(sim, _cfg(window_frames=448))
+    assert sim.mla_cache_set_attend_path(g, 2) == 0
+    st, d = _create(sim, c, dense=True)
+    assert sim.mla_cache_set_attend_path(d, 1) == 9 and sim.mla_attend_path(d, 16, 0) == -1
+
+
+def test_expand_attend_arguments_and_workspace(sim):
+    """The expand path: workspace = converted weights, expanded window, dense
+    attention workspace, in that order and disjoint; the rebuild reads the
+    resident keys from the ring, the dense attention reads the expanded window
+    from key 0 with the latent path's scale and a rotation that leaves the
+    d_nope content dimensions alone."""
+    c = _cfg()
+    st, h = _create(sim, c)
+    assert sim.mla_cache_set_state(h, 3, 23) == 0
+    ws = 1 << 40
+    for Lq, (oldest, newest) in ((4680, (3, 23)), (512, (40, 44)), (2000, (7, 7))):
+        assert sim.mla_cache_set_state(h, oldest, newest) == 0
+        Lk = (newest - oldest + 1) * 1560
+        need = sim.mla_attend_workspace_bytes(h, Lq, 0)
+        wx = 12 * 224 * 192 * 2
+        kv = 21 * 1560 * 2 * 12 * 128 * 2                 # sized for the full window
+        shape = expected_shape(Lq, 32)
+        lq_pad = -(-Lq // shape[0]) * shape[0]
+        R = 12 * lq_pad
+        assert need >= wx + kv + R * 128 * 2 + R * 128 * 4 + R * 8
+        assert sim.mla_attend(h, P(FAKE_PTR), 0, Lq, P(FAKE_PTR), P(FAKE_PTR), P(FAKE_PTR), 0,
+                              P(ws), need - 1, None) == 7
+        n = sim.fake_count()
+        assert sim.mla_attend(h, P(FAKE_PTR), 77, Lq, P(FAKE_PTR + 256), P(FAKE_PTR + 512),
+                              P(FAKE_PTR + 768), 0, P(ws), need, None) == 0
+        assert sim.fake_count() == n + 2 and sim.fake_kind() == 5
+        e = _expand_info(sim)
+        assert (e["B"], e["ring_rows"], e["key_slot0"], e["Lk"]) == \
+            (1, 21 * 1560, (oldest % 21) * 1560, Lk)
+        assert (e["n_h"], e["d_nope"], e["d_rope"], e["d_c"], e["d_v"], e["cache_type"]) == \
+            (12, 96, 32, 192, 128, 2)
+        assert e["ring"] == FAKE_STORAGE and e["w_uk"] == FAKE_PTR + 256
+        assert e["wx"] == ws and e["kv"] >= ws + wx and e["kv"] % 256 == 0
+        m = _mha_info(sim)
+        p = _mha_ptrs(sim)
+        assert (m["key_slot0"], m["Lk"], m["Lq"], m["q_token0"]) == (0, Lk, Lq, 77)
+        assert p["ring"] == e["kv"] and p["ring_rows"] == Lk and p["d_h"] == 128
+        assert p["q"] == FAKE_PTR and p["out"] == FAKE_PTR + 768
+        assert p["qscale_u"] == round(float(np.float32(math.log2(math.e) / math.sqrt(128))) * 1e6)
+        # disjoint regions inside the workspace
+        assert e["kv"] + kv <= p["qrot"] < p["opart"] < p["ml"] < ws + need
+        assert p["opart"] - p["qrot"] >= R * 128 * 2 and p["ml"] - p["opart"] >= R * 128 * 4
+        assert (m["block_rows"], m["key_tile"], m["stages"]) == shape
+        check_schedule(sim, m, R, which=1)
+    # rotation of the expanded queries: identity on the content pairs, the
+    # latent path's 3D table on the positional ones
+    axis = (ctypes.c_int * 64)()
+    inv = (ctypes.c_double * 64)()
+    n = sim.fake_rope(2, axis, inv)
+    want = O.rope_pair_table((6, 5, 5), 10000.0)
+    assert n == 48 + 16
+    assert all(inv[p] == 0.0 for p in range(48))
+    assert [(axis[48 + p], inv[48 + p]) for p in range(16)] == [(a, f) for a, f in want]
+    # a failed rebuild launch is reported and the attention is not launched
+    n = sim.fake_count()
+    sim.fake_fail_next()
+    assert sim.mla_attend(h, P(FAKE_PTR), 0, 2000, P(FAKE_PTR), P(FAKE_PTR), P(FAKE_PTR), 0,
+                          P(ws), 1 << 40, None) == 10
+    assert sim.fake_count() == n + 1 and sim.fake_kind() == 7
 
 
 def test_dense_attend_schedule(sim):

@@ -243,22 +243,26 @@ def test_frame_shift_changes_nothing_beyond_rounding():
 # attention at Wan sizes, sampled rows
 # --------------------------------------------------------------------------
 
+@pytest.mark.parametrize("path", ["absorbed", "expand"])
 @pytest.mark.parametrize("cache_dtype", ["f16", "bf16"])
-def test_wan_layer_sampled_rows(cache_dtype):
+def test_wan_layer_sampled_rows(cache_dtype, path):
     cfg = config("wan_layer").with_(cache_dtype=cache_dtype)
-    run = LatentRun(cfg)
+    run = LatentRun(cfg, path=path)
     run.write(0, cfg.prefill_frames)
     run.write(cfg.chunk_frame0, cfg.chunk_frames)
     q = run.query(cfg.Lq)
     rows = sample_rows(cfg.Lq, 96)
+    assert run.gpu.attend_path(cfg.Lq) == path
     got, ref, _ = run.attend(q, cfg.chunk_frame0 * cfg.T, rows=rows)
-    assert_parity(got, ref, "bf16", f"wan layer (6+3 frames) sampled {cache_dtype}")
+    assert_parity(got, ref, "bf16", f"wan layer (6+3 frames) sampled {cache_dtype} {path}")
 
 
-@pytest.mark.parametrize("batch,cache_dtype", [(1, "f16"), (2, "f16"), (1, "bf16")])
-def test_full_window_sampled_rows(batch, cache_dtype):
+@pytest.mark.parametrize("batch,cache_dtype,path",
+                         [(1, "f16", "absorbed"), (2, "f16", "absorbed"), (1, "bf16", "absorbed"),
+                          (1, "f16", "expand"), (2, "bf16", "expand"), (1, "f16", "auto")])
+def test_full_window_sampled_rows(batch, cache_dtype, path):
     cfg = config("wan_window").with_(batch=batch, cache_dtype=cache_dtype)
-    run = LatentRun(cfg)
+    run = LatentRun(cfg, path=path)
     run.write(0, cfg.prefill_frames)
     run.evict(cfg.evict_frames)
     run.write(cfg.chunk_frame0, cfg.chunk_frames)
@@ -266,21 +270,66 @@ def test_full_window_sampled_rows(batch, cache_dtype):
     q = run.query(cfg.Lq)
     rows = sample_rows(cfg.Lq, 48 if batch == 1 else 24)
     got, ref, _ = run.attend(q, cfg.chunk_frame0 * cfg.T, rows=rows)
-    assert_parity(got, ref, "bf16", f"21-frame window B={batch} {cache_dtype} sampled")
+    assert_parity(got, ref, "bf16", f"21-frame window B={batch} {cache_dtype} {path} sampled")
 
 
-@pytest.mark.parametrize("Lq", [1, 8])
-def test_small_queries_full_window(Lq):
+# Expand-then-attend on mid sizes, every element: Wan head widths on a small
+# frame grid (60 tokens); 300 resident keys through a ring wrap leave ragged
+# 32- and 64-key tiles and a ragged last 128-key rebuild block; the query
+# counts reach all three attention block shapes (3 -> 32-row blocks, 33 and
+# 120 -> 128-row blocks, 200 and 300 -> 256-row blocks with padded rows).
+@pytest.mark.parametrize("Lq,d_c", [(3, 192), (33, 64), (120, 128), (200, 192), (300, 64)])
+def test_expand_mid_ragged_with_wrap(Lq, d_c):
+    cfg = mid_cfg(d_nope=96, d_rope=32, d_v=128, d_c=d_c)
+    run = LatentRun(cfg, path="expand")
+    run.write(0, 4)
+    run.evict(2)
+    run.write(4, 2)
+    run.evict(1)
+    run.write(6, 2)       # frames 3..7 resident, Lk = 300
+    assert run.gpu.attend_path(Lq) == "expand"
+    q = run.query(Lq)
+    got, ref, _ = run.attend(q, 8 * cfg.T - Lq)
+    assert_parity(got, ref, "bf16", f"expand Lq={Lq} d_c={d_c}")
+
+
+def test_expand_poisoned_free_slots_and_agreement():
+    """Expand path: NaN in every free ring slot changes nothing (only resident
+    keys are rebuilt), repeated calls agree bit for bit, and the two paths agree
+    to within their rounding."""
+    cfg = wan_small()
+    runs = [LatentRun(cfg, poison=p, path="expand") for p in (False, True)]
+    for r in runs:
+        r.write(0, 4)
+        r.evict(2)
+        r.write(4, 2)
+    q = runs[0].query(2 * cfg.T)
+    outs = []
+    for r in runs:
+        for _ in range(2):
+            outs.append(r.gpu.attend(dev(q), 4 * cfg.T, r.wd["w_uk"], r.wd["w_uv"]).cpu())
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0]), "expand results differ between runs or with NaN free slots"
+    got, ref, _ = runs[1].attend(q, 4 * cfg.T)
+    assert_parity(got, ref, "bf16", "expand, poisoned ring")
+    runs[1].gpu.set_attend_path("absorbed")
+    absorbed = runs[1].gpu.attend(dev(q), 4 * cfg.T, runs[1].wd["w_uk"], runs[1].wd["w_uv"]).cpu()
+    mx, mean = parity_stats(outs[0].numpy(), absorbed.numpy())
+    assert mx < 1e-2 and mean < 2e-3, (mx, mean)
+
+
+@pytest.mark.parametrize("Lq,path", [(1, "absorbed"), (8, "absorbed"), (1, "expand")])
+def test_small_queries_full_window(Lq, path):
     """Decode-like shapes on the full 21-frame window: each sequence's few rows
     spread over many key ranges (about a hundred partials per row)."""
     cfg = config("wan_window").with_(batch=2)
-    run = LatentRun(cfg)
+    run = LatentRun(cfg, path=path)
     run.write(0, cfg.prefill_frames)
     run.evict(cfg.evict_frames)
     run.write(cfg.chunk_frame0, cfg.chunk_frames)
     q = run.query(Lq)
     got, ref, _ = run.attend(q, (cfg.chunk_frame0 + cfg.chunk_frames) * cfg.T - Lq)
-    assert_parity(got, ref, "bf16", f"21-frame window small query Lq={Lq}")
+    assert_parity(got, ref, "bf16", f"21-frame window small query Lq={Lq} {path}")
 
 
 # --------------------------------------------------------------------------
