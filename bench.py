@@ -3,15 +3,19 @@
 
 A step is one pass of the whole path for one layer: evict the 3 oldest frames
 of that layer's 21-frame window, fused cache write of the new 3-frame chunk
-(4680 tokens), absorbed attention of the chunk's 4680 queries over the 32760
-resident keys.  Steps cycle over the windows of 30 layers (440 MB of latent
-cache, more than the 256 MB last-level cache).  Printed metric: attended query
-tokens/s per layer = batch * 4680 / step time, plus MFMA utilisation.
+(4680 tokens), attention of the chunk's 4680 queries over the 32760 resident
+keys (the library's choice of path for this chunk length: expand-then-attend,
+which rebuilds the window's per-head keys and values from the latent and runs
+per-head attention; --path absorbed times the latent-space form instead).
+Steps cycle over the windows of 30 layers (440 MB of latent cache, more than
+the 256 MB last-level cache).  Printed metric: attended query tokens/s per
+layer = batch * 4680 / step time, plus MFMA utilisation.
 
 Also reported: the main attention kernel alone (HIP events recorded by the
-library on its stream) against the bf16 MFMA roofline, the dense per-head MHA
-comparison on the same shape, a cache-bound small-query case against HBM
-bandwidth, and the fp64 CPU oracle timed on a bounded sample.
+library on its stream) against the bf16 MFMA roofline, the other path's step
+time, the dense per-head MHA comparison on the same shape, a cache-bound
+small-query case against HBM bandwidth, and the fp64 CPU oracle timed on a
+bounded sample.
 """
 
 from __future__ import annotations
@@ -31,17 +35,36 @@ sys.path.insert(0, ROOT)
 METRIC = "attended query tokens/s per layer (21-frame window, 4680-q chunk) + MFMA util %"
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_core_wan_window_traffic.json")
-CORE_SOURCES = ["rank_latent_kv_absorbed_amd/csrc/mla_attn_core.h",
-                "rank_latent_kv_absorbed_amd/csrc/mla_attend.hip",
-                "rank_latent_kv_absorbed_amd/csrc/mla_device.h"]
+# Hardware traffic counters of each path's attention core (written from
+# rocprofv3 runs of this script), valid while the core's sources are unchanged.
+TRAFFIC_FILES = {"absorbed": os.path.join(ROOT, "profiles", "attend_core_wan_window_traffic.json"),
+                 "expand": os.path.join(ROOT, "profiles", "attend_expand_wan_window_traffic.json")}
+CORE_SOURCES = {
+    "absorbed": ["rank_latent_kv_absorbed_amd/csrc/mla_attn_core.h",
+                 "rank_latent_kv_absorbed_amd/csrc/mla_attend.hip",
+                 "rank_latent_kv_absorbed_amd/csrc/mla_device.h"],
+    "expand": ["rank_latent_kv_absorbed_amd/csrc/mla_attn_core.h",
+               "rank_latent_kv_absorbed_amd/csrc/mha_attend.hip",
+               "rank_latent_kv_absorbed_amd/csrc/mla_expand.hip",
+               "rank_latent_kv_absorbed_amd/csrc/mla_device.h"],
+}
+CORE_KERNELS = {"absorbed": "attn_core_kernel<E, 224, 192, ...> (latent scores and value sums)",
+                "expand": "attn_core_kernel<E, 128, 128, ...> (per-head attention over the "
+                          "rebuilt keys and values)"}
 
 
-def core_source_sha():
+def core_source_sha(path="absorbed"):
     h = hashlib.sha256()
-    for p in CORE_SOURCES:
+    for p in CORE_SOURCES[path]:
         h.update(open(os.path.join(ROOT, p), "rb").read())
     return h.hexdigest()[:16]
+
+
+def core_flop(cfg, path, B, Lq, Lk):
+    """Algorithmic FLOP of one launch of the path's attention core."""
+    if path == "expand":
+        return B * cfg.n_heads * Lq * Lk * 2 * (cfg.d_qk + cfg.d_v)
+    return B * cfg.n_heads * Lq * Lk * (2 * (cfg.d_c + cfg.d_rope) + 2 * cfg.d_c)
 
 
 class HipEvents:
@@ -118,6 +141,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--layers", type=int, default=30)
+    ap.add_argument("--path", choices=["auto", "absorbed", "expand"], default="auto",
+                    help="attention path of every layer's handle (auto: the library's choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip dense and small-query cases")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -132,7 +157,7 @@ def main():
 
     import torch
     from rank_latent_kv_absorbed_amd import LatentCache, DenseCache, attend_flops, attend_bytes
-    from rank_latent_kv_absorbed_amd.mla import mha_attend_flops
+    from rank_latent_kv_absorbed_amd.mla import expand_attend_flops, mha_attend_flops
     from synthetic import chunk_q, chunk_x, config, dense_weights, layer_weights
 
     dev = torch.device("cuda", 0)
@@ -155,11 +180,14 @@ def main():
     caches = []
     for l in range(L):
         c = LatentCache(cfg, device=dev)
+        c.set_attend_path(args.path)
         c.write(x_pre, weights[l]["w_dkr"], 0, W)
         caches.append(c)
+    path = caches[0].attend_path(Lq)
     newest = [W - 1] * L
     out = torch.empty((B, Lq, cfg.n_heads, cfg.d_v), dtype=torch.float32, device=dev)
-    ws = torch.empty(caches[0].workspace_bytes(Lq), dtype=torch.uint8, device=dev)
+    ws_bytes = max(caches[0].workspace_bytes(Lq), 1)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     if args.copy_calibration_mib > 0:
@@ -188,37 +216,45 @@ def main():
         if core_events is not None:
             c.set_profile_events(None, None)
 
+    def timed(n_steps):
+        """(ms per step, mean core-kernel ms) over n_steps steps."""
+        core_ev = [(ev.create(), ev.create()) for _ in range(n_steps)]
+        t_start = torch.cuda.Event(enable_timing=True)
+        t_stop = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t_start.record()
+        for k in range(n_steps):
+            step(core_ev[k])
+        t_stop.record()
+        torch.cuda.synchronize()
+        core_ms = [ev.elapsed_ms(a, b) for a, b in core_ev]
+        return t_start.elapsed_time(t_stop) / n_steps, sum(core_ms) / len(core_ms)
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    ms_step, core_avg = timed(args.steps)
 
-    core_ev = [(ev.create(), ev.create()) for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_stop = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record()
-    for k in range(args.steps):
-        step(core_ev[k])
-    t_stop.record()
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_stop)
-    core_ms = [ev.elapsed_ms(a, b) for a, b in core_ev]
-    ms_step = total_ms / args.steps
-    core_avg = sum(core_ms) / len(core_ms)
-
-    # algorithmic work
-    core_flop = B * cfg.n_heads * Lq * Lk * (2 * (cfg.d_c + cfg.d_rope) + 2 * cfg.d_c)
-    att_flop = attend_flops(cfg.n_heads, Lq, Lk, cfg.d_c, cfg.d_rope, cfg.d_nope, cfg.d_v, B)
+    # algorithmic work of the path that ran
+    c_flop = core_flop(cfg, path, B, Lq, Lk)
+    if path == "expand":
+        att_flop = expand_attend_flops(cfg.n_heads, Lq, Lk, cfg.d_c, cfg.d_rope, cfg.d_nope,
+                                       cfg.d_v, B)
+    else:
+        att_flop = attend_flops(cfg.n_heads, Lq, Lk, cfg.d_c, cfg.d_rope, cfg.d_nope, cfg.d_v, B)
     write_flop = 2 * B * Lq * cfg.hidden * cfg.width
     step_flop = att_flop + write_flop
+    absorbed_step_flop = write_flop + attend_flops(cfg.n_heads, Lq, Lk, cfg.d_c, cfg.d_rope,
+                                                   cfg.d_nope, cfg.d_v, B)
     value = B * Lq / (ms_step / 1e3)
     mfma_pct = 100.0 * step_flop / (ms_step / 1e3) / (PEAK_BF16_TFLOPS * 1e12)
-    achieved = core_flop / (core_avg / 1e3) / 1e12
+    absorbed_pct = 100.0 * absorbed_step_flop / (ms_step / 1e3) / (PEAK_BF16_TFLOPS * 1e12)
+    achieved = c_flop / (core_avg / 1e3) / 1e12
 
     traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        tr = json.load(open(TRAFFIC_FILE))
-        if tr.get("kernel_source_sha") == core_source_sha() and tr.get("batch") == B:
+    if os.path.exists(TRAFFIC_FILES[path]):
+        tr = json.load(open(TRAFFIC_FILES[path]))
+        if tr.get("kernel_source_sha") == core_source_sha(path) and tr.get("batch") == B:
             traffic = tr.get("hbm_bytes_per_launch")
 
     result = {
@@ -227,24 +263,49 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "wan_window: per layer, evict 3 frames + fused cache write of a "
-                               "3-frame chunk + absorbed attention of its queries over a 21-frame "
+                               "3-frame chunk + latent-KV attention of its queries over a 21-frame "
                                "window; 30 layer windows cycled",
+                   "attend_path": path,
                    "global_batch": B, "query_tokens": Lq, "resident_keys": Lk, "n_heads": cfg.n_heads,
                    "d_c": cfg.d_c, "d_rope": cfg.d_rope, "d_nope": cfg.d_nope, "d_v": cfg.d_v,
                    "hidden": cfg.hidden, "grid": [cfg.grid_h, cfg.grid_w], "layers_cycled": L,
                    "parallelism": "none (1 GPU)"},
         "mfma_util_pct": round(mfma_pct, 2),
-        "roofline": {"bound": "mfma", "kernel": "attn_core_kernel<224,192> (latent attention)",
+        "mfma_util_pct_absorbed_form": round(absorbed_pct, 2),
+        "roofline": {"bound": "mfma", "kernel": CORE_KERNELS[path],
                      "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "avg_launch_ms": round(core_avg, 4),
-                     "algorithmic_flop_per_launch": core_flop},
+                     "algorithmic_flop_per_launch": c_flop},
+        "step_flop": step_flop,
         "breakdown_ms": {"step": round(ms_step, 4), "attend_core": round(core_avg, 4)},
         "cache_bytes": {"latent_per_layer": caches[0].nbytes, "latent_30_layers": caches[0].nbytes * 30,
                         "dense_per_layer": None},
     }
 
     if not args.no_extras:
+        # the other attention path on the same steps
+        other = "absorbed" if path == "expand" else "expand"
+        try:
+            for c in caches:
+                c.set_attend_path(other)
+        except Exception as e:          # the handle cannot take that path
+            result["other_path"] = {"path": other, "error": str(e)}
+        else:
+            need = caches[0].workspace_bytes(Lq)
+            if need > ws.numel():
+                ws = torch.empty(need, dtype=torch.uint8, device=dev)
+            for _ in range(5):
+                step()
+            o_step, o_core = timed(min(args.steps, 20))
+            result["other_path"] = {"path": other, "ms_per_step": round(o_step, 4),
+                                    "attend_core_ms": round(o_core, 4),
+                                    "core_tflops": round(core_flop(cfg, other, B, Lq, Lk)
+                                                         / (o_core / 1e3) / 1e12, 1),
+                                    "value": round(B * Lq / (o_step / 1e3), 1)}
+            for c in caches:
+                c.set_attend_path(args.path)
+
         # dense per-head MHA on the same shape (one layer), for time and cache bytes
         dcache = DenseCache(cfg, device=dev)
         dw = {k: v.to(dev) for k, v in dense_weights(cfg).items()}
