@@ -161,11 +161,11 @@ hipError_t launch_mha_typed(const MhaAttendArgs& a, float* opart, float* ml, con
     bool launched = false;
 #define MLA_SHAPE(NW, KT, NS)                                                                  \
   if (!launched && br == 32 * NW && sched.key_tile == KT && sched.stages == NS) {             \
-    hipLaunchKernelGGL((attn_core_kernel<E, 128, 128, NW, KT, NS, false>), grid, dim3(NW * 64), \
+    hipLaunchKernelGGL((attn_core_kernel<E, 128, 128, NW, KT, NS, false, 1, (NW == 8)>), grid, dim3(NW * 64), \
                        0, s, c);                                                              \
     launched = true;                                                                          \
   }
-    MLA_SHAPE(8, 64, 2)
+    MLA_SHAPE(8, 64, 3)
     MLA_SHAPE(4, 32, 4)
     MLA_SHAPE(1, 32, 2)
 #undef MLA_SHAPE

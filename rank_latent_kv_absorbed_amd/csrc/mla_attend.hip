@@ -349,11 +349,11 @@ hipError_t launch_core(const AttnCore& c, hipStream_t s) {
   const dim3 grid((unsigned)sc.n_blocks);
 #define MLA_SHAPE(NW, KT, NS)                                                                   \
   if (sc.block_rows == 32 * NW && sc.key_tile == KT && sc.stages == NS) {                      \
-    hipLaunchKernelGGL((attn_core_kernel<E, DC + 32, DC, NW, KT, NS, true>), grid, dim3(NW * 64), \
+    hipLaunchKernelGGL((attn_core_kernel<E, DC + 32, DC, NW, KT, NS, true, 1, (NW == 8)>), grid, dim3(NW * 64), \
                        0, s, c);                                                               \
     return hipGetLastError();                                                                  \
   }
-  MLA_SHAPE(8, 64, 2)
+  MLA_SHAPE(8, 64, 3)
   MLA_SHAPE(4, 32, 4)
   MLA_SHAPE(1, 32, 2)
 #undef MLA_SHAPE

@@ -136,7 +136,8 @@ __device__ __forceinline__ void lds_barrier() {
 // Register budget: two waves per SIMD for one 32-row block per wave, so that
 // narrow blocks can share a compute unit; one wave per SIMD (the whole
 // register file, accumulators in AGPRs) when each wave owns RB > 1 row blocks.
-template <typename E, int DQK, int DV, int NW, int KT, int NS, bool SHARED_KV, int RB = 1>
+template <typename E, int DQK, int DV, int NW, int KT, int NS, bool SHARED_KV, int RB = 1,
+          bool PP = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 2 : 1, RB == 1 ? 2 : 1)))
 void attn_core_kernel(AttnCore a) {
   typedef typename Elem<E>::v8 V8;
@@ -154,6 +155,7 @@ void attn_core_kernel(AttnCore a) {
   static_assert(KT == 32 || KT == 64, "key tiles are one or two 32-key MFMA blocks");
   static_assert(!SHARED_KV || DV <= DQK, "shared rows hold V inside K");
   static_assert(NS >= 2 && NS <= 5, "two to five tile buffers");
+  static_assert(!PP || (NS == 3 && NW % 2 == 0 && NW >= 2), "ping-pong: two wave groups, three buffers");
   static_assert((SPANS + NW - 1) / NW * (NS - 1) <= 63, "tile loads in flight fit the vmcnt counter");
   // Whole spans with every lane active (exact load counts per wave); the chunk
   // permutation stays inside aligned groups of a row.
@@ -217,9 +219,8 @@ void attn_core_kernel(AttnCore a) {
   int lane_off[LKEEP];
 #pragma unroll
   for (int j = 0; j < LKEEP; ++j) lane_off[j] = lane_offset(NW == 1 ? j : w + j * NW);
-  auto load_tile = [&](int b, int rg, int kt, E* dst) MLA_INLINE {
+  auto load_tile = [&](int b, int head, int kt, E* dst) MLA_INLINE {
     const E* ring = (const E*)a.ring + (size_t)b * a.ring_rows * a.ring_stride;
-    const int head = (rg * BR) / a.rows_per_head;
     const int rows = (int)a.ring_rows;
     int s0 = (int)a.key_slot0 + kt * KT;
     s0 = s0 >= rows ? s0 - rows : s0;
@@ -288,10 +289,25 @@ void attn_core_kernel(AttnCore a) {
     const int a2 = n_steps - i - 2;
     return a2 < 0 ? 0 : (a2 < NS - 1 ? a2 : NS - 1);
   };
-  auto issue = [&](int i, E* dst) MLA_INLINE {
-    const StepInfo sn = sched_decode(sc, g, i);
-    const int b1 = sn.grp / sc.n_rg;
-    load_tile(b1, sn.grp - b1 * sc.n_rg, sn.kt, dst);
+  // Block-uniform walks over the block's steps: `wc` is the step being
+  // computed, `wi` the next tile to load (tiles are issued in step order).
+  // Each keeps its segment's batch element and head.
+  struct Walk {
+    SchedCursor c;
+    int b, head;
+  };
+  auto walk_segment = [&](Walk& x) MLA_INLINE {
+    x.b = x.c.si.grp / sc.n_rg;
+    x.head = ((x.c.si.grp - x.b * sc.n_rg) * BR) / a.rows_per_head;
+  };
+  auto walk_next = [&](Walk& x) MLA_INLINE {
+    if (sched_cursor_next(sc, g, n_steps, x.c)) walk_segment(x);
+  };
+  Walk wc, wi;
+  // Load the next tile of the block's walk into `dst`.
+  auto issue = [&](E* dst) MLA_INLINE {
+    load_tile(wi.b, wi.head, wi.c.si.kt, dst);
+    walk_next(wi);
   };
 
   // New row-group segment: query fragments in (global loads, not waited on
@@ -316,129 +332,208 @@ void attn_core_kernel(AttnCore a) {
     }
   };
 
+  // The three phases of a step on one key tile, for this wave's rows.
+  // Scores S^T = K Q^T of the tile in `cur`.
+  auto scores = [&](const E* cur, f32x16 (&sv)[RB][NKB]) MLA_INLINE {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sv[rb][kb][r] = 0.0f;
+      const E* krow = cur + (kb * 32 + lo) * KSTR;
+      auto kptr = [&](int ks) MLA_INLINE {
+        return SHARED_KV ? krow + 32 * (ks >> 1) + ((ks & 1) ? k_off1 : k_off0)
+                         : krow + 8 * ((2 * ks + hi) ^ k_sw);
+      };
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const V8 kf = ld8<E>(kptr(ks));
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) sv[rb][kb] = Elem<E>::mfma(kf, qf[rb][ks], sv[rb][kb]);
+      }
+    }
+  };
+  // Online softmax of key tile kt: mask keys past the window, lazy rescale,
+  // probabilities (in the cache type) into pf, running sums.
+  auto softmax = [&](int kt, f32x16 (&sv)[RB][NKB], V8 (&pf)[RB][NKB][2]) MLA_INLINE {
+    const int t0 = kt * KT;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      if (t0 + KT > a.Lk) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (t0 + kb * 32 + acc_row(r, hi) >= a.Lk) sv[rb][kb][r] = -INFINITY;
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sv[rb][kb][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      // lazy rescale: raise the max only when a score passes it by > 2^8
+      if (__ballot(mx > m[rb] + kRescaleThreshold)) {
+        const float mnew = fmaxf(m[rb], mx);
+        const float alpha = exp2_fast(m[rb] - mnew);
+        m[rb] = mnew;
+        lsum[rb] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[rb][dt][r] *= alpha;
+      }
+      float ps = 0.0f;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = exp2_fast(sv[rb][kb][r] - m[rb]);
+          ps += p;
+          pf[rb][kb][r >> 3][r & 7] = Elem<E>::from(p);
+        }
+      lsum[rb] += ps;
+    }
+  };
+  // Value sums O^T += V^T P^T of the tile in `cur`.
+  auto values = [&](const E* cur, const V8 (&pf)[RB][NKB][2]) MLA_INLINE {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const E* vrow = cur + (kb * 32 + 16 * st + tr_key) * KSTR + VOFF;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const int d0 = SHARED_KV ? dt : (dt ^ tr_dt0), d1 = SHARED_KV ? dt : (dt ^ tr_dt1);
+          const i16x4 lo4 = lds_read_tr16(vrow + 32 * d0 + tr_off0);
+          const i16x4 hi4 = lds_read_tr16(vrow + 8 * KSTR + 32 * d1 + tr_off1);
+          const V8 va = __builtin_bit_cast(V8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) o[rb][dt] = Elem<E>::mfma(va, pf[rb][kb][st], o[rb][dt]);
+        }
+      }
+  };
+  // Segment end: write this block's partial of the row group (slot si.slot)
+  // of batch element b.
+  auto write_partial = [&](const StepInfo& si, int b) MLA_INLINE {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const float ltot = lsum[rb] + __shfl_xor(lsum[rb], 32);
+      if (row[rb] < a.R) {
+        const size_t prow = ((size_t)si.slot * a.B + b) * a.R + row[rb];
+        float* op = a.opart + prow * DV;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int gg = 0; gg < 4; ++gg) {
+            f32x4 v = {o[rb][dt][4 * gg], o[rb][dt][4 * gg + 1], o[rb][dt][4 * gg + 2],
+                       o[rb][dt][4 * gg + 3]};
+            *reinterpret_cast<f32x4*>(op + dt * 32 + 8 * gg + 4 * hi) = v;
+          }
+        if (hi == 0) {
+          a.ml[prow * 2] = m[rb];
+          a.ml[prow * 2 + 1] = ltot;
+        }
+      }
+    }
+  };
+  // Start of step i: clear the keys past the window of a ragged last tile;
+  // a segment starting mid-block loads its queries.  Its query loads retire
+  // in order behind the tiles in flight, so it waits for all of them (rare:
+  // only blocks that cross from one row group to the next).
+  auto step_begin = [&](const StepInfo& si, int b, int i, E* cur) MLA_INLINE {
+    if (si.kt * KT + KT > a.Lk) {
+      scrub(si.kt, cur);
+      lds_barrier();
+    }
+    if (si.first && i > 0) {
+      begin_segment(b, si.grp - b * sc.n_rg);
+      asm volatile("" ::: "memory");  // keep the loads above the wait
+      __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
+    }
+  };
+
+  if (n_steps <= 0) return;
+  sched_cursor_seek(sc, g, n_steps, 0, wc.c);
+  walk_segment(wc);
+  wi = wc;
+  const StepInfo s0 = wc.c.si;
+  const int b0 = wc.b;
+
+  if constexpr (PP) {
+    // Two wave groups, one wave of each per SIMD, work half a step apart so
+    // that one group's softmax (vector ALU) overlaps the other's products
+    // (matrix units).  Every wave runs the same steps - scores, softmax,
+    // values of tile k - with one barrier per step, but group A (waves
+    // 0 .. NW/2 - 1) meets it after the values and group B before them.
+    // Between barriers k - 1 and k, A runs scores, softmax and values of tile
+    // k while B runs the values of tile k - 1 (its probabilities wait in
+    // registers across the barrier), then scores and softmax of tile k.
+    // Tiles k - 1 and k are read in that interval while tile k + 1 streams
+    // in: three buffers.  At its barrier a wave waits for its own loads of
+    // tile k + 1 first; after the barrier and its values of tile k, it issues
+    // its loads of tile k + 2 into the buffer of tile k - 1, which both groups
+    // are done with.
+    const bool grp_b = w >= NW / 2;
+    auto sync = [&](int k) MLA_INLINE {
+      if (k + 1 < n_steps) {
+        __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
+        lds_barrier();
+      }
+    };
+    auto step_pp = [&](int k, E* cur, E* refill) MLA_INLINE {
+      const StepInfo si = wc.c.si;
+      const int b = wc.b;
+      step_begin(si, b, k, cur);
+      V8 pf[RB][NKB][2];
+      if (live) {
+        f32x16 sv[RB][NKB];
+        scores(cur, sv);
+        softmax(si.kt, sv, pf);
+      }
+      if (grp_b) sync(k);
+      if (live) {
+        values(cur, pf);
+        if (si.last) write_partial(si, b);
+      }
+      if (!grp_b) sync(k);
+      // Group B issues its share of tile k + 2 after its values, so that the
+      // loads are not in flight while it reads tile k.
+      if (k + 2 < n_steps) issue(refill);
+      walk_next(wc);
+    };
+    begin_segment(b0, s0.grp - b0 * sc.n_rg);
+    issue(kt0);
+    if (n_steps > 1) issue(kt1);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
+    lds_barrier();
+    for (int k = 0; k < n_steps; k += 3) {
+      step_pp(k, kt0, kt2);
+      if (k + 1 < n_steps) step_pp(k + 1, kt1, kt0);
+      if (k + 2 < n_steps) step_pp(k + 2, kt2, kt1);
+    }
+    return;
+  }
+
   // One step: `cur` holds the key tile of step i.  Once every wave is done
   // with it, tile i + NS is issued into the same buffer.  (Issuing at the end
   // of a step keeps each buffer's write after its read within one unrolled
   // loop pass; the compiler then adds no wait of its own for the tile loads.)
   auto step = [&](int i, E* cur) MLA_INLINE {
-    const StepInfo si = sched_decode(sc, g, i);
-    const int b = si.grp / sc.n_rg;
-    const int rg = si.grp - b * sc.n_rg;
-    const int kt = si.kt;
-
-    if (kt * KT + KT > a.Lk) {  // ragged last tile: clear the keys past the window
-      scrub(kt, cur);
-      lds_barrier();
-    }
-    if (si.first && i > 0) {
-      // A segment starting mid-block: its query loads retire in order behind
-      // the tiles in flight, so wait for all of them here (rare: only blocks
-      // that cross from one row group to the next).
-      begin_segment(b, rg);
-      asm volatile("" ::: "memory");  // keep the loads above the wait
-      __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
-    }
-
+    const StepInfo si = wc.c.si;
+    const int b = wc.b;
+    step_begin(si, b, i, cur);
     if (live) {
       f32x16 sv[RB][NKB];
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sv[rb][kb][r] = 0.0f;
-        const E* krow = cur + (kb * 32 + lo) * KSTR;
-        auto kptr = [&](int ks) MLA_INLINE {
-          return SHARED_KV ? krow + 32 * (ks >> 1) + ((ks & 1) ? k_off1 : k_off0)
-                           : krow + 8 * ((2 * ks + hi) ^ k_sw);
-        };
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          const V8 kf = ld8<E>(kptr(ks));
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) sv[rb][kb] = Elem<E>::mfma(kf, qf[rb][ks], sv[rb][kb]);
-        }
-      }
-      const int t0 = kt * KT;
       V8 pf[RB][NKB][2];
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        if (t0 + KT > a.Lk) {
-#pragma unroll
-          for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-              if (t0 + kb * 32 + acc_row(r, hi) >= a.Lk) sv[rb][kb][r] = -INFINITY;
-        }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sv[rb][kb][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        // lazy rescale: raise the max only when a score passes it by > 2^8
-        if (__ballot(mx > m[rb] + kRescaleThreshold)) {
-          const float mnew = fmaxf(m[rb], mx);
-          const float alpha = exp2_fast(m[rb] - mnew);
-          m[rb] = mnew;
-          lsum[rb] *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[rb][dt][r] *= alpha;
-        }
-        float ps = 0.0f;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float p = exp2_fast(sv[rb][kb][r] - m[rb]);
-            ps += p;
-            pf[rb][kb][r >> 3][r & 7] = Elem<E>::from(p);
-          }
-        lsum[rb] += ps;
-      }
-
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const E* vrow = cur + (kb * 32 + 16 * st + tr_key) * KSTR + VOFF;
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) {
-            const int d0 = SHARED_KV ? dt : (dt ^ tr_dt0), d1 = SHARED_KV ? dt : (dt ^ tr_dt1);
-            const i16x4 lo4 = lds_read_tr16(vrow + 32 * d0 + tr_off0);
-            const i16x4 hi4 = lds_read_tr16(vrow + 8 * KSTR + 32 * d1 + tr_off1);
-            const V8 va = __builtin_bit_cast(V8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb) o[rb][dt] = Elem<E>::mfma(va, pf[rb][kb][st], o[rb][dt]);
-          }
-        }
-
-      if (si.last) {  // segment ends: write this block's partial
-        const int slot = si.slot;
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          const float ltot = lsum[rb] + __shfl_xor(lsum[rb], 32);
-          if (row[rb] < a.R) {
-            const size_t prow = ((size_t)slot * a.B + b) * a.R + row[rb];
-            float* op = a.opart + prow * DV;
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-              for (int gg = 0; gg < 4; ++gg) {
-                f32x4 v = {o[rb][dt][4 * gg], o[rb][dt][4 * gg + 1], o[rb][dt][4 * gg + 2],
-                           o[rb][dt][4 * gg + 3]};
-                *reinterpret_cast<f32x4*>(op + dt * 32 + 8 * gg + 4 * hi) = v;
-              }
-            if (hi == 0) {
-              a.ml[prow * 2] = m[rb];
-              a.ml[prow * 2 + 1] = ltot;
-            }
-          }
-        }
-      }
-    }  // live
+      scores(cur, sv);
+      softmax(si.kt, sv, pf);
+      values(cur, pf);
+      if (si.last) write_partial(si, b);
+    }
+    walk_next(wc);
     // After the last step nothing is read any more: no wait (the partial
     // stores above retire on their own; every tile load was waited for at
     // the end of the step before).
@@ -447,48 +542,45 @@ void attn_core_kernel(AttnCore a) {
         // one wave: refill `cur` before waiting for tile i + 1, so NS tiles
         // are in flight during the wait
         lds_barrier();
-        if (i + NS < n_steps) issue(i + NS, cur);
+        if (i + NS < n_steps) issue(cur);
         wait_vmem(n_ld * ahead(i));
         lds_barrier();
       } else {
         // several waves: one barrier per step; the refill follows it
         wait_vmem(n_ld * (ahead(i) < NS - 2 ? ahead(i) : NS - 2));
         lds_barrier();
-        if (i + NS < n_steps) issue(i + NS, cur);
+        if (i + NS < n_steps) issue(cur);
       }
     }
   };
 
-  if (n_steps <= 0) return;
   // Prologue: the block's first segment (queries) and one tile per buffer.
   // Every buffer access below names its LDS array directly, so that the
   // compiler can tell the tile being read from the tiles still being written.
-  const StepInfo s0 = sched_decode(sc, g, 0);
-  const int b0 = s0.grp / sc.n_rg;
   if constexpr (NW == 1) {
     // Tiles 0 .. NS - 2, then the queries; one full wait covers them all (the
     // compiler sees the query registers ready), and tile NS - 1 streams in
     // during step 0.
-    issue(0, kt0);
-    if (NS > 2 && n_steps > 1) issue(1, kt1);
-    if (NS > 3 && n_steps > 2) issue(2, kt2);
-    if (NS > 4 && n_steps > 3) issue(3, kt3);
+    issue(kt0);
+    if (NS > 2 && n_steps > 1) issue(kt1);
+    if (NS > 3 && n_steps > 2) issue(kt2);
+    if (NS > 4 && n_steps > 3) issue(kt3);
     begin_segment(b0, s0.grp - b0 * sc.n_rg);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
     if (n_steps > NS - 1) {
-      if constexpr (NS == 2) issue(1, kt1);
-      if constexpr (NS == 3) issue(2, kt2);
-      if constexpr (NS == 4) issue(3, kt3);
-      if constexpr (NS == 5) issue(4, kt4);
+      if constexpr (NS == 2) issue(kt1);
+      if constexpr (NS == 3) issue(kt2);
+      if constexpr (NS == 4) issue(kt3);
+      if constexpr (NS == 5) issue(kt4);
     }
   } else {
     begin_segment(b0, s0.grp - b0 * sc.n_rg);
-    issue(0, kt0);
-    if (n_steps > 1) issue(1, kt1);
-    if (NS > 2 && n_steps > 2) issue(2, kt2);
-    if (NS > 3 && n_steps > 3) issue(3, kt3);
-    if (NS > 4 && n_steps > 4) issue(4, kt4);
+    issue(kt0);
+    if (n_steps > 1) issue(kt1);
+    if (NS > 2 && n_steps > 2) issue(kt2);
+    if (NS > 3 && n_steps > 3) issue(kt3);
+    if (NS > 4 && n_steps > 4) issue(kt4);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
   }

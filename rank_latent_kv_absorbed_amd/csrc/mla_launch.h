@@ -56,7 +56,7 @@ struct CoreShape {
   int key_tile;
   int stages;
 };
-constexpr CoreShape kCoreShapes[] = {{8, 64, 2}, {4, 32, 4}, {1, 32, 2}};
+constexpr CoreShape kCoreShapes[] = {{8, 64, 3}, {4, 32, 4}, {1, 32, 2}};
 constexpr int kCoreMaxBlockRows = 256;
 
 // Shape for `rows` query rows of one row unit (latent: Lq * n_h rows of a
@@ -175,6 +175,49 @@ MLA_HD inline StepInfo sched_decode(const Schedule& s, int g, int i) {
   r.first = i2 == 0 || r.kt == s.main_len;
   r.last = i2 == sched_block_steps(s, g) - dp - 1 || r.kt == s.n_kt - 1;
   return r;
+}
+
+// Incremental walk over block g's steps i = 0, 1, 2, ... with the same
+// results as sched_decode(s, g, i), decoding the schedule (integer divisions)
+// only where a segment starts.  n_steps = sched_block_steps(s, g).
+struct SchedCursor {
+  StepInfo si;  // step i
+  int i;
+  int left;     // steps of the same segment after step i
+};
+
+// Last key tile of the segment that contains step i (decoded as si).
+MLA_HD inline int sched_segment_last_kt(const Schedule& s, int g, int i, const StepInfo& si,
+                                        int n_steps) {
+  if (i < s.full_rounds * s.n_kt) return s.n_kt - 1;
+  if (g < s.rem) return s.main_len - 1;
+  const int by_block = si.kt + (n_steps - 1 - i);
+  return by_block < s.n_kt - 1 ? by_block : s.n_kt - 1;
+}
+
+MLA_HD inline void sched_cursor_seek(const Schedule& s, int g, int n_steps, int i, SchedCursor& c) {
+  c.i = i;
+  c.si = sched_decode(s, g, i);
+  c.left = sched_segment_last_kt(s, g, i, c.si, n_steps) - c.si.kt;
+}
+
+// Advance to step c.i + 1; returns true when that step starts a new segment.
+// Past the block's last step only the index moves (nothing is decoded).
+MLA_HD inline bool sched_cursor_next(const Schedule& s, int g, int n_steps, SchedCursor& c) {
+  if (c.i + 1 >= n_steps) {
+    ++c.i;
+    return false;
+  }
+  if (c.left > 0) {
+    ++c.i;
+    ++c.si.kt;
+    c.si.first = false;
+    --c.left;
+    c.si.last = c.left == 0;
+    return false;
+  }
+  sched_cursor_seek(s, g, n_steps, c.i + 1, c);
+  return true;
 }
 
 // Partials left for group grp (its slots are 0 .. count-1).

@@ -93,6 +93,27 @@ void fake_sched_decode(int which, int g, int i, int* o) {
   o[3] = si.first;
   o[4] = si.last;
 }
+// Walk every block of the last schedule with the incremental cursor and
+// count the steps where it differs from sched_decode.
+int fake_sched_cursor_mismatches(int which) {
+  const mla::Schedule& s = sched_of(which);
+  int bad = 0;
+  for (int g = 0; g < s.n_blocks; ++g) {
+    const int n = mla::sched_block_steps(s, g);
+    if (n <= 0) continue;
+    mla::SchedCursor c;
+    mla::sched_cursor_seek(s, g, n, 0, c);
+    for (int i = 0; i < n; ++i) {
+      const mla::StepInfo d = mla::sched_decode(s, g, i);
+      if (c.i != i || c.si.grp != d.grp || c.si.kt != d.kt || c.si.slot != d.slot ||
+          c.si.first != d.first || c.si.last != d.last)
+        ++bad;
+      const bool seg = mla::sched_cursor_next(s, g, n, c);
+      if (i + 1 < n && seg != mla::sched_decode(s, g, i + 1).first) ++bad;
+    }
+  }
+  return bad;
+}
 int fake_sched_group_slots(int which, int grp) {
   return mla::sched_group_slots(sched_of(which), grp);
 }

@@ -130,7 +130,7 @@ def _mha_info(L):
 # many blocks of each fit one compute unit (stages LDS tiles of
 # key_tile * chunks * 16 bytes in 160 KiB; at most eight waves).
 def expected_shape(rows, chunks_per_key=28):
-    br, kt, ns = (32, 32, 2) if rows <= 32 else ((128, 32, 4) if rows <= 128 else (256, 64, 2))
+    br, kt, ns = (32, 32, 2) if rows <= 32 else ((128, 32, 4) if rows <= 128 else (256, 64, 3))
     spans = kt * chunks_per_key // 64 // (br // 32)   # tile loads per wave
     return br, kt, min(ns, 1 + 63 // spans)           # in-flight loads fit a 6-bit counter
 
@@ -172,6 +172,8 @@ def check_schedule(L, info, R, which=0):
         assert slots[grp] == set(range(k)) and k <= info["n_slots"]
     busy = [s for s in steps if s > 0]
     assert max(busy) <= -(-groups * n_kt // nb) + 1
+    # the kernels walk the same steps incrementally
+    assert L.fake_sched_cursor_mismatches(which) == 0
 
 
 P = ctypes.c_void_p
