@@ -9,25 +9,50 @@ namespace mla {
 
 namespace {
 
-// q [B][Lq][n_h][d_h] -> qrot [B][n_h * Lq_pad][d_h] bf16 (head-major rows).
+// q [B][Lq][n_h][d_h] -> qrot [B][n_h * Lq_pad][d_h] in the cache type
+// (head-major rows), rotated and scaled.  A block takes kQprepTokens tokens of
+// one sequence: the rotation's cos/sin per (token, pair) are evaluated once
+// into LDS and shared by every head; then each thread moves 8-element chunks
+// (16-byte loads and stores).  Pairs whose frequency is 0 keep angle 0.
+constexpr int kQprepTokens = 4;
+
 template <typename E>
 __global__ __launch_bounds__(256) void mha_qprep_bf16_kernel(MhaAttendArgs a, int lq_pad) {
+  typedef typename Elem<E>::v8 V8;
+  __shared__ float cs[kQprepTokens][kMaxRopePairs][2];
   const int P = a.d_h / 2;
-  const int64_t n = (int64_t)a.B * a.Lq * a.n_h * P;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= n) return;
-  const int p = (int)(idx % P);
-  int64_t r = idx / P;
-  const int h = (int)(r % a.n_h);
-  r /= a.n_h;
-  const int tok = (int)(r % a.Lq);
-  const int b = (int)(r / a.Lq);
-  const bf16_t* qs = (const bf16_t*)a.q + (((size_t)b * a.Lq + tok) * a.n_h + h) * a.d_h + 2 * p;
-  float x0 = (float)qs[0], x1 = (float)qs[1];
-  rope_pair(a.rope, p, token_pos(a.q_token0 + tok, a.T, a.grid_w), x0, x1);
-  E* o = (E*)a.qrot + ((size_t)b * a.n_h * lq_pad + (size_t)h * lq_pad + tok) * a.d_h + 2 * p;
-  o[0] = Elem<E>::from(x0 * a.qscale);
-  o[1] = Elem<E>::from(x1 * a.qscale);
+  const int b = blockIdx.y;
+  const int tok0 = blockIdx.x * kQprepTokens;
+  for (int i = threadIdx.x; i < kQprepTokens * P; i += blockDim.x) {
+    const int tt = i / P, p = i - tt * P;
+    float c = 1.0f, s = 0.0f;
+    if (tok0 + tt < a.Lq && a.rope.inv_freq[p] != 0.0)
+      rope_cos_sin(pos_axis(token_pos(a.q_token0 + tok0 + tt, a.T, a.grid_w), a.rope.axis[p]) *
+                       a.rope.inv_freq[p],
+                   c, s);
+    cs[tt][p][0] = c;
+    cs[tt][p][1] = s;
+  }
+  __syncthreads();
+  const int C = a.d_h / 8;
+  const int per_tok = a.n_h * C;
+  for (int i = threadIdx.x; i < kQprepTokens * per_tok; i += blockDim.x) {
+    const int tt = i / per_tok, rem = i - tt * per_tok;
+    const int h = rem / C, ch = rem - h * C;
+    const int tok = tok0 + tt;
+    if (tok >= a.Lq) continue;
+    const bf16x8 v = ld_bf16x8((const bf16_t*)a.q + (((size_t)b * a.Lq + tok) * a.n_h + h) * a.d_h + 8 * ch);
+    V8 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float c = cs[tt][4 * ch + j][0], s = cs[tt][4 * ch + j][1];
+      const float x0 = (float)v[2 * j], x1 = (float)v[2 * j + 1];
+      o[2 * j] = Elem<E>::from((x0 * c - x1 * s) * a.qscale);
+      o[2 * j + 1] = Elem<E>::from((x0 * s + x1 * c) * a.qscale);
+    }
+    *reinterpret_cast<V8*>((E*)a.qrot + ((size_t)b * a.n_h * lq_pad + (size_t)h * lq_pad + tok) * a.d_h +
+                           8 * ch) = o;
+  }
 }
 
 // Merge a row group's partials and normalise: one thread per (row, 4 dims).
@@ -129,9 +154,9 @@ hipError_t launch_mha_typed(const MhaAttendArgs& a, float* opart, float* ml, con
   const int br = sched.block_rows;
   const int lq_pad = (a.Lq + br - 1) / br * br;
   {
-    const int64_t n = (int64_t)a.B * a.Lq * a.n_h * (a.d_h / 2);
-    hipLaunchKernelGGL(mha_qprep_bf16_kernel<E>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                       a, lq_pad);
+    hipLaunchKernelGGL(mha_qprep_bf16_kernel<E>,
+                       dim3((unsigned)((a.Lq + kQprepTokens - 1) / kQprepTokens), (unsigned)a.B),
+                       dim3(256), 0, s, a, lq_pad);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -13,11 +13,14 @@
 //  2. expand_kv_kernel: for every resident key j and head h,
 //       K[j][h] = [ W^K_up,h c_j | k^R_j ],   V[j][h] = W^V_up,h c_j,
 //     written as [B][Lk][2][n_h][d_h] in the ring's element type - the layout
-//     of the dense cache, so the same attention core reads it.  One GEMM per
-//     32-key block: D[key][col] = c[key][:] . W[col][:], on 32x32x16 MFMA with
-//     the latent rows (A operand) in registers and each 32-row weight tile
-//     (B operand) staged in LDS by direct global->LDS loads, shared by the
-//     four waves (four 32-key blocks) of a workgroup.
+//     of the dense cache, so the same attention core reads it.  A workgroup
+//     owns one head and a range of keys of one sequence: the head's whole
+//     [d_nope + d_v][d_c] matrix is loaded into LDS once (direct
+//     global->LDS loads), then each wave independently walks 32-key blocks:
+//     latent rows into registers (MFMA A operand), D[key][col] =
+//     c[key][:] . W[col][:] on 32x32x16 MFMA per 32-row weight tile (B
+//     operand from LDS), the head's key and value blocks staged in the wave's
+//     own LDS area and written out as whole 256-byte rows.
 #include "mla_attn_core.h"
 
 namespace mla {
@@ -44,104 +47,137 @@ __global__ __launch_bounds__(256) void weights_to_cache_kernel(ExpandArgs a) {
   *reinterpret_cast<typename Elem<E>::v8*>((E*)a.wx + idx) = o;
 }
 
-// DC: latent width.  A workgroup of 4 waves owns 128 keys (32 per wave) of one
-// sequence and walks every 32-row weight tile of every head.
+constexpr int kExpandWaves = 8;       // waves per workgroup (two per SIMD)
+// Head shape of the rebuild: d_nope = 96 content and d_rope = 32 positional
+// key columns, d_v = 128 value columns (the Wan shape); 7 weight tiles of 32
+// rows per head, 3 of them for keys.
+constexpr int kExpandNope = 96, kExpandRope = 32, kExpandDv = 128;
+constexpr int kExpandKTiles = kExpandNope / 32, kExpandTiles = kExpandKTiles + kExpandDv / 32;
+
+// DC: latent width.  Workgroup (x, h, b): head h of sequence b, keys
+// [x * keys_per_block, (x + 1) * keys_per_block).
 template <typename E, int DC>
-__global__ __launch_bounds__(256) void expand_kv_kernel(ExpandArgs a) {
+__global__ __launch_bounds__(kExpandWaves * 64) void expand_kv_kernel(ExpandArgs a, int keys_per_block) {
   typedef typename Elem<E>::v8 V8;
   constexpr int NKS = DC / 16;         // MFMA depth steps
   constexpr int CPR = DC / 8;          // 16-byte chunks per weight row
   constexpr int TILE = 32 * DC;        // elements per weight tile (32 rows)
-  constexpr int SPANS = TILE * 2 / 1024;
+  constexpr int DH = 128;              // per-head key width (d_nope + d_rope) and value width
+  constexpr int WSPANS = kExpandTiles * TILE * 2 / 1024;
   static_assert(DC % 64 == 0 && (TILE * 2) % 1024 == 0, "whole 1-KiB spans per tile");
   static_assert(CPR % 8 == 0, "the chunk permutation stays inside groups of 8");
-  __shared__ __attribute__((aligned(1024))) E wt0[TILE];
-  __shared__ __attribute__((aligned(1024))) E wt1[TILE];
+  static_assert(kExpandNope + kExpandRope == DH && kExpandDv == DH, "128-wide heads");
+  __shared__ __attribute__((aligned(1024))) E wts[kExpandTiles * TILE];
+  __shared__ __attribute__((aligned(16))) E stg[kExpandWaves][32 * DH];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63, lo = l & 31, hi = l >> 5;
-  const int b = blockIdx.y;
-  const int key0 = blockIdx.x * 128 + w * 32;
-  const int d_h = a.d_nope + a.d_rope;
-  const int tph = (a.d_nope + a.d_v) / 32;   // weight tiles per head
-  const int n_tiles = a.n_h * tph;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int kbeg = blockIdx.x * keys_per_block;
+  const int kend = kbeg + keys_per_block < a.Lk ? kbeg + keys_per_block : a.Lk;
+  E* st = stg[w];
 
-  // This lane's latent row (A operand: key lo, depth 16 ks + 8 hi .. + 8).
-  const int key = key0 + lo;
-  const bool kvalid = key < a.Lk;
-  int64_t slot = a.key_slot0 + (kvalid ? key : 0);
-  if (slot >= a.ring_rows) slot -= a.ring_rows;
-  const E* crow = (const E*)a.ring + ((size_t)b * a.ring_rows + slot) * (DC + a.d_rope);
-  V8 cf[NKS];
-#pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) cf[ks] = ld8<E>(crow + 16 * ks + 8 * hi);
-
-  // Weight tile t = rows [32 t, 32 t + 32) of the converted [n_h * (d_nope +
-  // d_v)][DC] matrix.  In LDS, chunk q of tile row r sits at q ^ ((r >> 1) & 7)
-  // (inside aligned groups of 8 chunks): the 16 lanes of a B-operand read,
-  // rows 0..15 at one chunk, then touch 64 distinct banks.  Lane l of span sp
-  // fills LDS chunk c = 64 sp + l: row c / CPR, position c % CPR.
-  auto load_tile = [&](int t, E* dst) __attribute__((always_inline)) {
-    const E* src = (const E*)a.wx + (size_t)t * TILE;
-#pragma unroll
-    for (int j = 0; j < SPANS / 4; ++j) {
-      const int sp = w + 4 * j;
+  // The head's weight tiles: rows [32 t, 32 t + 32) of its converted matrix.
+  // In LDS, chunk q of tile row r sits at q ^ ((r >> 1) & 7) (inside aligned
+  // groups of 8 chunks): the 16 lanes of a B-operand read, rows 0..15 at one
+  // chunk, then touch 64 distinct banks.  Lane l of span sp fills LDS chunk
+  // c = 64 sp + l: row c / CPR, position c % CPR of the rows of all tiles.
+  {
+    const E* src = (const E*)a.wx + (size_t)h * kExpandTiles * TILE;
+    for (int sp = w; sp < WSPANS; sp += kExpandWaves) {
       const int c = sp * 64 + l;
       const int r = c / CPR, p = c - r * CPR;
       const int q = p ^ ((r >> 1) & 7);
-      global_to_lds16(src + r * DC + q * 8, dst + sp * 512);
+      global_to_lds16(src + r * DC + q * 8, wts + sp * 512);
     }
-  };
-  static_assert(SPANS % 4 == 0, "spans divide over the four waves");
-
-  // B-operand read: lane (col lo, hi) takes chunk 2 ks + hi of row lo.
-  const int rsw = (lo >> 1) & 7;
-
-  auto tile_product = [&](const E* wt, int t) __attribute__((always_inline)) {
-    f32x16 acc;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-    const E* wrow = wt + lo * DC;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-      acc = Elem<E>::mfma(cf[ks], ld8<E>(wrow + 8 * ((2 * ks + hi) ^ rsw)), acc);
-    // D[key][col]: lane holds col lo of keys 8 (r / 4) + 4 hi + r % 4.
-    const int h = t / tph;
-    const int c0 = (t - h * tph) * 32;   // row of the head's [K nope ; V] block
-    const bool kpart = c0 < a.d_nope;
-    const int col = (kpart ? c0 : c0 - a.d_nope) + lo;
-    E* base = (E*)a.kv + (((size_t)b * a.Lk) * 2 + (kpart ? 0 : 1)) * a.n_h * d_h + (size_t)h * d_h + col;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int kk = key0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-      if (kk < a.Lk) base[(size_t)kk * 2 * a.n_h * d_h] = Elem<E>::from(acc[r]);
-    }
-  };
-
-  load_tile(0, wt0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (int t = 0; t < n_tiles; t += 2) {
-    if (t + 1 < n_tiles) load_tile(t + 1, wt1);
-    tile_product(wt0, t);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (t + 1 < n_tiles) {
-      if (t + 2 < n_tiles) load_tile(t + 2, wt0);
-      tile_product(wt1, t + 1);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-    }
   }
 
-  // k^R of each key into every head's positional columns.
-  if (kvalid) {
-    const E* kr = crow + DC;
-    E* dst = (E*)a.kv + ((size_t)b * a.Lk + key) * 2 * a.n_h * d_h + a.d_nope;
-    for (int h = 0; h < a.n_h; ++h)
-      for (int i = 8 * hi; i < a.d_rope; i += 16)
-        *reinterpret_cast<V8*>(dst + (size_t)h * d_h + i) = ld8<E>(kr + i);
+  // B-operand read: lane (col lo, hi) takes chunk 2 ks + hi of tile row lo.
+  const int rsw = (lo >> 1) & 7;
+  // Staged block: key kk's 128 columns at st[kk * DH ..]; column chunk q
+  // (8 columns) of key kk sits at chunk q ^ (kk & 15), so the two half-waves
+  // of a tile store (keys 4 apart) and the key-row reads spread over the banks.
+  auto stage_at = [&](int kk, int col) __attribute__((always_inline)) {
+    return kk * DH + ((((col >> 3) ^ kk) & 15) << 3) + (col & 7);
+  };
+  // Write the staged 32 x 128 block of keys k0.. as part `part` (0 keys,
+  // 1 values): 16 lanes per key row, 16 bytes each.
+  auto flush = [&](int k0, int part) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = i * 64 + l;
+      const int kk = c >> 4, q = c & 15;
+      const V8 v = *reinterpret_cast<const V8*>(st + kk * DH + ((q ^ kk) & 15) * 8);
+      const int kg = k0 + kk;
+      if (kg < kend)
+        *reinterpret_cast<V8*>((E*)a.kv + ((((size_t)b * a.Lk + kg) * 2 + part) * a.n_h + h) * DH +
+                               q * 8) = v;
+    }
+  };
+  // This lane's latent row of the 32-key block at k0 (A operand: key lo,
+  // depth 16 ks + 8 hi .. + 8, then k^R as 8-column pieces 8 hi + 16 j);
+  // keys past the range load key k0's row (never written out).
+  constexpr int NR = kExpandRope / 16;  // k^R pieces per lane
+  auto load_row = [&](int k0, V8 (&c)[NKS], V8 (&r)[NR]) __attribute__((always_inline)) {
+    const int key = k0 + lo < kend ? k0 + lo : k0;
+    int64_t slot = a.key_slot0 + key;
+    if (slot >= a.ring_rows) slot -= a.ring_rows;
+    const E* crow = (const E*)a.ring + ((size_t)b * a.ring_rows + slot) * (DC + kExpandRope);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) c[ks] = ld8<E>(crow + 16 * ks + 8 * hi);
+#pragma unroll
+    for (int j = 0; j < NR; ++j) r[j] = ld8<E>(crow + DC + 16 * j + 8 * hi);
+  };
+
+  for (int k0 = kbeg + 32 * w; k0 < kend; k0 += 32 * kExpandWaves) {
+    V8 cf[NKS], rf[NR];
+    load_row(k0, cf, rf);
+
+    // k^R into columns d_nope .. 127 of the staged key block
+#pragma unroll
+    for (int j = 0; j < NR; ++j)
+      *reinterpret_cast<V8*>(st + stage_at(lo, kExpandNope + 16 * j + 8 * hi)) = rf[j];
+#pragma unroll 1
+    for (int t = 0; t < kExpandTiles; ++t) {
+      f32x16 acc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+      const E* wrow = wts + t * TILE + lo * DC;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+        acc = Elem<E>::mfma(cf[ks], ld8<E>(wrow + 8 * ((2 * ks + hi) ^ rsw)), acc);
+      // D[key][col]: lane holds column c0 + lo of keys 8 (r / 4) + 4 hi + r % 4.
+      const int c0 = t < kExpandKTiles ? 32 * t : 32 * (t - kExpandKTiles);
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        st[stage_at(8 * (r >> 2) + 4 * hi + (r & 3), c0 + lo)] = Elem<E>::from(acc[r]);
+      if (t == kExpandKTiles - 1) flush(k0, 0);
+      if (t == kExpandTiles - 1) flush(k0, 1);
+    }
   }
+}
+
+// Workgroups per (head, sequence): the key split with the fewest rounds of
+// workgroups per unit of keys (one workgroup per compute unit at a time);
+// measured faster than one round of longer key ranges, since each wave's
+// key blocks run one after another.
+int expand_splits(int n_h, int B, int Lk) {
+  const int cus = device_cu_count();
+  const int units = n_h * B;
+  const int max_split = (Lk + 255) / 256;
+  int best = 1;
+  double best_cost = 1e30;
+  for (int s = 1; s <= max_split && s <= 256; ++s) {
+    const double rounds = (double)((units * s + cus - 1) / cus);
+    const double cost = rounds / s;
+    if (cost < best_cost - 1e-12) {
+      best_cost = cost;
+      best = s;
+    }
+  }
+  return best;
 }
 
 template <typename E, int DC>
@@ -153,8 +189,10 @@ hipError_t launch_expand_dc(const ExpandArgs& a, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  dim3 grid((unsigned)((a.Lk + 127) / 128), (unsigned)a.B);
-  hipLaunchKernelGGL((expand_kv_kernel<E, DC>), grid, dim3(256), 0, s, a);
+  const int splits = expand_splits(a.n_h, a.B, a.Lk);
+  const int kpb = ((a.Lk + splits - 1) / splits + 31) / 32 * 32;
+  dim3 grid((unsigned)((a.Lk + kpb - 1) / kpb), (unsigned)a.n_h, (unsigned)a.B);
+  hipLaunchKernelGGL((expand_kv_kernel<E, DC>), grid, dim3(kExpandWaves * 64), 0, s, a, kpb);
   return hipGetLastError();
 }
 
@@ -171,8 +209,8 @@ hipError_t launch_expand_typed(const ExpandArgs& a, hipStream_t s) {
 }  // namespace
 
 bool expand_supported(int d_c, int d_rope, int d_nope, int d_v) {
-  return (d_c == 64 || d_c == 128 || d_c == 192) && d_nope + d_rope == 128 && d_v == 128 &&
-         d_nope % 32 == 0 && d_rope % 8 == 0;
+  return (d_c == 64 || d_c == 128 || d_c == 192) && d_nope == kExpandNope && d_rope == kExpandRope &&
+         d_v == kExpandDv;
 }
 
 hipError_t launch_expand_kv(const ExpandArgs& a, hipStream_t s) {

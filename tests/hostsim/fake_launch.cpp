@@ -53,8 +53,7 @@ hipError_t launch_mha_attend_bf16_ws(const MhaAttendArgs& a, float* opart, float
   return rec(5);
 }
 bool expand_supported(int d_c, int d_rope, int d_nope, int d_v) {
-  return (d_c == 64 || d_c == 128 || d_c == 192) && d_nope + d_rope == 128 && d_v == 128 &&
-         d_nope % 32 == 0 && d_rope % 8 == 0;
+  return (d_c == 64 || d_c == 128 || d_c == 192) && d_nope == 96 && d_rope == 32 && d_v == 128;
 }
 hipError_t launch_expand_kv(const ExpandArgs& a, hipStream_t) { g_expand = a; return rec(7); }
 hipError_t launch_mha_attend_f32(const MhaAttendArgs& a, hipStream_t) { g_mha = a; return rec(6); }

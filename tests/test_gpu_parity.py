@@ -278,9 +278,11 @@ def test_full_window_sampled_rows(batch, cache_dtype, path):
 # 32- and 64-key tiles and a ragged last 128-key rebuild block; the query
 # counts reach all three attention block shapes (3 -> 32-row blocks, 33 and
 # 120 -> 128-row blocks, 200 and 300 -> 256-row blocks with padded rows).
-@pytest.mark.parametrize("Lq,d_c", [(3, 192), (33, 64), (120, 128), (200, 192), (300, 64)])
-def test_expand_mid_ragged_with_wrap(Lq, d_c):
-    cfg = mid_cfg(d_nope=96, d_rope=32, d_v=128, d_c=d_c)
+# 6 heads: the rebuild's last head group is partial (4 + 2 heads).
+@pytest.mark.parametrize("Lq,d_c,n_heads", [(3, 192, 4), (33, 64, 4), (120, 128, 6), (200, 192, 4),
+                                            (300, 64, 4)])
+def test_expand_mid_ragged_with_wrap(Lq, d_c, n_heads):
+    cfg = mid_cfg(d_nope=96, d_rope=32, d_v=128, d_c=d_c, n_heads=n_heads)
     run = LatentRun(cfg, path="expand")
     run.write(0, 4)
     run.evict(2)
@@ -290,7 +292,7 @@ def test_expand_mid_ragged_with_wrap(Lq, d_c):
     assert run.gpu.attend_path(Lq) == "expand"
     q = run.query(Lq)
     got, ref, _ = run.attend(q, 8 * cfg.T - Lq)
-    assert_parity(got, ref, "bf16", f"expand Lq={Lq} d_c={d_c}")
+    assert_parity(got, ref, "bf16", f"expand Lq={Lq} d_c={d_c} n_h={n_heads}")
 
 
 def test_expand_poisoned_free_slots_and_agreement():
