@@ -4,27 +4,30 @@
 // to its ring slot.  The same kernel serves the dense comparison cache (K and
 // V of every head; K rotated per head).
 //
-// 2-byte path (bf16 inputs; bf16 or fp16 ring): each wave computes a tile of
-// 32 tokens x 32 output columns over the whole hidden dimension, with the
-// next four depth steps' fragments in flight; a block holds
-// four column tiles of the same 32 tokens (their x rows are shared in cache).
-// The product is laid out transposed (columns on the MFMA M side, tokens on
-// the N side) so that a lane holds one token and both elements of every
-// rotary pair.
+// 2-byte path (bf16 inputs; bf16 or fp16 ring): a block computes one tile of
+// 32 tokens x 32 output columns, its four waves each taking a quarter of the
+// hidden dimension (so a tile's long dependent MFMA chain is four short ones
+// running on four SIMDs, and four times as many waves hide the load latency);
+// the quarters are summed through LDS and each wave finishes 8 of the tile's
+// 32 columns.  The product is laid out transposed (columns on the MFMA M
+// side, tokens on the N side) so that a lane holds one token and both
+// elements of every rotary pair.
 #include "mla_device.h"
+
+#define MLA_INLINE __attribute__((always_inline))
 
 namespace mla {
 
 namespace {
 
-constexpr int kWaves = 4;     // column tiles per block
+constexpr int kSplitK = 4;     // waves per block = hidden-dimension quarters
 
 template <typename E>
-__global__ __launch_bounds__(256) void cache_write_bf16_kernel(CacheWriteArgs a) {
+__global__ __launch_bounds__(kSplitK * 64) void cache_write_bf16_kernel(CacheWriteArgs a) {
+  __shared__ float red[kSplitK][16][64];
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63, lo = l & 31, hi = l >> 5;
-  const int ct = blockIdx.y * kWaves + w;  // column tile of this wave
-  if (ct * 32 >= a.width) return;
+  const int ct = blockIdx.y;               // column tile
   const int64_t tok = (int64_t)blockIdx.x * 32 + lo;
   const bool valid = tok < a.M;
   const int col = ct * 32 + lo;            // W row this lane feeds
@@ -36,9 +39,13 @@ __global__ __launch_bounds__(256) void cache_write_bf16_kernel(CacheWriteArgs a)
                                         : (const bf16_t*)a.w2 + (int64_t)(col - a.w_split) * a.hidden) +
                        32 * hi;
   const int ng = a.hidden / 64;            // groups of four 16-deep steps
+  const int g0 = w * ng / kSplitK, g1 = (w + 1) * ng / kSplitK;  // this wave's groups
 
-  bf16x8 xf[2][4], wf[2][4];
-  auto load_group = [&](int gi, int slot) {
+  // A ring of kDepth groups in flight: the loads of group g + kDepth - 1 go
+  // out before the products of group g.
+  constexpr int kDepth = 3;
+  bf16x8 xf[kDepth][4], wf[kDepth][4];
+  auto load_group = [&](int gi, int slot) MLA_INLINE {
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
       xf[slot][s4] = valid ? ld_bf16x8(xrow + gi * 64 + 8 * s4) : zero_bf16x8();
@@ -48,18 +55,34 @@ __global__ __launch_bounds__(256) void cache_write_bf16_kernel(CacheWriteArgs a)
   f32x16 acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-  load_group(0, 0);
-  for (int gi = 0; gi < ng; gi += 2) {
-    if (gi + 1 < ng) load_group(gi + 1, 1);
 #pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) acc = mfma32(wf[0][s4], xf[0][s4], acc);
-    if (gi + 1 < ng) {
-      if (gi + 2 < ng) load_group(gi + 2, 0);
+  for (int d = 0; d < kDepth - 1; ++d)
+    if (g0 + d < g1) load_group(g0 + d, d);
+  for (int gi = g0; gi < g1; gi += kDepth) {
 #pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) acc = mfma32(wf[1][s4], xf[1][s4], acc);
+    for (int d = 0; d < kDepth; ++d) {
+      if (gi + d < g1) {
+        if (gi + d + kDepth - 1 < g1) load_group(gi + d + kDepth - 1, (d + kDepth - 1) % kDepth);
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) acc = mfma32(wf[d][s4], xf[d][s4], acc);
+      }
     }
   }
+  // Sum the quarters: every wave stores its partial tile; wave w then owns
+  // accumulator group g = w (columns 8 g + 4 hi .. + 4 of every token).
+#pragma unroll
+  for (int r = 0; r < 16; ++r) red[w][r][l] = acc[r];
+  __syncthreads();
   if (!valid) return;
+  const int g = w;
+  float v[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float sum = 0.0f;
+#pragma unroll
+    for (int q = 0; q < kSplitK; ++q) sum += red[q][4 * g + k][l];
+    v[k] = sum;
+  }
 
   const int64_t b = tok / a.tokens_per_batch;
   const int i = (int)(tok - b * a.tokens_per_batch);
@@ -71,22 +94,18 @@ __global__ __launch_bounds__(256) void cache_write_bf16_kernel(CacheWriteArgs a)
   pos.x = tau - pos.y * a.grid_w;
   const int64_t slot = (frame % a.W) * a.T + tau;
   E* dst = (E*)a.ring + (b * a.ring_rows + slot) * a.width;
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const int c0 = ct * 32 + 8 * g + 4 * hi;
-    float v[4] = {acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
-    if (c0 >= a.rot_begin && c0 < a.rot_end) {
-      const int p0 = ((c0 - a.rot_begin) % a.rot_group) >> 1;
-      rope_pair(a.rope, p0, pos, v[0], v[1]);
-      rope_pair(a.rope, p0 + 1, pos, v[2], v[3]);
-    }
-    typename Elem<E>::v4 o;
-    o[0] = Elem<E>::from(v[0]);
-    o[1] = Elem<E>::from(v[1]);
-    o[2] = Elem<E>::from(v[2]);
-    o[3] = Elem<E>::from(v[3]);
-    *reinterpret_cast<typename Elem<E>::v4*>(dst + c0) = o;
+  const int c0 = ct * 32 + 8 * g + 4 * hi;
+  if (c0 >= a.rot_begin && c0 < a.rot_end) {
+    const int p0 = ((c0 - a.rot_begin) % a.rot_group) >> 1;
+    rope_pair(a.rope, p0, pos, v[0], v[1]);
+    rope_pair(a.rope, p0 + 1, pos, v[2], v[3]);
   }
+  typename Elem<E>::v4 o;
+  o[0] = Elem<E>::from(v[0]);
+  o[1] = Elem<E>::from(v[1]);
+  o[2] = Elem<E>::from(v[2]);
+  o[3] = Elem<E>::from(v[3]);
+  *reinterpret_cast<typename Elem<E>::v4*>(dst + c0) = o;
 }
 
 // fp32 path (small shapes): one thread per (token, column pair), plain fp32
@@ -128,9 +147,8 @@ __global__ __launch_bounds__(256) void cache_write_f32_kernel(CacheWriteArgs a) 
 
 template <typename E>
 hipError_t launch_typed(const CacheWriteArgs& a, hipStream_t s) {
-  const int tiles = a.width / 32;
-  dim3 grid((unsigned)((a.M + 31) / 32), (unsigned)((tiles + kWaves - 1) / kWaves));
-  hipLaunchKernelGGL(cache_write_bf16_kernel<E>, grid, dim3(kWaves * 64), 0, s, a);
+  dim3 grid((unsigned)((a.M + 31) / 32), (unsigned)(a.width / 32));
+  hipLaunchKernelGGL(cache_write_bf16_kernel<E>, grid, dim3(kSplitK * 64), 0, s, a);
   return hipGetLastError();
 }
 
