@@ -332,44 +332,110 @@ def main():
         result["cache_bytes"]["dense_per_layer"] = dcache.nbytes
         del dcache, dws, dout
 
-        # cache-bound small-query case: Lq queries per sequence, batch 8, 30 layers cycled
+        # cache-bound small-query shapes: Lq queries per sequence over the full
+        # window, latent widths 64 / 128 / 192, batch 8 and 11, 30 layer windows
+        # cycled (3.5-4.8 GB of windows, far above the last-level cache)
         sq = {}
-        Bs = 8
-        scfg = cfg.with_(batch=Bs)
-        scaches = []
-        for l in range(L):
-            c = LatentCache(scfg, device=dev)
-            c.ring().copy_(torch.randn(c.ring().shape, generator=gen, device=dev).to(torch.bfloat16))
-            c.set_state(0, W - 1)
-            scaches.append(c)
-        for Lqs in (1, 8):
-            qs = torch.randn((Bs, Lqs, cfg.n_heads, cfg.d_qk), generator=gen, device=dev).to(torch.bfloat16)
-            so = torch.empty((Bs, Lqs, cfg.n_heads, cfg.d_v), dtype=torch.float32, device=dev)
-            sws = torch.empty(scaches[0].workspace_bytes(Lqs), dtype=torch.uint8, device=dev)
-            for l in range(L):
-                scaches[l].attend(qs, Lk - Lqs, weights[l]["w_uk"], weights[l]["w_uv"], out=so, workspace=sws)
-            sev = [(ev.create(), ev.create()) for _ in range(2 * L)]
+        for d_c in (192, 128, 64):
+            for Bs in (8, 11):
+                scfg = cfg.with_(batch=Bs, d_c=d_c)
+                sw = [layer_weights(scfg, layer=l) for l in range(2)]
+                sw = [{k: v.to(dev) for k, v in w_.items()} for w_ in sw]
+                scaches = []
+                for l in range(L):
+                    c = LatentCache(scfg, device=dev)
+                    c.ring().copy_(torch.randn(c.ring().shape, generator=gen, device=dev).to(c.ring().dtype))
+                    c.set_state(0, W - 1)
+                    scaches.append(c)
+                for Lqs in (1, 4, 8):
+                    qs = torch.randn((Bs, Lqs, cfg.n_heads, cfg.d_qk), generator=gen, device=dev).to(torch.bfloat16)
+                    so = torch.empty((Bs, Lqs, cfg.n_heads, cfg.d_v), dtype=torch.float32, device=dev)
+                    sws = torch.empty(max(scaches[0].workspace_bytes(Lqs), 1), dtype=torch.uint8, device=dev)
+                    for l in range(L):
+                        scaches[l].attend(qs, Lk - Lqs, sw[l % 2]["w_uk"], sw[l % 2]["w_uv"], out=so, workspace=sws)
+                    # whole calls back to back (no profiling events), then the
+                    # core kernel alone by the library's events
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    torch.cuda.synchronize()
+                    e0.record()
+                    for i in range(2 * L):
+                        scaches[i % L].attend(qs, Lk - Lqs, sw[i % 2]["w_uk"], sw[i % 2]["w_uv"], out=so,
+                                              workspace=sws)
+                    e1.record()
+                    torch.cuda.synchronize()
+                    call_ms = e0.elapsed_time(e1) / (2 * L)
+                    sev = [(ev.create(), ev.create()) for _ in range(2 * L)]
+                    for i, (a_, b_) in enumerate(sev):
+                        c = scaches[i % L]
+                        c.set_profile_events(a_, b_)
+                        c.attend(qs, Lk - Lqs, sw[i % 2]["w_uk"], sw[i % 2]["w_uv"], out=so, workspace=sws)
+                        c.set_profile_events(None, None)
+                    torch.cuda.synchronize()
+                    kms = sum(ev.elapsed_ms(a_, b_) for a_, b_ in sev) / len(sev)
+                    win = Bs * Lk * (d_c + cfg.d_rope) * 2
+                    nbytes = attend_bytes(cfg.n_heads, Lqs, Lk, d_c, cfg.d_rope, cfg.d_nope, cfg.d_v, Bs)
+                    sq[f"dc{d_c}_Lq{Lqs}_B{Bs}"] = {
+                        "attend_ms": round(call_ms, 4), "core_kernel_ms": round(kms, 4),
+                        "algorithmic_bytes": nbytes,
+                        "core_GBps": round(win / (kms / 1e3) / 1e9, 1),
+                        "call_GBps": round(nbytes / (call_ms / 1e3) / 1e9, 1),
+                        "hbm_frac_call": round(nbytes / (call_ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+                        "query_tokens_per_s": round(Bs * Lqs / (call_ms / 1e3), 1)}
+                    del sws, so, qs
+                del scaches, sw
+        result["small_query_cache_bound"] = sq
+
+        # batch scaling of the chunk step (evict + write + attend), 4 layer
+        # windows cycled per batch size
+        scale = {}
+        for Bb in (1, 2, 4, 8):
+            bcfg = cfg.with_(batch=Bb)
+            bw = [{k: v.to(dev) for k, v in layer_weights(bcfg, layer=l).items()} for l in range(2)]
+            bx = torch.randn((Bb, W * T, cfg.hidden), generator=gen, device=dev).to(torch.bfloat16)
+            bxc = bx[:, :Lq].contiguous()
+            bq = torch.randn((Bb, Lq, cfg.n_heads, cfg.d_qk), generator=gen, device=dev).to(torch.bfloat16)
+            bcs = []
+            for l in range(4):
+                c = LatentCache(bcfg, device=dev)
+                c.set_attend_path(args.path)
+                c.write(bx, bw[l % 2]["w_dkr"], 0, W)
+                bcs.append(c)
+            bnew = [W - 1] * 4
+            bout = torch.empty((Bb, Lq, cfg.n_heads, cfg.d_v), dtype=torch.float32, device=dev)
+            bws = torch.empty(max(bcs[0].workspace_bytes(Lq), 1), dtype=torch.uint8, device=dev)
+            del bx
+
+            def bstep(k):
+                l = k % 4
+                c = bcs[l]
+                c.evict(cfg.chunk_frames)
+                f0 = bnew[l] + 1
+                c.write(bxc, bw[l % 2]["w_dkr"], f0, cfg.chunk_frames)
+                bnew[l] = f0 + cfg.chunk_frames - 1
+                c.attend(bq, f0 * T, bw[l % 2]["w_uk"], bw[l % 2]["w_uv"], out=bout, workspace=bws)
+
+            for k in range(4):
+                bstep(k)
+            n_b = 12
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             torch.cuda.synchronize()
             e0.record()
-            for i, (a_, b_) in enumerate(sev):
-                c = scaches[i % L]
-                c.set_profile_events(a_, b_)
-                c.attend(qs, Lk - Lqs, weights[i % L]["w_uk"], weights[i % L]["w_uv"], out=so, workspace=sws)
-                c.set_profile_events(None, None)
+            for k in range(n_b):
+                bstep(k)
             e1.record()
             torch.cuda.synchronize()
-            call_ms = e0.elapsed_time(e1) / len(sev)
-            kms = sum(ev.elapsed_ms(a_, b_) for a_, b_ in sev) / len(sev)
-            nbytes = attend_bytes(cfg.n_heads, Lqs, Lk, cfg.d_c, cfg.d_rope, cfg.d_nope, cfg.d_v, Bs)
-            sq[f"Lq{Lqs}_B{Bs}"] = {"attend_ms": round(call_ms, 4), "core_kernel_ms": round(kms, 4),
-                                   "algorithmic_bytes": nbytes,
-                                   "core_GBps": round(Bs * Lk * cfg.width * 2 / (kms / 1e3) / 1e9, 1),
-                                   "call_GBps": round(nbytes / (call_ms / 1e3) / 1e9, 1),
-                                   "hbm_frac_core": round(Bs * Lk * cfg.width * 2 / (kms / 1e3) / 1e9 / PEAK_HBM_GBS, 4)}
-        result["small_query_cache_bound"] = sq
-        del scaches
+            b_ms = e0.elapsed_time(e1) / n_b
+            bflop = (attend_flops(cfg.n_heads, Lq, Lk, cfg.d_c, cfg.d_rope, cfg.d_nope, cfg.d_v, Bb)
+                     + 2 * Bb * Lq * cfg.hidden * cfg.width)
+            scale[f"B{Bb}"] = {"ms_per_step": round(b_ms, 4),
+                               "query_tokens_per_s": round(Bb * Lq / (b_ms / 1e3), 1),
+                               "path": bcs[0].attend_path(Lq),
+                               "mfma_util_pct_absorbed_form": round(100.0 * bflop / (b_ms / 1e3)
+                                                                    / (PEAK_BF16_TFLOPS * 1e12), 2)}
+            del bcs, bws, bout, bq, bxc, bw
+        result["batch_scaling"] = scale
 
     ev.close()
     if not args.no_cpu_baseline:
