@@ -222,6 +222,8 @@ __global__ __launch_bounds__(256) void epilogue_rows_kernel(AttendArgs a) {
   const int c4 = tid % C4, j = tid / C4;
   if (j < LANES) {
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    // unrolled so that several partial loads are in flight per thread
+#pragma unroll 8
     for (int k = j; k < n_part; k += LANES) {
       const size_t pr = prow_of(k);
       const float wgt = exp2_fast(a.ml[pr * 2] - M);
