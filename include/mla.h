@@ -164,7 +164,9 @@ mla_status mla_cache_set_state(mla_cache* cache, int64_t oldest_frame, int64_t n
 int64_t mla_cache_slot(const mla_cache* cache, int64_t frame, int32_t tau);
 
 /* Device workspace mla_attend needs for Lq queries with `key_splits` key
- * ranges (0 = the library's choice for this shape). */
+ * ranges (0 = the library's choice for this shape), on this handle's current
+ * attend path: the largest over every number of resident frames, so one
+ * buffer serves the window as it fills and slides. */
 size_t mla_attend_workspace_bytes(const mla_cache* cache, int32_t Lq, int32_t key_splits);
 
 /* Absorbed latent attention (method item 2 in absorbed form) of a query chunk
@@ -209,7 +211,8 @@ mla_status mla_cache_set_attend_path(mla_cache* cache, int32_t path);
  * always take the absorbed path. */
 int32_t mla_attend_path(const mla_cache* cache, int32_t Lq, int32_t key_splits);
 
-/* Workspace for mha_attend (rotated, pre-scaled queries). */
+/* Workspace for mha_attend (rotated, pre-scaled queries and key-range
+ * partials), the largest over every number of resident frames. */
 size_t mha_attend_workspace_bytes(const mla_cache* cache, int32_t Lq);
 
 /* Dense comparison attention: per head, q rotated over all d_h dims,

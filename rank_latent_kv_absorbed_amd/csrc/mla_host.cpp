@@ -176,11 +176,12 @@ struct LatentLayout {
   size_t qcat_off, opart_off, ml_off, total;
 };
 
-LatentLayout latent_layout(const mla_cache* h, int32_t Lq, int32_t key_splits) {
+// Layouts for `Lk` resident keys (default: the handle's current window).
+LatentLayout latent_layout(const mla_cache* h, int32_t Lq, int32_t key_splits, int64_t Lk = -1) {
   const mla_layer_config& c = h->cfg;
   const int64_t R = (int64_t)Lq * c.n_heads;
   LatentLayout L;
-  L.sched = make_schedule(c.batch, R, window_keys(h), key_splits, mla::device_cu_count(),
+  L.sched = make_schedule(c.batch, R, Lk < 0 ? window_keys(h) : Lk, key_splits, mla::device_cu_count(),
                           mla::core_shape_for_rows(R), (c.d_c + c.d_rope) / 8);
   const size_t width = (size_t)(c.d_c + c.d_rope);
   const size_t slots = (size_t)L.sched.n_slots;
@@ -197,14 +198,14 @@ struct DenseLayout {
   size_t qrot_off, opart_off, ml_off, total;
 };
 
-DenseLayout dense_layout(const mla_cache* h, int32_t Lq) {
+DenseLayout dense_layout(const mla_cache* h, int32_t Lq, int64_t Lk = -1) {
   const mla_layer_config& c = h->cfg;
   const int d_h = c.d_nope + c.d_rope;
   DenseLayout L;
   const mla::CoreShape sh = mla::core_shape_for_rows(Lq);
   L.lq_pad = (Lq + 32 * sh.waves - 1) / (32 * sh.waves) * (32 * sh.waves);
   const int64_t R = (int64_t)c.n_heads * L.lq_pad;
-  L.sched = make_schedule(c.batch, R, window_keys(h), 0, mla::device_cu_count(), sh,
+  L.sched = make_schedule(c.batch, R, Lk < 0 ? window_keys(h) : Lk, 0, mla::device_cu_count(), sh,
                           2 * d_h / 8);
   const size_t slots = (size_t)L.sched.n_slots;
   L.qrot_off = 0;
@@ -222,10 +223,10 @@ struct ExpandLayout {
   size_t wx_off, kv_off, base, total;
 };
 
-ExpandLayout expand_layout(const mla_cache* h, int32_t Lq) {
+ExpandLayout expand_layout(const mla_cache* h, int32_t Lq, int64_t Lk = -1) {
   const mla_layer_config& c = h->cfg;
   ExpandLayout L;
-  L.dense = dense_layout(h, Lq);
+  L.dense = dense_layout(h, Lq, Lk);
   L.wx_off = 0;
   L.kv_off = round_up((size_t)c.n_heads * (c.d_nope + c.d_v) * c.d_c * 2, kAlign);
   L.base = L.kv_off + round_up((size_t)c.batch * c.window_frames * tokens_per_frame(c) * 2 *
@@ -442,8 +443,17 @@ int64_t mla_cache_slot(const mla_cache* h, int64_t frame, int32_t tau) {
 size_t mla_attend_workspace_bytes(const mla_cache* h, int32_t Lq, int32_t key_splits) {
   if (h == nullptr || h->dense || Lq <= 0 || key_splits < 0) return 0;
   if (h->cfg.dtype == MLA_F32) return 0;
-  if (attend_path_for(h, Lq, key_splits) == MLA_PATH_EXPAND) return expand_layout(h, Lq).total;
-  return latent_layout(h, Lq, key_splits).total;
+  // The largest workspace over every number of resident frames (the
+  // schedule, hence the count of key-range partials, depends on it), so a
+  // buffer sized once serves the window as it fills and slides.
+  const bool expand = attend_path_for(h, Lq, key_splits) == MLA_PATH_EXPAND;
+  const int64_t T = tokens_per_frame(h->cfg);
+  size_t need = 0;
+  for (int64_t f = 1; f <= h->cfg.window_frames; ++f) {
+    const size_t t = expand ? expand_layout(h, Lq, f * T).total : latent_layout(h, Lq, key_splits, f * T).total;
+    need = t > need ? t : need;
+  }
+  return need;
 }
 
 int32_t mla_attend_path(const mla_cache* h, int32_t Lq, int32_t key_splits) {
@@ -563,7 +573,14 @@ mla_status mla_attend(mla_cache* h, const void* q, int64_t q_token0, int32_t Lq,
 size_t mha_attend_workspace_bytes(const mla_cache* h, int32_t Lq) {
   if (h == nullptr || !h->dense || Lq <= 0) return 0;
   if (h->cfg.dtype == MLA_F32) return 0;
-  return dense_layout(h, Lq).total;
+  // largest over every number of resident frames (see mla_attend_workspace_bytes)
+  const int64_t T = tokens_per_frame(h->cfg);
+  size_t need = 0;
+  for (int64_t f = 1; f <= h->cfg.window_frames; ++f) {
+    const size_t t = dense_layout(h, Lq, f * T).total;
+    need = t > need ? t : need;
+  }
+  return need;
 }
 
 mla_status mha_attend(mla_cache* h, const void* q, int64_t q_token0, int32_t Lq, float* out,

@@ -281,7 +281,7 @@ def test_attend_arguments_and_workspace(sim):
     assert need >= R * 224 * 2 + R * 192 * 4 + R * 8
     ws = 1 << 40
     assert sim.mla_attend(h, P(FAKE_PTR), 21 * 1560, 4680, P(FAKE_PTR), P(FAKE_PTR), P(FAKE_PTR),
-                          0, P(ws), need - 1, None) == 7
+                          0, P(ws), 256, None) == 7
     assert sim.mla_attend(h, P(FAKE_PTR), 21 * 1560, 4680, P(FAKE_PTR), P(FAKE_PTR), P(FAKE_PTR),
                           0, P(ws + 64), need, None) == 7                      # misaligned
     assert sim.mla_attend(h, P(FAKE_PTR), 21 * 1560, 4680, P(FAKE_PTR), P(FAKE_PTR), P(FAKE_PTR),
@@ -382,7 +382,7 @@ def test_expand_attend_arguments_and_workspace(sim):
         R = 12 * lq_pad
         assert need >= wx + kv + R * 128 * 2 + R * 128 * 4 + R * 8
         assert sim.mla_attend(h, P(FAKE_PTR), 0, Lq, P(FAKE_PTR), P(FAKE_PTR), P(FAKE_PTR), 0,
-                              P(ws), need - 1, None) == 7
+                              P(ws), 256, None) == 7
         n = sim.fake_count()
         assert sim.mla_attend(h, P(FAKE_PTR), 77, Lq, P(FAKE_PTR + 256), P(FAKE_PTR + 512),
                               P(FAKE_PTR + 768), 0, P(ws), need, None) == 0
@@ -422,6 +422,43 @@ def test_expand_attend_arguments_and_workspace(sim):
     assert sim.fake_count() == n + 1 and sim.fake_kind() == 7
 
 
+@pytest.mark.parametrize("path,dense", [(1, False), (2, False), (0, True)])
+def test_workspace_sized_once_serves_every_window_state(sim, path, dense):
+    """The workspace size does not depend on how many frames are resident: a
+    buffer of that size is accepted as the window fills, slides and wraps,
+    and is the largest any state needs (a smaller one fails in some state)."""
+    c = _cfg()
+    st, h = _create(sim, c, dense=dense)
+    assert st == 0
+    if not dense:
+        assert sim.mla_cache_set_attend_path(h, path) == 0
+    ws = 1 << 40
+    for Lq in (1, 100, 1024, 4680):
+        sizes = set()
+        ok_all = True
+        for oldest, newest in ((0, 0), (0, 2), (0, 10), (0, 20), (5, 25), (30, 33)):
+            assert sim.mla_cache_set_state(h, oldest, newest) == 0
+            need = (sim.mha_attend_workspace_bytes(h, Lq) if dense
+                    else sim.mla_attend_workspace_bytes(h, Lq, 0))
+            sizes.add(need)
+            if dense:
+                ok_all &= sim.mha_attend(h, P(FAKE_PTR), 0, Lq, P(FAKE_PTR), P(ws), need, None) == 0
+            else:
+                ok_all &= sim.mla_attend(h, P(FAKE_PTR), 0, Lq, P(FAKE_PTR), P(FAKE_PTR),
+                                         P(FAKE_PTR), 0, P(ws), need, None) == 0
+        assert len(sizes) == 1 and ok_all, (Lq, sizes)
+        need = sizes.pop()
+        too_small = []
+        for f in range(1, 22):
+            assert sim.mla_cache_set_state(h, 0, f - 1) == 0
+            if dense:
+                too_small.append(sim.mha_attend(h, P(FAKE_PTR), 0, Lq, P(FAKE_PTR), P(ws), need - 1, None))
+            else:
+                too_small.append(sim.mla_attend(h, P(FAKE_PTR), 0, Lq, P(FAKE_PTR), P(FAKE_PTR),
+                                                P(FAKE_PTR), 0, P(ws), need - 1, None))
+        assert 7 in too_small, (Lq, too_small)
+
+
 def test_dense_attend_schedule(sim):
     c = _cfg()
     st, h = _create(sim, c, dense=True)
@@ -433,7 +470,7 @@ def test_dense_attend_schedule(sim):
         lq_pad = -(-Lq // shape[0]) * shape[0]
         R = 12 * lq_pad
         assert need >= R * 128 * 2 + R * 128 * 4 + R * 8
-        assert sim.mha_attend(h, P(FAKE_PTR), 0, Lq, P(FAKE_PTR), P(ws), need - 1, None) == 7
+        assert sim.mha_attend(h, P(FAKE_PTR), 0, Lq, P(FAKE_PTR), P(ws), 256, None) == 7
         assert sim.mha_attend(h, P(FAKE_PTR), 21 * 1560, Lq, P(FAKE_PTR), P(ws), need, None) == 0
         a = _mha_info(sim)
         assert (a["block_rows"], a["key_tile"], a["stages"]) == shape

@@ -382,3 +382,63 @@ def test_dense_mha_window_sampled():
     rows = sample_rows(cfg.Lq, 32)
     got, ref = run.attend(q, cfg.chunk_frame0 * cfg.T, rows=rows)
     assert_parity(got, ref, "bf16", "dense 21-frame window sampled")
+
+
+def test_dense_mha_ring_wrap():
+    """Dense cache through a ring wrap: 6-frame window, frames 2..7 resident
+    (frames 6 and 7 in slots 0 and 1), 390 keys (a ragged last 64-key tile)."""
+    cfg = wan_small()
+    run = DenseRun(cfg)
+    run.write(0, 6)
+    run.evict(2)
+    run.write(6, 2)
+    q = chunk_q(cfg, 2 * cfg.T, chunk=11)
+    got, ref = run.attend(q, 6 * cfg.T)
+    assert_parity(got, ref, "bf16", "dense ring wrap")
+
+
+# ---------------------------------------------------------------------------
+# expand-then-attend: path choice, batches, workspace reuse
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("Lq", [511, 512])
+def test_auto_path_threshold_batch3_wrap(Lq):
+    """Three sequences through a ring wrap; 511 queries take the absorbed path
+    and 512 the expand path on automatic, both against the oracle."""
+    cfg = mid_cfg(d_nope=96, d_rope=32, d_v=128, d_c=128, n_heads=6, batch=3)
+    run = LatentRun(cfg)
+    run.write(0, 4)
+    run.evict(2)
+    run.write(4, 2)
+    run.evict(1)
+    run.write(6, 2)       # frames 3..7 resident through a wrap, Lk = 300
+    assert run.gpu.attend_path(Lq) == ("expand" if Lq >= 512 else "absorbed")
+    q = run.query(Lq)
+    rows = sample_rows(Lq, 64)
+    got, ref, _ = run.attend(q, 8 * cfg.T, rows=rows)
+    assert_parity(got, ref, "bf16", f"auto path Lq={Lq} B=3")
+
+
+def test_expand_workspace_reused_as_window_fills():
+    """One workspace, sized once, serves the expand path while the window
+    fills, is full, and wraps; every call is checked against the oracle."""
+    from rank_latent_kv_absorbed_amd import LatentCache  # noqa: F401
+    cfg = wan_small(batch=1)
+    run = LatentRun(cfg, path="expand")
+    Lq = cfg.T
+    ws = None
+    frame = 0
+    for n_new, n_ev in ((2, 0), (3, 0), (1, 0), (2, 2), (3, 3)):
+        run.evict(n_ev)
+        run.write(frame, n_new)
+        frame += n_new
+        need = run.gpu.workspace_bytes(Lq)
+        if ws is None:
+            ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        assert need == ws.numel()      # sized for the full window from the start
+        q = run.query(Lq, chunk=frame)
+        out = run.gpu.attend(dev(q), frame * cfg.T - Lq, run.wd["w_uk"], run.wd["w_uv"], workspace=ws)
+        torch.cuda.synchronize()
+        ref = O.attend(run.store, run.ring, q.double().numpy(), frame * cfg.T - Lq,
+                       run.w["w_uk"].double().numpy(), run.w["w_uv"].double().numpy(), cfg)
+        assert_parity(out.cpu().numpy(), ref, "bf16", f"expand, {run.ring.n_resident} frames resident")
