@@ -145,6 +145,9 @@ def main():
                     help="attention path of every layer's handle (auto: the library's choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip dense and small-query cases")
+    ap.add_argument("--rollout", action="store_true",
+                    help="full rollout sweep: latent widths 64/128/192 x batch 1/4/8/11 (default "
+                         "extras run latent width 192 at batch 1 only)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device-to-device copy of this size first (a known-byte "
                          "kernel for scaling hardware traffic counters)")
@@ -436,6 +439,52 @@ def main():
                                                                     / (PEAK_BF16_TFLOPS * 1e12), 2)}
             del bcs, bws, bout, bq, bxc, bw
         result["batch_scaling"] = scale
+
+        # rollout: 80 chunks of 3 frames through every layer's 21-frame window
+        # (evict to make room, write the chunk, attend its 4680 queries), the
+        # whole loop bracketed by events; the window grows over the first 7
+        # chunks, so the keys per attend average 1617 / 80 frames
+        def rollout(d_c, Bb, n_chunks=80):
+            rcfg = cfg.with_(batch=Bb, d_c=d_c)
+            rw = [{k: v.to(dev) for k, v in layer_weights(rcfg, layer=l).items()} for l in range(L)]
+            rx = torch.randn((Bb, Lq, cfg.hidden), generator=gen, device=dev).to(torch.bfloat16)
+            rq = torch.randn((Bb, Lq, cfg.n_heads, cfg.d_qk), generator=gen, device=dev).to(torch.bfloat16)
+            rcs = [LatentCache(rcfg, device=dev) for _ in range(L)]
+            for c in rcs:
+                c.set_attend_path(args.path)
+            rout = torch.empty((Bb, Lq, cfg.n_heads, cfg.d_v), dtype=torch.float32, device=dev)
+            rws = torch.empty(max(rcs[0].workspace_bytes(Lq), 1), dtype=torch.uint8, device=dev)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for k in range(n_chunks):
+                for l in range(L):
+                    c = rcs[l]
+                    res = 0 if k == 0 else min(3 * k, W)
+                    c.evict(max(0, res + cfg.chunk_frames - W))
+                    c.write(rx, rw[l]["w_dkr"], 3 * k, cfg.chunk_frames)
+                    c.attend(rq, 3 * k * T, rw[l]["w_uk"], rw[l]["w_uv"], out=rout, workspace=rws)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            frames = sum(min(3 * (k + 1), W) for k in range(n_chunks))
+            flop = L * (sum(attend_flops(cfg.n_heads, Lq, min(3 * (k + 1), W) * T, d_c, cfg.d_rope,
+                                         cfg.d_nope, cfg.d_v, Bb) for k in range(n_chunks))
+                        + n_chunks * 2 * Bb * Lq * cfg.hidden * (d_c + cfg.d_rope))
+            out = {"ms_total": round(ms, 2), "chunks": n_chunks, "layers": L,
+                   "resident_frames_summed": frames,
+                   "query_tokens_per_s_per_layer": round(Bb * Lq * n_chunks * L / (ms / 1e3), 1),
+                   "mfma_util_pct_absorbed_form": round(100.0 * flop / (ms / 1e3) / (PEAK_BF16_TFLOPS * 1e12), 2)}
+            del rcs, rws, rout, rw, rx, rq
+            return out
+
+        sweep = [(d, b_) for d in (192, 128, 64) for b_ in (1, 4, 8, 11)] if args.rollout else [(192, 1)]
+        result["rollout"] = {}
+        for d, b_ in sweep:
+            result["rollout"][f"dc{d}_B{b_}"] = rollout(d, b_)
+            print(f"rollout d_c={d} B={b_}: {result['rollout'][f'dc{d}_B{b_}']}", file=sys.stderr,
+                  flush=True)
 
     ev.close()
     if not args.no_cpu_baseline:

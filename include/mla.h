@@ -192,10 +192,13 @@ mla_status mla_attend(mla_cache* cache, const void* q, int64_t q_token0, int32_t
  *   of the whole window rebuilt once per call into the workspace, then plain
  *   per-head attention over them (method item 2 taken literally: the per-head
  *   keys and values are reconstructed from the latent on demand).  Needs fewer
- *   products per query than the absorbed form; the rebuild is a fixed cost per
- *   call, paid back from a few hundred queries on.
- * MLA_PATH_AUTO: the library picks by chunk length (expand from 512 queries,
- *   when the handle supports it and key_splits is 0).  Both paths compute the
+ *   products per query than the absorbed form when d_c is large; the rebuild
+ *   is a fixed cost per call, paid back from a few hundred queries on.
+ * MLA_PATH_AUTO: the library picks: expand from 512 queries when the handle
+ *   supports it, key_splits is 0 and the latent products per (query, key,
+ *   head), 2 (d_c + d_rope) + 2 d_c, are at least 1.5 times the per-head ones,
+ *   2 (d_nope + d_rope) + 2 d_v (d_c = 192 for the Wan head shape; not 128 or
+ *   64, where the latent form is as fast or faster).  Both paths compute the
  * same function; they differ in rounding (the expanded keys and values are
  * rounded to the cache's element type). */
 typedef enum { MLA_PATH_AUTO = 0, MLA_PATH_ABSORBED = 1, MLA_PATH_EXPAND = 2 } mla_attend_path_kind;

@@ -182,6 +182,9 @@ __global__ __launch_bounds__(64) void epilogue_bf16_kernel(AttendArgs a) {
 // (column chunk c, slot lane j) sums the partials j, j + LANES, ... of four
 // columns; the lanes are added through LDS, normalised, and the W^V_up,h
 // product runs in plain fp32 with one output dimension per thread.
+// Above this many partial slots per row group the per-row epilogue is used.
+constexpr int kLaneMergeMaxSlots = 4;
+
 template <int DC>
 __global__ __launch_bounds__(256) void epilogue_rows_kernel(AttendArgs a) {
   constexpr int C4 = DC / 4;       // 4-column chunks of a partial row
@@ -400,7 +403,10 @@ hipError_t launch_dc(const AttendArgs& a, hipStream_t s) {
       if (e != hipSuccess) return e;
     }
   }
-  if (a.sched.block_rows < kCoreMaxBlockRows) {
+  // Rows with many key-range partials each (narrow blocks, or few row groups
+  // spread over the whole device) merge one row per block; otherwise one lane
+  // per row, whose merge walks the partials one after another.
+  if (a.sched.block_rows < kCoreMaxBlockRows || a.sched.n_slots > kLaneMergeMaxSlots) {
     hipLaunchKernelGGL(epilogue_rows_kernel<DC>, dim3((unsigned)(a.Lq * a.n_h), (unsigned)a.B),
                        dim3(256), 0, s, a);
     return hipGetLastError();

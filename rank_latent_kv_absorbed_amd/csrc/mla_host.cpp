@@ -236,13 +236,19 @@ ExpandLayout expand_layout(const mla_cache* h, int32_t Lq, int64_t Lk = -1) {
   return L;
 }
 
-// Queries of at least this many tokens take the expand-then-attend path when
-// the handle is left on automatic.  The rebuild of the window is a fixed cost
-// per call; the per-head products it enables need 1.6x fewer flops per query
-// than the latent ones for the Wan head shape.  Measured on the 21-frame
-// window (32760 keys, 12 heads, d_c 192) the whole call breaks even between
-// 256 and 512 queries and is 11% faster at 1024, 18% at 4680.
+// On automatic, a chunk takes the expand-then-attend path when it has at
+// least kExpandMinQueries queries and the latent form's products per (query,
+// key, head), 2 (d_c + d_rope) + 2 d_c, are at least kExpandFlopRatio times the
+// per-head ones, 2 (d_nope + d_rope) + 2 d_v.  The rebuild of the window is a
+// fixed cost per call, and the latent core does more work per cycle than the
+// per-head one, so the expansion pays only when it saves enough products.
+// Measured on the 21-frame window (32760 keys, 12 heads) for whole calls:
+// d_c 192 (832 vs 512 FLOP): absorbed faster at 256 queries (0.14 vs 0.16 ms),
+// expand faster from 1024 (0.32 vs 0.44 ms) up to 4680 (1.18 vs 1.47 ms);
+// d_c 128 (576 vs 512): even or absorbed faster at every chunk length;
+// d_c 64: absorbed faster throughout.
 constexpr int32_t kExpandMinQueries = 512;
+constexpr double kExpandFlopRatio = 1.5;
 
 // The expansion serves 16-bit handles of the dense core's head width whose
 // expanded full window (every key, every head) keeps one sequence's offsets
@@ -260,7 +266,10 @@ int32_t attend_path_for(const mla_cache* h, int32_t Lq, int32_t key_splits) {
   const mla_layer_config& c = h->cfg;
   if (!expand_possible(h) || key_splits > 0 || h->attend_path == MLA_PATH_ABSORBED) return MLA_PATH_ABSORBED;
   if (h->attend_path == MLA_PATH_EXPAND) return MLA_PATH_EXPAND;
-  return Lq >= kExpandMinQueries ? MLA_PATH_EXPAND : MLA_PATH_ABSORBED;
+  const double latent = 2.0 * (c.d_c + c.d_rope) + 2.0 * c.d_c;
+  const double per_head = 2.0 * (c.d_nope + c.d_rope) + 2.0 * c.d_v;
+  return Lq >= kExpandMinQueries && latent >= kExpandFlopRatio * per_head ? MLA_PATH_EXPAND
+                                                                          : MLA_PATH_ABSORBED;
 }
 
 // Rotation table of the expanded queries: the d_nope content dimensions stay

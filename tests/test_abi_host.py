@@ -357,6 +357,12 @@ def test_attend_path_choice(sim):
         assert sim.mla_attend_path(g, 4680, 0) == 1, kw
     st, g = _create(sim, _cfg(window_frames=448))
     assert sim.mla_cache_set_attend_path(g, 2) == 0
+    # narrower latents: the latent form needs few enough products to stay on
+    # automatic (2 (d_c + 32) + 2 d_c < 1.5 * 512), yet the expansion can be chosen
+    for d_c in (64, 128):
+        st, g = _create(sim, _cfg(d_c=d_c))
+        assert st == 0 and sim.mla_attend_path(g, 4680, 0) == 1, d_c
+        assert sim.mla_cache_set_attend_path(g, 2) == 0 and sim.mla_attend_path(g, 4680, 0) == 2
     st, d = _create(sim, c, dense=True)
     assert sim.mla_cache_set_attend_path(d, 1) == 9 and sim.mla_attend_path(d, 16, 0) == -1
 

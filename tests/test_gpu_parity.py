@@ -405,7 +405,7 @@ def test_dense_mha_ring_wrap():
 def test_auto_path_threshold_batch3_wrap(Lq):
     """Three sequences through a ring wrap; 511 queries take the absorbed path
     and 512 the expand path on automatic, both against the oracle."""
-    cfg = mid_cfg(d_nope=96, d_rope=32, d_v=128, d_c=128, n_heads=6, batch=3)
+    cfg = mid_cfg(d_nope=96, d_rope=32, d_v=128, d_c=192, n_heads=6, batch=3)
     run = LatentRun(cfg)
     run.write(0, 4)
     run.evict(2)
