@@ -309,6 +309,27 @@ def main():
             for c in caches:
                 c.set_attend_path(args.path)
 
+        # several attends per written chunk (denoising steps): with reuse on, the
+        # expand path rebuilds the window once per chunk
+        if path == "expand":
+            c = caches[0]
+            reuse = {}
+            for flag in (False, True):
+                c.set_expand_reuse(flag)
+                for _ in range(3):
+                    c.attend(q, newest[0] * T, weights[0]["w_uk"], weights[0]["w_uv"], out=out, workspace=ws)
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                e0.record()
+                for _ in range(10):
+                    c.attend(q, newest[0] * T, weights[0]["w_uk"], weights[0]["w_uv"], out=out, workspace=ws)
+                e1.record()
+                torch.cuda.synchronize()
+                reuse["reuse_on" if flag else "reuse_off"] = round(e0.elapsed_time(e1) / 10, 4)
+            c.set_expand_reuse(False)
+            result["attend_ms_repeated_on_one_window"] = reuse
+
         # dense per-head MHA on the same shape (one layer), for time and cache bytes
         dcache = DenseCache(cfg, device=dev)
         dw = {k: v.to(dev) for k, v in dense_weights(cfg).items()}

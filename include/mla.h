@@ -209,6 +209,19 @@ typedef enum { MLA_PATH_AUTO = 0, MLA_PATH_ABSORBED = 1, MLA_PATH_EXPAND = 2 } m
  * d_nope a multiple of 32; MLA_ERR_WRONG_KIND on a dense handle. */
 mla_status mla_cache_set_attend_path(mla_cache* cache, int32_t path);
 
+/* Reuse of the expanded window across attends (enable = 1; 0 switches it off;
+ * either call forgets the last expansion).  With reuse on, an expand-path
+ * mla_attend skips rebuilding the per-head keys and values when the previous
+ * expand-path attend on this handle used the same workspace pointer and the
+ * same w_uk / w_uv pointers and no write, eviction or state change happened
+ * since: several attends on one window state (denoising steps of a chunk,
+ * several query chunks) then pay the rebuild once.  The caller guarantees
+ * that it did not modify that workspace, the weights or the ring storage
+ * outside this library in between, and orders the calls on one stream (or
+ * synchronises between streams).  Off by default.  MLA_ERR_WRONG_KIND on a
+ * dense handle. */
+mla_status mla_cache_set_expand_reuse(mla_cache* cache, int32_t enable);
+
 /* The path mla_attend takes for Lq queries and `key_splits` (MLA_PATH_ABSORBED
  * or MLA_PATH_EXPAND; -1 for bad arguments).  key_splits > 0 and fp32 handles
  * always take the absorbed path. */

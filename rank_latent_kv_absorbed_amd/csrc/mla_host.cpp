@@ -25,6 +25,16 @@ struct mla_cache {
   hipEvent_t prof_start;
   hipEvent_t prof_stop;
   int32_t attend_path;  // mla_attend_path: auto, absorbed or expand
+  // Window generation: bumped by every write, eviction and state change.
+  uint64_t gen;
+  // mla_cache_set_expand_reuse: the last expansion (workspace, weights,
+  // generation) may serve later expand-path attends while nothing changed.
+  int32_t expand_reuse;
+  bool ex_valid;
+  const void* ex_ws;
+  const void* ex_wuk;
+  const void* ex_wuv;
+  uint64_t ex_gen;
 };
 
 namespace {
@@ -112,6 +122,7 @@ mla_status check_write(const mla_cache* h, int64_t frame0, int32_t n_frames) {
 void commit_write(mla_cache* h, int64_t frame0, int32_t n_frames) {
   if (n_resident(h) <= 0) h->oldest = frame0;
   h->newest = frame0 + n_frames - 1;
+  ++h->gen;
 }
 
 // Schedule of the attention core (see mla::Schedule) for core shape `sh`
@@ -311,6 +322,11 @@ mla_status create(const mla_layer_config* cfg, void* storage, size_t storage_byt
   h->prof_start = nullptr;
   h->prof_stop = nullptr;
   h->attend_path = MLA_PATH_AUTO;
+  h->gen = 0;
+  h->expand_reuse = 0;
+  h->ex_valid = false;
+  h->ex_ws = h->ex_wuk = h->ex_wuv = nullptr;
+  h->ex_gen = 0;
   *out = h;
   return MLA_OK;
 }
@@ -423,6 +439,7 @@ mla_status mla_cache_evict(mla_cache* h, int32_t n_frames) {
   if (h == nullptr) return MLA_ERR_INVALID_ARG;
   if (n_frames < 0 || n_frames > n_resident(h)) return MLA_ERR_EVICT_RANGE;
   h->oldest += n_frames;
+  ++h->gen;
   return MLA_OK;
 }
 
@@ -441,6 +458,7 @@ mla_status mla_cache_set_state(mla_cache* h, int64_t oldest, int64_t newest) {
     return MLA_ERR_INVALID_ARG;
   h->oldest = oldest;
   h->newest = newest;
+  ++h->gen;
   return MLA_OK;
 }
 
@@ -463,6 +481,14 @@ size_t mla_attend_workspace_bytes(const mla_cache* h, int32_t Lq, int32_t key_sp
     need = t > need ? t : need;
   }
   return need;
+}
+
+mla_status mla_cache_set_expand_reuse(mla_cache* h, int32_t enable) {
+  if (h == nullptr || (enable != 0 && enable != 1)) return MLA_ERR_INVALID_ARG;
+  if (h->dense) return MLA_ERR_WRONG_KIND;
+  h->expand_reuse = enable;
+  h->ex_valid = false;
+  return MLA_OK;
 }
 
 int32_t mla_attend_path(const mla_cache* h, int32_t Lq, int32_t key_splits) {
@@ -562,12 +588,26 @@ mla_status mla_attend(mla_cache* h, const void* q, int64_t q_token0, int32_t Lq,
     m.ev_start = h->prof_start;
     m.ev_stop = h->prof_stop;
     m.rope = expand_rope(c);
-    const hipError_t err = mla::launch_expand_kv(e, s);
-    if (err != hipSuccess) return MLA_ERR_HIP;
+    // The rebuilt window in this workspace is still current when reuse is on
+    // and neither the window, the weights nor the workspace changed since it
+    // was written (several attends per chunk, e.g. denoising steps).
+    const bool reuse = h->expand_reuse && h->ex_valid && h->ex_ws == workspace &&
+                       h->ex_wuk == w_uk && h->ex_wuv == w_uv && h->ex_gen == h->gen;
+    if (!reuse) {
+      h->ex_valid = false;
+      const hipError_t err = mla::launch_expand_kv(e, s);
+      if (err != hipSuccess) return MLA_ERR_HIP;
+      h->ex_valid = true;
+      h->ex_ws = workspace;
+      h->ex_wuk = w_uk;
+      h->ex_wuv = w_uv;
+      h->ex_gen = h->gen;
+    }
     return launch_status(mla::launch_mha_attend_bf16_ws(m, (float*)(ws + X.base + X.dense.opart_off),
                                                         (float*)(ws + X.base + X.dense.ml_off),
                                                         X.dense.sched, s));
   }
+  h->ex_valid = false;  // the absorbed path overwrites the workspace
   const LatentLayout L = latent_layout(h, Lq, key_splits);
   if (workspace == nullptr || ((uintptr_t)workspace % kAlign) != 0 || workspace_bytes < L.total)
     return MLA_ERR_WORKSPACE;

@@ -76,6 +76,7 @@ SIGNATURES = {
     "mla_cache_set_profile_events": (_I32, [_HANDLE, _VP, _VP]),
     "mla_cache_set_attend_path": (_I32, [_HANDLE, _I32]),
     "mla_attend_path": (_I32, [_HANDLE, _I32, _I32]),
+    "mla_cache_set_expand_reuse": (_I32, [_HANDLE, _I32]),
     "mla_status_str": (ctypes.c_char_p, [_I32]),
     "mla_version": (ctypes.c_char_p, []),
 }
@@ -243,6 +244,11 @@ class LatentCache(_CacheBase):
     def set_attend_path(self, path):
         """'auto', 'absorbed' or 'expand' (see ATTEND_PATHS)."""
         _check(lib().mla_cache_set_attend_path(self._h, ATTEND_PATHS[path]), "set_attend_path")
+
+    def set_expand_reuse(self, enable=True):
+        """Let expand-path attends reuse the rebuilt window while it is unchanged
+        (same workspace and weights; see mla_cache_set_expand_reuse)."""
+        _check(lib().mla_cache_set_expand_reuse(self._h, 1 if enable else 0), "set_expand_reuse")
 
     def attend_path(self, Lq, key_splits=0):
         """Name of the path an attend of Lq queries takes on this handle."""

@@ -465,6 +465,42 @@ def test_workspace_sized_once_serves_every_window_state(sim, path, dense):
         assert 7 in too_small, (Lq, too_small)
 
 
+def test_expand_reuse_skips_rebuild_only_while_unchanged(sim):
+    """With reuse on, a second expand-path attend on the same window state,
+    workspace and weights launches no rebuild; a write, an eviction, a state
+    change, another workspace, other weights, an absorbed attend in between
+    or switching reuse off again bring the rebuild back."""
+    c = _cfg()
+    st, h = _create(sim, c)
+    assert sim.mla_cache_set_state(h, 0, 17) == 0 and sim.mla_cache_set_attend_path(h, 2) == 0
+    ws, ws2 = 1 << 40, (1 << 40) + (1 << 36)
+    wuk, wuv = FAKE_PTR + 256, FAKE_PTR + 512
+
+    def attend(w=ws, uk=wuk, uv=wuv, Lq=4680):
+        n = sim.fake_count()
+        assert sim.mla_attend(h, P(FAKE_PTR), 0, Lq, P(uk), P(uv), P(FAKE_PTR), 0, P(w), 1 << 40,
+                              None) == 0
+        return sim.fake_count() - n      # 2 with a rebuild, 1 without
+
+    assert attend() == 2 and attend() == 2          # reuse off by default
+    assert sim.mla_cache_set_expand_reuse(h, 1) == 0
+    assert attend() == 2 and attend() == 1 and attend(Lq=1000) == 1
+    assert sim.mla_cache_write(h, P(FAKE_PTR), P(FAKE_PTR), 18, 3, None) == 0
+    assert attend() == 2 and attend() == 1
+    assert sim.mla_cache_evict(h, 3) == 0
+    assert attend() == 2 and attend() == 1
+    assert sim.mla_cache_set_state(h, 3, 20) == 0
+    assert attend() == 2 and attend() == 1
+    assert attend(w=ws2) == 2 and attend(w=ws) == 2 and attend() == 1
+    assert attend(uk=wuk + 256) == 2 and attend() == 2
+    assert sim.mla_cache_set_attend_path(h, 1) == 0 and attend() == 1   # one absorbed launch
+    assert sim.mla_cache_set_attend_path(h, 2) == 0 and attend() == 2 and attend() == 1
+    assert sim.mla_cache_set_expand_reuse(h, 0) == 0 and attend() == 2 and attend() == 2
+    assert sim.mla_cache_set_expand_reuse(h, 2) == 1
+    st, d = _create(sim, c, dense=True)
+    assert sim.mla_cache_set_expand_reuse(d, 1) == 9
+
+
 def test_dense_attend_schedule(sim):
     c = _cfg()
     st, h = _create(sim, c, dense=True)

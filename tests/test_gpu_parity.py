@@ -442,3 +442,28 @@ def test_expand_workspace_reused_as_window_fills():
         ref = O.attend(run.store, run.ring, q.double().numpy(), frame * cfg.T - Lq,
                        run.w["w_uk"].double().numpy(), run.w["w_uv"].double().numpy(), cfg)
         assert_parity(out.cpu().numpy(), ref, "bf16", f"expand, {run.ring.n_resident} frames resident")
+
+
+def test_expand_reuse_across_attends_and_after_write():
+    """Reuse of the rebuilt window: three attends with different queries on
+    one window state (one rebuild), then a new chunk is written and the next
+    attend must see it; every result against the oracle."""
+    cfg = wan_small(batch=2)
+    run = LatentRun(cfg, path="expand")
+    run.gpu.set_expand_reuse(True)
+    run.write(0, 4)
+    Lq = cfg.T
+    ws = torch.empty(run.gpu.workspace_bytes(Lq), dtype=torch.uint8, device="cuda")
+    for step, (frame0, n_new, n_ev) in enumerate(((None, 0, 0), (None, 0, 0), (None, 0, 0),
+                                                  (4, 2, 1), (None, 0, 0))):
+        if frame0 is not None:
+            run.evict(n_ev)
+            run.write(frame0, n_new)
+        newest = run.ring.newest
+        q = run.query(Lq, chunk=50 + step)
+        out = run.gpu.attend(dev(q), (newest + 1) * cfg.T - Lq, run.wd["w_uk"], run.wd["w_uv"],
+                             workspace=ws)
+        torch.cuda.synchronize()
+        ref = O.attend(run.store, run.ring, q.double().numpy(), (newest + 1) * cfg.T - Lq,
+                       run.w["w_uk"].double().numpy(), run.w["w_uv"].double().numpy(), cfg)
+        assert_parity(out.cpu().numpy(), ref, "bf16", f"expand reuse, call {step}")
