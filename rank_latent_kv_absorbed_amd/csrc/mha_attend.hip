@@ -184,15 +184,16 @@ hipError_t launch_mha_typed(const MhaAttendArgs& a, float* opart, float* ml, con
     }
     const dim3 grid((unsigned)sched.n_blocks);
     bool launched = false;
-#define MLA_SHAPE(NW, KT, NS)                                                                  \
-  if (!launched && br == 32 * NW && sched.key_tile == KT && sched.stages == NS) {             \
-    hipLaunchKernelGGL((attn_core_kernel<E, 128, 128, NW, KT, NS, false, 1, (NW == 8)>), grid, dim3(NW * 64), \
-                       0, s, c);                                                              \
+#define MLA_SHAPE(NW, KT, NS, ROWS)                                                            \
+  if (!launched && br == ROWS * NW && sched.key_tile == KT && sched.stages == NS) {           \
+    hipLaunchKernelGGL((attn_core_kernel<E, 128, 128, NW, KT, NS, false, 1, (NW == 8), ROWS>), \
+                       grid, dim3(NW * 64), 0, s, c);                                         \
     launched = true;                                                                          \
   }
-    MLA_SHAPE(8, 64, 3)
-    MLA_SHAPE(4, 32, 4)
-    MLA_SHAPE(1, 32, 2)
+    MLA_SHAPE(8, 64, 3, 32)
+    MLA_SHAPE(4, 32, 4, 32)
+    MLA_SHAPE(1, 32, 2, 32)
+    MLA_SHAPE(1, 32, 2, 16)
 #undef MLA_SHAPE
     if (!launched) return hipErrorInvalidValue;
     hipError_t e = hipGetLastError();

@@ -352,15 +352,16 @@ template <typename E, int DC>
 hipError_t launch_core(const AttnCore& c, hipStream_t s) {
   const Schedule& sc = c.sched;
   const dim3 grid((unsigned)sc.n_blocks);
-#define MLA_SHAPE(NW, KT, NS)                                                                   \
-  if (sc.block_rows == 32 * NW && sc.key_tile == KT && sc.stages == NS) {                      \
-    hipLaunchKernelGGL((attn_core_kernel<E, DC + 32, DC, NW, KT, NS, true, 1, (NW == 8)>), grid, dim3(NW * 64), \
-                       0, s, c);                                                               \
+#define MLA_SHAPE(NW, KT, NS, ROWS)                                                             \
+  if (sc.block_rows == ROWS * NW && sc.key_tile == KT && sc.stages == NS) {                    \
+    hipLaunchKernelGGL((attn_core_kernel<E, DC + 32, DC, NW, KT, NS, true, 1, (NW == 8), ROWS>), \
+                       grid, dim3(NW * 64), 0, s, c);                                          \
     return hipGetLastError();                                                                  \
   }
-  MLA_SHAPE(8, 64, 3)
-  MLA_SHAPE(4, 32, 4)
-  MLA_SHAPE(1, 32, 2)
+  MLA_SHAPE(8, 64, 3, 32)
+  MLA_SHAPE(4, 32, 4, 32)
+  MLA_SHAPE(1, 32, 2, 32)
+  MLA_SHAPE(1, 32, 2, 16)
 #undef MLA_SHAPE
   return hipErrorInvalidValue;
 }

@@ -91,6 +91,19 @@ __device__ __forceinline__ void global_to_lds16(const void* g, void* lds) {
 // turn its reference captures into loads through a stack frame.
 #define MLA_INLINE __attribute__((always_inline))
 
+// Accumulator fragment of one MFMA shape: 32x32 (16 values per lane) or
+// 16x16 (4 values per lane).
+template <int ROWS>
+struct AccOf;
+template <>
+struct AccOf<32> {
+  typedef f32x16 type;
+};
+template <>
+struct AccOf<16> {
+  typedef f32x4 type;
+};
+
 // Raise-the-max threshold of the lazy rescale (log2 units).
 constexpr float kRescaleThreshold = 8.0f;
 
@@ -137,14 +150,24 @@ __device__ __forceinline__ void lds_barrier() {
 // narrow blocks can share a compute unit; one wave per SIMD (the whole
 // register file, accumulators in AGPRs) when each wave owns RB > 1 row blocks.
 template <typename E, int DQK, int DV, int NW, int KT, int NS, bool SHARED_KV, int RB = 1,
-          bool PP = false>
+          bool PP = false, int ROWS = 32>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 2 : 1, RB == 1 ? 2 : 1)))
 void attn_core_kernel(AttnCore a) {
   typedef typename Elem<E>::v8 V8;
-  constexpr int NKS = DQK / 16;               // MFMA depth steps of the score product
-  constexpr int NDT = DV / 32;                // 32-wide tiles of the value product
-  constexpr int BR = NW * 32 * RB;            // rows per row group (32 * RB per wave)
-  constexpr int NKB = KT / 32;                // 32-key blocks per tile
+  // ROWS = 32: 32x32x16 MFMAs, a lane owns one row (MFMA column) with its two
+  // half-waves splitting the keys.  ROWS = 16: 16x16x32 MFMAs, a row is shared
+  // by the four 16-lane groups (lanes l, l ^ 16, l ^ 32, l ^ 48).
+  constexpr bool R16 = ROWS == 16;
+  typedef typename AccOf<ROWS>::type AccT;   // accumulator fragment
+  constexpr int AV = R16 ? 4 : 16;            // accumulator values per lane
+  constexpr int NKS = R16 ? DQK / 32 : DQK / 16;  // MFMA depth steps of the score product
+  constexpr int NDT = R16 ? DV / 16 : DV / 32;    // MFMA column tiles of the value product
+  constexpr int BR = NW * ROWS * RB;          // rows per row group (ROWS * RB per wave)
+  constexpr int NKB = KT / ROWS;              // MFMA key blocks per tile
+  constexpr int NPF = R16 ? 1 : 2 * NKB;      // probability operands per row block
+  static_assert(ROWS == 32 || (ROWS == 16 && NW == 1 && KT == 32 && RB == 1 && !PP &&
+                               DQK % 32 == 0 && DV % 16 == 0),
+                "16-row waves: one-wave blocks on 32-key tiles");
   constexpr int KCH = DQK / 8;                // 16-byte chunks of K per key
   constexpr int CPK = SHARED_KV ? KCH : KCH + DV / 8;  // chunks staged per key
   constexpr int KSTR = CPK * 8;               // LDS row stride (elements)
@@ -267,12 +290,21 @@ void attn_core_kernel(AttnCore a) {
   const int tr_sw0 = swz(tr_key), tr_sw1 = swz(tr_key + 8);
   const int tr_off0 = tr_h + 8 * (tr_c ^ (tr_sw0 & 3)), tr_off1 = tr_h + 8 * (tr_c ^ (tr_sw1 & 3));
   const int tr_dt0 = tr_sw0 >> 2, tr_dt1 = tr_sw1 >> 2;  // 0 for latent rows
+  // 16-row waves: lane (r16, g16) is MFMA row/column r16 of 16-lane group g16.
+  // Score reads: chunk 4 s + g16 of key kb * 16 + r16.  Transpose reads: the
+  // lane addresses key 4 g16 + t16 (+ 16 for the second key block) and the
+  // 8 bytes of columns 4 c16 .. + 4 of a 16-column tile, so that lane i of the
+  // group receives column i of keys 4 g16 .. 4 g16 + 3.
+  const int r16 = l & 15, g16 = l >> 4;
+  const int k_sw16 = swz(r16);
+  const int t16 = r16 >> 2, c16 = r16 & 3;
+  const int tsw16 = swz(4 * g16 + t16);
 
   // Per row block rb of the wave: query fragments, value sums, running max
   // and sum, the lane's row.  Each key fragment read from LDS feeds RB
   // products, so LDS traffic per product falls as 1 / RB.
   V8 qf[RB][NKS];
-  f32x16 o[RB][NDT];
+  AccT o[RB][NDT];
   float m[RB], lsum[RB];
   int row[RB];
 #pragma unroll
@@ -313,20 +345,20 @@ void attn_core_kernel(AttnCore a) {
   // New row-group segment: query fragments in (global loads, not waited on
   // here), running state reset.
   auto begin_segment = [&](int b, int rg) MLA_INLINE {
-    const int row0 = rg * BR + w * 32 * RB;  // rows of a wave never straddle a head
+    const int row0 = rg * BR + w * ROWS * RB;  // rows of a wave never straddle a head
     live = row0 < a.R && (row0 % a.rows_per_head) < a.valid_per_head;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      row[rb] = row0 + 32 * rb + lo;
+      row[rb] = row0 + ROWS * rb + (R16 ? r16 : lo);
       const int r = row[rb];
       const bool ok = r < a.R && (r % a.rows_per_head) < a.valid_per_head;
-      const E* src = (const E*)a.qrows + ((size_t)b * a.R + (ok ? r : 0)) * DQK + 8 * hi;
+      const E* src = (const E*)a.qrows + ((size_t)b * a.R + (ok ? r : 0)) * DQK + (R16 ? 8 * g16 : 8 * hi);
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) qf[rb][ks] = ok ? ld8<E>(src + 16 * ks) : zero8<E>();
+      for (int ks = 0; ks < NKS; ++ks) qf[rb][ks] = ok ? ld8<E>(src + (R16 ? 32 : 16) * ks) : zero8<E>();
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-        for (int q = 0; q < 16; ++q) o[rb][dt][q] = 0.0f;
+        for (int q = 0; q < AV; ++q) o[rb][dt][q] = 0.0f;
       m[rb] = -INFINITY;
       lsum[rb] = 0.0f;
     }
@@ -334,29 +366,45 @@ void attn_core_kernel(AttnCore a) {
 
   // The three phases of a step on one key tile, for this wave's rows.
   // Scores S^T = K Q^T of the tile in `cur`.
-  auto scores = [&](const E* cur, f32x16 (&sv)[RB][NKB]) MLA_INLINE {
+  auto scores = [&](const E* cur, AccT (&sv)[RB][NKB]) MLA_INLINE {
+    if constexpr (R16) {
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
+      for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
+        for (int r = 0; r < AV; ++r) sv[0][kb][r] = 0.0f;
+        const E* krow = cur + (kb * 16 + r16) * KSTR;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sv[rb][kb][r] = 0.0f;
-      const E* krow = cur + (kb * 32 + lo) * KSTR;
-      auto kptr = [&](int ks) MLA_INLINE {
-        return SHARED_KV ? krow + 32 * (ks >> 1) + ((ks & 1) ? k_off1 : k_off0)
-                         : krow + 8 * ((2 * ks + hi) ^ k_sw);
-      };
+        for (int ks = 0; ks < NKS; ++ks)
+          sv[0][kb] = Elem<E>::mfma16(ld8<E>(krow + 8 * ((4 * ks + g16) ^ k_sw16)), qf[0][ks], sv[0][kb]);
+      }
+    } else {
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const V8 kf = ld8<E>(kptr(ks));
+      for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) sv[rb][kb] = Elem<E>::mfma(kf, qf[rb][ks], sv[rb][kb]);
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sv[rb][kb][r] = 0.0f;
+        const E* krow = cur + (kb * 32 + lo) * KSTR;
+        auto kptr = [&](int ks) MLA_INLINE {
+          return SHARED_KV ? krow + 32 * (ks >> 1) + ((ks & 1) ? k_off1 : k_off0)
+                           : krow + 8 * ((2 * ks + hi) ^ k_sw);
+        };
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          const V8 kf = ld8<E>(kptr(ks));
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) sv[rb][kb] = Elem<E>::mfma(kf, qf[rb][ks], sv[rb][kb]);
+        }
       }
     }
   };
   // Online softmax of key tile kt: mask keys past the window, lazy rescale,
   // probabilities (in the cache type) into pf, running sums.
-  auto softmax = [&](int kt, f32x16 (&sv)[RB][NKB], V8 (&pf)[RB][NKB][2]) MLA_INLINE {
+  // Key of accumulator value r of key block kb held by this lane.
+  auto key_of = [&](int kb, int r) MLA_INLINE {
+    return R16 ? kb * 16 + 4 * g16 + r : kb * 32 + acc_row(r, hi);
+  };
+  auto softmax = [&](int kt, AccT (&sv)[RB][NKB], V8 (&pf)[RB][NPF]) MLA_INLINE {
     const int t0 = kt * KT;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -364,14 +412,15 @@ void attn_core_kernel(AttnCore a) {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (t0 + kb * 32 + acc_row(r, hi) >= a.Lk) sv[rb][kb][r] = -INFINITY;
+          for (int r = 0; r < AV; ++r)
+            if (t0 + key_of(kb, r) >= a.Lk) sv[rb][kb][r] = -INFINITY;
       }
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sv[rb][kb][r]);
+        for (int r = 0; r < AV; ++r) mx = fmaxf(mx, sv[rb][kb][r]);
+      if constexpr (R16) mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       // lazy rescale: raise the max only when a score passes it by > 2^8
       if (__ballot(mx > m[rb] + kRescaleThreshold)) {
@@ -382,58 +431,93 @@ void attn_core_kernel(AttnCore a) {
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) o[rb][dt][r] *= alpha;
+          for (int r = 0; r < AV; ++r) o[rb][dt][r] *= alpha;
       }
       float ps = 0.0f;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
+        for (int r = 0; r < AV; ++r) {
           const float p = exp2_fast(sv[rb][kb][r] - m[rb]);
           ps += p;
-          pf[rb][kb][r >> 3][r & 7] = Elem<E>::from(p);
+          // 16-row waves: value-product slot 8 g16 + 4 kb + r is key
+          // kb * 16 + 4 g16 + r, so the lane's own scores form its operand
+          if constexpr (R16)
+            pf[rb][0][4 * kb + r] = Elem<E>::from(p);
+          else
+            pf[rb][2 * kb + (r >> 3)][r & 7] = Elem<E>::from(p);
         }
       lsum[rb] += ps;
     }
   };
   // Value sums O^T += V^T P^T of the tile in `cur`.
-  auto values = [&](const E* cur, const V8 (&pf)[RB][NKB][2]) MLA_INLINE {
+  auto values = [&](const E* cur, const V8 (&pf)[RB][NPF]) MLA_INLINE {
+    if constexpr (R16) {
+      // slots 8 g16 .. + 3: keys 4 g16 + t (block 0); + 4 .. + 7: keys 16 + 4 g16 + t
+      const E* v0 = cur + (4 * g16 + t16) * KSTR + VOFF + 4 * (c16 & 1);
+      const E* v1 = v0 + 16 * KSTR;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const E* vrow = cur + (kb * 32 + 16 * st + tr_key) * KSTR + VOFF;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          const int d0 = SHARED_KV ? dt : (dt ^ tr_dt0), d1 = SHARED_KV ? dt : (dt ^ tr_dt1);
-          const i16x4 lo4 = lds_read_tr16(vrow + 32 * d0 + tr_off0);
-          const i16x4 hi4 = lds_read_tr16(vrow + 8 * KSTR + 32 * d1 + tr_off1);
-          const V8 va = __builtin_bit_cast(V8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) o[rb][dt] = Elem<E>::mfma(va, pf[rb][kb][st], o[rb][dt]);
-        }
+      for (int dt = 0; dt < NDT; ++dt) {
+        const int q = (2 * dt + (c16 >> 1)) ^ tsw16;
+        const i16x4 lo4 = lds_read_tr16(v0 + 8 * q);
+        const i16x4 hi4 = lds_read_tr16(v1 + 8 * q);
+        const V8 va = __builtin_bit_cast(V8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[0][dt] = Elem<E>::mfma16(va, pf[0][0], o[0][dt]);
       }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const E* vrow = cur + (kb * 32 + 16 * st + tr_key) * KSTR + VOFF;
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) {
+            const int d0 = SHARED_KV ? dt : (dt ^ tr_dt0), d1 = SHARED_KV ? dt : (dt ^ tr_dt1);
+            const i16x4 lo4 = lds_read_tr16(vrow + 32 * d0 + tr_off0);
+            const i16x4 hi4 = lds_read_tr16(vrow + 8 * KSTR + 32 * d1 + tr_off1);
+            const V8 va = __builtin_bit_cast(V8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) o[rb][dt] = Elem<E>::mfma(va, pf[rb][2 * kb + st], o[rb][dt]);
+          }
+        }
+    }
   };
   // Segment end: write this block's partial of the row group (slot si.slot)
   // of batch element b.
   auto write_partial = [&](const StepInfo& si, int b) MLA_INLINE {
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const float ltot = lsum[rb] + __shfl_xor(lsum[rb], 32);
-      if (row[rb] < a.R) {
-        const size_t prow = ((size_t)si.slot * a.B + b) * a.R + row[rb];
+    if constexpr (R16) {
+      // lane (r16, g16) holds columns 16 dt + 4 g16 .. + 4 of row r16
+      float ltot = lsum[0] + __shfl_xor(lsum[0], 16);
+      ltot += __shfl_xor(ltot, 32);
+      if (row[0] < a.R) {
+        const size_t prow = ((size_t)si.slot * a.B + b) * a.R + row[0];
         float* op = a.opart + prow * DV;
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-          for (int gg = 0; gg < 4; ++gg) {
-            f32x4 v = {o[rb][dt][4 * gg], o[rb][dt][4 * gg + 1], o[rb][dt][4 * gg + 2],
-                       o[rb][dt][4 * gg + 3]};
-            *reinterpret_cast<f32x4*>(op + dt * 32 + 8 * gg + 4 * hi) = v;
-          }
-        if (hi == 0) {
-          a.ml[prow * 2] = m[rb];
+        for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4*>(op + 16 * dt + 4 * g16) = o[0][dt];
+        if (g16 == 0) {
+          a.ml[prow * 2] = m[0];
           a.ml[prow * 2 + 1] = ltot;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const float ltot = lsum[rb] + __shfl_xor(lsum[rb], 32);
+        if (row[rb] < a.R) {
+          const size_t prow = ((size_t)si.slot * a.B + b) * a.R + row[rb];
+          float* op = a.opart + prow * DV;
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int gg = 0; gg < 4; ++gg) {
+              f32x4 v = {o[rb][dt][4 * gg], o[rb][dt][4 * gg + 1], o[rb][dt][4 * gg + 2],
+                         o[rb][dt][4 * gg + 3]};
+              *reinterpret_cast<f32x4*>(op + dt * 32 + 8 * gg + 4 * hi) = v;
+            }
+          if (hi == 0) {
+            a.ml[prow * 2] = m[rb];
+            a.ml[prow * 2 + 1] = ltot;
+          }
         }
       }
     }
@@ -486,9 +570,9 @@ void attn_core_kernel(AttnCore a) {
       const StepInfo si = wc.c.si;
       const int b = wc.b;
       step_begin(si, b, k, cur);
-      V8 pf[RB][NKB][2];
+      V8 pf[RB][NPF];
       if (live) {
-        f32x16 sv[RB][NKB];
+        AccT sv[RB][NKB];
         scores(cur, sv);
         softmax(si.kt, sv, pf);
       }
@@ -526,8 +610,8 @@ void attn_core_kernel(AttnCore a) {
     const int b = wc.b;
     step_begin(si, b, i, cur);
     if (live) {
-      f32x16 sv[RB][NKB];
-      V8 pf[RB][NKB][2];
+      AccT sv[RB][NKB];
+      V8 pf[RB][NPF];
       scores(cur, sv);
       softmax(si.kt, sv, pf);
       values(cur, pf);

@@ -28,6 +28,12 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// v_mfma_f32_16x16x32_{f16,bf16} (Elem<E>::mfma16), lane l holds
+//   A[m = l % 16][k = 8 * (l / 16) + t]      (t = 0..7)
+//   B[k = 8 * (l / 16) + t][n = l % 16]
+//   D[m = 4 * (l / 16) + i][n = l % 16]      (i = 0..3)
+// (checked on gfx950 hardware against a host matmul).
+
 // Row of the 32x32 accumulator held in register r by lane half `hi`.
 __device__ __forceinline__ int acc_row(int r, int hi) { return 8 * (r >> 2) + 4 * hi + (r & 3); }
 
@@ -49,8 +55,8 @@ __device__ __forceinline__ bf16x8 zero_bf16x8() {
 __device__ __forceinline__ bf16_t to_bf16(float f) { return (bf16_t)f; }
 
 // Element types of the cache, prepared queries and probabilities.  Both are
-// 2-byte types fed to 32x32x16 MFMA with fp32 accumulation; the operand lane
-// layout is the same for both.
+// 2-byte types fed to 32x32x16 or 16x16x32 MFMA with fp32 accumulation; the
+// operand lane layouts are the same for both.
 template <typename E>
 struct Elem;
 
@@ -61,6 +67,9 @@ struct Elem<bf16_t> {
   static __device__ __forceinline__ f32x16 mfma(v8 a, v8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
+  static __device__ __forceinline__ f32x4 mfma16(v8 a, v8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
   static __device__ __forceinline__ bf16_t from(float f) { return (bf16_t)f; }
 };
 
@@ -70,6 +79,9 @@ struct Elem<f16_t> {
   typedef f16x4 v4;
   static __device__ __forceinline__ f32x16 mfma(v8 a, v8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mfma16(v8 a, v8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
   }
   static __device__ __forceinline__ f16_t from(float f) { return (f16_t)f; }
 };

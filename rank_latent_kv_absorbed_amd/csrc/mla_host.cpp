@@ -138,7 +138,7 @@ mla::Schedule make_schedule(int64_t B, int64_t R, int64_t Lk, int32_t key_splits
                             mla::CoreShape sh, int chunks_per_key) {
   mla::Schedule s;
   sh = mla::core_shape_for_keys(sh, chunks_per_key);
-  const int64_t br = 32 * sh.waves;
+  const int64_t br = (int64_t)sh.rows * sh.waves;
   const int64_t n_rg = (R + br - 1) / br;
   const int64_t n_kt = (Lk + sh.key_tile - 1) / sh.key_tile;
   const int64_t groups = B * n_rg;
@@ -214,7 +214,8 @@ DenseLayout dense_layout(const mla_cache* h, int32_t Lq, int64_t Lk = -1) {
   const int d_h = c.d_nope + c.d_rope;
   DenseLayout L;
   const mla::CoreShape sh = mla::core_shape_for_rows(Lq);
-  L.lq_pad = (Lq + 32 * sh.waves - 1) / (32 * sh.waves) * (32 * sh.waves);
+  const int br = sh.rows * sh.waves;
+  L.lq_pad = (Lq + br - 1) / br * br;
   const int64_t R = (int64_t)c.n_heads * L.lq_pad;
   L.sched = make_schedule(c.batch, R, Lk < 0 ? window_keys(h) : Lk, 0, mla::device_cu_count(), sh,
                           2 * d_h / 8);

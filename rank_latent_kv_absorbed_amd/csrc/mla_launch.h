@@ -51,17 +51,23 @@ struct CacheWriteArgs {
 // chunk case) take the widest block, which reuses each staged key tile most;
 // a few rows (cache-bound small-query shapes) take narrow blocks on short
 // tiles with deeper buffer rings, to keep more key bytes in flight per CU.
+// `rows` is the query rows per wave: 32 on 32x32x16 MFMAs, or 16 on
+// 16x16x32 MFMAs for row units of at most 16 rows (one query per sequence
+// over 12 heads, say), which then waste a quarter of the matrix work instead
+// of five eighths.
 struct CoreShape {
   int waves;
   int key_tile;
   int stages;
+  int rows;
 };
-constexpr CoreShape kCoreShapes[] = {{8, 64, 3}, {4, 32, 4}, {1, 32, 2}};
+constexpr CoreShape kCoreShapes[] = {{8, 64, 3, 32}, {4, 32, 4, 32}, {1, 32, 2, 32}, {1, 32, 2, 16}};
 constexpr int kCoreMaxBlockRows = 256;
 
 // Shape for `rows` query rows of one row unit (latent: Lq * n_h rows of a
 // batch element; dense: Lq rows of one head).
 inline CoreShape core_shape_for_rows(int64_t rows) {
+  if (rows <= 16) return kCoreShapes[3];
   if (rows <= 32) return kCoreShapes[2];
   if (rows <= 128) return kCoreShapes[1];
   return kCoreShapes[0];
@@ -101,7 +107,7 @@ inline int core_blocks_per_cu(CoreShape sh, int chunks_per_key) {
 // sum) per block, merged exactly by log-sum-exp: slot 0 = main block, slots
 // 1.. = tail blocks in order.
 struct Schedule {
-  int block_rows;       // rows per group (32 * waves of the core shape)
+  int block_rows;       // rows per group (rows per wave * waves of the core shape)
   int key_tile;         // keys per step
   int stages;           // LDS tile buffers of the core shape
   int n_rg;             // row groups per batch element

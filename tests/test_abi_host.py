@@ -130,14 +130,22 @@ def _mha_info(L):
 # many blocks of each fit one compute unit (stages LDS tiles of
 # key_tile * chunks * 16 bytes in 160 KiB; at most eight waves).
 def expected_shape(rows, chunks_per_key=28):
-    br, kt, ns = (32, 32, 2) if rows <= 32 else ((128, 32, 4) if rows <= 128 else (256, 64, 3))
-    spans = kt * chunks_per_key // 64 // (br // 32)   # tile loads per wave
+    if rows <= 16:
+        br, kt, ns, waves = 16, 32, 2, 1                # one wave of 16 rows (16x16x32 MFMAs)
+    elif rows <= 32:
+        br, kt, ns, waves = 32, 32, 2, 1
+    elif rows <= 128:
+        br, kt, ns, waves = 128, 32, 4, 4
+    else:
+        br, kt, ns, waves = 256, 64, 3, 8
+    spans = kt * chunks_per_key // 64 // waves         # tile loads per wave
     return br, kt, min(ns, 1 + 63 // spans)           # in-flight loads fit a 6-bit counter
 
 
 def blocks_per_cu(shape, chunks_per_key):
     br, kt, ns = shape
-    return min(160 * 1024 // (ns * kt * chunks_per_key * 16), 8 // (br // 32))
+    waves = 1 if br <= 32 else br // 32
+    return min(160 * 1024 // (ns * kt * chunks_per_key * 16), 8 // waves)
 
 
 def check_schedule(L, info, R, which=0):
