@@ -642,22 +642,20 @@ void attn_core_kernel(AttnCore a) {
   // Every buffer access below names its LDS array directly, so that the
   // compiler can tell the tile being read from the tiles still being written.
   if constexpr (NW == 1) {
-    // Tiles 0 .. NS - 2, then the queries; one full wait covers them all (the
-    // compiler sees the query registers ready), and tile NS - 1 streams in
-    // during step 0.
+    // One tile per buffer, then the queries; one full wait covers them all.
+    // The loop is entered with no tile load in flight: a load left in flight
+    // here (say tile NS - 1 streaming in during step 0) makes the compiler's
+    // own LDS-write tracking put a full vector-memory wait in front of the
+    // first tile read of every pass of the step loop, which drains the ring
+    // at every NS-th step.
     issue(kt0);
-    if (NS > 2 && n_steps > 1) issue(kt1);
-    if (NS > 3 && n_steps > 2) issue(kt2);
-    if (NS > 4 && n_steps > 3) issue(kt3);
+    if (n_steps > 1) issue(kt1);
+    if (NS > 2 && n_steps > 2) issue(kt2);
+    if (NS > 3 && n_steps > 3) issue(kt3);
+    if (NS > 4 && n_steps > 4) issue(kt4);
     begin_segment(b0, s0.grp - b0 * sc.n_rg);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
-    if (n_steps > NS - 1) {
-      if constexpr (NS == 2) issue(kt1);
-      if constexpr (NS == 3) issue(kt2);
-      if constexpr (NS == 4) issue(kt3);
-      if constexpr (NS == 5) issue(kt4);
-    }
   } else {
     begin_segment(b0, s0.grp - b0 * sc.n_rg);
     issue(kt0);
