@@ -104,6 +104,97 @@ __global__ __launch_bounds__(256) void qprep_bf16_kernel(AttendArgs a) {
   }
 }
 
+// Query prologue for a few tokens per sequence (decode-like calls): one block
+// per (head, batch element).  Thread (column chunk j, row group g) holds
+// W^K_up,h[n][8 j .. 8 j + 7] for rows n = g, g + NG, ... in registers, all
+// loaded up front straight from global memory (the product is too small to
+// pay for staging), and forms its share of q_lat for every token; the row
+// groups are summed through LDS.  The MFMA kernel above serves longer chunks.
+constexpr int kQprepRowsMaxLq = 8;   // tokens per sequence
+constexpr int kQprepRowsMaxK = 12;   // W rows per thread (d_nope <= NG * 12)
+
+template <int DC>
+constexpr int qprep_rows_max_nope() {
+  return (256 / (DC / 8)) * kQprepRowsMaxK;
+}
+
+template <typename E, int DC>
+__global__ __launch_bounds__(256) void qprep_rows_kernel(AttendArgs a) {
+  constexpr int CH = DC / 8;                      // 8-column chunks of a W row
+  constexpr int NG = 256 / CH;                    // row groups
+  constexpr int NMAX = NG * kQprepRowsMaxK;       // largest d_nope served
+  constexpr int QPT = (kQprepRowsMaxLq * NMAX + 255) / 256;  // query elements per thread
+  __shared__ float qs[kQprepRowsMaxLq * NMAX];    // [tok][n] fp32 queries
+  __shared__ float red[NG][DC];                   // one token's row-group sums
+  const int tid = threadIdx.x;
+  const int j = tid % CH, g = tid / CH;
+  const bool active = g < NG;
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int d_nope = a.d_nope, d_qk = d_nope + a.d_rope;
+  const int width = DC + a.d_rope;
+  const int R = a.Lq * a.n_h;
+  const bf16_t* q = (const bf16_t*)a.q;
+
+  // Loads are unconditional (indices clamped into range) so that they all
+  // issue before the first wait; rows past d_nope meet a zero query below.
+  const bf16_t* wuk = (const bf16_t*)a.w_uk + (size_t)h * d_nope * DC + 8 * j;
+  bf16x8 w[kQprepRowsMaxK];
+#pragma unroll
+  for (int k = 0; k < kQprepRowsMaxK; ++k) {
+    const int n = min(min(g, NG - 1) + NG * k, d_nope - 1);
+    w[k] = ld_bf16x8(wuk + (size_t)n * DC);
+  }
+  const int nq = a.Lq * d_nope;
+  float qv[QPT];
+#pragma unroll
+  for (int i = 0; i < QPT; ++i) {
+    const int e = min(tid + 256 * i, nq - 1);
+    const int tok = e / d_nope, n = e - tok * d_nope;
+    qv[i] = (float)q[(((size_t)b * a.Lq + tok) * a.n_h + h) * d_qk + n];
+  }
+#pragma unroll
+  for (int i = 0; i < QPT; ++i)
+    if (tid + 256 * i < nq) qs[tid + 256 * i] = qv[i];
+  __syncthreads();
+
+  for (int tok = 0; tok < a.Lq; ++tok) {
+    float acc[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc[t] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kQprepRowsMaxK; ++k) {
+      const int n = g + NG * k;
+      const float qn = n < d_nope ? qs[tok * d_nope + n] : 0.0f;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) acc[t] = fmaf(qn, (float)w[k][t], acc[t]);
+    }
+    if (active) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) red[g][8 * j + t] = acc[t];
+    }
+    __syncthreads();
+    E* out = (E*)a.qcat + ((size_t)b * R + (size_t)tok * a.n_h + h) * width;
+    for (int c = tid; c < DC; c += 256) {
+      float sum = 0.0f;
+#pragma unroll
+      for (int gg = 0; gg < NG; ++gg) sum += red[gg][c];
+      out[c] = Elem<E>::from(sum * a.qscale);
+    }
+    __syncthreads();
+  }
+  // rotary part: threads walk (token, pair)
+  const int P = a.d_rope / 2;
+  for (int e = tid; e < a.Lq * P; e += 256) {
+    const int tok = e / P, p = e - tok * P;
+    const bf16_t* qr = q + (((size_t)b * a.Lq + tok) * a.n_h + h) * d_qk + d_nope + 2 * p;
+    float x0 = (float)qr[0], x1 = (float)qr[1];
+    rope_pair(a.rope, p, token_pos(a.q_token0 + tok, a.T, a.grid_w), x0, x1);
+    E* o = (E*)a.qcat + ((size_t)b * R + (size_t)tok * a.n_h + h) * width + DC + 2 * p;
+    o[0] = Elem<E>::from(x0 * a.qscale);
+    o[1] = Elem<E>::from(x1 * a.qscale);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // 3. merge of key ranges + W^V_up epilogue
 // ---------------------------------------------------------------------------
@@ -178,61 +269,110 @@ __global__ __launch_bounds__(64) void epilogue_bf16_kernel(AttendArgs a) {
   }
 }
 
-// Few-row variant: one 256-thread block per (token, head) row.  Thread
-// (column chunk c, slot lane j) sums the partials j, j + LANES, ... of four
-// columns; the lanes are added through LDS, normalised, and the W^V_up,h
-// product runs in plain fp32 with one output dimension per thread.
+// Few-row variant: one 256-thread block per (token, head) row, for rows with
+// many key-range partials.  Every load the row needs is in flight at once
+// before any of them is used: the thread's slice of W^V_up,h (one output
+// dimension per thread), the slot maxima and sums (one slot per thread), and
+// its first run of partials (thread (column chunk c4, slot lane j) sums slots
+// j, j + LANES, ... of four columns).  The slot weights 2^(m_k - max) go
+// through LDS; the lanes are added through LDS, normalised, and the
+// W^V_up,h product runs in plain fp32.
 // Above this many partial slots per row group the per-row epilogue is used.
 constexpr int kLaneMergeMaxSlots = 4;
+// With many rows in flight (more blocks than a couple per compute unit) the
+// kernel is run lean instead: a shorter run of partial loads and W^V_up,h
+// read after the merge, so that several blocks share a compute unit.
+constexpr int kEpiWeights = 1024;    // slot weights kept in LDS
+constexpr int kEpiMaxDv = 256;       // output dimensions (one per thread)
+constexpr int kEpiLeanRows = 256;    // rows (blocks) from which the lean form runs
 
-template <int DC>
+template <int DC, bool LEAN>
 __global__ __launch_bounds__(256) void epilogue_rows_kernel(AttendArgs a) {
+  constexpr int kEpiRun = LEAN ? 8 : 26;  // partial loads in flight per thread
   constexpr int C4 = DC / 4;       // 4-column chunks of a partial row
   constexpr int LANES = 256 / C4;  // slot lanes
-  __shared__ float red[256];
+  constexpr int NW8 = DC / 8;      // 16-byte pieces of a W^V_up row
+  __shared__ float wts[kEpiWeights];
+  __shared__ float red[2][4];
   __shared__ float part[LANES][DC];
   __shared__ float olat[DC];
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int row = blockIdx.x, b = blockIdx.y;  // row = tok * n_h + h
   const int R = a.Lq * a.n_h;
   const int tok = row / a.n_h, h = row - tok * a.n_h;
   const int n_part = sched_group_slots(a.sched, b * a.sched.n_rg + row / a.sched.block_rows);
   auto prow_of = [&](int k) { return ((size_t)k * a.B + b) * R + row; };
+  const int c4 = tid % C4, j = tid / C4;
+  const bool lane_ok = j < LANES;
 
-  float mx = -INFINITY;
-  for (int k = tid; k < n_part; k += 256) mx = fmaxf(mx, a.ml[prow_of(k) * 2]);
-  red[tid] = mx;
-  __syncthreads();
-  for (int st = 128; st > 0; st >>= 1) {
-    if (tid < st) red[tid] = fmaxf(red[tid], red[tid + st]);
-    __syncthreads();
+  // loads, all issued before the first use
+  // (Indices are clamped into range instead of predicating the loads, so
+  // that none of them waits for another; slots past n_part get weight 0.)
+  const bool v_ok = tid < a.d_v;
+  const bf16_t* wr = (const bf16_t*)a.w_uv + ((size_t)h * a.d_v + (v_ok ? tid : 0)) * DC;
+  bf16x8 wv[LEAN ? 1 : NW8];
+  if constexpr (!LEAN) {
+#pragma unroll
+    for (int i = 0; i < NW8; ++i) wv[i] = ld_bf16x8(wr + 8 * i);
   }
-  const float M = red[0];
+  const float2 ml2 = *reinterpret_cast<const float2*>(a.ml + prow_of(min(tid, n_part - 1)) * 2);
+  f32x4 x[kEpiRun];
+#pragma unroll
+  for (int u = 0; u < kEpiRun; ++u) {
+    const int k = min(j + LANES * u, n_part - 1);
+    x[u] = *reinterpret_cast<const f32x4*>(a.opart + prow_of(k) * DC + 4 * c4);
+  }
+  const float m0 = tid < n_part ? ml2.x : -INFINITY, l0 = ml2.y;
+
+  // block maximum of the slot maxima (slots past the first 256 by a loop)
+  float mx = m0;
+  for (int k = tid + 256; k < n_part; k += 256) mx = fmaxf(mx, a.ml[prow_of(k) * 2]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  if (lane == 0) red[0][wave] = mx;
   __syncthreads();
+  const float M = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
+  // weights and the weighted sum of the slot sums
   float ls = 0.0f;
   for (int k = tid; k < n_part; k += 256) {
-    const size_t pr = prow_of(k);
-    ls += exp2_fast(a.ml[pr * 2] - M) * a.ml[pr * 2 + 1];
+    float mk = m0, lk = l0;
+    if (k != tid) {
+      mk = a.ml[prow_of(k) * 2];
+      lk = a.ml[prow_of(k) * 2 + 1];
+    }
+    const float wk = exp2_fast(mk - M);
+    if (k < kEpiWeights) wts[k] = wk;
+    ls += wk * lk;
   }
-  red[tid] = ls;
-  __syncthreads();
-  for (int st = 128; st > 0; st >>= 1) {
-    if (tid < st) red[tid] += red[tid + st];
-    __syncthreads();
-  }
-  const float inv = 1.0f / red[0];
-
-  const int c4 = tid % C4, j = tid / C4;
-  if (j < LANES) {
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    // unrolled so that several partial loads are in flight per thread
-#pragma unroll 8
-    for (int k = j; k < n_part; k += LANES) {
-      const size_t pr = prow_of(k);
-      const float wgt = exp2_fast(a.ml[pr * 2] - M);
-      const f32x4 x = *reinterpret_cast<const f32x4*>(a.opart + pr * DC + 4 * c4);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) acc[t] += wgt * x[t];
+  for (int o = 32; o > 0; o >>= 1) ls += __shfl_xor(ls, o);
+  if (lane == 0) red[1][wave] = ls;
+  __syncthreads();
+  const float inv = 1.0f / (red[1][0] + red[1][1] + red[1][2] + red[1][3]);
+  auto weight = [&](int k) { return k < kEpiWeights ? wts[k] : exp2_fast(a.ml[prow_of(k) * 2] - M); };
+
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (lane_ok) {
+#pragma unroll
+    for (int u = 0; u < kEpiRun; ++u) {
+      const int k = j + LANES * u;
+      const float wk = k < n_part ? weight(k) : 0.0f;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[t] = fmaf(wk, x[u][t], acc[t]);
+    }
+    // slots past the first run, a run of loads at a time
+    for (int k0 = j + LANES * kEpiRun; k0 < n_part; k0 += LANES * kEpiRun) {
+#pragma unroll
+      for (int u = 0; u < kEpiRun; ++u)
+        x[u] = *reinterpret_cast<const f32x4*>(a.opart + prow_of(min(k0 + LANES * u, n_part - 1)) * DC +
+                                               4 * c4);
+#pragma unroll
+      for (int u = 0; u < kEpiRun; ++u) {
+        const int k = k0 + LANES * u;
+        const float wk = k < n_part ? weight(k) : 0.0f;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[t] = fmaf(wk, x[u][t], acc[t]);
+      }
     }
 #pragma unroll
     for (int t = 0; t < 4; ++t) part[j][4 * c4 + t] = acc[t];
@@ -246,18 +386,15 @@ __global__ __launch_bounds__(256) void epilogue_rows_kernel(AttendArgs a) {
   }
   __syncthreads();
 
-  const bf16_t* wuv = (const bf16_t*)a.w_uv + (size_t)h * a.d_v * DC;
-  float* out = a.out + (((size_t)b * a.Lq + tok) * a.n_h + h) * a.d_v;
-  for (int v = tid; v < a.d_v; v += 256) {
-    const bf16_t* wr = wuv + (size_t)v * DC;
+  if (v_ok) {
     float sum = 0.0f;
-#pragma unroll 4
-    for (int i = 0; i < DC; i += 8) {
-      const bf16x8 w8 = ld_bf16x8(wr + i);
 #pragma unroll
-      for (int t = 0; t < 8; ++t) sum = fmaf((float)w8[t], olat[i + t], sum);
+    for (int i = 0; i < NW8; ++i) {
+      const bf16x8 w8 = LEAN ? ld_bf16x8(wr + 8 * i) : wv[i];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) sum = fmaf((float)w8[t], olat[8 * i + t], sum);
     }
-    out[v] = sum;
+    a.out[(((size_t)b * a.Lq + tok) * a.n_h + h) * a.d_v + tid] = sum;
   }
 }
 
@@ -368,7 +505,12 @@ hipError_t launch_core(const AttnCore& c, hipStream_t s) {
 
 template <typename E, int DC>
 hipError_t launch_dc(const AttendArgs& a, hipStream_t s) {
-  {
+  if (a.Lq <= kQprepRowsMaxLq && a.d_nope <= qprep_rows_max_nope<DC>()) {
+    hipLaunchKernelGGL((qprep_rows_kernel<E, DC>), dim3((unsigned)a.n_h, (unsigned)a.B), dim3(256), 0,
+                       s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  } else {
     const size_t lds = (size_t)a.d_nope * (DC + 8) * sizeof(bf16_t);
     dim3 grid((unsigned)((a.Lq + 127) / 128), (unsigned)a.n_h, (unsigned)a.B);
     hipLaunchKernelGGL((qprep_bf16_kernel<E, DC>), grid, dim3(256), lds, s, a);
@@ -407,9 +549,13 @@ hipError_t launch_dc(const AttendArgs& a, hipStream_t s) {
   // Rows with many key-range partials each (narrow blocks, or few row groups
   // spread over the whole device) merge one row per block; otherwise one lane
   // per row, whose merge walks the partials one after another.
-  if (a.sched.block_rows < kCoreMaxBlockRows || a.sched.n_slots > kLaneMergeMaxSlots) {
-    hipLaunchKernelGGL(epilogue_rows_kernel<DC>, dim3((unsigned)(a.Lq * a.n_h), (unsigned)a.B),
-                       dim3(256), 0, s, a);
+  if ((a.sched.block_rows < kCoreMaxBlockRows || a.sched.n_slots > kLaneMergeMaxSlots) &&
+      a.d_v <= kEpiMaxDv) {
+    const dim3 grid((unsigned)(a.Lq * a.n_h), (unsigned)a.B);
+    if (grid.x * grid.y >= (unsigned)kEpiLeanRows)
+      hipLaunchKernelGGL((epilogue_rows_kernel<DC, true>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((epilogue_rows_kernel<DC, false>), grid, dim3(256), 0, s, a);
     return hipGetLastError();
   }
   {

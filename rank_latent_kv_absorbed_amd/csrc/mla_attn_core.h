@@ -81,9 +81,10 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const void* p) {
 
 // Direct 16-byte global -> LDS load (global_load_lds_dwordx4): lane l of the
 // wave writes LDS bytes [lds + 16 l, lds + 16 l + 16); `lds` must be uniform.
-__device__ __forceinline__ void global_to_lds16(const void* g, void* lds) {
+typedef __attribute__((address_space(3))) char lds_char;
+__device__ __forceinline__ void global_to_lds16(const void* g, lds_char* lds) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
 #endif
 }
 
@@ -199,7 +200,7 @@ void attn_core_kernel(AttnCore a) {
   // compiler does not fold, even for one-wave blocks.  All waits for tile
   // loads are explicit (exact per-wave counts, then a barrier); loads the
   // compiler cannot count are ones it does not try to wait for itself.
-  const int w = tid >> 6, l = tid & 63, lo = l & 31, hi = l >> 5;
+  const int w = NW == 1 ? 0 : tid >> 6, l = tid & 63, lo = l & 31, hi = l >> 5;
   const int g = blockIdx.x;
   const int n_steps = sched_block_steps(sc, g);
   const int n_ld = (SPANS - w + NW - 1) / NW;  // direct loads this wave issues per tile
@@ -240,8 +241,12 @@ void attn_core_kernel(AttnCore a) {
   };
   constexpr int LKEEP = NW == 1 ? (PER < SPANS ? PER : SPANS) : LPW;
   int lane_off[LKEEP];
+  uint32_t lane_bytes[LKEEP];  // the same in bytes (non-negative)
 #pragma unroll
-  for (int j = 0; j < LKEEP; ++j) lane_off[j] = lane_offset(NW == 1 ? j : w + j * NW);
+  for (int j = 0; j < LKEEP; ++j) {
+    lane_off[j] = lane_offset(NW == 1 ? j : w + j * NW);
+    lane_bytes[j] = (uint32_t)lane_off[j] * (uint32_t)sizeof(E);
+  }
   auto load_tile = [&](int b, int head, int kt, E* dst) MLA_INLINE {
     const E* ring = (const E*)a.ring + (size_t)b * a.ring_rows * a.ring_stride;
     const int rows = (int)a.ring_rows;
@@ -253,14 +258,30 @@ void attn_core_kernel(AttnCore a) {
     // (Keys past the window still read ring rows - allocated, possibly stale
     // memory; the step that uses the tile clears them in LDS.)
     const bool wraps = s0 + KT > rows;
+    // (The LDS address space is taken before any offset is added, so that
+    // the buffer's address folds to a constant.)
+    lds_char* const ldst = (lds_char*)dst;
+    if (!wraps) {
+      // Common case: a wave-uniform base per 16-key period plus the lane's
+      // 32-bit byte offset, which maps onto the load's scalar-base form.
+#pragma unroll
+      for (int j = 0; j < LPW; ++j) {
+        const int sp = w + j * NW;
+        if (NW == 1 || sp < SPANS) {
+          const char* pb = (const char*)(NW == 1 ? base + (j / PER) * 16 * a.ring_stride : base);
+          global_to_lds16(pb + lane_bytes[NW == 1 ? j % PER : j], ldst + sp * 1024);
+        }
+      }
+      return;
+    }
     const int split = (rows - s0) * a.ring_stride, back = rows * a.ring_stride;
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
       const int sp = w + j * NW;
-      if (sp < SPANS) {
+      if (NW == 1 || sp < SPANS) {
         int off = NW == 1 ? (j / PER) * 16 * a.ring_stride + lane_off[j % PER] : lane_off[j];
-        if (wraps) off = off >= split ? off - back : off;
-        global_to_lds16(base + off, dst + sp * 512);
+        off = off >= split ? off - back : off;
+        global_to_lds16(base + off, ldst + sp * 1024);
       }
     }
   };
@@ -368,15 +389,25 @@ void attn_core_kernel(AttnCore a) {
   // Scores S^T = K Q^T of the tile in `cur`.
   auto scores = [&](const E* cur, AccT (&sv)[RB][NKB]) MLA_INLINE {
     if constexpr (R16) {
+      // All key fragments of the tile first, then the products (the two key
+      // blocks' chains interleaved): a narrow block has too few waves per
+      // SIMD to hide one LDS round trip per product.
+      V8 kf[NKB][NKS];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-        for (int r = 0; r < AV; ++r) sv[0][kb][r] = 0.0f;
         const E* krow = cur + (kb * 16 + r16) * KSTR;
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
-          sv[0][kb] = Elem<E>::mfma16(ld8<E>(krow + 8 * ((4 * ks + g16) ^ k_sw16)), qf[0][ks], sv[0][kb]);
+        for (int ks = 0; ks < NKS; ++ks) kf[kb][ks] = ld8<E>(krow + 8 * ((4 * ks + g16) ^ k_sw16));
       }
+      __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < AV; ++r) sv[0][kb][r] = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) sv[0][kb] = Elem<E>::mfma16(kf[kb][ks], qf[0][ks], sv[0][kb]);
     } else {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
@@ -456,12 +487,19 @@ void attn_core_kernel(AttnCore a) {
       // slots 8 g16 .. + 3: keys 4 g16 + t (block 0); + 4 .. + 7: keys 16 + 4 g16 + t
       const E* v0 = cur + (4 * g16 + t16) * KSTR + VOFF + 4 * (c16 & 1);
       const E* v1 = v0 + 16 * KSTR;
+      // all transpose reads first, then the products
+      i16x4 lo4[NDT], hi4[NDT];
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
         const int q = (2 * dt + (c16 >> 1)) ^ tsw16;
-        const i16x4 lo4 = lds_read_tr16(v0 + 8 * q);
-        const i16x4 hi4 = lds_read_tr16(v1 + 8 * q);
-        const V8 va = __builtin_bit_cast(V8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+        lo4[dt] = lds_read_tr16(v0 + 8 * q);
+        hi4[dt] = lds_read_tr16(v1 + 8 * q);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const V8 va =
+            __builtin_bit_cast(V8, __builtin_shufflevector(lo4[dt], hi4[dt], 0, 1, 2, 3, 4, 5, 6, 7));
         o[0][dt] = Elem<E>::mfma16(va, pf[0][0], o[0][dt]);
       }
     } else {

@@ -84,11 +84,12 @@ __global__ __launch_bounds__(kExpandWaves * 64) void expand_kv_kernel(ExpandArgs
   // c = 64 sp + l: row c / CPR, position c % CPR of the rows of all tiles.
   {
     const E* src = (const E*)a.wx + (size_t)h * kExpandTiles * TILE;
+    lds_char* const wl = (lds_char*)wts;
     for (int sp = w; sp < WSPANS; sp += kExpandWaves) {
       const int c = sp * 64 + l;
       const int r = c / CPR, p = c - r * CPR;
       const int q = p ^ ((r >> 1) & 7);
-      global_to_lds16(src + r * DC + q * 8, wts + sp * 512);
+      global_to_lds16(src + r * DC + q * 8, wl + sp * 1024);
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();

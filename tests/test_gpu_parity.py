@@ -205,6 +205,19 @@ def test_attend_small_queries_cache_bound_shapes(Lq, cache_dtype):
     assert_parity(got, ref, "bf16", f"small query Lq={Lq} {cache_dtype}")
 
 
+# Few-token prologue and per-row epilogue at every latent width; batch 3
+# puts Lq = 8 (288 rows) on the lean epilogue and Lq = 1 on the wide one.
+@pytest.mark.parametrize("d_c", [64, 128])
+@pytest.mark.parametrize("Lq", [1, 8])
+def test_attend_small_queries_latent_widths(Lq, d_c):
+    cfg = config("wan_layer").with_(window_frames=3, batch=3, d_c=d_c, cache_dtype="f16")
+    run = LatentRun(cfg)
+    run.write(0, 3)
+    q = run.query(Lq)
+    got, ref, _ = run.attend(q, 3 * cfg.T - Lq)
+    assert_parity(got, ref, "bf16", f"small query Lq={Lq} d_c={d_c}")
+
+
 def test_nan_poison_determinism_and_split_agreement():
     cfg = wan_small()
     runs = [LatentRun(cfg, poison=p) for p in (False, True)]
