@@ -6,6 +6,7 @@
 // frames enter at the newest end and leave from the oldest end; token tau of
 // frame f always lives at ring slot (f mod W)*T + tau.  Every check runs
 // before anything is enqueued, so a failed call changes nothing.
+#include <algorithm>
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
@@ -133,9 +134,14 @@ void commit_write(mla_cache* h, int64_t frame0, int32_t n_frames) {
 // every row group key_splits blocks' worth of work, cutting its key range into
 // about that many pieces.
 constexpr int64_t kMinStepsPerBlock = 8;
+// Cost of starting a segment, in key-tile steps (block finish times on the
+// 4680-query chunk: a tail block's extra segments cost it about three steps
+// each on the latent rows, about six on the shorter per-head steps).
+constexpr int64_t kSegmentCostLatent = 3;
+constexpr int64_t kSegmentCostDense = 6;
 
 mla::Schedule make_schedule(int64_t B, int64_t R, int64_t Lk, int32_t key_splits, int64_t cus,
-                            mla::CoreShape sh, int chunks_per_key) {
+                            mla::CoreShape sh, int chunks_per_key, int64_t seg_cost) {
   mla::Schedule s;
   sh = mla::core_shape_for_keys(sh, chunks_per_key);
   const int64_t br = (int64_t)sh.rows * sh.waves;
@@ -158,6 +164,19 @@ mla::Schedule make_schedule(int64_t B, int64_t R, int64_t Lk, int32_t key_splits
   if (rem > 0) {
     main_len = (rem * n_kt + nb - 1) / nb;
     if (main_len > n_kt) main_len = n_kt;
+    // A tail block starts a segment (queries in, tile ring drained, a partial
+    // written) for every group its run touches - on average 1 + run / tail
+    // length of them - and a main block once.  Counting seg_cost steps per
+    // segment, move key tiles from the tail runs to the main blocks while that
+    // lowers the larger of the two costs.
+    auto cost = [&](int64_t ml) {
+      const int64_t tail_len = n_kt - ml;
+      if (tail_len <= 0 || nb <= rem) return (double)(ml + seg_cost);
+      const int64_t run = (rem * tail_len + (nb - rem) - 1) / (nb - rem);
+      const double tail_cost = run + seg_cost * (1.0 + (double)run / tail_len);
+      return std::max((double)(ml + seg_cost), tail_cost);
+    };
+    while (main_len < n_kt && cost(main_len + 1) < cost(main_len)) ++main_len;
     const int64_t tail = rem * (n_kt - main_len);
     if (tail > 0) tpb = (tail + (nb - rem) - 1) / (nb - rem);
   }
@@ -193,7 +212,7 @@ LatentLayout latent_layout(const mla_cache* h, int32_t Lq, int32_t key_splits, i
   const int64_t R = (int64_t)Lq * c.n_heads;
   LatentLayout L;
   L.sched = make_schedule(c.batch, R, Lk < 0 ? window_keys(h) : Lk, key_splits, mla::device_cu_count(),
-                          mla::core_shape_for_rows(R), (c.d_c + c.d_rope) / 8);
+                          mla::core_shape_for_rows(R), (c.d_c + c.d_rope) / 8, kSegmentCostLatent);
   const size_t width = (size_t)(c.d_c + c.d_rope);
   const size_t slots = (size_t)L.sched.n_slots;
   L.qcat_off = 0;
@@ -218,7 +237,7 @@ DenseLayout dense_layout(const mla_cache* h, int32_t Lq, int64_t Lk = -1) {
   L.lq_pad = (Lq + br - 1) / br * br;
   const int64_t R = (int64_t)c.n_heads * L.lq_pad;
   L.sched = make_schedule(c.batch, R, Lk < 0 ? window_keys(h) : Lk, 0, mla::device_cu_count(), sh,
-                          2 * d_h / 8);
+                          2 * d_h / 8, kSegmentCostDense);
   const size_t slots = (size_t)L.sched.n_slots;
   L.qrot_off = 0;
   L.opart_off = round_up((size_t)c.batch * R * d_h * 2, kAlign);

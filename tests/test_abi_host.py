@@ -148,6 +148,19 @@ def blocks_per_cu(shape, chunks_per_key):
     return min(160 * 1024 // (ns * kt * chunks_per_key * 16), 8 // waves)
 
 
+# Steps charged per segment start by the library's schedule (latent, dense).
+SEG_COST = (3, 6)
+
+
+def _block_segments(L, which, g, n):
+    out = (ctypes.c_int * 5)()
+    k = 0
+    for i in range(n):
+        L.fake_sched_decode(which, g, i, out)
+        k += out[3]
+    return k
+
+
 def check_schedule(L, info, R, which=0):
     """Walk the last attend's schedule exactly as the kernel decodes it: every
     (row group, key tile) step runs once; each block's steps form segments
@@ -178,8 +191,13 @@ def check_schedule(L, info, R, which=0):
     for grp in range(groups):
         k = L.fake_sched_group_slots(which, grp)
         assert slots[grp] == set(range(k)) and k <= info["n_slots"]
+    # balanced once every segment start counts SEG_COST[which] steps
+    seg_cost = SEG_COST[which]
+    segs = [L.fake_sched_steps(which, g) and _block_segments(L, which, g, steps[g]) for g in range(nb)]
     busy = [s for s in steps if s > 0]
-    assert max(busy) <= -(-groups * n_kt // nb) + 1
+    assert max(busy) <= -(-groups * n_kt // nb) + seg_cost * max(segs) + 1
+    costs = [s + seg_cost * k for s, k in zip(steps, segs) if s > 0]
+    assert max(costs) <= min(max(busy), -(-groups * n_kt // nb)) + 2 * seg_cost + 1
     # the kernels walk the same steps incrementally
     assert L.fake_sched_cursor_mismatches(which) == 0
 
@@ -298,11 +316,13 @@ def test_attend_arguments_and_workspace(sim):
     assert a["key_slot0"] == (3 % 21) * 1560 and a["Lk"] == 21 * 1560 and a["Lq"] == 4680
     assert a["q_token0"] == 21 * 1560
     assert sim.fake_attend_qscale() == np.float32(math.log2(math.e) / math.sqrt(128))
-    # full window, one sequence: 220 main blocks walk key tiles 0..439 in
-    # lockstep, 36 tail blocks share tiles 440..511 of every group, 440 each
+    # full window, one sequence: 220 main blocks walk key tiles 0..442 in
+    # lockstep, 36 tail blocks share tiles 443..511 of every group, 422 each
+    # (a tail run starts about 7 segments, 3 steps each, so it gets fewer
+    # tiles than the 440 of an even split)
     assert (a["block_rows"], a["key_tile"]) == (256, 64)
     assert (a["n_blocks"], a["n_rg"], a["n_kt"], a["rem"], a["main_len"], a["tpb"]) == \
-        (256, 220, 512, 220, 440, 440)
+        (256, 220, 512, 220, 443, 422)
     check_schedule(sim, a, R)
     # forced key splits: every row group gets about that many pieces
     for s in (1, 2, 7, 64):
