@@ -15,6 +15,7 @@ namespace {
 // into LDS and shared by every head; then each thread moves 8-element chunks
 // (16-byte loads and stores).  Pairs whose frequency is 0 keep angle 0.
 constexpr int kQprepTokens = 4;
+constexpr int kQprepRun = 4;
 
 template <typename E>
 __global__ __launch_bounds__(256) void mha_qprep_bf16_kernel(MhaAttendArgs a, int lq_pad) {
@@ -36,22 +37,37 @@ __global__ __launch_bounds__(256) void mha_qprep_bf16_kernel(MhaAttendArgs a, in
   __syncthreads();
   const int C = a.d_h / 8;
   const int per_tok = a.n_h * C;
-  for (int i = threadIdx.x; i < kQprepTokens * per_tok; i += blockDim.x) {
-    const int tt = i / per_tok, rem = i - tt * per_tok;
-    const int h = rem / C, ch = rem - h * C;
-    const int tok = tok0 + tt;
-    if (tok >= a.Lq) continue;
-    const bf16x8 v = ld_bf16x8((const bf16_t*)a.q + (((size_t)b * a.Lq + tok) * a.n_h + h) * a.d_h + 8 * ch);
-    V8 o;
+  const int total = kQprepTokens * per_tok;
+  // kQprepRun chunks per thread at a time, all loaded before any is stored
+  // (a chunk past the block's tokens re-reads a valid one and is not stored)
+  for (int i0 = threadIdx.x; i0 < total; i0 += kQprepRun * blockDim.x) {
+    bf16x8 v[kQprepRun];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float c = cs[tt][4 * ch + j][0], s = cs[tt][4 * ch + j][1];
-      const float x0 = (float)v[2 * j], x1 = (float)v[2 * j + 1];
-      o[2 * j] = Elem<E>::from((x0 * c - x1 * s) * a.qscale);
-      o[2 * j + 1] = Elem<E>::from((x0 * s + x1 * c) * a.qscale);
+    for (int u = 0; u < kQprepRun; ++u) {
+      const int i = i0 + u * blockDim.x;
+      const int tt = i < total ? i / per_tok : 0, rem = i < total ? i - tt * per_tok : 0;
+      const int h = rem / C, ch = rem - h * C;
+      const int tok = tok0 + tt < a.Lq ? tok0 + tt : a.Lq - 1;
+      v[u] = ld_bf16x8((const bf16_t*)a.q + (((size_t)b * a.Lq + tok) * a.n_h + h) * a.d_h + 8 * ch);
     }
-    *reinterpret_cast<V8*>((E*)a.qrot + ((size_t)b * a.n_h * lq_pad + (size_t)h * lq_pad + tok) * a.d_h +
-                           8 * ch) = o;
+#pragma unroll
+    for (int u = 0; u < kQprepRun; ++u) {
+      const int i = i0 + u * blockDim.x;
+      const int tt = i / per_tok, rem = i - tt * per_tok;
+      const int h = rem / C, ch = rem - h * C;
+      const int tok = tok0 + tt;
+      if (i >= total || tok >= a.Lq) continue;
+      V8 o;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float c = cs[tt][4 * ch + j][0], s = cs[tt][4 * ch + j][1];
+        const float x0 = (float)v[u][2 * j], x1 = (float)v[u][2 * j + 1];
+        o[2 * j] = Elem<E>::from((x0 * c - x1 * s) * a.qscale);
+        o[2 * j + 1] = Elem<E>::from((x0 * s + x1 * c) * a.qscale);
+      }
+      *reinterpret_cast<V8*>((E*)a.qrot + ((size_t)b * a.n_h * lq_pad + (size_t)h * lq_pad + tok) * a.d_h +
+                             8 * ch) = o;
+    }
   }
 }
 

@@ -201,7 +201,7 @@ void attn_core_kernel(AttnCore a) {
   // loads are explicit (exact per-wave counts, then a barrier); loads the
   // compiler cannot count are ones it does not try to wait for itself.
   const int w = NW == 1 ? 0 : tid >> 6, l = tid & 63, lo = l & 31, hi = l >> 5;
-  const int g = blockIdx.x;
+  const int g = sched_block_of(sc, blockIdx.x);
   const int n_steps = sched_block_steps(sc, g);
   const int n_ld = (SPANS - w + NW - 1) / NW;  // direct loads this wave issues per tile
 

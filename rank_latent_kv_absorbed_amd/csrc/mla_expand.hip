@@ -6,17 +6,15 @@
 // needs fewer products than the absorbed form, whose every score and value
 // product runs in the d_c-wide latent space.
 //
-// Two kernels, then the per-head attention path of the dense cache:
-//  1. weights_to_cache_kernel: [W^K_up,h ; W^V_up,h] (bf16) -> one matrix per
-//     head in the ring's element type, [n_h][d_nope + d_v][d_c] (fp16 is exact
-//     for these weights' range; bf16 is a copy).
-//  2. expand_kv_kernel: for every resident key j and head h,
+// One kernel, then the per-head attention path of the dense cache:
+//  expand_kv_kernel: for every resident key j and head h,
 //       K[j][h] = [ W^K_up,h c_j | k^R_j ],   V[j][h] = W^V_up,h c_j,
 //     written as [B][Lk][2][n_h][d_h] in the ring's element type - the layout
 //     of the dense cache, so the same attention core reads it.  A workgroup
 //     owns one head and a range of keys of one sequence: the head's whole
 //     [d_nope + d_v][d_c] matrix is loaded into LDS once (direct
-//     global->LDS loads), then each wave independently walks 32-key blocks:
+//     global->LDS loads for a bf16 ring, converted to fp16 on the way for an
+//     fp16 ring), then each wave independently walks 32-key blocks:
 //     latent rows into registers (MFMA A operand), D[key][col] =
 //     c[key][:] . W[col][:] on 32x32x16 MFMA per 32-row weight tile (B
 //     operand from LDS), the head's key and value blocks staged in the wave's
@@ -26,26 +24,6 @@
 namespace mla {
 
 namespace {
-
-template <typename E>
-__global__ __launch_bounds__(256) void weights_to_cache_kernel(ExpandArgs a) {
-  const int rows = a.d_nope + a.d_v;
-  const int64_t n = (int64_t)a.n_h * rows * a.d_c;
-  const int64_t idx = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 8;
-  if (idx >= n) return;
-  const int i = (int)(idx % a.d_c);
-  const int64_t hr = idx / a.d_c;
-  const int r = (int)(hr % rows);
-  const int h = (int)(hr / rows);
-  const bf16_t* src = r < a.d_nope
-                          ? (const bf16_t*)a.w_uk + ((size_t)h * a.d_nope + r) * a.d_c + i
-                          : (const bf16_t*)a.w_uv + ((size_t)h * a.d_v + (r - a.d_nope)) * a.d_c + i;
-  const bf16x8 v = ld_bf16x8(src);
-  typename Elem<E>::v8 o;
-#pragma unroll
-  for (int t = 0; t < 8; ++t) o[t] = Elem<E>::from((float)v[t]);
-  *reinterpret_cast<typename Elem<E>::v8*>((E*)a.wx + idx) = o;
-}
 
 constexpr int kExpandWaves = 8;       // waves per workgroup (two per SIMD)
 // Head shape of the rebuild: d_nope = 96 content and d_rope = 32 positional
@@ -82,14 +60,40 @@ __global__ __launch_bounds__(kExpandWaves * 64) void expand_kv_kernel(ExpandArgs
   // groups of 8 chunks): the 16 lanes of a B-operand read, rows 0..15 at one
   // chunk, then touch 64 distinct banks.  Lane l of span sp fills LDS chunk
   // c = 64 sp + l: row c / CPR, position c % CPR of the rows of all tiles.
+  // The rows come straight from W^K_up,h and W^V_up,h (bf16): a bf16 ring
+  // copies them into LDS with direct loads, an fp16 ring converts them on the
+  // way (exact for these weights' range).
   {
-    const E* src = (const E*)a.wx + (size_t)h * kExpandTiles * TILE;
+    const bf16_t* src_k = (const bf16_t*)a.w_uk + (size_t)h * kExpandNope * DC;
+    const bf16_t* src_v = (const bf16_t*)a.w_uv + (size_t)h * kExpandDv * DC;
     lds_char* const wl = (lds_char*)wts;
-    for (int sp = w; sp < WSPANS; sp += kExpandWaves) {
+    constexpr int SPW = (WSPANS + kExpandWaves - 1) / kExpandWaves;  // spans per wave
+    auto chunk_src = [&](int sp) MLA_INLINE {
       const int c = sp * 64 + l;
       const int r = c / CPR, p = c - r * CPR;
       const int q = p ^ ((r >> 1) & 7);
-      global_to_lds16(src + r * DC + q * 8, wl + sp * 1024);
+      return (r < kExpandNope ? src_k + r * DC : src_v + (r - kExpandNope) * DC) + q * 8;
+    };
+    if constexpr (__is_same(E, bf16_t)) {
+      for (int sp = w; sp < WSPANS; sp += kExpandWaves) global_to_lds16(chunk_src(sp), wl + sp * 1024);
+    } else {
+      // every load of the wave first, then the conversions and LDS stores
+      bf16x8 v[SPW];
+#pragma unroll
+      for (int j = 0; j < SPW; ++j) {
+        const int sp = w + j * kExpandWaves;
+        v[j] = ld_bf16x8(chunk_src(sp < WSPANS ? sp : w));
+      }
+#pragma unroll
+      for (int j = 0; j < SPW; ++j) {
+        const int sp = w + j * kExpandWaves;
+        if (sp < WSPANS) {
+          V8 o;
+#pragma unroll
+          for (int t = 0; t < 8; ++t) o[t] = Elem<E>::from((float)v[j][t]);
+          *reinterpret_cast<V8*>(wts + (size_t)(sp * 64 + l) * 8) = o;
+        }
+      }
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -183,13 +187,6 @@ int expand_splits(int n_h, int B, int Lk) {
 
 template <typename E, int DC>
 hipError_t launch_expand_dc(const ExpandArgs& a, hipStream_t s) {
-  {
-    const int64_t n = (int64_t)a.n_h * (a.d_nope + a.d_v) * a.d_c / 8;
-    hipLaunchKernelGGL(weights_to_cache_kernel<E>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
-                       s, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
   const int splits = expand_splits(a.n_h, a.B, a.Lk);
   const int kpb = ((a.Lk + splits - 1) / splits + 31) / 32 * 32;
   dim3 grid((unsigned)((a.Lk + kpb - 1) / kpb), (unsigned)a.n_h, (unsigned)a.B);

@@ -246,20 +246,18 @@ DenseLayout dense_layout(const mla_cache* h, int32_t Lq, int64_t Lk = -1) {
   return L;
 }
 
-// Expand-then-attend workspace: converted up-projections, the expanded
-// per-head keys and values of the window, then the per-head attention
-// workspace of the dense path.
+// Expand-then-attend workspace: the expanded per-head keys and values of
+// the window, then the per-head attention workspace of the dense path.
 struct ExpandLayout {
   DenseLayout dense;
-  size_t wx_off, kv_off, base, total;
+  size_t kv_off, base, total;
 };
 
 ExpandLayout expand_layout(const mla_cache* h, int32_t Lq, int64_t Lk = -1) {
   const mla_layer_config& c = h->cfg;
   ExpandLayout L;
   L.dense = dense_layout(h, Lq, Lk);
-  L.wx_off = 0;
-  L.kv_off = round_up((size_t)c.n_heads * (c.d_nope + c.d_v) * c.d_c * 2, kAlign);
+  L.kv_off = 0;
   L.base = L.kv_off + round_up((size_t)c.batch * c.window_frames * tokens_per_frame(c) * 2 *
                                     c.n_heads * (c.d_nope + c.d_rope) * 2,
                                 kAlign);
@@ -575,7 +573,6 @@ mla_status mla_attend(mla_cache* h, const void* q, int64_t q_token0, int32_t Lq,
     e.ring = h->storage;
     e.w_uk = w_uk;
     e.w_uv = w_uv;
-    e.wx = ws + X.wx_off;
     e.kv = ws + X.kv_off;
     e.B = c.batch;
     e.n_h = c.n_heads;

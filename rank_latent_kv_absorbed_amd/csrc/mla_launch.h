@@ -150,6 +150,18 @@ MLA_HD inline int sched_block_steps(const Schedule& s, int g) {
   return n;
 }
 
+// Logical block of hardware workgroup hw.  Workgroups are dealt round-robin
+// to the kDies accelerator dies (die hw % kDies), each with its own L2; die x
+// runs the contiguous logical blocks [O_x, O_x + c_x), so consecutive row
+// groups - the same head on the per-head path, whose blocks read the same key
+// and value tiles in lockstep - share one L2 instead of spreading over all.
+constexpr int kDies = 8;
+MLA_HD inline int sched_block_of(const Schedule& s, int hw) {
+  const int nb = s.n_blocks, q = nb / kDies, r = nb % kDies;
+  const int x = hw % kDies, k = hw / kDies;
+  return x * q + (x < r ? x : r) + k;
+}
+
 // Step i (0 <= i < sched_block_steps(s, g)) of block g.
 MLA_HD inline StepInfo sched_decode(const Schedule& s, int g, int i) {
   StepInfo r;
@@ -283,7 +295,6 @@ struct ExpandArgs {
   const void* ring;       // [B][ring_rows][d_c + d_rope] cache type
   const void* w_uk;       // [n_h][d_nope][d_c] bf16
   const void* w_uv;       // [n_h][d_v][d_c] bf16
-  void* wx;               // workspace [n_h][d_nope + d_v][d_c] cache type
   void* kv;               // workspace [B][Lk][2][n_h][d_nope + d_rope] cache type
   int B, n_h, d_nope, d_rope, d_c, d_v;
   int64_t ring_rows;

@@ -127,12 +127,12 @@ void fake_mha_info(long long* o) {
   memcpy(o, v, sizeof(v));
 }
 // The last expand: B, ring_rows, key_slot0, Lk, n_h, d_nope, d_rope, d_c, d_v,
-// cache_type, then the wx, kv, ring and w_uk pointers as integers.
+// cache_type, then the kv, ring and w_uk pointers as integers.
 void fake_expand_info(long long* o) {
   const mla::ExpandArgs& a = g_expand;
-  long long v[14] = {a.B, a.ring_rows, a.key_slot0, a.Lk, a.n_h, a.d_nope, a.d_rope, a.d_c, a.d_v,
-                     a.cache_type, (long long)(intptr_t)a.wx, (long long)(intptr_t)a.kv,
-                     (long long)(intptr_t)a.ring, (long long)(intptr_t)a.w_uk};
+  long long v[13] = {a.B, a.ring_rows, a.key_slot0, a.Lk, a.n_h, a.d_nope, a.d_rope, a.d_c, a.d_v,
+                     a.cache_type, (long long)(intptr_t)a.kv, (long long)(intptr_t)a.ring,
+                     (long long)(intptr_t)a.w_uk};
   memcpy(o, v, sizeof(v));
 }
 // The last dense attend's ring_rows, d_h, ring, qrot, opart, ml, q, out pointers and qscale*1e6.

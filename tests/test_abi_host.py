@@ -346,10 +346,10 @@ def test_attend_arguments_and_workspace(sim):
 
 
 def _expand_info(L):
-    a = (ctypes.c_longlong * 14)()
+    a = (ctypes.c_longlong * 13)()
     L.fake_expand_info(a)
     keys = ["B", "ring_rows", "key_slot0", "Lk", "n_h", "d_nope", "d_rope", "d_c", "d_v",
-            "cache_type", "wx", "kv", "ring", "w_uk"]
+            "cache_type", "kv", "ring", "w_uk"]
     return dict(zip(keys, list(a)))
 
 
@@ -409,12 +409,11 @@ def test_expand_attend_arguments_and_workspace(sim):
         assert sim.mla_cache_set_state(h, oldest, newest) == 0
         Lk = (newest - oldest + 1) * 1560
         need = sim.mla_attend_workspace_bytes(h, Lq, 0)
-        wx = 12 * 224 * 192 * 2
         kv = 21 * 1560 * 2 * 12 * 128 * 2                 # sized for the full window
         shape = expected_shape(Lq, 32)
         lq_pad = -(-Lq // shape[0]) * shape[0]
         R = 12 * lq_pad
-        assert need >= wx + kv + R * 128 * 2 + R * 128 * 4 + R * 8
+        assert need >= kv + R * 128 * 2 + R * 128 * 4 + R * 8
         assert sim.mla_attend(h, P(FAKE_PTR), 0, Lq, P(FAKE_PTR), P(FAKE_PTR), P(FAKE_PTR), 0,
                               P(ws), 256, None) == 7
         n = sim.fake_count()
@@ -427,7 +426,7 @@ def test_expand_attend_arguments_and_workspace(sim):
         assert (e["n_h"], e["d_nope"], e["d_rope"], e["d_c"], e["d_v"], e["cache_type"]) == \
             (12, 96, 32, 192, 128, 2)
         assert e["ring"] == FAKE_STORAGE and e["w_uk"] == FAKE_PTR + 256
-        assert e["wx"] == ws and e["kv"] >= ws + wx and e["kv"] % 256 == 0
+        assert e["kv"] == ws
         m = _mha_info(sim)
         p = _mha_ptrs(sim)
         assert (m["key_slot0"], m["Lk"], m["Lq"], m["q_token0"]) == (0, Lk, Lq, 77)
