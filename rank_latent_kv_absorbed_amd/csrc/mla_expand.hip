@@ -55,11 +55,13 @@ __global__ __launch_bounds__(kExpandWaves * 64) void expand_kv_kernel(ExpandArgs
   const int kend = kbeg + keys_per_block < a.Lk ? kbeg + keys_per_block : a.Lk;
   E* st = stg[w];
 
-  // The head's weight tiles: rows [32 t, 32 t + 32) of its converted matrix.
-  // In LDS, chunk q of tile row r sits at q ^ ((r >> 1) & 7) (inside aligned
-  // groups of 8 chunks): the 16 lanes of a B-operand read, rows 0..15 at one
-  // chunk, then touch 64 distinct banks.  Lane l of span sp fills LDS chunk
-  // c = 64 sp + l: row c / CPR, position c % CPR of the rows of all tiles.
+  // The head's weight tiles: rows [32 t, 32 t + 32) of its [d_nope + d_v][d_c]
+  // matrix, row m of a tile in LDS holding matrix row 32 t + 16 ((m >> 2) & 1)
+  // + 4 (m >> 3) + (m & 3) (see the products below).  In LDS, chunk q of tile
+  // row r sits at q ^ ((r >> 1) & 7) (inside aligned groups of 8 chunks): the
+  // 16 lanes of an operand read, rows 0..15 at one chunk, then touch 64
+  // distinct banks.  Lane l of span sp fills LDS chunk c = 64 sp + l: row
+  // c / CPR, position c % CPR of the rows of all tiles.
   // The rows come straight from W^K_up,h and W^V_up,h (bf16): a bf16 ring
   // copies them into LDS with direct loads, an fp16 ring converts them on the
   // way (exact for these weights' range).
@@ -72,7 +74,9 @@ __global__ __launch_bounds__(kExpandWaves * 64) void expand_kv_kernel(ExpandArgs
       const int c = sp * 64 + l;
       const int r = c / CPR, p = c - r * CPR;
       const int q = p ^ ((r >> 1) & 7);
-      return (r < kExpandNope ? src_k + r * DC : src_v + (r - kExpandNope) * DC) + q * 8;
+      const int m = r & 31;
+      const int wr = (r & ~31) + 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3);
+      return (wr < kExpandNope ? src_k + wr * DC : src_v + (wr - kExpandNope) * DC) + q * 8;
     };
     if constexpr (__is_same(E, bf16_t)) {
       for (int sp = w; sp < WSPANS; sp += kExpandWaves) global_to_lds16(chunk_src(sp), wl + sp * 1024);
@@ -99,68 +103,125 @@ __global__ __launch_bounds__(kExpandWaves * 64) void expand_kv_kernel(ExpandArgs
     __syncthreads();
   }
 
-  // B-operand read: lane (col lo, hi) takes chunk 2 ks + hi of tile row lo.
+  // Products D[col][key] = W[col][:] . c[key][:] on 32x32x16 MFMA: weight
+  // rows are the A operand (lane (lo, hi) reads chunk 2 ks + hi of LDS tile
+  // row lo), latent rows the B operand.  Lane (lo, hi) receives D rows
+  // 8 g + 4 hi + j (g, j < 4) of key lo; by the row order of the LDS tiles
+  // those are output columns 16 hi + 4 g + j, so accumulator r holds column
+  // 16 hi + r of the lane's key: 16 consecutive columns, staged as two 16-byte
+  // LDS writes.
   const int rsw = (lo >> 1) & 7;
   // Staged block: key kk's 128 columns at st[kk * DH ..]; column chunk q
-  // (8 columns) of key kk sits at chunk q ^ (kk & 15), so the two half-waves
-  // of a tile store (keys 4 apart) and the key-row reads spread over the banks.
-  auto stage_at = [&](int kk, int col) __attribute__((always_inline)) {
+  // (8 columns) of key kk sits at chunk q ^ (kk & 15), so the 16-byte stores
+  // of 16 consecutive keys and the key-row reads spread over the banks.
+  auto stage_at = [&](int kk, int col) MLA_INLINE {
     return kk * DH + ((((col >> 3) ^ kk) & 15) << 3) + (col & 7);
   };
-  // Write the staged 32 x 128 block of keys k0.. as part `part` (0 keys,
-  // 1 values): 16 lanes per key row, 16 bytes each.
-  auto flush = [&](int k0, int part) __attribute__((always_inline)) {
+  auto mma = [&](int t, const V8 (&c)[NKS]) MLA_INLINE {
+    const E* wrow = wts + t * TILE + lo * DC;
+    V8 wf[NKS];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = i * 64 + l;
-      const int kk = c >> 4, q = c & 15;
-      const V8 v = *reinterpret_cast<const V8*>(st + kk * DH + ((q ^ kk) & 15) * 8);
-      const int kg = k0 + kk;
-      if (kg < kend)
-        *reinterpret_cast<V8*>((E*)a.kv + ((((size_t)b * a.Lk + kg) * 2 + part) * a.n_h + h) * DH +
-                               q * 8) = v;
+    for (int ks = 0; ks < NKS; ++ks) wf[ks] = ld8<E>(wrow + 8 * ((2 * ks + hi) ^ rsw));
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) acc = Elem<E>::mfma(wf[ks], c[ks], acc);
+    return acc;
+  };
+  // Tile t's columns: key columns 32 t for t < 3, value columns 32 (t - 3).
+  auto stage = [&](int t, const f32x16& acc) MLA_INLINE {
+    const int c0 = t < kExpandKTiles ? 32 * t : 32 * (t - kExpandKTiles);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      V8 o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = Elem<E>::from(acc[8 * u + e]);
+      *reinterpret_cast<V8*>(st + stage_at(lo, c0 + 16 * hi + 8 * u)) = o;
     }
   };
-  // This lane's latent row of the 32-key block at k0 (A operand: key lo,
+  // Output rows: key j of sequence b is a record of 2 parts x n_h heads x DH
+  // elements.  Flush i of a staged block writes keys 4 i + l / 16, 16 bytes
+  // at column chunk l % 16 per lane: a uniform base per (block, part, i) plus
+  // one 32-bit lane offset (a sequence's expanded window stays below 2^31
+  // elements, checked on the host).
+  const size_t rec = (size_t)2 * a.n_h * DH;
+  E* const kv_b = (E*)a.kv + (size_t)b * a.Lk * rec + (size_t)h * DH;
+  const uint32_t fl_off = (uint32_t)(((l >> 4) * rec + (l & 15) * 8) * sizeof(E));
+  auto flush = [&](int k0, int part) MLA_INLINE {
+    const char* base = (const char*)(kv_b + (size_t)k0 * rec + (size_t)part * a.n_h * DH);
+    const bool whole = k0 + 32 <= kend;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int kk = 4 * i + (l >> 4), q = l & 15;
+      const V8 v = *reinterpret_cast<const V8*>(st + kk * DH + ((q ^ kk) & 15) * 8);
+      char* p = (char*)base + (size_t)i * 4 * rec * sizeof(E) + fl_off;
+      if (whole || k0 + kk < kend) *reinterpret_cast<V8*>(p) = v;
+    }
+  };
+  // This lane's latent row of the 32-key block at k0 (B operand: key lo,
   // depth 16 ks + 8 hi .. + 8, then k^R as 8-column pieces 8 hi + 16 j);
-  // keys past the range load key k0's row (never written out).
+  // keys past the range load key k0's row (never written out).  Ring offsets
+  // of one sequence fit 32 bits (checked when the cache is created).
   constexpr int NR = kExpandRope / 16;  // k^R pieces per lane
-  auto load_row = [&](int k0, V8 (&c)[NKS], V8 (&r)[NR]) __attribute__((always_inline)) {
+  constexpr int RW = DC + kExpandRope;  // elements per cached row
+  const char* const ring_b = (const char*)a.ring + (size_t)b * a.ring_rows * RW * sizeof(E);
+  const int rows = (int)a.ring_rows;
+  auto load_row = [&](int k0, V8 (&c)[NKS], V8 (&r)[NR]) MLA_INLINE {
     const int key = k0 + lo < kend ? k0 + lo : k0;
-    int64_t slot = a.key_slot0 + key;
-    if (slot >= a.ring_rows) slot -= a.ring_rows;
-    const E* crow = (const E*)a.ring + ((size_t)b * a.ring_rows + slot) * (DC + kExpandRope);
+    int slot = (int)a.key_slot0 + key;
+    slot = slot >= rows ? slot - rows : slot;
+    const char* p = ring_b + ((uint32_t)slot * (uint32_t)(RW * sizeof(E)) + 16 * hi);
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) c[ks] = ld8<E>(crow + 16 * ks + 8 * hi);
+    for (int ks = 0; ks < NKS; ++ks) c[ks] = *reinterpret_cast<const V8*>(p + 32 * ks);
 #pragma unroll
-    for (int j = 0; j < NR; ++j) r[j] = ld8<E>(crow + DC + 16 * j + 8 * hi);
+    for (int j = 0; j < NR; ++j) r[j] = *reinterpret_cast<const V8*>(p + 2 * DC + 32 * j);
   };
 
-  for (int k0 = kbeg + 32 * w; k0 < kend; k0 += 32 * kExpandWaves) {
-    V8 cf[NKS], rf[NR];
-    load_row(k0, cf, rf);
-
+  // Each wave walks its 32-key blocks with the next block's rows in flight.
+  // The seven weight tiles run as a two-deep pipeline: tile t + 1's products
+  // are issued before tile t's results are converted and staged.
+  int k0 = kbeg + 32 * w;
+  V8 cf[NKS], rf[NR];
+  if (k0 < kend) load_row(k0, cf, rf);
+  for (; k0 < kend; k0 += 32 * kExpandWaves) {
+    V8 cn[NKS], rn[NR];
+    const int k1 = k0 + 32 * kExpandWaves;
+    if (k1 < kend) load_row(k1, cn, rn);
     // k^R into columns d_nope .. 127 of the staged key block
 #pragma unroll
     for (int j = 0; j < NR; ++j)
       *reinterpret_cast<V8*>(st + stage_at(lo, kExpandNope + 16 * j + 8 * hi)) = rf[j];
-#pragma unroll 1
-    for (int t = 0; t < kExpandTiles; ++t) {
-      f32x16 acc;
+    static_assert(kExpandTiles == 7 && kExpandKTiles == 3, "pipeline below is written for 3 + 4 tiles");
+    // (Scheduling fences keep each tile's operand reads next to its
+    // products; hoisted, the reads of all tiles would not fit in registers.)
+    f32x16 acc0 = mma(0, cf);
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 acc1 = mma(1, cf);
+    stage(0, acc0);
+    __builtin_amdgcn_sched_barrier(0);
+    acc0 = mma(2, cf);
+    stage(1, acc1);
+    __builtin_amdgcn_sched_barrier(0);
+    acc1 = mma(3, cf);
+    stage(2, acc0);
+    flush(k0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    acc0 = mma(4, cf);
+    stage(3, acc1);
+    __builtin_amdgcn_sched_barrier(0);
+    acc1 = mma(5, cf);
+    stage(4, acc0);
+    __builtin_amdgcn_sched_barrier(0);
+    acc0 = mma(6, cf);
+    stage(5, acc1);
+    __builtin_amdgcn_sched_barrier(0);
+    stage(6, acc0);
+    flush(k0, 1);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-      const E* wrow = wts + t * TILE + lo * DC;
+    for (int ks = 0; ks < NKS; ++ks) cf[ks] = cn[ks];
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
-        acc = Elem<E>::mfma(cf[ks], ld8<E>(wrow + 8 * ((2 * ks + hi) ^ rsw)), acc);
-      // D[key][col]: lane holds column c0 + lo of keys 8 (r / 4) + 4 hi + r % 4.
-      const int c0 = t < kExpandKTiles ? 32 * t : 32 * (t - kExpandKTiles);
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        st[stage_at(8 * (r >> 2) + 4 * hi + (r & 3), c0 + lo)] = Elem<E>::from(acc[r]);
-      if (t == kExpandKTiles - 1) flush(k0, 0);
-      if (t == kExpandTiles - 1) flush(k0, 1);
-    }
+    for (int j = 0; j < NR; ++j) rf[j] = rn[j];
   }
 }
 
