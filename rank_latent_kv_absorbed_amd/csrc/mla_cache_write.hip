@@ -4,108 +4,186 @@
 // to its ring slot.  The same kernel serves the dense comparison cache (K and
 // V of every head; K rotated per head).
 //
-// 2-byte path (bf16 inputs; bf16 or fp16 ring): a block computes one tile of
-// 32 tokens x 32 output columns, its four waves each taking a quarter of the
-// hidden dimension (so a tile's long dependent MFMA chain is four short ones
-// running on four SIMDs, and four times as many waves hide the load latency);
-// the quarters are summed through LDS and each wave finishes 8 of the tile's
-// 32 columns.  The product is laid out transposed (columns on the MFMA M
-// side, tokens on the N side) so that a lane holds one token and both
-// elements of every rotary pair.
-#include "mla_device.h"
-
-#define MLA_INLINE __attribute__((always_inline))
+// 2-byte path (bf16 inputs; bf16 or fp16 ring): a workgroup owns 32 tokens
+// and NT <= 8 32-column tiles of the output, one tile per wave (a d_c = 192
+// latent row [c | k^R] is 7 tiles: one workgroup of 7 when there are enough
+// tokens to fill the chip, else two of 4).  The hidden dimension is walked in
+// 64-element chunks through a ring of three LDS stages, each holding the
+// chunk's 32 token rows and NT * 32 weight rows at 128 bytes per row, filled
+// with direct global->LDS loads that cover whole 128-byte lines (the x tile
+// is read from memory once, every weight row once per workgroup).  Products
+// are D[col][token] = W[col][:] . x[token][:] on 32x32x16 MFMA with the
+// weights as the A operand; the weight rows of a tile are staged in a
+// permuted order so that lane (token lo, hi) ends up holding 16 consecutive
+// output columns of its token, every rotary pair whole, which it rotates,
+// rounds and writes as two 16-byte pieces of the token's ring row.
+#include "mla_attn_core.h"
 
 namespace mla {
 
 namespace {
 
-constexpr int kSplitK = 4;     // waves per block = hidden-dimension quarters
+constexpr int kChunk = 64;  // hidden elements per staged chunk (128-byte rows)
 
-template <typename E>
-__global__ __launch_bounds__(kSplitK * 64) void cache_write_bf16_kernel(CacheWriteArgs a) {
-  __shared__ float red[kSplitK][16][64];
+template <typename E, int NT>
+__global__ __launch_bounds__(NT * 64) void cache_write_bf16_kernel(CacheWriteArgs a) {
+  constexpr int RB = kChunk * 2;              // staged bytes per row
+  constexpr int ROWS = 32 + 32 * NT;          // token rows, then weight rows
+  constexpr int SB = ROWS * RB;               // bytes per stage
+  constexpr int SPANS = SB / 1024;            // 1-KiB load spans per stage (8 rows each)
+  constexpr int SPW = (SPANS + NT - 1) / NT;  // spans per wave; surplus slots repeat the last span
+  static_assert(SB % 1024 == 0, "whole spans per stage");
+  __shared__ __attribute__((aligned(1024))) char st0[SB], st1[SB], st2[SB];
+  __shared__ float2 rcs[32][kMaxRopePairs];  // cos, sin per (token, rotary pair)
+  __shared__ int64_t rowoff[32];             // ring row of each token (elements)
   const int tid = threadIdx.x;
-  const int w = tid >> 6, l = tid & 63, lo = l & 31, hi = l >> 5;
-  const int ct = blockIdx.y;               // column tile
-  const int64_t tok = (int64_t)blockIdx.x * 32 + lo;
-  const bool valid = tok < a.M;
-  const int col = ct * 32 + lo;            // W row this lane feeds
-  // k-order: step 4g + s gives lane half hi the 8 elements
-  // [64 g + 32 hi + 8 s, +8): over four steps a lane reads 64 contiguous
-  // bytes of its row, and the wave covers whole 128-byte lines.
-  const bf16_t* xrow = (const bf16_t*)a.x + (valid ? tok : 0) * a.hidden + 32 * hi;
-  const bf16_t* wrow = (col < a.w_split ? (const bf16_t*)a.w + (int64_t)col * a.hidden
-                                        : (const bf16_t*)a.w2 + (int64_t)(col - a.w_split) * a.hidden) +
-                       32 * hi;
-  const int ng = a.hidden / 64;            // groups of four 16-deep steps
-  const int g0 = w * ng / kSplitK, g1 = (w + 1) * ng / kSplitK;  // this wave's groups
+  const int w = NT == 1 ? 0 : __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63, lo = l & 31, hi = l >> 5;
+  const int64_t tok0 = (int64_t)blockIdx.x * 32;
+  const int col0 = blockIdx.y * 32 * NT;
 
-  // A ring of kDepth groups in flight: the loads of group g + kDepth - 1 go
-  // out before the products of group g.
-  constexpr int kDepth = 3;
-  bf16x8 xf[kDepth][4], wf[kDepth][4];
-  auto load_group = [&](int gi, int slot) MLA_INLINE {
+  // Staged row r, 16-byte slot s holds chunk s ^ ((r >> 1) & 7) of the row's
+  // 128 bytes: the 16 lanes of an operand read (rows 0..15 at one chunk)
+  // then touch 64 distinct banks.  Rows 0..31 are tokens tok0.. (past the
+  // last token: the last token again, never written out); row 32 + 32 t + m
+  // is weight row col0 + 32 t + 16 ((m >> 2) & 1) + 4 (m >> 3) + (m & 3).
+  // Lane l of span sp fills row 8 sp + l / 8, slot l % 8.
+  const bf16_t* const xg = (const bf16_t*)a.x;
+  const char* src[SPW];
 #pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) {
-      xf[slot][s4] = valid ? ld_bf16x8(xrow + gi * 64 + 8 * s4) : zero_bf16x8();
-      wf[slot][s4] = ld_bf16x8(wrow + gi * 64 + 8 * s4);
+  for (int j = 0; j < SPW; ++j) {
+    const int sp = w + j * NT < SPANS ? w + j * NT : SPANS - 1;
+    const int row = 8 * sp + (l >> 3);
+    const int q = (l & 7) ^ ((row >> 1) & 7);
+    const bf16_t* p;
+    if (row < 32) {
+      const int64_t t = tok0 + row < a.M ? tok0 + row : a.M - 1;
+      p = xg + t * a.hidden;
+    } else {
+      const int m = row - 32, mm = m & 31;
+      int col = col0 + (m & ~31) + 16 * ((mm >> 2) & 1) + 4 * (mm >> 3) + (mm & 3);
+      col = col < a.width ? col : a.width - 1;  // tiles past the row: loaded, never written
+      p = col < a.w_split ? (const bf16_t*)a.w + (int64_t)col * a.hidden
+                          : (const bf16_t*)a.w2 + (int64_t)(col - a.w_split) * a.hidden;
+    }
+    src[j] = (const char*)(p + q * 8);
+  }
+  // Workgroups walk the chunks from different starting points: the rows
+  // are hidden * 2 bytes apart, so one chunk of every weight row sits in a
+  // few L2 channels, which workgroups in lockstep would all hit at once.
+  const int NC = a.hidden / kChunk;
+  const int rot = (int)(blockIdx.x % (unsigned)NC);
+  auto issue = [&](int c, char* stg) MLA_INLINE {
+    lds_char* const ls = (lds_char*)stg;
+    const int cr = c + rot < NC ? c + rot : c + rot - NC;
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+      const int sp = w + j * NT < SPANS ? w + j * NT : SPANS - 1;
+      global_to_lds16(src[j] + cr * RB, ls + sp * 1024);
     }
   };
+
+  // Operand reads for k-step ks of a chunk: chunk 2 ks + hi of token row lo
+  // (B) and of the wave's weight row lo (A).
+  const int sw = (lo >> 1) & 7;
+  int xo[4], wo[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    xo[ks] = lo * RB + 16 * ((2 * ks + hi) ^ sw);
+    wo[ks] = (32 + 32 * w + lo) * RB + 16 * ((2 * ks + hi) ^ sw);
+  }
   f32x16 acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+  auto compute = [&](const char* stg) MLA_INLINE {
+    bf16x8 av[4], bv[4];
 #pragma unroll
-  for (int d = 0; d < kDepth - 1; ++d)
-    if (g0 + d < g1) load_group(g0 + d, d);
-  for (int gi = g0; gi < g1; gi += kDepth) {
+    for (int ks = 0; ks < 4; ++ks) {
+      av[ks] = *reinterpret_cast<const bf16x8*>(stg + wo[ks]);
+      bv[ks] = *reinterpret_cast<const bf16x8*>(stg + xo[ks]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int d = 0; d < kDepth; ++d) {
-      if (gi + d < g1) {
-        if (gi + d + kDepth - 1 < g1) load_group(gi + d + kDepth - 1, (d + kDepth - 1) % kDepth);
-#pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) acc = mfma32(wf[d][s4], xf[d][s4], acc);
-      }
+    for (int ks = 0; ks < 4; ++ks) acc = mfma32(av[ks], bv[ks], acc);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // Chunk c is computed from its stage; then, once this wave's loads of
+  // chunk c + 1 are in (loads retire in order; chunk c + 2 stays in flight),
+  // a barrier publishes every wave's loads of it and frees the stage just
+  // read, which is refilled with chunk c + 3 (past the end: the last chunk
+  // again, into a stage nobody reads any more).  Every step is the same
+  // straight-line code and each stage is refilled right after it was read,
+  // so the compiler's own tracking of the loads into LDS adds no waits.
+  auto step = [&](int c, char* cur) MLA_INLINE {
+    compute(cur);
+    wait_vmem(SPW);
+    lds_barrier();
+    issue(c + 3 < NC ? c + 3 : NC - 1, cur);
+  };
+  issue(0, st0);
+  issue(NC > 1 ? 1 : 0, st1);
+  issue(NC > 2 ? 2 : 0, st2);
+  // While the first chunks load: each token's ring row, and cos / sin of
+  // every rotary pair of every token (rotated columns c use pair
+  // ((c - rot_begin) % rot_group) / 2).
+  const int npairs = a.rot_end > a.rot_begin ? a.rot_group / 2 : 0;
+  for (int e = tid; e < 32 * (npairs + 1); e += NT * 64) {
+    const int r = e & 31, p = (e >> 5) - 1;
+    const int64_t t = tok0 + r < a.M ? tok0 + r : a.M - 1;
+    const int64_t b = t / a.tokens_per_batch;
+    const int i = (int)(t - b * a.tokens_per_batch);
+    const int64_t frame = a.frame0 + i / a.T;
+    const int tau = i % a.T;
+    if (p < 0) {
+      rowoff[r] = (b * a.ring_rows + (frame % a.W) * a.T + tau) * a.width;
+    } else {
+      TokPos pos;
+      pos.f = frame;
+      pos.y = tau / a.grid_w;
+      pos.x = tau - pos.y * a.grid_w;
+      float cs, sn;
+      rope_cos_sin(pos_axis(pos, a.rope.axis[p]) * a.rope.inv_freq[p], cs, sn);
+      rcs[r][p] = make_float2(cs, sn);
     }
   }
-  // Sum the quarters: every wave stores its partial tile; wave w then owns
-  // accumulator group g = w (columns 8 g + 4 hi .. + 4 of every token).
-#pragma unroll
-  for (int r = 0; r < 16; ++r) red[w][r][l] = acc[r];
-  __syncthreads();
-  if (!valid) return;
-  const int g = w;
-  float v[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    float sum = 0.0f;
-#pragma unroll
-    for (int q = 0; q < kSplitK; ++q) sum += red[q][4 * g + k][l];
-    v[k] = sum;
+  wait_vmem(2 * SPW);
+  lds_barrier();
+  int c = 0;
+  for (; c + 3 <= NC; c += 3) {
+    step(c, st0);
+    step(c + 1, st1);
+    step(c + 2, st2);
   }
+  if (c < NC) step(c, st0);
+  if (c + 1 < NC) step(c + 1, st1);
+  // No load into LDS may still be in flight when the workgroup ends.
+  __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
 
-  const int64_t b = tok / a.tokens_per_batch;
-  const int i = (int)(tok - b * a.tokens_per_batch);
-  const int64_t frame = a.frame0 + i / a.T;
-  const int tau = i % a.T;
-  TokPos pos;
-  pos.f = frame;
-  pos.y = tau / a.grid_w;
-  pos.x = tau - pos.y * a.grid_w;
-  const int64_t slot = (frame % a.W) * a.T + tau;
-  E* dst = (E*)a.ring + (b * a.ring_rows + slot) * a.width;
-  const int c0 = ct * 32 + 8 * g + 4 * hi;
-  if (c0 >= a.rot_begin && c0 < a.rot_end) {
-    const int p0 = ((c0 - a.rot_begin) % a.rot_group) >> 1;
-    rope_pair(a.rope, p0, pos, v[0], v[1]);
-    rope_pair(a.rope, p0 + 1, pos, v[2], v[3]);
+  // Lane (lo, hi) holds columns cb .. cb + 15 of token tok0 + lo.
+  if (tok0 + lo >= a.M || col0 + 32 * w >= a.width) return;
+  const int cb = col0 + 32 * w + 16 * hi;
+  float v[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) v[r] = acc[r];
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const int c = cb + 2 * p;
+    if (c >= a.rot_begin && c < a.rot_end) {
+      const float2 t = rcs[lo][((c - a.rot_begin) % a.rot_group) >> 1];
+      const float ra = v[2 * p] * t.x - v[2 * p + 1] * t.y;
+      const float rb = v[2 * p] * t.y + v[2 * p + 1] * t.x;
+      v[2 * p] = ra;
+      v[2 * p + 1] = rb;
+    }
   }
-  typename Elem<E>::v4 o;
-  o[0] = Elem<E>::from(v[0]);
-  o[1] = Elem<E>::from(v[1]);
-  o[2] = Elem<E>::from(v[2]);
-  o[3] = Elem<E>::from(v[3]);
-  *reinterpret_cast<typename Elem<E>::v4*>(dst + c0) = o;
+  E* dst = (E*)a.ring + rowoff[lo] + cb;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    typename Elem<E>::v8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = Elem<E>::from(v[8 * u + e]);
+    *reinterpret_cast<typename Elem<E>::v8*>(dst + 8 * u) = o;
+  }
 }
 
 // fp32 path (small shapes): one thread per (token, column pair), plain fp32
@@ -145,11 +223,35 @@ __global__ __launch_bounds__(256) void cache_write_f32_kernel(CacheWriteArgs a) 
   dst[1] = y1;
 }
 
+template <typename E, int NT>
+hipError_t launch_nt(const CacheWriteArgs& a, hipStream_t s) {
+  dim3 grid((unsigned)((a.M + 31) / 32), (unsigned)((a.width / 32 + NT - 1) / NT));
+  hipLaunchKernelGGL((cache_write_bf16_kernel<E, NT>), grid, dim3(NT * 64), 0, s, a);
+  return hipGetLastError();
+}
+
+// Tiles per workgroup: a row's 32-column tiles split over the fewest
+// workgroups per token tile (at most 8 tiles each) that still give every
+// compute unit a workgroup; the last workgroup of a row may own fewer tiles
+// than waves.
 template <typename E>
 hipError_t launch_typed(const CacheWriteArgs& a, hipStream_t s) {
-  dim3 grid((unsigned)((a.M + 31) / 32), (unsigned)(a.width / 32));
-  hipLaunchKernelGGL(cache_write_bf16_kernel<E>, grid, dim3(kSplitK * 64), 0, s, a);
-  return hipGetLastError();
+  const int tiles = a.width / 32;
+  const int64_t token_tiles = (a.M + 31) / 32;
+  int groups = (tiles + 7) / 8;
+  const int cus = device_cu_count();
+  while (groups < tiles && token_tiles * groups < cus) ++groups;
+  const int nt = (tiles + groups - 1) / groups;
+  switch (nt) {
+    case 8: return launch_nt<E, 8>(a, s);
+    case 7: return launch_nt<E, 7>(a, s);
+    case 6: return launch_nt<E, 6>(a, s);
+    case 5: return launch_nt<E, 5>(a, s);
+    case 4: return launch_nt<E, 4>(a, s);
+    case 3: return launch_nt<E, 3>(a, s);
+    case 2: return launch_nt<E, 2>(a, s);
+    default: return launch_nt<E, 1>(a, s);
+  }
 }
 
 }  // namespace
