@@ -396,8 +396,8 @@ def test_attend_path_choice(sim):
 
 
 def test_expand_attend_arguments_and_workspace(sim):
-    """The expand path: workspace = converted weights, expanded window, dense
-    attention workspace, in that order and disjoint; the rebuild reads the
+    """The expand path: workspace = expanded window, dense attention
+    workspace, in that order and disjoint; the rebuild reads the
     resident keys from the ring, the dense attention reads the expanded window
     from key 0 with the latent path's scale and a rotation that leaves the
     d_nope content dimensions alone."""
