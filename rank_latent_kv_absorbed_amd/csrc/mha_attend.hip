@@ -84,9 +84,39 @@ __global__ __launch_bounds__(256) void mha_merge_kernel(MhaAttendArgs a, AttnCor
   const int h = (int)(r % a.n_h);
   const int b = (int)(r / a.n_h);
   const int row = h * c.rows_per_head + tok;
-  float acc[4];
-  merge_row_partials(c, a.d_h, b, row, 4 * c4, 4, acc);
-  f32x4 o = {acc[0], acc[1], acc[2], acc[3]};
+  const Schedule& sc = c.sched;
+  const int n_part = sched_group_slots(sc, b * sc.n_rg + row / sc.block_rows);
+  f32x4 o;
+  constexpr int kFew = 4;
+  if (n_part <= kFew) {
+    // Every slot's loads go out together (slots past n_part re-read slot 0
+    // and get weight 0), then the log-sum-exp combination.
+    f32x4 x[kFew];
+    float2 ml[kFew];
+#pragma unroll
+    for (int k = 0; k < kFew; ++k) {
+      const size_t prow = ((size_t)(k < n_part ? k : 0) * c.B + b) * c.R + row;
+      x[k] = *reinterpret_cast<const f32x4*>(c.opart + prow * a.d_h + 4 * c4);
+      ml[k] = *reinterpret_cast<const float2*>(c.ml + prow * 2);
+    }
+    float M = ml[0].x;
+#pragma unroll
+    for (int k = 1; k < kFew; ++k)
+      if (k < n_part) M = fmaxf(M, ml[k].x);
+    float L = 0.0f;
+    o = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int k = 0; k < kFew; ++k) {
+      const float wgt = k < n_part ? exp2_fast(ml[k].x - M) : 0.0f;
+      L += wgt * ml[k].y;
+      o += wgt * x[k];
+    }
+    o *= 1.0f / L;
+  } else {
+    float acc[4];
+    merge_row_partials(c, a.d_h, b, row, 4 * c4, 4, acc);
+    o = {acc[0], acc[1], acc[2], acc[3]};
+  }
   *reinterpret_cast<f32x4*>(a.out + (((size_t)b * a.Lq + tok) * a.n_h + h) * a.d_h + 4 * c4) = o;
 }
 
