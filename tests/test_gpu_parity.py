@@ -114,6 +114,35 @@ def test_cache_write_values_within_one_ulp(cache_dtype):
     assert np.mean(g == r) > 0.97
 
 
+@pytest.mark.parametrize("batch", [1, 2])
+def test_cache_write_wan_chunk_values_and_placement(batch):
+    """A 3-frame Wan chunk (4680 tokens per sequence) into the 21-frame ring:
+    at B = 1 each 32-token tile's 7 column tiles are split over two
+    workgroups of 4 (the 8th tile past the row is loaded but never written),
+    at B = 2 one workgroup of 7 takes them all.  Stored rows are the oracle's
+    rounded values or a neighbour (fp32 summation), and no slot outside the
+    chunk is touched."""
+    cfg = config("wan_window").with_(batch=batch)
+    run = LatentRun(cfg, poison=True)
+    f0 = cfg.chunk_frame0
+    x = run.write(f0, cfg.chunk_frames)
+    torch.cuda.synchronize()
+    got = run.gpu.ring().double().cpu().numpy()
+    ref = run.store
+    slot0 = (f0 % cfg.window_frames) * cfg.T
+    written = np.zeros(cfg.window_frames * cfg.T, bool)
+    written[slot0:slot0 + cfg.chunk_frames * cfg.T] = True
+    assert np.isnan(got[:, ~written]).all(), "kernel wrote outside the chunk's slots"
+    g, r = got[:, written], ref[:, written]
+    ulp = np.ldexp(1.0, np.frexp(np.abs(r))[1] - SIG_BITS[cfg.cache_dtype])
+    for b in range(batch):
+        mag = np.abs(x.double().numpy()[b]) @ np.abs(run.w["w_dkr"].double().numpy()).T
+        acc = cfg.hidden * 2.0 ** -24 * np.concatenate([mag[:, :cfg.d_c], np.repeat(
+            mag[:, cfg.d_c:].reshape(-1, cfg.d_rope // 2, 2).sum(-1), 2, axis=-1)], -1)
+        assert (np.abs(g[b] - r[b]) <= ulp[b] + acc).all(), f"sequence {b}"
+    assert np.mean(g == r) > 0.97
+
+
 @pytest.mark.parametrize("cache_dtype", ["f16", "bf16"])
 def test_rollout_ring_bit_exact_through_wraps(cache_dtype):
     """A 12-chunk rollout through a 5-frame window (the ring wraps four times):
