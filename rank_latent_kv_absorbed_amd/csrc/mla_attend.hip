@@ -497,6 +497,7 @@ hipError_t launch_core(const AttnCore& c, hipStream_t s) {
   }
   MLA_SHAPE(8, 64, 3, 32)
   MLA_SHAPE(4, 32, 4, 32)
+  MLA_SHAPE(4, 32, 4, 16)
   MLA_SHAPE(1, 32, 2, 32)
   MLA_SHAPE(1, 32, 2, 16)
 #undef MLA_SHAPE

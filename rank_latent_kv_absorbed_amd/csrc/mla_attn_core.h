@@ -166,9 +166,9 @@ void attn_core_kernel(AttnCore a) {
   constexpr int BR = NW * ROWS * RB;          // rows per row group (ROWS * RB per wave)
   constexpr int NKB = KT / ROWS;              // MFMA key blocks per tile
   constexpr int NPF = R16 ? 1 : 2 * NKB;      // probability operands per row block
-  static_assert(ROWS == 32 || (ROWS == 16 && NW == 1 && KT == 32 && RB == 1 && !PP &&
+  static_assert(ROWS == 32 || (ROWS == 16 && (NW == 1 || NW == 4) && KT == 32 && RB == 1 && !PP &&
                                DQK % 32 == 0 && DV % 16 == 0),
-                "16-row waves: one-wave blocks on 32-key tiles");
+                "16-row waves: one- or four-wave blocks on 32-key tiles");
   constexpr int KCH = DQK / 8;                // 16-byte chunks of K per key
   constexpr int CPK = SHARED_KV ? KCH : KCH + DV / 8;  // chunks staged per key
   constexpr int KSTR = CPK * 8;               // LDS row stride (elements)

@@ -61,7 +61,8 @@ struct CoreShape {
   int stages;
   int rows;
 };
-constexpr CoreShape kCoreShapes[] = {{8, 64, 3, 32}, {4, 32, 4, 32}, {1, 32, 2, 32}, {1, 32, 2, 16}};
+constexpr CoreShape kCoreShapes[] = {{8, 64, 3, 32}, {4, 32, 4, 32}, {1, 32, 2, 32}, {1, 32, 2, 16},
+                                     {4, 32, 4, 16}};
 constexpr int kCoreMaxBlockRows = 256;
 
 // Shape for `rows` query rows of one row unit (latent: Lq * n_h rows of a
@@ -69,6 +70,7 @@ constexpr int kCoreMaxBlockRows = 256;
 inline CoreShape core_shape_for_rows(int64_t rows) {
   if (rows <= 16) return kCoreShapes[3];
   if (rows <= 32) return kCoreShapes[2];
+  if (rows <= 64) return kCoreShapes[4];
   if (rows <= 128) return kCoreShapes[1];
   return kCoreShapes[0];
 }

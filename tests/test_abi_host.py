@@ -134,6 +134,8 @@ def expected_shape(rows, chunks_per_key=28):
         br, kt, ns, waves = 16, 32, 2, 1                # one wave of 16 rows (16x16x32 MFMAs)
     elif rows <= 32:
         br, kt, ns, waves = 32, 32, 2, 1
+    elif rows <= 64:
+        br, kt, ns, waves = 64, 32, 4, 4               # four waves of 16 rows
     elif rows <= 128:
         br, kt, ns, waves = 128, 32, 4, 4
     else:
@@ -144,7 +146,7 @@ def expected_shape(rows, chunks_per_key=28):
 
 def blocks_per_cu(shape, chunks_per_key):
     br, kt, ns = shape
-    waves = 1 if br <= 32 else br // 32
+    waves = 1 if br <= 32 else (4 if br == 64 else br // 32)
     return min(160 * 1024 // (ns * kt * chunks_per_key * 16), 8 // waves)
 
 
