@@ -40,9 +40,17 @@
  *     [c (d_c) | k^R rotated (d_rope)]; dense rows hold [K: n_h x d_h | V: n_h x d_h].
  *   - x, q and weights have the config's dtype (bf16 or fp32); the ring stores
  *     cache_dtype (fp32 with fp32 inputs; bf16 or fp16 with bf16 inputs: two
- *     bytes per stored scalar either way).  Prepared queries and softmax
- *     weights enter the matrix units in the cache type; every sum is fp32 and
- *     the attention output is always fp32.
+ *     bytes per stored scalar either way, the per-token count of method
+ *     item 4 at the 2-byte width the problem definition's ~6.0 GB implies).
+ *     Prepared queries and softmax weights enter the matrix units in the
+ *     cache type; with a bf16 ring each of them is carried as two bf16 parts
+ *     (the value and the bf16 rounding of its remainder; twice the matrix
+ *     work), since bf16's 8 significant bits alone move the output by about
+ *     1e-3 of its size.  Every sum is fp32 and the attention output is fp32.
+ *   - Range: an fp16 ring holds magnitudes up to 65504; a computed c or k^R
+ *     value beyond that is stored as +-infinity (IEEE round to nearest),
+ *     and attention over such a row returns NaN for its sequence.  bf16 and
+ *     fp32 rings have the fp32 exponent range.
  *
  * Ownership: the caller owns every device buffer (ring storage, weights,
  * activations, outputs, workspace).  The library owns only the small host
@@ -109,7 +117,8 @@ typedef struct {
 
 typedef struct mla_cache mla_cache; /* opaque host handle, one per cached layer */
 
-/* Bytes of ring storage for one latent layer:
+/* Bytes of ring storage for one latent layer (method item 4: d_c + d_rope
+ * scalars per token instead of 2 * n_h * d_h):
  * batch * window_frames * T * (d_c + d_rope) * sizeof(cache_dtype).  0 on a bad config. */
 size_t mla_cache_bytes(const mla_layer_config* cfg);
 
@@ -147,8 +156,9 @@ mla_status mla_cache_write(mla_cache* cache, const void* x, const void* w_dkr, i
 mla_status mha_cache_write(mla_cache* cache, const void* x, const void* w_k, const void* w_v,
                            int64_t frame0, int32_t n_frames, void* stream);
 
-/* Slide the window: drop the n_frames oldest resident frames (host-side
- * bookkeeping only; launches nothing).  MLA_ERR_EVICT_RANGE if n_frames is
+/* Slide the window (abstract: a fixed-size sliding-window KV cache; problem
+ * definition: a window of 21 latent frames): drop the n_frames oldest
+ * resident frames (host-side bookkeeping only; launches nothing).  MLA_ERR_EVICT_RANGE if n_frames is
  * negative or larger than the resident count. Works on both handle kinds. */
 mla_status mla_cache_evict(mla_cache* cache, int32_t n_frames);
 
@@ -200,13 +210,15 @@ mla_status mla_attend(mla_cache* cache, const void* q, int64_t q_token0, int32_t
  *   2 (d_nope + d_rope) + 2 d_v (d_c = 192 for the Wan head shape; not 128 or
  *   64, where the latent form is as fast or faster).  Both paths compute the
  * same function; they differ in rounding (the expanded keys and values are
- * rounded to the cache's element type). */
+ * rounded to the cache's element type, fp16: only fp16 rings expand). */
 typedef enum { MLA_PATH_AUTO = 0, MLA_PATH_ABSORBED = 1, MLA_PATH_EXPAND = 2 } mla_attend_path_kind;
 
 /* Selects the path of later mla_attend calls on this latent handle.
- * MLA_ERR_UNSUPPORTED for MLA_PATH_EXPAND when the handle is not a 16-bit
- * storage handle with d_nope + d_rope == d_v == 128, d_c in {64, 128, 192},
- * d_nope a multiple of 32; MLA_ERR_WRONG_KIND on a dense handle. */
+ * MLA_ERR_UNSUPPORTED for MLA_PATH_EXPAND unless the handle has bf16 inputs,
+ * an fp16 ring, d_nope = 96, d_rope = 32, d_v = 128 and d_c in {64, 128, 192}
+ * (a bf16 ring is refused: its expanded keys and values, rounded to bf16,
+ * would each move the output by about 1e-3 of its size); MLA_ERR_WRONG_KIND
+ * on a dense handle. */
 mla_status mla_cache_set_attend_path(mla_cache* cache, int32_t path);
 
 /* Reuse of the expanded window across attends (enable = 1; 0 switches it off;

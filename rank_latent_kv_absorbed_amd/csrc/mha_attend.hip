@@ -10,14 +10,16 @@ namespace mla {
 namespace {
 
 // q [B][Lq][n_h][d_h] -> qrot [B][n_h * Lq_pad][d_h] in the cache type
-// (head-major rows), rotated and scaled.  A block takes kQprepTokens tokens of
-// one sequence: the rotation's cos/sin per (token, pair) are evaluated once
+// (head-major rows), rotated and scaled; with SPLIT (bf16 cache) also the
+// remainders' rounding into qrot_lo, for the split-operand core.  A block
+// takes kQprepTokens tokens of one sequence: the rotation's cos/sin per
+// (token, pair) are evaluated once
 // into LDS and shared by every head; then each thread moves 8-element chunks
 // (16-byte loads and stores).  Pairs whose frequency is 0 keep angle 0.
 constexpr int kQprepTokens = 4;
 constexpr int kQprepRun = 4;
 
-template <typename E>
+template <typename E, bool SPLIT>
 __global__ __launch_bounds__(256) void mha_qprep_bf16_kernel(MhaAttendArgs a, int lq_pad) {
   typedef typename Elem<E>::v8 V8;
   __shared__ float cs[kQprepTokens][kMaxRopePairs][2];
@@ -57,16 +59,20 @@ __global__ __launch_bounds__(256) void mha_qprep_bf16_kernel(MhaAttendArgs a, in
       const int h = rem / C, ch = rem - h * C;
       const int tok = tok0 + tt;
       if (i >= total || tok >= a.Lq) continue;
-      V8 o;
+      V8 o, ol;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float c = cs[tt][4 * ch + j][0], s = cs[tt][4 * ch + j][1];
         const float x0 = (float)v[u][2 * j], x1 = (float)v[u][2 * j + 1];
-        o[2 * j] = Elem<E>::from((x0 * c - x1 * s) * a.qscale);
-        o[2 * j + 1] = Elem<E>::from((x0 * s + x1 * c) * a.qscale);
+        const float y0 = (x0 * c - x1 * s) * a.qscale, y1 = (x0 * s + x1 * c) * a.qscale;
+        o[2 * j] = Elem<E>::from(y0);
+        o[2 * j + 1] = Elem<E>::from(y1);
+        ol[2 * j] = Elem<E>::from(y0 - (float)o[2 * j]);
+        ol[2 * j + 1] = Elem<E>::from(y1 - (float)o[2 * j + 1]);
       }
-      *reinterpret_cast<V8*>((E*)a.qrot + ((size_t)b * a.n_h * lq_pad + (size_t)h * lq_pad + tok) * a.d_h +
-                             8 * ch) = o;
+      const size_t off = ((size_t)b * a.n_h * lq_pad + (size_t)h * lq_pad + tok) * a.d_h + 8 * ch;
+      *reinterpret_cast<V8*>((E*)a.qrot + off) = o;
+      if constexpr (SPLIT) *reinterpret_cast<V8*>((E*)a.qrot_lo + off) = ol;
     }
   }
 }
@@ -199,8 +205,11 @@ hipError_t launch_mha_typed(const MhaAttendArgs& a, float* opart, float* ml, con
                             hipStream_t s) {
   const int br = sched.block_rows;
   const int lq_pad = (a.Lq + br - 1) / br * br;
+  // a bf16 cache runs the core on split operands (see mla_attn_core.h)
+  constexpr bool SPLIT = __is_same(E, bf16_t);
+  if ((a.qrot_lo != nullptr) != SPLIT) return hipErrorInvalidValue;
   {
-    hipLaunchKernelGGL(mha_qprep_bf16_kernel<E>,
+    hipLaunchKernelGGL((mha_qprep_bf16_kernel<E, SPLIT>),
                        dim3((unsigned)((a.Lq + kQprepTokens - 1) / kQprepTokens), (unsigned)a.B),
                        dim3(256), 0, s, a, lq_pad);
     hipError_t e = hipGetLastError();
@@ -208,6 +217,7 @@ hipError_t launch_mha_typed(const MhaAttendArgs& a, float* opart, float* ml, con
   }
   AttnCore c;
   c.qrows = a.qrot;
+  c.qrows_lo = a.qrot_lo;
   c.ring = a.ring;
   c.opart = opart;
   c.ml = ml;
@@ -230,13 +240,17 @@ hipError_t launch_mha_typed(const MhaAttendArgs& a, float* opart, float* ml, con
     }
     const dim3 grid((unsigned)sched.n_blocks);
     bool launched = false;
-#define MLA_SHAPE(NW, KT, NS, ROWS)                                                            \
-  if (!launched && br == ROWS * NW && sched.key_tile == KT && sched.stages == NS) {           \
-    hipLaunchKernelGGL((attn_core_kernel<E, 128, 128, NW, KT, NS, false, 1, (NW == 8), ROWS>), \
-                       grid, dim3(NW * 64), 0, s, c);                                         \
-    launched = true;                                                                          \
+#define MLA_SHAPE(NW, KT, NS, ROWS)                                                                   \
+  if (!launched && br == ROWS * NW && sched.key_tile == KT && sched.stages == NS) {                  \
+    hipLaunchKernelGGL((attn_core_kernel<E, 128, 128, NW, KT, NS, false, 1, (NW == 8), ROWS, SPLIT>), \
+                       grid, dim3(NW * 64), 0, s, c);                                                \
+    launched = true;                                                                                 \
   }
-    MLA_SHAPE(8, 64, 3, 32)
+    if constexpr (SPLIT) {
+      MLA_SHAPE(4, 64, 3, 32)
+    } else {
+      MLA_SHAPE(8, 64, 3, 32)
+    }
     MLA_SHAPE(4, 32, 4, 32)
     MLA_SHAPE(4, 32, 4, 16)
     MLA_SHAPE(1, 32, 2, 32)

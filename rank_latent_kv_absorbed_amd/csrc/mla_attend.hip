@@ -4,7 +4,9 @@
 // Three kernels run back to back on the caller's stream:
 //  1. qprep:    q_lat,h = W^K_up,h^T q^nope_h and q^R rotated at the query's
 //               position, both scaled by log2(e)/sqrt(d_nope + d_rope), written
-//               as one bf16 row [q_lat | q^R_rot] per (token, head) pair.
+//               as one row [q_lat | q^R_rot] of the cache type per (token, head)
+//               pair (a bf16 cache also gets the row of remainders, the bf16
+//               rounding of q - bf16(q), for the split-operand core).
 //  2. attend:   the shared flash-style core (mla_attn_core.h).  Rows are
 //               (token, head) pairs; every row scores against the same cached
 //               rows [c | k^R], so a key tile staged once in LDS serves all heads
@@ -30,7 +32,15 @@ namespace {
 // transpose read, which hands lane (i, half hi) the k-slots t = 0..7 as
 // n = 16 ks + 8 (t / 4) + 4 hi + t % 4.  The query operand uses the same
 // k-slot order: two 8-byte loads per step.
-template <typename E, int DC>
+// Store v as the cache type; with SPLIT also the remainder's rounding at lo.
+template <typename E, bool SPLIT>
+__device__ __forceinline__ void store_q(E* hi, E* lo, float v) {
+  const E h = Elem<E>::from(v);
+  *hi = h;
+  if constexpr (SPLIT) *lo = Elem<E>::from(v - (float)h);
+}
+
+template <typename E, int DC, bool SPLIT>
 __global__ __launch_bounds__(256) void qprep_bf16_kernel(AttendArgs a) {
   constexpr int NT = DC / 32;
   constexpr int WSTR = DC + 8;                 // padded LDS row (elements)
@@ -76,16 +86,23 @@ __global__ __launch_bounds__(256) void qprep_bf16_kernel(AttendArgs a) {
       acc[it] = mfma32(wa, bq, acc[it]);
     }
   }
-  E* out = (E*)a.qcat + ((size_t)b * R + (size_t)tok * a.n_h + h) * width;
+  const size_t orow = ((size_t)b * R + (size_t)tok * a.n_h + h) * width;
+  E* out = (E*)a.qcat + orow;
   if (valid) {
 #pragma unroll
     for (int it = 0; it < NT; ++it)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        typename Elem<E>::v4 o;
+        typename Elem<E>::v4 o, ol;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) o[j] = Elem<E>::from(acc[it][4 * g + j] * a.qscale);
+        for (int j = 0; j < 4; ++j) {
+          const float v = acc[it][4 * g + j] * a.qscale;
+          o[j] = Elem<E>::from(v);
+          ol[j] = Elem<E>::from(v - (float)o[j]);
+        }
         *reinterpret_cast<typename Elem<E>::v4*>(out + it * 32 + 8 * g + 4 * hi) = o;
+        if constexpr (SPLIT)
+          *reinterpret_cast<typename Elem<E>::v4*>((E*)a.qcat_lo + orow + it * 32 + 8 * g + 4 * hi) = ol;
       }
   }
   // rotary part: lanes walk (token, pair) of this wave's 32 tokens
@@ -98,9 +115,10 @@ __global__ __launch_bounds__(256) void qprep_bf16_kernel(AttendArgs a) {
         (const bf16_t*)a.q + (((size_t)b * a.Lq + tt) * a.n_h + h) * d_qk + a.d_nope + 2 * p;
     float x0 = (float)qr[0], x1 = (float)qr[1];
     rope_pair(a.rope, p, token_pos(a.q_token0 + tt, a.T, a.grid_w), x0, x1);
-    E* o = (E*)a.qcat + ((size_t)b * R + (size_t)tt * a.n_h + h) * width + DC + 2 * p;
-    o[0] = Elem<E>::from(x0 * a.qscale);
-    o[1] = Elem<E>::from(x1 * a.qscale);
+    const size_t off = ((size_t)b * R + (size_t)tt * a.n_h + h) * width + DC + 2 * p;
+    E* lo = SPLIT ? (E*)a.qcat_lo + off : nullptr;
+    store_q<E, SPLIT>((E*)a.qcat + off, lo, x0 * a.qscale);
+    store_q<E, SPLIT>((E*)a.qcat + off + 1, lo + 1, x1 * a.qscale);
   }
 }
 
@@ -118,7 +136,7 @@ constexpr int qprep_rows_max_nope() {
   return (256 / (DC / 8)) * kQprepRowsMaxK;
 }
 
-template <typename E, int DC>
+template <typename E, int DC, bool SPLIT>
 __global__ __launch_bounds__(256) void qprep_rows_kernel(AttendArgs a) {
   constexpr int CH = DC / 8;                      // 8-column chunks of a W row
   constexpr int NG = 256 / CH;                    // row groups
@@ -173,12 +191,12 @@ __global__ __launch_bounds__(256) void qprep_rows_kernel(AttendArgs a) {
       for (int t = 0; t < 8; ++t) red[g][8 * j + t] = acc[t];
     }
     __syncthreads();
-    E* out = (E*)a.qcat + ((size_t)b * R + (size_t)tok * a.n_h + h) * width;
+    const size_t orow = ((size_t)b * R + (size_t)tok * a.n_h + h) * width;
     for (int c = tid; c < DC; c += 256) {
       float sum = 0.0f;
 #pragma unroll
       for (int gg = 0; gg < NG; ++gg) sum += red[gg][c];
-      out[c] = Elem<E>::from(sum * a.qscale);
+      store_q<E, SPLIT>((E*)a.qcat + orow + c, SPLIT ? (E*)a.qcat_lo + orow + c : nullptr, sum * a.qscale);
     }
     __syncthreads();
   }
@@ -189,9 +207,10 @@ __global__ __launch_bounds__(256) void qprep_rows_kernel(AttendArgs a) {
     const bf16_t* qr = q + (((size_t)b * a.Lq + tok) * a.n_h + h) * d_qk + d_nope + 2 * p;
     float x0 = (float)qr[0], x1 = (float)qr[1];
     rope_pair(a.rope, p, token_pos(a.q_token0 + tok, a.T, a.grid_w), x0, x1);
-    E* o = (E*)a.qcat + ((size_t)b * R + (size_t)tok * a.n_h + h) * width + DC + 2 * p;
-    o[0] = Elem<E>::from(x0 * a.qscale);
-    o[1] = Elem<E>::from(x1 * a.qscale);
+    const size_t off = ((size_t)b * R + (size_t)tok * a.n_h + h) * width + DC + 2 * p;
+    E* lo = SPLIT ? (E*)a.qcat_lo + off : nullptr;
+    store_q<E, SPLIT>((E*)a.qcat + off, lo, x0 * a.qscale);
+    store_q<E, SPLIT>((E*)a.qcat + off + 1, lo + 1, x1 * a.qscale);
   }
 }
 
@@ -484,18 +503,27 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(AttendArgs a) {
   }
 }
 
+// A bf16 cache runs the core on split operands (see mla_attn_core.h).
+template <typename E>
+constexpr bool kSplitOf = __is_same(E, bf16_t);
+
 // Core launch for the schedule's shape (block rows, key tile, stages).
 template <typename E, int DC>
 hipError_t launch_core(const AttnCore& c, hipStream_t s) {
   const Schedule& sc = c.sched;
   const dim3 grid((unsigned)sc.n_blocks);
-#define MLA_SHAPE(NW, KT, NS, ROWS)                                                             \
-  if (sc.block_rows == ROWS * NW && sc.key_tile == KT && sc.stages == NS) {                    \
-    hipLaunchKernelGGL((attn_core_kernel<E, DC + 32, DC, NW, KT, NS, true, 1, (NW == 8), ROWS>), \
-                       grid, dim3(NW * 64), 0, s, c);                                          \
-    return hipGetLastError();                                                                  \
+  constexpr bool SPLIT = kSplitOf<E>;
+#define MLA_SHAPE(NW, KT, NS, ROWS)                                                                    \
+  if (sc.block_rows == ROWS * NW && sc.key_tile == KT && sc.stages == NS) {                           \
+    hipLaunchKernelGGL((attn_core_kernel<E, DC + 32, DC, NW, KT, NS, true, 1, (NW == 8), ROWS, SPLIT>), \
+                       grid, dim3(NW * 64), 0, s, c);                                                 \
+    return hipGetLastError();                                                                         \
   }
-  MLA_SHAPE(8, 64, 3, 32)
+  if constexpr (SPLIT) {
+    MLA_SHAPE(4, 64, 3, 32)
+  } else {
+    MLA_SHAPE(8, 64, 3, 32)
+  }
   MLA_SHAPE(4, 32, 4, 32)
   MLA_SHAPE(4, 32, 4, 16)
   MLA_SHAPE(1, 32, 2, 32)
@@ -506,21 +534,24 @@ hipError_t launch_core(const AttnCore& c, hipStream_t s) {
 
 template <typename E, int DC>
 hipError_t launch_dc(const AttendArgs& a, hipStream_t s) {
+  constexpr bool SPLIT = kSplitOf<E>;
+  if ((a.qcat_lo != nullptr) != SPLIT) return hipErrorInvalidValue;
   if (a.Lq <= kQprepRowsMaxLq && a.d_nope <= qprep_rows_max_nope<DC>()) {
-    hipLaunchKernelGGL((qprep_rows_kernel<E, DC>), dim3((unsigned)a.n_h, (unsigned)a.B), dim3(256), 0,
+    hipLaunchKernelGGL((qprep_rows_kernel<E, DC, SPLIT>), dim3((unsigned)a.n_h, (unsigned)a.B), dim3(256), 0,
                        s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   } else {
     const size_t lds = (size_t)a.d_nope * (DC + 8) * sizeof(bf16_t);
     dim3 grid((unsigned)((a.Lq + 127) / 128), (unsigned)a.n_h, (unsigned)a.B);
-    hipLaunchKernelGGL((qprep_bf16_kernel<E, DC>), grid, dim3(256), lds, s, a);
+    hipLaunchKernelGGL((qprep_bf16_kernel<E, DC, SPLIT>), grid, dim3(256), lds, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   {
     AttnCore c;
     c.qrows = a.qcat;
+    c.qrows_lo = a.qcat_lo;
     c.ring = a.ring;
     c.opart = a.opart;
     c.ml = a.ml;
@@ -547,10 +578,11 @@ hipError_t launch_dc(const AttendArgs& a, hipStream_t s) {
       if (e != hipSuccess) return e;
     }
   }
-  // Rows with many key-range partials each (narrow blocks, or few row groups
-  // spread over the whole device) merge one row per block; otherwise one lane
-  // per row, whose merge walks the partials one after another.
-  if ((a.sched.block_rows < kCoreMaxBlockRows || a.sched.n_slots > kLaneMergeMaxSlots) &&
+  // Rows with many key-range partials each (narrow blocks on 32-key tiles,
+  // or few row groups spread over the whole device) merge one row per block;
+  // otherwise one lane per row, whose merge walks the partials one after
+  // another.
+  if ((a.sched.key_tile < 64 || a.sched.n_slots > kLaneMergeMaxSlots) &&
       a.d_v <= kEpiMaxDv) {
     const dim3 grid((unsigned)(a.Lq * a.n_h), (unsigned)a.B);
     if (grid.x * grid.y >= (unsigned)kEpiLeanRows)

@@ -46,6 +46,16 @@
 // Latent rows (SHARED_KV): K = [c | k^R] and V = c are one cached row, so the
 // value operand reads the first DV columns of the key tile.  Dense rows: K and
 // V of head h are separate slices of the cached row, both staged per key.
+//
+// Split operands (SPLIT, used with a bf16 cache): bf16 keeps 8 significant
+// bits, and the rounding of the prepared query and of the probabilities to
+// bf16 does not average out over the window (keys and values come from the
+// same cached rows, so the softmax's tilt carries it coherently into the
+// output).  Each of the two is then carried as a pair of bf16 values, a
+// leading part and the bf16 rounding of the remainder, and every product is
+// issued for both parts with the same cached operand: 16 significant bits,
+// at twice the matrix work.  The extra registers take the whole register
+// file of a SIMD, so split blocks run one wave per SIMD.
 #pragma once
 
 #include "mla_device.h"
@@ -54,6 +64,7 @@ namespace mla {
 
 struct AttnCore {
   const void* qrows;     // [B][R][DQK] elements of the cache type
+  const void* qrows_lo;  // split operands: the remainders, same layout
   const void* ring;      // [B][ring_rows][ring_stride]
   float* opart;          // [n_slots][B][R][DV]  un-normalised value sums
   float* ml;             // [n_slots][B][R][2]   running max (log2 units), sum
@@ -151,8 +162,9 @@ __device__ __forceinline__ void lds_barrier() {
 // narrow blocks can share a compute unit; one wave per SIMD (the whole
 // register file, accumulators in AGPRs) when each wave owns RB > 1 row blocks.
 template <typename E, int DQK, int DV, int NW, int KT, int NS, bool SHARED_KV, int RB = 1,
-          bool PP = false, int ROWS = 32>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 2 : 1, RB == 1 ? 2 : 1)))
+          bool PP = false, int ROWS = 32, bool SPLIT = false>
+__global__ __launch_bounds__(NW * 64)
+__attribute__((amdgpu_waves_per_eu((RB == 1 && !SPLIT) ? 2 : 1, (RB == 1 && !SPLIT) ? 2 : 1)))
 void attn_core_kernel(AttnCore a) {
   typedef typename Elem<E>::v8 V8;
   // ROWS = 32: 32x32x16 MFMAs, a lane owns one row (MFMA column) with its two
@@ -180,6 +192,8 @@ void attn_core_kernel(AttnCore a) {
   static_assert(!SHARED_KV || DV <= DQK, "shared rows hold V inside K");
   static_assert(NS >= 2 && NS <= 5, "two to five tile buffers");
   static_assert(!PP || (NS == 3 && NW % 2 == 0 && NW >= 2), "ping-pong: two wave groups, three buffers");
+  static_assert(!SPLIT || (NW <= 4 && RB == 1), "split operands: one wave per SIMD");
+  constexpr int NQ = SPLIT ? 2 : 1;           // operand parts (leading, remainder)
   static_assert((SPANS + NW - 1) / NW * (NS - 1) <= 63, "tile loads in flight fit the vmcnt counter");
   // Whole spans with every lane active (exact load counts per wave); the chunk
   // permutation stays inside aligned groups of a row.
@@ -324,7 +338,7 @@ void attn_core_kernel(AttnCore a) {
   // Per row block rb of the wave: query fragments, value sums, running max
   // and sum, the lane's row.  Each key fragment read from LDS feeds RB
   // products, so LDS traffic per product falls as 1 / RB.
-  V8 qf[RB][NKS];
+  V8 qf[NQ][RB][NKS];
   AccT o[RB][NDT];
   float m[RB], lsum[RB];
   int row[RB];
@@ -373,9 +387,13 @@ void attn_core_kernel(AttnCore a) {
       row[rb] = row0 + ROWS * rb + (R16 ? r16 : lo);
       const int r = row[rb];
       const bool ok = r < a.R && (r % a.rows_per_head) < a.valid_per_head;
-      const E* src = (const E*)a.qrows + ((size_t)b * a.R + (ok ? r : 0)) * DQK + (R16 ? 8 * g16 : 8 * hi);
+      const size_t qoff = ((size_t)b * a.R + (ok ? r : 0)) * DQK + (R16 ? 8 * g16 : 8 * hi);
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) qf[rb][ks] = ok ? ld8<E>(src + (R16 ? 32 : 16) * ks) : zero8<E>();
+      for (int u = 0; u < NQ; ++u) {
+        const E* src = (const E*)(u == 0 ? a.qrows : a.qrows_lo) + qoff;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) qf[u][rb][ks] = ok ? ld8<E>(src + (R16 ? 32 : 16) * ks) : zero8<E>();
+      }
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -407,7 +425,9 @@ void attn_core_kernel(AttnCore a) {
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) sv[0][kb] = Elem<E>::mfma16(kf[kb][ks], qf[0][ks], sv[0][kb]);
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int u = 0; u < NQ; ++u) sv[0][kb] = Elem<E>::mfma16(kf[kb][ks], qf[u][0][ks], sv[0][kb]);
     } else {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
@@ -424,7 +444,9 @@ void attn_core_kernel(AttnCore a) {
         for (int ks = 0; ks < NKS; ++ks) {
           const V8 kf = ld8<E>(kptr(ks));
 #pragma unroll
-          for (int rb = 0; rb < RB; ++rb) sv[rb][kb] = Elem<E>::mfma(kf, qf[rb][ks], sv[rb][kb]);
+          for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int u = 0; u < NQ; ++u) sv[rb][kb] = Elem<E>::mfma(kf, qf[u][rb][ks], sv[rb][kb]);
         }
       }
     }
@@ -435,7 +457,7 @@ void attn_core_kernel(AttnCore a) {
   auto key_of = [&](int kb, int r) MLA_INLINE {
     return R16 ? kb * 16 + 4 * g16 + r : kb * 32 + acc_row(r, hi);
   };
-  auto softmax = [&](int kt, AccT (&sv)[RB][NKB], V8 (&pf)[RB][NPF]) MLA_INLINE {
+  auto softmax = [&](int kt, AccT (&sv)[RB][NKB], V8 (&pf)[NQ][RB][NPF]) MLA_INLINE {
     const int t0 = kt * KT;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -473,16 +495,16 @@ void attn_core_kernel(AttnCore a) {
           ps += p;
           // 16-row waves: value-product slot 8 g16 + 4 kb + r is key
           // kb * 16 + 4 g16 + r, so the lane's own scores form its operand
-          if constexpr (R16)
-            pf[rb][0][4 * kb + r] = Elem<E>::from(p);
-          else
-            pf[rb][2 * kb + (r >> 3)][r & 7] = Elem<E>::from(p);
+          const E ph = Elem<E>::from(p);
+          const int fi = R16 ? 0 : 2 * kb + (r >> 3), fe = R16 ? 4 * kb + r : (r & 7);
+          pf[0][rb][fi][fe] = ph;
+          if constexpr (SPLIT) pf[1][rb][fi][fe] = Elem<E>::from(p - (float)ph);
         }
       lsum[rb] += ps;
     }
   };
   // Value sums O^T += V^T P^T of the tile in `cur`.
-  auto values = [&](const E* cur, const V8 (&pf)[RB][NPF]) MLA_INLINE {
+  auto values = [&](const E* cur, const V8 (&pf)[NQ][RB][NPF]) MLA_INLINE {
     if constexpr (R16) {
       // slots 8 g16 .. + 3: keys 4 g16 + t (block 0); + 4 .. + 7: keys 16 + 4 g16 + t
       const E* v0 = cur + (4 * g16 + t16) * KSTR + VOFF + 4 * (c16 & 1);
@@ -500,7 +522,8 @@ void attn_core_kernel(AttnCore a) {
       for (int dt = 0; dt < NDT; ++dt) {
         const V8 va =
             __builtin_bit_cast(V8, __builtin_shufflevector(lo4[dt], hi4[dt], 0, 1, 2, 3, 4, 5, 6, 7));
-        o[0][dt] = Elem<E>::mfma16(va, pf[0][0], o[0][dt]);
+#pragma unroll
+        for (int u = 0; u < NQ; ++u) o[0][dt] = Elem<E>::mfma16(va, pf[u][0][0], o[0][dt]);
       }
     } else {
 #pragma unroll
@@ -515,7 +538,9 @@ void attn_core_kernel(AttnCore a) {
             const i16x4 hi4 = lds_read_tr16(vrow + 8 * KSTR + 32 * d1 + tr_off1);
             const V8 va = __builtin_bit_cast(V8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb) o[rb][dt] = Elem<E>::mfma(va, pf[rb][2 * kb + st], o[rb][dt]);
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+              for (int u = 0; u < NQ; ++u) o[rb][dt] = Elem<E>::mfma(va, pf[u][rb][2 * kb + st], o[rb][dt]);
           }
         }
     }
@@ -608,7 +633,7 @@ void attn_core_kernel(AttnCore a) {
       const StepInfo si = wc.c.si;
       const int b = wc.b;
       step_begin(si, b, k, cur);
-      V8 pf[RB][NPF];
+      V8 pf[NQ][RB][NPF];
       if (live) {
         AccT sv[RB][NKB];
         scores(cur, sv);
@@ -649,7 +674,7 @@ void attn_core_kernel(AttnCore a) {
     step_begin(si, b, i, cur);
     if (live) {
       AccT sv[RB][NKB];
-      V8 pf[RB][NPF];
+      V8 pf[NQ][RB][NPF];
       scores(cur, sv);
       softmax(si.kt, sv, pf);
       values(cur, pf);

@@ -7,11 +7,14 @@
 // frame f always lives at ring slot (f mod W)*T + tau.  Every check runs
 // before anything is enqueued, so a failed call changes nothing.
 #include <algorithm>
+#include <functional>
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
+#include <vector>
 
 #include "../../include/mla.h"
 #include "mla_launch.h"
@@ -36,6 +39,7 @@ struct mla_cache {
   const void* ex_wuk;
   const void* ex_wuv;
   uint64_t ex_gen;
+  uint64_t ex_token;  // the expansion's entry in the workspace record below
 };
 
 namespace {
@@ -59,6 +63,55 @@ bool aligned16(const void* p) { return p != nullptr && ((uintptr_t)p & 15u) == 0
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 int64_t tokens_per_frame(const mla_layer_config& c) { return (int64_t)c.grid_h * c.grid_w; }
+
+// Process-wide record of the workspace ranges that hold an expanded window:
+// every attend on any handle first erases the entries its writes overlap, and
+// an expansion then enters its own range under a fresh token.  A handle reuses
+// an expansion only while that token is still on record, so a workspace
+// written in between by another handle (or another attend of the same one)
+// forces a rebuild.
+struct WsRecord {
+  uintptr_t lo, hi;
+  uint64_t token;
+};
+std::mutex g_ws_mu;
+std::vector<WsRecord> g_ws;
+uint64_t g_ws_next_token = 1;
+
+void ws_erase_if(const std::function<bool(const WsRecord&)>& pred) {
+  g_ws.erase(std::remove_if(g_ws.begin(), g_ws.end(), pred), g_ws.end());
+}
+
+// The caller's next kernels write [p, p + n).
+void ws_clobber(const void* p, size_t n) {
+  const uintptr_t lo = (uintptr_t)p, hi = lo + n;
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  ws_erase_if([&](const WsRecord& r) { return r.lo < hi && lo < r.hi; });
+}
+
+// [p, p + n) now holds a new expansion; returns its token.
+uint64_t ws_enter(const void* p, size_t n) {
+  const uintptr_t lo = (uintptr_t)p, hi = lo + n;
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  ws_erase_if([&](const WsRecord& r) { return r.lo < hi && lo < r.hi; });
+  const uint64_t t = g_ws_next_token++;
+  g_ws.push_back({lo, hi, t});
+  return t;
+}
+
+bool ws_holds(const void* p, size_t n, uint64_t token) {
+  const uintptr_t lo = (uintptr_t)p, hi = lo + n;
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  for (const WsRecord& r : g_ws)
+    if (r.token == token) return r.lo == lo && r.hi == hi;
+  return false;
+}
+
+void ws_forget(uint64_t token) {
+  if (token == 0) return;
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  ws_erase_if([&](const WsRecord& r) { return r.token == token; });
+}
 
 int64_t dense_width(const mla_layer_config& c) {
   return 2LL * c.n_heads * (c.d_nope + c.d_rope);
@@ -141,7 +194,7 @@ constexpr int64_t kSegmentCostLatent = 3;
 constexpr int64_t kSegmentCostDense = 6;
 
 mla::Schedule make_schedule(int64_t B, int64_t R, int64_t Lk, int32_t key_splits, int64_t cus,
-                            mla::CoreShape sh, int chunks_per_key, int64_t seg_cost) {
+                            mla::CoreShape sh, int chunks_per_key, int64_t seg_cost, bool split) {
   mla::Schedule s;
   sh = mla::core_shape_for_keys(sh, chunks_per_key);
   const int64_t br = (int64_t)sh.rows * sh.waves;
@@ -154,7 +207,7 @@ mla::Schedule make_schedule(int64_t B, int64_t R, int64_t Lk, int32_t key_splits
     nb = groups * key_splits;
   } else {
     const int64_t by_work = (total + kMinStepsPerBlock - 1) / kMinStepsPerBlock;
-    const int64_t resident = cus * mla::core_blocks_per_cu(sh, chunks_per_key);
+    const int64_t resident = cus * mla::core_blocks_per_cu(sh, chunks_per_key, split);
     nb = resident < by_work ? resident : by_work;
   }
   if (nb < 1) nb = 1;
@@ -201,9 +254,14 @@ int64_t window_keys(const mla_cache* h) {
                            : (int64_t)c.window_frames * tokens_per_frame(c);
 }
 
+// A bf16 ring runs the attention core on split operands (query and
+// probabilities as two bf16 parts; see mla_attn_core.h): bf16 keeps too few
+// bits for them on their own.  fp16 rings and fp32 handles do not split.
+bool split_operands(const mla_layer_config& c) { return c.cache_dtype == MLA_BF16; }
+
 struct LatentLayout {
   mla::Schedule sched;
-  size_t qcat_off, opart_off, ml_off, total;
+  size_t qcat_off, qlo_off, opart_off, ml_off, total;
 };
 
 // Layouts for `Lk` resident keys (default: the handle's current window).
@@ -211,12 +269,16 @@ LatentLayout latent_layout(const mla_cache* h, int32_t Lq, int32_t key_splits, i
   const mla_layer_config& c = h->cfg;
   const int64_t R = (int64_t)Lq * c.n_heads;
   LatentLayout L;
+  const bool split = split_operands(c);
   L.sched = make_schedule(c.batch, R, Lk < 0 ? window_keys(h) : Lk, key_splits, mla::device_cu_count(),
-                          mla::core_shape_for_rows(R), (c.d_c + c.d_rope) / 8, kSegmentCostLatent);
+                          mla::core_shape_for_rows(R, split), (c.d_c + c.d_rope) / 8, kSegmentCostLatent,
+                          split);
   const size_t width = (size_t)(c.d_c + c.d_rope);
   const size_t slots = (size_t)L.sched.n_slots;
+  const size_t qbytes = round_up((size_t)c.batch * R * width * 2, kAlign);
   L.qcat_off = 0;
-  L.opart_off = round_up((size_t)c.batch * R * width * 2, kAlign);
+  L.qlo_off = qbytes;
+  L.opart_off = split ? 2 * qbytes : qbytes;
   L.ml_off = L.opart_off + round_up(slots * c.batch * R * c.d_c * 4, kAlign);
   L.total = L.ml_off + round_up(slots * c.batch * R * 2 * 4, kAlign);
   return L;
@@ -225,22 +287,25 @@ LatentLayout latent_layout(const mla_cache* h, int32_t Lq, int32_t key_splits, i
 struct DenseLayout {
   mla::Schedule sched;
   int lq_pad;
-  size_t qrot_off, opart_off, ml_off, total;
+  size_t qrot_off, qlo_off, opart_off, ml_off, total;
 };
 
 DenseLayout dense_layout(const mla_cache* h, int32_t Lq, int64_t Lk = -1) {
   const mla_layer_config& c = h->cfg;
   const int d_h = c.d_nope + c.d_rope;
   DenseLayout L;
-  const mla::CoreShape sh = mla::core_shape_for_rows(Lq);
+  const bool split = split_operands(c);
+  const mla::CoreShape sh = mla::core_shape_for_rows(Lq, split);
   const int br = sh.rows * sh.waves;
   L.lq_pad = (Lq + br - 1) / br * br;
   const int64_t R = (int64_t)c.n_heads * L.lq_pad;
   L.sched = make_schedule(c.batch, R, Lk < 0 ? window_keys(h) : Lk, 0, mla::device_cu_count(), sh,
-                          2 * d_h / 8, kSegmentCostDense);
+                          2 * d_h / 8, kSegmentCostDense, split);
   const size_t slots = (size_t)L.sched.n_slots;
+  const size_t qbytes = round_up((size_t)c.batch * R * d_h * 2, kAlign);
   L.qrot_off = 0;
-  L.opart_off = round_up((size_t)c.batch * R * d_h * 2, kAlign);
+  L.qlo_off = qbytes;
+  L.opart_off = split ? 2 * qbytes : qbytes;
   L.ml_off = L.opart_off + round_up(slots * c.batch * R * d_h * 4, kAlign);
   L.total = L.ml_off + round_up(slots * c.batch * R * 2 * 4, kAlign);
   return L;
@@ -279,13 +344,18 @@ ExpandLayout expand_layout(const mla_cache* h, int32_t Lq, int64_t Lk = -1) {
 constexpr int32_t kExpandMinQueries = 512;
 constexpr double kExpandFlopRatio = 1.5;
 
-// The expansion serves 16-bit handles of the dense core's head width whose
+// The expansion serves fp16-ring handles of the dense core's head width whose
 // expanded full window (every key, every head) keeps one sequence's offsets
 // below 2^31 elements, like a dense cache.  The expanded window is sized for
 // the full window so the workspace size does not change as frames arrive.
+// A bf16 ring has no expansion: the rebuilt per-head keys and values would be
+// rounded to bf16, and those roundings (like the query's and the
+// probabilities') each move the attention output by about 1e-3 of its size
+// on Gaussian inputs, independent of the window length.
 bool expand_possible(const mla_cache* h) {
   const mla_layer_config& c = h->cfg;
-  return c.dtype == MLA_BF16 && mla::expand_supported(c.d_c, c.d_rope, c.d_nope, c.d_v) &&
+  return c.dtype == MLA_BF16 && c.cache_dtype == MLA_F16 &&
+         mla::expand_supported(c.d_c, c.d_rope, c.d_nope, c.d_v) &&
          (int64_t)c.window_frames * tokens_per_frame(c) * 2 * c.n_heads * (c.d_nope + c.d_rope) <
              (1LL << 31);
 }
@@ -345,6 +415,7 @@ mla_status create(const mla_layer_config* cfg, void* storage, size_t storage_byt
   h->ex_valid = false;
   h->ex_ws = h->ex_wuk = h->ex_wuv = nullptr;
   h->ex_gen = 0;
+  h->ex_token = 0;
   *out = h;
   return MLA_OK;
 }
@@ -375,7 +446,10 @@ mla_status mha_cache_create(const mla_layer_config* cfg, void* storage, size_t s
   return create(cfg, storage, storage_bytes, true, out);
 }
 
-void mla_cache_destroy(mla_cache* cache) { delete cache; }
+void mla_cache_destroy(mla_cache* cache) {
+  if (cache != nullptr) ws_forget(cache->ex_token);
+  delete cache;
+}
 
 mla_status mla_cache_write(mla_cache* h, const void* x, const void* w_dkr, int64_t frame0,
                            int32_t n_frames, void* stream) {
@@ -506,6 +580,8 @@ mla_status mla_cache_set_expand_reuse(mla_cache* h, int32_t enable) {
   if (h->dense) return MLA_ERR_WRONG_KIND;
   h->expand_reuse = enable;
   h->ex_valid = false;
+  ws_forget(h->ex_token);
+  h->ex_token = 0;
   return MLA_OK;
 }
 
@@ -590,6 +666,7 @@ mla_status mla_attend(mla_cache* h, const void* q, int64_t q_token0, int32_t Lq,
     m.ring = e.kv;
     m.out = out;
     m.qrot = ws + X.base + X.dense.qrot_off;
+    m.qrot_lo = nullptr;  // fp16 ring only
     m.B = c.batch;
     m.Lq = Lq;
     m.n_h = c.n_heads;
@@ -605,13 +682,19 @@ mla_status mla_attend(mla_cache* h, const void* q, int64_t q_token0, int32_t Lq,
     m.ev_start = h->prof_start;
     m.ev_stop = h->prof_stop;
     m.rope = expand_rope(c);
-    // The rebuilt window in this workspace is still current when reuse is on
-    // and neither the window, the weights nor the workspace changed since it
-    // was written (several attends per chunk, e.g. denoising steps).
+    // The rebuilt window in this workspace is still current when reuse is on,
+    // neither the window nor the weights changed since it was written, and no
+    // attend on any handle has written over it since (several attends per
+    // chunk, e.g. denoising steps).
+    const size_t kv_bytes = X.base - X.kv_off;
     const bool reuse = h->expand_reuse && h->ex_valid && h->ex_ws == workspace &&
-                       h->ex_wuk == w_uk && h->ex_wuv == w_uv && h->ex_gen == h->gen;
+                       h->ex_wuk == w_uk && h->ex_wuv == w_uv && h->ex_gen == h->gen &&
+                       ws_holds(ws + X.kv_off, kv_bytes, h->ex_token);
     if (!reuse) {
       h->ex_valid = false;
+      ws_forget(h->ex_token);
+      h->ex_token = 0;
+      ws_clobber(ws, X.total);
       const hipError_t err = mla::launch_expand_kv(e, s);
       if (err != hipSuccess) return MLA_ERR_HIP;
       h->ex_valid = true;
@@ -619,7 +702,9 @@ mla_status mla_attend(mla_cache* h, const void* q, int64_t q_token0, int32_t Lq,
       h->ex_wuk = w_uk;
       h->ex_wuv = w_uv;
       h->ex_gen = h->gen;
+      h->ex_token = ws_enter(ws + X.kv_off, kv_bytes);
     }
+    ws_clobber(ws + X.base, X.total - X.base);
     return launch_status(mla::launch_mha_attend_bf16_ws(m, (float*)(ws + X.base + X.dense.opart_off),
                                                         (float*)(ws + X.base + X.dense.ml_off),
                                                         X.dense.sched, s));
@@ -629,7 +714,9 @@ mla_status mla_attend(mla_cache* h, const void* q, int64_t q_token0, int32_t Lq,
   if (workspace == nullptr || ((uintptr_t)workspace % kAlign) != 0 || workspace_bytes < L.total)
     return MLA_ERR_WORKSPACE;
   char* ws = (char*)workspace;
+  ws_clobber(ws, L.total);
   a.qcat = ws + L.qcat_off;
+  a.qcat_lo = split_operands(c) ? ws + L.qlo_off : nullptr;
   a.opart = (float*)(ws + L.opart_off);
   a.ml = (float*)(ws + L.ml_off);
   a.sched = L.sched;
@@ -686,7 +773,9 @@ mla_status mha_attend(mla_cache* h, const void* q, int64_t q_token0, int32_t Lq,
   if (workspace == nullptr || ((uintptr_t)workspace % kAlign) != 0 || workspace_bytes < L.total)
     return MLA_ERR_WORKSPACE;
   char* ws = (char*)workspace;
+  ws_clobber(ws, L.total);
   a.qrot = ws + L.qrot_off;
+  a.qrot_lo = split_operands(c) ? ws + L.qlo_off : nullptr;
   return launch_status(mla::launch_mha_attend_bf16_ws(a, (float*)(ws + L.opart_off),
                                                       (float*)(ws + L.ml_off), L.sched, s));
 }

@@ -63,16 +63,18 @@ struct CoreShape {
 };
 constexpr CoreShape kCoreShapes[] = {{8, 64, 3, 32}, {4, 32, 4, 32}, {1, 32, 2, 32}, {1, 32, 2, 16},
                                      {4, 32, 4, 16}};
-constexpr int kCoreMaxBlockRows = 256;
+// Chunk shape of split-operand cores (bf16 cache: query and probabilities
+// carried as two bf16 parts, one wave per SIMD): four waves on 64-key tiles.
+constexpr CoreShape kCoreShapeSplitChunk = {4, 64, 3, 32};
 
 // Shape for `rows` query rows of one row unit (latent: Lq * n_h rows of a
-// batch element; dense: Lq rows of one head).
-inline CoreShape core_shape_for_rows(int64_t rows) {
+// batch element; dense: Lq rows of one head).  `split`: split-operand core.
+inline CoreShape core_shape_for_rows(int64_t rows, bool split = false) {
   if (rows <= 16) return kCoreShapes[3];
   if (rows <= 32) return kCoreShapes[2];
   if (rows <= 64) return kCoreShapes[4];
   if (rows <= 128) return kCoreShapes[1];
-  return kCoreShapes[0];
+  return split ? kCoreShapeSplitChunk : kCoreShapes[0];
 }
 
 // Stages of a shape for key rows of `chunks_per_key` 16-byte chunks: the
@@ -88,11 +90,12 @@ inline CoreShape core_shape_for_keys(CoreShape sh, int chunks_per_key) {
 
 // Blocks of a shape that fit one compute unit at once: LDS (160 KiB per CU)
 // holds `stages` key tiles of `chunks_per_key` 16-byte chunks per key, and
-// the core's register use allows two waves per SIMD (eight per CU).
-inline int core_blocks_per_cu(CoreShape sh, int chunks_per_key) {
+// the core's register use allows two waves per SIMD (eight per CU), or one
+// (four per CU) for split operands.
+inline int core_blocks_per_cu(CoreShape sh, int chunks_per_key, bool split = false) {
   const int lds = sh.stages * sh.key_tile * chunks_per_key * 16;
   const int by_lds = (160 * 1024) / lds;
-  const int by_waves = 8 / sh.waves;
+  const int by_waves = (split ? 4 : 8) / sh.waves;
   return by_lds < by_waves ? by_lds : by_waves;
 }
 
@@ -256,6 +259,7 @@ struct AttendArgs {
   const void* w_uv;       // [n_h][d_v][d_c]
   float* out;             // [B][Lq][n_h][d_v]
   void* qcat;             // workspace [B][R][d_c + d_rope] cache type, R = Lq * n_h
+  void* qcat_lo;          // bf16 cache: the remainders of qcat (same layout); else null
   float* opart;           // workspace [n_split][B][R][d_c]
   float* ml;              // workspace [n_split][B][R][2]  (running max (log2 units), sum)
   int B, Lq, n_h, d_nope, d_rope, d_v, d_c;
@@ -278,6 +282,7 @@ struct MhaAttendArgs {
   const void* ring;       // [B][ring_rows][2][n_h][d_h]
   float* out;             // [B][Lq][n_h][d_h]
   void* qrot;             // workspace [B][n_h * Lq_pad][d_h] cache type (rotated, pre-scaled)
+  void* qrot_lo;          // bf16 cache: the remainders of qrot (same layout); else null
   int B, Lq, n_h, d_h;
   int64_t q_token0;
   int T, grid_w;

@@ -10,7 +10,6 @@ fallback implementation.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 
 import torch
@@ -148,6 +147,16 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _alloc(nbytes_or_shape, dtype, device, stream):
+    """A new tensor whose memory the caching allocator ties to `stream` (the
+    stream the library's kernels use), so that it is not handed out again
+    while those kernels may still run."""
+    if stream is None or stream == torch.cuda.current_stream(device):
+        return torch.empty(nbytes_or_shape, dtype=dtype, device=device)
+    with torch.cuda.stream(stream):
+        return torch.empty(nbytes_or_shape, dtype=dtype, device=device)
+
+
 def _need(t, name, dtype, shape, device):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch tensor")
@@ -264,12 +273,11 @@ class LatentCache(_CacheBase):
         _need(w_uk, "w_uk", self.tdtype, (cfg.n_heads, cfg.d_nope, cfg.d_c), self.device)
         _need(w_uv, "w_uv", self.tdtype, (cfg.n_heads, cfg.d_v, cfg.d_c), self.device)
         if out is None:
-            out = torch.empty((self.batch, Lq, cfg.n_heads, cfg.d_v), dtype=torch.float32,
-                              device=self.device)
+            out = _alloc((self.batch, Lq, cfg.n_heads, cfg.d_v), torch.float32, self.device, stream)
         _need(out, "out", torch.float32, (self.batch, Lq, cfg.n_heads, cfg.d_v), self.device)
         need = self.workspace_bytes(Lq, key_splits)
         if workspace is None and need > 0:
-            workspace = torch.empty(need, dtype=torch.uint8, device=self.device)
+            workspace = _alloc(need, torch.uint8, self.device, stream)
         wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
         _check(lib().mla_attend(self._h, _ptr(q), int(q_token0), int(Lq), _ptr(w_uk), _ptr(w_uv),
                                 _ptr(out), int(key_splits), _ptr(workspace), wbytes,
@@ -310,12 +318,11 @@ class DenseCache(_CacheBase):
         Lq = q.shape[1]
         _need(q, "q", self.tdtype, (self.batch, Lq, cfg.n_heads, self.d_h), self.device)
         if out is None:
-            out = torch.empty((self.batch, Lq, cfg.n_heads, self.d_h), dtype=torch.float32,
-                              device=self.device)
+            out = _alloc((self.batch, Lq, cfg.n_heads, self.d_h), torch.float32, self.device, stream)
         _need(out, "out", torch.float32, (self.batch, Lq, cfg.n_heads, self.d_h), self.device)
         need = self.workspace_bytes(Lq)
         if workspace is None and need > 0:
-            workspace = torch.empty(need, dtype=torch.uint8, device=self.device)
+            workspace = _alloc(need, torch.uint8, self.device, stream)
         wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
         _check(lib().mha_attend(self._h, _ptr(q), int(q_token0), int(Lq), _ptr(out),
                                 _ptr(workspace), wbytes, _stream(stream)), "mha_attend")
@@ -347,6 +354,3 @@ def expand_attend_flops(n_heads, Lq, Lk, d_c, d_rope, d_nope, d_v, batch=1):
 def mha_attend_flops(n_heads, Lq, Lk, d_h, batch=1):
     return batch * n_heads * Lq * Lk * 4 * d_h
 
-
-def qscale(d_qk):
-    return math.log2(math.e) / math.sqrt(d_qk)

@@ -117,6 +117,12 @@ int fake_sched_group_slots(int which, int grp) {
   return mla::sched_group_slots(sched_of(which), grp);
 }
 float fake_attend_qscale() { return g_attend.qscale; }
+// The last latent attend's workspace pointers: qcat, qcat_lo, opart, ml.
+void fake_attend_ptrs(long long* o) {
+  long long v[4] = {(long long)(intptr_t)g_attend.qcat, (long long)(intptr_t)g_attend.qcat_lo,
+                    (long long)(intptr_t)g_attend.opart, (long long)(intptr_t)g_attend.ml};
+  memcpy(o, v, sizeof(v));
+}
 // key_slot0, Lk, B, Lq, q_token0, n_rg, n_kt, n_groups, n_blocks, full_rounds, rem,
 // main_len, tail_per_block, n_slots, block_rows, key_tile, stages
 void fake_mha_info(long long* o) {
@@ -135,13 +141,14 @@ void fake_expand_info(long long* o) {
                      (long long)(intptr_t)a.w_uk};
   memcpy(o, v, sizeof(v));
 }
-// The last dense attend's ring_rows, d_h, ring, qrot, opart, ml, q, out pointers and qscale*1e6.
+// The last dense attend's ring_rows, d_h, ring, qrot, opart, ml, q, out pointers,
+// qscale*1e6 and the qrot_lo pointer.
 void fake_mha_ptrs(long long* o) {
   const mla::MhaAttendArgs& a = g_mha;
-  long long v[9] = {a.ring_rows, a.d_h, (long long)(intptr_t)a.ring, (long long)(intptr_t)a.qrot,
-                    (long long)(intptr_t)g_mha_opart, (long long)(intptr_t)g_mha_ml,
-                    (long long)(intptr_t)a.q, (long long)(intptr_t)a.out,
-                    (long long)llround((double)a.qscale * 1e6)};
+  long long v[10] = {a.ring_rows, a.d_h, (long long)(intptr_t)a.ring, (long long)(intptr_t)a.qrot,
+                     (long long)(intptr_t)g_mha_opart, (long long)(intptr_t)g_mha_ml,
+                     (long long)(intptr_t)a.q, (long long)(intptr_t)a.out,
+                     (long long)llround((double)a.qscale * 1e6), (long long)(intptr_t)a.qrot_lo};
   memcpy(o, v, sizeof(v));
 }
 // which: 0 = last write, 1 = last attend, 2 = last dense attend

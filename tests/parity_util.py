@@ -26,10 +26,16 @@ def parity_stats(got, ref):
     return float(err.max() / np.abs(ref).max()), float(err.sum() / np.abs(ref).sum())
 
 
-def assert_parity(got, ref, dtype="bf16", what=""):
+# bf16 ring (split operands): the gate with a 25% margin.
+BF16_RING_MEAN_REL = 1.5e-3
+
+
+def assert_parity(got, ref, dtype="bf16", what="", mean_lim=None):
     assert np.isfinite(got).all(), f"{what}: non-finite output"
     mx, mean = parity_stats(got, ref)
     lim = (BF16_MAX_REL, BF16_MEAN_REL) if dtype == "bf16" else (F32_MAX_REL, F32_MEAN_REL)
+    if mean_lim is not None:
+        lim = (lim[0], min(lim[1], mean_lim))
     print(f"[parity] {what}: max_rel={mx:.3e} mean_rel={mean:.3e} (limits {lim[0]:.0e}/{lim[1]:.0e})",
           flush=True)
     assert mx <= lim[0] and mean <= lim[1], (what, mx, mean)
@@ -86,12 +92,25 @@ class LatentRun:
         self.gpu.evict(n)
         O.cache_evict(self.ring, n)
 
+    def fill(self, oldest, newest, rows):
+        """Make frames oldest..newest resident with the given stored rows
+        [B, n_frames*T, width] (values exact in the cache type), on the GPU
+        ring (set_state + copy into the resident slots) and in the oracle."""
+        self.gpu.set_state(oldest, newest)
+        self.ring.oldest, self.ring.newest = oldest, newest
+        slots = self.ring.resident_slots()
+        self.store[:, slots, :] = rows
+        ring = self.gpu.ring()
+        t = torch.from_numpy(np.ascontiguousarray(rows)).to(ring.dtype)
+        ring[:, torch.from_numpy(slots)] = t.to(ring.device)
+        torch.cuda.synchronize()
+
     def query(self, Lq, chunk=1000):
         return chunk_q(self.cfg, Lq, layer=self.layer, chunk=chunk)
 
-    def attend(self, q, q_token0, key_splits=0, rows=None):
+    def attend(self, q, q_token0, key_splits=0, rows=None, workspace=None):
         out = self.gpu.attend(dev(q), q_token0, self.wd["w_uk"], self.wd["w_uv"],
-                              key_splits=key_splits)
+                              key_splits=key_splits, workspace=workspace)
         torch.cuda.synchronize()
         ref = O.attend(self.store, self.ring, q.double().numpy(), q_token0,
                        self.w["w_uk"].double().numpy(), self.w["w_uv"].double().numpy(), self.cfg,

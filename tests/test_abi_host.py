@@ -128,8 +128,9 @@ def _mha_info(L):
 
 # Core shapes (block rows, key tile, LDS stages) by rows per row unit, and how
 # many blocks of each fit one compute unit (stages LDS tiles of
-# key_tile * chunks * 16 bytes in 160 KiB; at most eight waves).
-def expected_shape(rows, chunks_per_key=28):
+# key_tile * chunks * 16 bytes in 160 KiB; at most eight waves, or four for
+# the split-operand cores of a bf16 ring, whose chunk shape has four waves).
+def expected_shape(rows, chunks_per_key=28, split=False):
     if rows <= 16:
         br, kt, ns, waves = 16, 32, 2, 1                # one wave of 16 rows (16x16x32 MFMAs)
     elif rows <= 32:
@@ -138,16 +139,18 @@ def expected_shape(rows, chunks_per_key=28):
         br, kt, ns, waves = 64, 32, 4, 4               # four waves of 16 rows
     elif rows <= 128:
         br, kt, ns, waves = 128, 32, 4, 4
+    elif split:
+        br, kt, ns, waves = 128, 64, 3, 4
     else:
         br, kt, ns, waves = 256, 64, 3, 8
     spans = kt * chunks_per_key // 64 // waves         # tile loads per wave
     return br, kt, min(ns, 1 + 63 // spans)           # in-flight loads fit a 6-bit counter
 
 
-def blocks_per_cu(shape, chunks_per_key):
+def blocks_per_cu(shape, chunks_per_key, split=False):
     br, kt, ns = shape
     waves = 1 if br <= 32 else (4 if br == 64 else br // 32)
-    return min(160 * 1024 // (ns * kt * chunks_per_key * 16), 8 // waves)
+    return min(160 * 1024 // (ns * kt * chunks_per_key * 16), (4 if split else 8) // waves)
 
 
 # Steps charged per segment start by the library's schedule (latent, dense).
@@ -199,7 +202,8 @@ def check_schedule(L, info, R, which=0):
     busy = [s for s in steps if s > 0]
     assert max(busy) <= -(-groups * n_kt // nb) + seg_cost * max(segs) + 1
     costs = [s + seg_cost * k for s, k in zip(steps, segs) if s > 0]
-    assert max(costs) <= min(max(busy), -(-groups * n_kt // nb)) + 2 * seg_cost + 1
+    # (every data-parallel round adds one segment start to every block)
+    assert max(costs) <= min(max(busy), -(-groups * n_kt // nb)) + (2 + info["full_rounds"]) * seg_cost + 1
     # the kernels walk the same steps incrementally
     assert L.fake_sched_cursor_mismatches(which) == 0
 
@@ -356,10 +360,66 @@ def _expand_info(L):
 
 
 def _mha_ptrs(L):
-    a = (ctypes.c_longlong * 9)()
+    a = (ctypes.c_longlong * 10)()
     L.fake_mha_ptrs(a)
-    return dict(zip(["ring_rows", "d_h", "ring", "qrot", "opart", "ml", "q", "out", "qscale_u"],
-                    list(a)))
+    return dict(zip(["ring_rows", "d_h", "ring", "qrot", "opart", "ml", "q", "out", "qscale_u",
+                     "qrot_lo"], list(a)))
+
+
+def _attend_ptrs(L):
+    a = (ctypes.c_longlong * 4)()
+    L.fake_attend_ptrs(a)
+    return dict(zip(["qcat", "qcat_lo", "opart", "ml"], list(a)))
+
+
+def test_bf16_ring_split_operands_and_no_expansion(sim):
+    """A bf16 ring runs the attention core on split operands: the workspace
+    carries the query remainders after the queries, the chunk shape has four
+    waves (one per SIMD), and there is no expand path (MLA_ERR_UNSUPPORTED
+    when asked for, the absorbed form on automatic).  fp16 rings do not split."""
+    ws = 1 << 40
+    for cache_dtype in ("bf16", "f16"):
+        split = cache_dtype == "bf16"
+        st, h = _create(sim, _cfg(cache_dtype=cache_dtype))
+        assert st == 0 and sim.mla_cache_set_state(h, 3, 23) == 0
+        assert sim.mla_cache_set_attend_path(h, 2) == (8 if split else 0)
+        assert sim.mla_attend_path(h, 4680, 0) == (1 if split else 2)
+        assert sim.mla_cache_set_attend_path(h, 1) == 0
+        for Lq in (1, 4, 8, 11, 100, 4680):
+            R = Lq * 12
+            need = sim.mla_attend_workspace_bytes(h, Lq, 0)
+            assert sim.mla_attend(h, P(FAKE_PTR), 21 * 1560, Lq, P(FAKE_PTR), P(FAKE_PTR),
+                                  P(FAKE_PTR), 0, P(ws), need, None) == 0
+            a = _attend_info(sim)
+            shape = expected_shape(R, split=split)
+            assert (a["block_rows"], a["key_tile"], a["stages"]) == shape, (cache_dtype, Lq)
+            check_schedule(sim, a, R)
+            resident = 256 * blocks_per_cu(shape, 224 // 8, split)
+            assert a["n_blocks"] == min(resident, -(-a["n_groups"] * a["n_kt"] // 8))
+            p = _attend_ptrs(sim)
+            qbytes = -(-R * 224 * 2 // 256) * 256
+            assert p["qcat"] == ws
+            if split:
+                assert p["qcat_lo"] == ws + qbytes and p["opart"] == ws + 2 * qbytes
+            else:
+                assert p["qcat_lo"] == 0 and p["opart"] == ws + qbytes
+            slots = a["n_slots"]
+            assert p["ml"] == p["opart"] + -(-slots * R * 192 * 4 // 256) * 256
+            assert need >= p["ml"] - ws + slots * R * 8
+        st, d = _create(sim, _cfg(cache_dtype=cache_dtype), dense=True)
+        assert sim.mla_cache_set_state(d, 0, 20) == 0
+        for Lq in (1, 40, 129, 4680):
+            need = sim.mha_attend_workspace_bytes(d, Lq)
+            assert sim.mha_attend(d, P(FAKE_PTR), 0, Lq, P(FAKE_PTR), P(ws), need, None) == 0
+            a, p = _mha_info(sim), _mha_ptrs(sim)
+            shape = expected_shape(Lq, 32, split)
+            assert (a["block_rows"], a["key_tile"], a["stages"]) == shape
+            lq_pad = -(-Lq // shape[0]) * shape[0]
+            qbytes = -(-12 * lq_pad * 128 * 2 // 256) * 256
+            assert p["qrot"] == ws
+            assert p["qrot_lo"] == (ws + qbytes if split else 0)
+            assert p["opart"] == ws + (2 if split else 1) * qbytes
+            check_schedule(sim, a, 12 * lq_pad, which=1)
 
 
 def test_attend_path_choice(sim):
@@ -528,6 +588,52 @@ def test_expand_reuse_skips_rebuild_only_while_unchanged(sim):
     assert sim.mla_cache_set_expand_reuse(h, 2) == 1
     st, d = _create(sim, c, dense=True)
     assert sim.mla_cache_set_expand_reuse(d, 1) == 9
+
+
+def test_expand_reuse_sees_writes_by_other_handles(sim):
+    """Expand reuse is process-wide aware of the workspace: another handle's
+    attend (latent expand or absorbed, or dense) on the same or an overlapping
+    workspace between two attends of handle A forces A to rebuild; another
+    handle on a disjoint workspace does not."""
+    c = _cfg()
+    _, a = _create(sim, c)
+    _, b = _create(sim, c)
+    _, d = _create(sim, c, dense=True)
+    for h in (a, b, d):
+        assert sim.mla_cache_set_state(h, 0, 20) == 0
+    assert sim.mla_cache_set_attend_path(a, 2) == 0 and sim.mla_cache_set_expand_reuse(a, 1) == 0
+    ws = 1 << 40
+    other = ws + (1 << 37)
+    wuk, wuv = FAKE_PTR + 256, FAKE_PTR + 512
+
+    def attend_a():
+        n = sim.fake_count()
+        assert sim.mla_attend(a, P(FAKE_PTR), 0, 4680, P(wuk), P(wuv), P(FAKE_PTR), 0, P(ws),
+                              1 << 36, None) == 0
+        return sim.fake_count() - n      # 2 with a rebuild, 1 without
+
+    def attend_b(w, path):
+        assert sim.mla_cache_set_attend_path(b, path) == 0
+        assert sim.mla_attend(b, P(FAKE_PTR), 0, 4680, P(wuk), P(wuv), P(FAKE_PTR), 0, P(w),
+                              1 << 36, None) == 0
+
+    assert attend_a() == 2 and attend_a() == 1
+    attend_b(ws, 2)                      # B expands into A's workspace
+    assert attend_a() == 2 and attend_a() == 1
+    attend_b(ws, 1)                      # B's absorbed attend overwrites it
+    assert attend_a() == 2 and attend_a() == 1
+    attend_b(ws + 4096, 2)               # overlapping range
+    assert attend_a() == 2 and attend_a() == 1
+    need = sim.mha_attend_workspace_bytes(d, 16)
+    assert sim.mha_attend(d, P(FAKE_PTR), 0, 16, P(FAKE_PTR), P(ws + 256), need, None) == 0
+    assert attend_a() == 2 and attend_a() == 1
+    attend_b(other, 2)                   # a disjoint workspace leaves A's window alone
+    attend_b(other, 1)
+    assert attend_a() == 1
+    sim.mla_cache_destroy(b)
+    sim.mla_cache_destroy(d)
+    assert attend_a() == 1
+    sim.mla_cache_destroy(a)
 
 
 def test_dense_attend_schedule(sim):

@@ -84,6 +84,16 @@ def test_f16_rounding_matches_torch():
     np.testing.assert_array_equal(O.round_to_f16(v.astype(np.float64)), want)
 
 
+def test_f16_rounding_overflows_to_infinity_past_the_range():
+    """IEEE binary16: the largest finite value is 65504; values round to it up
+    to half an ulp (16) past it, and to infinity from 65520 on."""
+    v = np.array([65504.0, 65519.99, 65520.0, 1e6, -65520.0, -65504.0])
+    got = O.round_to_f16(v)
+    np.testing.assert_array_equal(got, [65504.0, 65504.0, np.inf, np.inf, -np.inf, -65504.0])
+    want = torch.from_numpy(v.astype(np.float32)).to(torch.float16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(got, want)
+
+
 def test_f32_rounding_matches_torch():
     v = np.random.default_rng(2).standard_normal(1000) * 1e3
     want = torch.from_numpy(v).to(torch.float32).to(torch.float64).numpy()
