@@ -86,7 +86,8 @@ typedef enum {
   MLA_ERR_WORKSPACE = 7,         /* workspace missing or smaller than required     */
   MLA_ERR_UNSUPPORTED = 8,       /* shape valid but not built for this dtype       */
   MLA_ERR_WRONG_KIND = 9,        /* latent call on a dense handle or vice versa    */
-  MLA_ERR_HIP = 10               /* kernel launch failed                           */
+  MLA_ERR_HIP = 10,              /* kernel launch failed                           */
+  MLA_ERR_SCRATCH = 11           /* call needs more than the static scratch        */
 } mla_status;
 
 typedef enum { MLA_F32 = 0, MLA_BF16 = 1, MLA_F16 = 2 } mla_dtype;
@@ -194,6 +195,25 @@ size_t mla_attend_workspace_bytes(const mla_cache* cache, int32_t Lq, int32_t ke
 mla_status mla_attend(mla_cache* cache, const void* q, int64_t q_token0, int32_t Lq,
                       const void* w_uk, const void* w_uv, float* out, int32_t key_splits,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Allocation-free mla_attend, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same computation on the same path as mla_attend (the
+ * handle's mla_attend_path for Lq and key_splits), with the workspace taken
+ * from a static device array inside the library instead of the caller.  That
+ * array holds mla_attend_noalloc_max_bytes() bytes (64 MiB) on every GPU the
+ * library runs on, until the process ends; a call whose workspace in the
+ * window's current state would exceed it returns MLA_ERR_SCRATCH and enqueues
+ * nothing (decode-like calls of up to 16 queries fit at any batch up to 16).
+ * Every call on one GPU shares that GPU's array: calls that may overlap in
+ * time on one GPU (different streams, different host threads) race and must
+ * be ordered by the caller.  Other errors as mla_attend. */
+mla_status mla_attend_noalloc(mla_cache* cache, const void* q, int64_t q_token0, int32_t Lq,
+                              const void* w_uk, const void* w_uv, float* out, int32_t key_splits,
+                              void* stream);
+
+/* Size of mla_attend_noalloc's static scratch in bytes. */
+size_t mla_attend_noalloc_max_bytes(void);
 
 /* How mla_attend computes (mla_cache_set_attend_path / mla_attend_path).
  * MLA_PATH_ABSORBED: scores and value sums in the d_c-wide latent space with

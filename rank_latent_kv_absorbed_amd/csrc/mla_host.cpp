@@ -723,6 +723,26 @@ mla_status mla_attend(mla_cache* h, const void* q, int64_t q_token0, int32_t Lq,
   return launch_status(mla::launch_attend_bf16(a, s));
 }
 
+mla_status mla_attend_noalloc(mla_cache* h, const void* q, int64_t q_token0, int32_t Lq,
+                              const void* w_uk, const void* w_uv, float* out, int32_t key_splits,
+                              void* stream) {
+  if (h == nullptr || Lq <= 0 || key_splits < 0) return MLA_ERR_INVALID_ARG;
+  if (h->dense) return MLA_ERR_WRONG_KIND;
+  if (n_resident(h) <= 0) return MLA_ERR_EMPTY;
+  if ((int64_t)Lq * h->cfg.n_heads >= (1LL << 30)) return MLA_ERR_INVALID_ARG;
+  // The workspace this call needs in the window's current state.
+  size_t need = 0;
+  if (h->cfg.dtype != MLA_F32)
+    need = attend_path_for(h, Lq, key_splits) == MLA_PATH_EXPAND ? expand_layout(h, Lq).total
+                                                                 : latent_layout(h, Lq, key_splits).total;
+  if (need > mla::kScratchBytes) return MLA_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (mla::scratch_for_current_device(&ws) != hipSuccess || ws == nullptr) return MLA_ERR_HIP;
+  return mla_attend(h, q, q_token0, Lq, w_uk, w_uv, out, key_splits, ws, mla::kScratchBytes, stream);
+}
+
+size_t mla_attend_noalloc_max_bytes(void) { return mla::kScratchBytes; }
+
 size_t mha_attend_workspace_bytes(const mla_cache* h, int32_t Lq) {
   if (h == nullptr || !h->dense || Lq <= 0) return 0;
   if (h->cfg.dtype == MLA_F32) return 0;
@@ -800,6 +820,7 @@ const char* mla_status_str(mla_status st) {
     case MLA_ERR_UNSUPPORTED: return "shape not supported for this dtype";
     case MLA_ERR_WRONG_KIND: return "latent call on a dense handle or vice versa";
     case MLA_ERR_HIP: return "kernel launch failed";
+    case MLA_ERR_SCRATCH: return "call needs more workspace than the library's static scratch";
   }
   return "unknown status";
 }

@@ -324,6 +324,12 @@ bool attend_bf16_supported(int d_c, int d_rope, int d_nope, int d_v);
 hipError_t launch_mha_attend_bf16_ws(const MhaAttendArgs& a, float* opart, float* ml,
                                      const Schedule& sched, hipStream_t s);
 
+// Static device scratch of mla_attend_noalloc (mla_noalloc.hip): its size, and
+// its address on the calling thread's current device (looked up once per
+// device; hipErrorInvalidSymbol if the lookup gives nothing).
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+hipError_t scratch_for_current_device(void** out);
+
 // Compute units of the current device (queried once per device).
 int device_cu_count();
 hipError_t launch_mha_attend_f32(const MhaAttendArgs& a, hipStream_t s);

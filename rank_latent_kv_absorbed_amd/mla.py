@@ -30,7 +30,7 @@ class MlaError(RuntimeError):
 
 # status codes (include/mla.h)
 OK, ERR_INVALID_ARG, ERR_STORAGE_TOO_SMALL, ERR_FULL, ERR_NOT_CONTIGUOUS, ERR_EVICT_RANGE, \
-    ERR_EMPTY, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_WRONG_KIND, ERR_HIP = range(11)
+    ERR_EMPTY, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_WRONG_KIND, ERR_HIP, ERR_SCRATCH = range(12)
 F32, BF16, F16 = 0, 1, 2
 _DTYPES = {"f32": (F32, torch.float32), "bf16": (BF16, torch.bfloat16), "f16": (F16, torch.float16)}
 
@@ -70,6 +70,8 @@ SIGNATURES = {
     "mla_cache_slot": (_I64, [_HANDLE, _I64, _I32]),
     "mla_attend_workspace_bytes": (_SZ, [_HANDLE, _I32, _I32]),
     "mla_attend": (_I32, [_HANDLE, _VP, _I64, _I32, _VP, _VP, _VP, _I32, _VP, _SZ, _VP]),
+    "mla_attend_noalloc": (_I32, [_HANDLE, _VP, _I64, _I32, _VP, _VP, _VP, _I32, _VP]),
+    "mla_attend_noalloc_max_bytes": (_SZ, []),
     "mha_attend_workspace_bytes": (_SZ, [_HANDLE, _I32]),
     "mha_attend": (_I32, [_HANDLE, _VP, _I64, _I32, _VP, _VP, _SZ, _VP]),
     "mla_cache_set_profile_events": (_I32, [_HANDLE, _VP, _VP]),
@@ -282,6 +284,21 @@ class LatentCache(_CacheBase):
         _check(lib().mla_attend(self._h, _ptr(q), int(q_token0), int(Lq), _ptr(w_uk), _ptr(w_uv),
                                 _ptr(out), int(key_splits), _ptr(workspace), wbytes,
                                 _stream(stream)), "attend")
+        return out
+
+
+    def attend_noalloc(self, q, q_token0, w_uk, w_uv, out, key_splits=0, stream=None):
+        """mla_attend_noalloc: the workspace comes from the library's static
+        device scratch; `out` must be given (nothing is allocated)."""
+        cfg = self.cfg
+        Lq = q.shape[1]
+        _need(q, "q", self.tdtype, (self.batch, Lq, cfg.n_heads, cfg.d_nope + cfg.d_rope), self.device)
+        _need(w_uk, "w_uk", self.tdtype, (cfg.n_heads, cfg.d_nope, cfg.d_c), self.device)
+        _need(w_uv, "w_uv", self.tdtype, (cfg.n_heads, cfg.d_v, cfg.d_c), self.device)
+        _need(out, "out", torch.float32, (self.batch, Lq, cfg.n_heads, cfg.d_v), self.device)
+        _check(lib().mla_attend_noalloc(self._h, _ptr(q), int(q_token0), int(Lq), _ptr(w_uk),
+                                        _ptr(w_uv), _ptr(out), int(key_splits), _stream(stream)),
+               "attend_noalloc")
         return out
 
 

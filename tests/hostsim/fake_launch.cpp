@@ -57,6 +57,11 @@ bool expand_supported(int d_c, int d_rope, int d_nope, int d_v) {
 }
 hipError_t launch_expand_kv(const ExpandArgs& a, hipStream_t) { g_expand = a; return rec(7); }
 hipError_t launch_mha_attend_f32(const MhaAttendArgs& a, hipStream_t) { g_mha = a; return rec(6); }
+// The static scratch stands at a fixed fake address (never dereferenced).
+hipError_t scratch_for_current_device(void** out) {
+  *out = (void*)(uintptr_t)(3ULL << 40);
+  return hipSuccess;
+}
 }  // namespace mla
 
 extern "C" {
