@@ -12,9 +12,9 @@
 //     written as [B][Lk][2][n_h][d_h] in the ring's element type - the layout
 //     of the dense cache, so the same attention core reads it.  A workgroup
 //     owns one head and a range of keys of one sequence: the head's whole
-//     [d_nope + d_v][d_c] matrix is loaded into LDS once (direct
-//     global->LDS loads for a bf16 ring, converted to fp16 on the way for an
-//     fp16 ring), then each wave independently walks 32-key blocks:
+//     [d_nope + d_v][d_c] matrix is loaded into LDS once (converted from bf16
+//     to fp16 on the way; only fp16 rings expand), then each wave
+//     independently walks 32-key blocks:
 //     latent rows into registers (MFMA A operand), D[key][col] =
 //     c[key][:] . W[col][:] on 32x32x16 MFMA per 32-row weight tile (B
 //     operand from LDS), the head's key and value blocks staged in the wave's
@@ -36,6 +36,7 @@ constexpr int kExpandKTiles = kExpandNope / 32, kExpandTiles = kExpandKTiles + k
 // [x * keys_per_block, (x + 1) * keys_per_block).
 template <typename E, int DC>
 __global__ __launch_bounds__(kExpandWaves * 64) void expand_kv_kernel(ExpandArgs a, int keys_per_block) {
+  static_assert(__is_same(E, f16_t), "only fp16 rings expand");
   typedef typename Elem<E>::v8 V8;
   constexpr int NKS = DC / 16;         // MFMA depth steps
   constexpr int CPR = DC / 8;          // 16-byte chunks per weight row
@@ -62,13 +63,12 @@ __global__ __launch_bounds__(kExpandWaves * 64) void expand_kv_kernel(ExpandArgs
   // 16 lanes of an operand read, rows 0..15 at one chunk, then touch 64
   // distinct banks.  Lane l of span sp fills LDS chunk c = 64 sp + l: row
   // c / CPR, position c % CPR of the rows of all tiles.
-  // The rows come straight from W^K_up,h and W^V_up,h (bf16): a bf16 ring
-  // copies them into LDS with direct loads, an fp16 ring converts them on the
-  // way (exact for these weights' range).
+  // The rows come straight from W^K_up,h and W^V_up,h (bf16), converted to
+  // fp16 on the way (exact for magnitudes in [6.1e-5, 65504]; smaller weights
+  // land in fp16's subnormal range with an absolute quantum of 2^-24).
   {
     const bf16_t* src_k = (const bf16_t*)a.w_uk + (size_t)h * kExpandNope * DC;
     const bf16_t* src_v = (const bf16_t*)a.w_uv + (size_t)h * kExpandDv * DC;
-    lds_char* const wl = (lds_char*)wts;
     constexpr int SPW = (WSPANS + kExpandWaves - 1) / kExpandWaves;  // spans per wave
     auto chunk_src = [&](int sp) MLA_INLINE {
       const int c = sp * 64 + l;
@@ -78,9 +78,7 @@ __global__ __launch_bounds__(kExpandWaves * 64) void expand_kv_kernel(ExpandArgs
       const int wr = (r & ~31) + 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3);
       return (wr < kExpandNope ? src_k + wr * DC : src_v + (wr - kExpandNope) * DC) + q * 8;
     };
-    if constexpr (__is_same(E, bf16_t)) {
-      for (int sp = w; sp < WSPANS; sp += kExpandWaves) global_to_lds16(chunk_src(sp), wl + sp * 1024);
-    } else {
+    {
       // every load of the wave first, then the conversions and LDS stores
       bf16x8 v[SPW];
 #pragma unroll
@@ -272,8 +270,9 @@ bool expand_supported(int d_c, int d_rope, int d_nope, int d_v) {
          d_v == kExpandDv;
 }
 
+// Only fp16 rings expand (the host refuses the expansion for a bf16 ring).
 hipError_t launch_expand_kv(const ExpandArgs& a, hipStream_t s) {
-  return a.cache_type == 2 ? launch_expand_typed<f16_t>(a, s) : launch_expand_typed<bf16_t>(a, s);
+  return a.cache_type == 2 ? launch_expand_typed<f16_t>(a, s) : hipErrorInvalidValue;
 }
 
 }  // namespace mla
