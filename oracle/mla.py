@@ -230,11 +230,21 @@ def new_store(batch, window_frames, tokens_per_frame, width, fill=0.0):
     return np.full((batch, window_frames * tokens_per_frame, width), fill, dtype=np.float64)
 
 
-def cache_write(store, ring, x, w_dkr, frame0, n_frames, cfg, storage="bf16"):
+def rms_norm(v, gamma, eps):
+    """Root-mean-square normalisation over the last axis:
+    gamma * v / sqrt(mean(v^2) + eps)."""
+    v = np.asarray(v, dtype=np.float64)
+    ms = np.mean(v * v, axis=-1, keepdims=True)
+    return np.asarray(gamma, dtype=np.float64) * v / np.sqrt(ms + eps)
+
+
+def cache_write(store, ring, x, w_dkr, frame0, n_frames, cfg, storage="bf16", kv_norm=None):
     """Write n_frames whole latent frames of layer input x into the ring.
 
-    store : [B, W*T, d_c + d_rope] float64, updated in place
-    x     : [B, n_frames*T, hidden]
+    store   : [B, W*T, d_c + d_rope] float64, updated in place
+    x       : [B, n_frames*T, hidden]
+    kv_norm : optional (gamma [d_c], eps): the latent c is RMS-normalised
+              (rms_norm) before it is stored; k^R is not.
     Returns the (unrounded) rows [B, n_frames*T, d_c + d_rope] for inspection.
     """
     T = cfg.grid_h * cfg.grid_w
@@ -244,6 +254,8 @@ def cache_write(store, ring, x, w_dkr, frame0, n_frames, cfg, storage="bf16"):
     ring.write(frame0, n_frames)
     y = x @ w.T                                          # [B, n*T, d_c + d_rope]
     c = y[..., :cfg.d_c]
+    if kv_norm is not None:
+        c = rms_norm(c, kv_norm[0], kv_norm[1])
     g = frame0 * T + np.arange(n_frames * T)
     kr = rope3d(y[..., cfg.d_c:], token_position(g, cfg.grid_h, cfg.grid_w),
                 cfg.rope_split, cfg.rope_base)
@@ -300,6 +312,34 @@ def attend(store, ring, q, q_token0, w_uk, w_uv, cfg, rows=None, block=512):
             p /= p.sum(axis=-1, keepdims=True)
             out[:, r0:r0 + len(rb), h, :] = p @ V
     return out
+
+
+# ----------------------------------------------------------------------------
+# The attention block from the layer input to model width.  Around the steps
+# above sit the layer's query projection (each head's [q^nope | q^R], the
+# split of 手法 item 3) and its output projection W^O over the heads'
+# concatenated outputs; the pages print neither, and the readings here are the
+# plain ones: q = W_q x, out = W_O [o_1; ...; o_n_h].
+#   w_q : [n_h * (d_nope + d_rope), hidden]   head h's rows are [W^nope_q,h ; W^R_q,h]
+#   w_o : [hidden, n_h * d_v]                 head h's columns follow o_h
+# ----------------------------------------------------------------------------
+
+
+def query_projection(x, w_q, cfg):
+    """Per-head queries [B, L, n_h, d_nope + d_rope] (q^R not yet rotated)."""
+    x = np.asarray(x, dtype=np.float64)
+    B, L, _ = x.shape
+    return (x @ np.asarray(w_q, dtype=np.float64).T).reshape(B, L, cfg.n_heads, cfg.d_nope + cfg.d_rope)
+
+
+def attend_block(store, ring, x, q_token0, w_q, w_uk, w_uv, w_o, cfg, rows=None):
+    """Query tokens' layer input x [B, Lq, hidden] -> [B, len(rows), hidden]:
+    queries from the projection, attention over the window exactly as in
+    attend (explicit per-head rebuild), then W_O over the heads' outputs."""
+    q = query_projection(x, w_q, cfg)
+    o = attend(store, ring, q, q_token0, w_uk, w_uv, cfg, rows=rows)
+    B, R = o.shape[:2]
+    return o.reshape(B, R, cfg.n_heads * cfg.d_v) @ np.asarray(w_o, dtype=np.float64).T
 
 
 # ----------------------------------------------------------------------------

@@ -7,5 +7,5 @@ oracle side and the HIP side of a parity test receive the same arrays from it.
 
 from .configs import LayerConfig, CONFIGS, config  # noqa: F401
 from .generators import (  # noqa: F401
-    layer_weights, chunk_x, chunk_q, dense_weights, to_storage_tensor,
+    layer_weights, chunk_x, chunk_q, dense_weights, block_weights, to_storage_tensor,
 )

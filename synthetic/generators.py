@@ -2,7 +2,8 @@
 
 Every draw comes from NumPy's PCG64 seeded with SeedSequence([seed, layer,
 chunk, stream]); stream 0 = latent-path weights, 1 = layer input x, 2 = query,
-3 = dense-comparison weights.  Values are drawn in float64 and rounded to the
+3 = dense-comparison weights, 4 = the attention block's query and output
+projections and the latent's normalisation gain.  Values are drawn in float64 and rounded to the
 storage dtype by torch's own dtype conversion (round to nearest even), so the
 arrays handed to the GPU and to the oracle hold identical values.
 
@@ -41,6 +42,19 @@ def layer_weights(cfg, layer=0, seed=None):
     w_uv = g.standard_normal((cfg.n_heads, cfg.d_v, cfg.d_c)) / np.sqrt(cfg.d_c)
     return {k: to_storage_tensor(v, cfg.dtype)
             for k, v in (("w_dkr", w_dkr), ("w_uk", w_uk), ("w_uv", w_uv))}
+
+
+def block_weights(cfg, layer=0, seed=None):
+    """Weights around the latent path: w_q [n_h * (d_nope + d_rope), hidden]
+    (query projection, N(0, 1/hidden)), w_o [hidden, n_h * d_v] (output
+    projection, N(0, 1/(n_h d_v))), kv_gamma [d_c] (RMS-norm gain of the
+    latent, 1 + N(0, 1/16))."""
+    seed = cfg.seed if seed is None else seed
+    g = _rng(seed, layer, 0, 4)
+    w_q = g.standard_normal((cfg.n_heads * cfg.d_qk, cfg.hidden)) / np.sqrt(cfg.hidden)
+    w_o = g.standard_normal((cfg.hidden, cfg.n_heads * cfg.d_v)) / np.sqrt(cfg.n_heads * cfg.d_v)
+    gamma = 1.0 + 0.25 * g.standard_normal(cfg.d_c)
+    return {k: to_storage_tensor(v, cfg.dtype) for k, v in (("w_q", w_q), ("w_o", w_o), ("kv_gamma", gamma))}
 
 
 def dense_weights(cfg, layer=0, seed=None):

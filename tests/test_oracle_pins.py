@@ -449,3 +449,91 @@ def test_dense_mha_oracle_against_torch_sdpa():
         v = (x @ w_v.T)[..., h * d_h:(h + 1) * d_h]
         qh = O.rope3d(q[:, :, h], pos_q, split, cfg.rope_base)
         np.testing.assert_allclose(got[:, :, h], _sdpa(qh, k, v, 1 / math.sqrt(d_h)), rtol=1e-11, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# Steps around the path: latent RMS normalisation, the attention block
+# --------------------------------------------------------------------------
+
+def test_rms_norm_matches_torch_and_its_invariants():
+    rng = np.random.default_rng(31)
+    v = rng.standard_normal((7, 192)) * 3.0
+    gamma = 1.0 + 0.25 * rng.standard_normal(192)
+    got = O.rms_norm(v, gamma, 1e-6)
+    want = torch.nn.functional.rms_norm(torch.from_numpy(v), (192,), torch.from_numpy(gamma), 1e-6).numpy()
+    np.testing.assert_allclose(got, want, rtol=1e-14, atol=1e-14)
+    unit = O.rms_norm(v, np.ones(192), 0.0)
+    np.testing.assert_allclose(np.mean(unit * unit, axis=-1), 1.0, rtol=1e-14)     # unit mean square
+    np.testing.assert_allclose(O.rms_norm(37.5 * v, gamma, 0.0), O.rms_norm(v, gamma, 0.0), rtol=1e-13)
+
+
+def test_cache_write_with_latent_norm_normalises_only_c():
+    cfg = config("tiny").with_(batch=2)
+    rng = np.random.default_rng(32)
+    x = rng.standard_normal((2, cfg.T, cfg.hidden))
+    w = rng.standard_normal((cfg.width, cfg.hidden)) / math.sqrt(cfg.hidden)
+    plain, normed = (O.new_store(2, cfg.window_frames, cfg.T, cfg.width) for _ in range(2))
+    r1, r2 = O.RingModel(cfg.window_frames, cfg.T), O.RingModel(cfg.window_frames, cfg.T)
+    O.cache_write(plain, r1, x, w, 0, 1, cfg, storage=None)
+    O.cache_write(normed, r2, x, w, 0, 1, cfg, storage=None, kv_norm=(np.ones(cfg.d_c), 0.0))
+    slots = r1.resident_slots()
+    np.testing.assert_array_equal(normed[:, slots, cfg.d_c:], plain[:, slots, cfg.d_c:])  # k^R untouched
+    c = normed[:, slots, :cfg.d_c]
+    np.testing.assert_allclose(np.mean(c * c, axis=-1), 1.0, rtol=1e-13)
+    # direction kept: the normalised row is a positive multiple of the plain one
+    ratio = c / plain[:, slots, :cfg.d_c]
+    np.testing.assert_allclose(ratio, ratio[..., :1] * np.ones_like(ratio), rtol=1e-12)
+    assert (ratio > 0).all()
+
+
+def test_attention_block_with_identity_projections_is_the_attention():
+    """hidden = n_h * d_qk = n_h * d_v and identity W_q, W_O: the block is the
+    per-head attention of x read as queries, the heads concatenated."""
+    cfg = config("tiny").with_(hidden=2 * 32)
+    assert cfg.n_heads * cfg.d_qk == cfg.hidden == cfg.n_heads * cfg.d_v
+    rng = np.random.default_rng(33)
+    store = O.round_storage(rng.standard_normal((1, cfg.window_frames * cfg.T, cfg.width)), "f32")
+    ring = O.RingModel(cfg.window_frames, cfg.T)
+    ring.write(0, 3)
+    x = rng.standard_normal((1, 5, cfg.hidden))
+    w_uk = rng.standard_normal((cfg.n_heads, cfg.d_nope, cfg.d_c))
+    w_uv = rng.standard_normal((cfg.n_heads, cfg.d_v, cfg.d_c))
+    eye = np.eye(cfg.hidden)
+    got = O.attend_block(store, ring, x, 40, eye, w_uk, w_uv, eye, cfg)
+    want = O.attend(store, ring, x.reshape(1, 5, cfg.n_heads, cfg.d_qk), 40, w_uk, w_uv, cfg)
+    np.testing.assert_allclose(got, want.reshape(1, 5, cfg.hidden), rtol=1e-13, atol=1e-13)
+
+
+def test_weight_level_folds_give_the_same_block():
+    """The folds the library applies at the weight level -- W^K_up folded into
+    the query projection (q_lat,h = (W_uk,h^T W^nope_q,h) x) and W^V_up into
+    W^O (out = sum_h (W^O_h W_uv,h) o_lat,h) -- compute the explicit block."""
+    cfg = config("tiny")
+    rng = np.random.default_rng(34)
+    store = O.round_storage(rng.standard_normal((1, cfg.window_frames * cfg.T, cfg.width)), "f32")
+    ring = O.RingModel(cfg.window_frames, cfg.T)
+    ring.write(0, 3)
+    n_h, dq, dn, dv, dc = cfg.n_heads, cfg.d_qk, cfg.d_nope, cfg.d_v, cfg.d_c
+    x = rng.standard_normal((1, 6, cfg.hidden))
+    w_q = rng.standard_normal((n_h * dq, cfg.hidden))
+    w_o = rng.standard_normal((cfg.hidden, n_h * dv))
+    w_uk = rng.standard_normal((n_h, dn, dc))
+    w_uv = rng.standard_normal((n_h, dv, dc))
+    want = O.attend_block(store, ring, x, 33, w_q, w_uk, w_uv, w_o, cfg)
+    # folded weights: per head [W_uk,h^T W^nope_q,h ; W^R_q,h] and W^O_h W_uv,h
+    wq = w_q.reshape(n_h, dq, cfg.hidden)
+    w_qf = np.concatenate([np.einsum("hni,hnk->hik", w_uk, wq[:, :dn]), wq[:, dn:]], axis=1)
+    w_fo = np.einsum("chv,hvi->chi", w_o.reshape(cfg.hidden, n_h, dv), w_uv)
+    # absorbed attention with the folded weights, written out directly
+    slots = ring.resident_slots()
+    C, KR = store[0, slots, :dc], store[0, slots, dc:]
+    pos = O.token_position(33 + np.arange(6), cfg.grid_h, cfg.grid_w)
+    got = np.zeros((6, cfg.hidden))
+    for h in range(n_h):
+        qh = x[0] @ w_qf[h].T                                  # [6, d_c + d_rope]
+        qr = O.rope3d(qh[:, dc:], pos, cfg.rope_split, cfg.rope_base)
+        s = (qh[:, :dc] @ C.T + qr @ KR.T) / math.sqrt(dq)
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        got += (p @ C) @ w_fo[:, h, :].T
+    np.testing.assert_allclose(got, want[0], rtol=1e-11, atol=1e-11)
