@@ -151,6 +151,17 @@ void mla_cache_destroy(mla_cache* cache);
 mla_status mla_cache_write(mla_cache* cache, const void* x, const void* w_dkr, int64_t frame0,
                            int32_t n_frames, void* stream);
 
+/* Fused cache write with the latent RMS-normalised before it is stored:
+ *   c = gamma * (W^KV_down x) / sqrt(mean((W^KV_down x)^2) + eps),
+ *   k^R = RoPE3D(W^KR x, position) (not normalised),
+ * otherwise as mla_cache_write.  The pages store the latent of method item 1
+ * and print no normalisation of it; this is the normalisation an MLA layer
+ * commonly applies to its latent before the up-projections, offered for
+ * layers that have one.  gamma: [d_c] gain in the input dtype (bf16); eps >= 0.
+ * MLA_ERR_UNSUPPORTED unless bf16 inputs and d_c + d_rope in {96, 160, 224}. */
+mla_status mla_cache_write_norm(mla_cache* cache, const void* x, const void* w_dkr, const void* gamma,
+                                float eps, int64_t frame0, int32_t n_frames, void* stream);
+
 /* Dense comparison write: per head k_h = RoPE3D((w_k x)_h) over all d_h dims
  * (pairs split t/h/w as P - 2*floor(P/3), floor(P/3), floor(P/3), P = d_h/2),
  * v_h = (w_v x)_h, rounded to cache_dtype. Same window rules. */
@@ -214,6 +225,43 @@ mla_status mla_attend_noalloc(mla_cache* cache, const void* q, int64_t q_token0,
 
 /* Size of mla_attend_noalloc's static scratch in bytes. */
 size_t mla_attend_noalloc_max_bytes(void);
+
+/* The attention block around the absorbed path, from the query tokens' layer
+ * input to model width.  The layer's query projection gives each head
+ * [q^nope | q^R] (method item 3: each head's q.k width split into content and
+ * positional parts) and its output projection W^O maps the heads' outputs,
+ * concatenated, to model width:
+ *   w_q [n_h * (d_nope + d_rope)][hidden]   head h's rows [W^nope_q,h ; W^R_q,h]
+ *   w_o [hidden][n_h * d_v]                 head h's columns take o_h
+ * Folded at the weight level (once per weight set), W^K_up enters the query
+ * projection and W^V_up the output projection:
+ *   w_qf[h] = [W_uk,h^T W^nope_q,h ; W^R_q,h]     [n_h][d_c + d_rope][hidden]
+ *   w_fo    = [W^O_1 W_uv,1 | ... | W^O_n W_uv,n]  [hidden][n_h * d_c]
+ * each stored as two bf16 parts (the fp32 product rounded to bf16, then the
+ * bf16 rounding of the remainder), so the folds keep 16 significant bits:
+ * w_qf is [2][n_h][d_c + d_rope][hidden], w_fo is [2][hidden][n_h * d_c].
+ * mla_fold_*_bytes give their sizes; the folds run on `stream`. */
+size_t mla_fold_query_bytes(const mla_cache* cache);
+size_t mla_fold_output_bytes(const mla_cache* cache);
+mla_status mla_fold_query_weights(const mla_cache* cache, const void* w_q, const void* w_uk, void* w_qf,
+                                  size_t w_qf_bytes, void* stream);
+mla_status mla_fold_output_weights(const mla_cache* cache, const void* w_o, const void* w_uv, void* w_fo,
+                                   size_t w_fo_bytes, void* stream);
+
+/* Workspace of mla_attend_block (the largest over every number of resident
+ * frames), 0 for handles without the block. */
+size_t mla_attend_block_workspace_bytes(const mla_cache* cache, int32_t Lq, int32_t key_splits);
+
+/* out = W_O [o_1; ...; o_n_h] for the queries q = W_q x of x [batch][Lq][hidden]
+ * (row i at global token q_token0 + i), o_h the attention of mla_attend, in
+ * absorbed form with the folded weights: [q_lat | q^R] from x in one product
+ * (rotated and scaled in its epilogue), the latent core, the merged latent
+ * outputs, then out [batch][Lq][hidden] fp32 = w_fo o_lat in one product.
+ * MLA_ERR_UNSUPPORTED unless bf16 inputs, the absorbed core's head shapes,
+ * hidden % 64 == 0 and n_h * d_c % 64 == 0.  Other errors as mla_attend. */
+mla_status mla_attend_block(mla_cache* cache, const void* x, int64_t q_token0, int32_t Lq,
+                            const void* w_qf, const void* w_fo, float* out, int32_t key_splits,
+                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* How mla_attend computes (mla_cache_set_attend_path / mla_attend_path).
  * MLA_PATH_ABSORBED: scores and value sums in the d_c-wide latent space with

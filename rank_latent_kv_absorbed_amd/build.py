@@ -19,7 +19,7 @@ OUT = os.path.join(PKG, "libmla.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
 SOURCES = ["mla_host.cpp", "mla_cache_write.hip", "mla_attend.hip", "mha_attend.hip", "mla_expand.hip",
-           "mla_noalloc.hip"]
+           "mla_noalloc.hip", "mla_block.hip"]
 ARCH = "gfx950"
 
 

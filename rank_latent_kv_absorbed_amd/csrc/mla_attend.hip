@@ -532,6 +532,70 @@ hipError_t launch_core(const AttnCore& c, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+// The core over the prepared queries in a.qcat (profiling events around it).
+template <typename E, int DC>
+hipError_t launch_core_of(const AttendArgs& a, hipStream_t s) {
+  AttnCore c;
+  c.qrows = a.qcat;
+  c.qrows_lo = a.qcat_lo;
+  c.ring = a.ring;
+  c.opart = a.opart;
+  c.ml = a.ml;
+  c.ring_rows = a.ring_rows;
+  c.ring_stride = DC + 32;
+  c.k_off = 0;
+  c.v_off = 0;
+  c.head_stride = 0;
+  c.R = a.Lq * a.n_h;
+  c.rows_per_head = c.R;
+  c.valid_per_head = c.R;
+  c.B = a.B;
+  c.Lk = a.Lk;
+  c.sched = a.sched;
+  c.key_slot0 = a.key_slot0;
+  if (a.ev_start != nullptr) {
+    hipError_t e = hipEventRecord(a.ev_start, s);
+    if (e != hipSuccess) return e;
+  }
+  hipError_t e = launch_core<E, DC>(c, s);
+  if (e != hipSuccess) return e;
+  if (a.ev_stop != nullptr) e = hipEventRecord(a.ev_stop, s);
+  return e;
+}
+
+// Latent outputs of the attention block: thread per (row, 8 latent columns)
+// merges the row's partials by log-sum-exp, normalises, and writes the 8
+// values as two bf16 parts (value, remainder) into token rows
+// [B * Lq][n_h * DC] (row tok * n_h + h of sequence b is that token's head h).
+template <int DC>
+__global__ __launch_bounds__(256) void merge_latent_kernel(AttendArgs a, bf16_t* o_hi, bf16_t* o_lo) {
+  constexpr int C8 = DC / 8;
+  const int R = a.Lq * a.n_h;
+  const int64_t n = (int64_t)a.B * R * C8;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= n) return;
+  const int c8 = (int)(idx % C8);
+  const int64_t br = idx / C8;
+  const int b = (int)(br / R), row = (int)(br - (int64_t)b * R);
+  AttnCore c;
+  c.opart = a.opart;
+  c.ml = a.ml;
+  c.R = R;
+  c.B = a.B;
+  c.sched = a.sched;
+  float acc[8];
+  merge_row_partials(c, DC, b, row, 8 * c8, 8, acc);
+  bf16x8 h8, l8;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    h8[t] = to_bf16(acc[t]);
+    l8[t] = to_bf16(acc[t] - (float)h8[t]);
+  }
+  const size_t off = (size_t)br * DC + 8 * c8;
+  st_bf16x8(o_hi + off, h8);
+  st_bf16x8(o_lo + off, l8);
+}
+
 template <typename E, int DC>
 hipError_t launch_dc(const AttendArgs& a, hipStream_t s) {
   constexpr bool SPLIT = kSplitOf<E>;
@@ -549,34 +613,8 @@ hipError_t launch_dc(const AttendArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   {
-    AttnCore c;
-    c.qrows = a.qcat;
-    c.qrows_lo = a.qcat_lo;
-    c.ring = a.ring;
-    c.opart = a.opart;
-    c.ml = a.ml;
-    c.ring_rows = a.ring_rows;
-    c.ring_stride = DC + 32;
-    c.k_off = 0;
-    c.v_off = 0;
-    c.head_stride = 0;
-    c.R = a.Lq * a.n_h;
-    c.rows_per_head = c.R;
-    c.valid_per_head = c.R;
-    c.B = a.B;
-    c.Lk = a.Lk;
-    c.sched = a.sched;
-    c.key_slot0 = a.key_slot0;
-    if (a.ev_start != nullptr) {
-      hipError_t e = hipEventRecord(a.ev_start, s);
-      if (e != hipSuccess) return e;
-    }
-    hipError_t e = launch_core<E, DC>(c, s);
+    hipError_t e = launch_core_of<E, DC>(a, s);
     if (e != hipSuccess) return e;
-    if (a.ev_stop != nullptr) {
-      e = hipEventRecord(a.ev_stop, s);
-      if (e != hipSuccess) return e;
-    }
   }
   // Rows with many key-range partials each (narrow blocks on 32-key tiles,
   // or few row groups spread over the whole device) merge one row per block;
@@ -613,6 +651,29 @@ hipError_t launch_typed(const AttendArgs& a, hipStream_t s) {
     case 192: return launch_dc<E, 192>(a, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_attend_core_only(const AttendArgs& a, hipStream_t s) {
+  const bool f16 = a.cache_type == 2;
+  if ((a.qcat_lo != nullptr) == f16) return hipErrorInvalidValue;
+  switch (a.d_c) {
+    case 64: return f16 ? launch_core_of<f16_t, 64>(a, s) : launch_core_of<bf16_t, 64>(a, s);
+    case 128: return f16 ? launch_core_of<f16_t, 128>(a, s) : launch_core_of<bf16_t, 128>(a, s);
+    case 192: return f16 ? launch_core_of<f16_t, 192>(a, s) : launch_core_of<bf16_t, 192>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_merge_latent(const AttendArgs& a, void* o_hi, void* o_lo, hipStream_t s) {
+  const int64_t n = (int64_t)a.B * a.Lq * a.n_h * (a.d_c / 8);
+  const dim3 grid((unsigned)((n + 255) / 256));
+  switch (a.d_c) {
+    case 64: hipLaunchKernelGGL(merge_latent_kernel<64>, grid, dim3(256), 0, s, a, (bf16_t*)o_hi, (bf16_t*)o_lo); break;
+    case 128: hipLaunchKernelGGL(merge_latent_kernel<128>, grid, dim3(256), 0, s, a, (bf16_t*)o_hi, (bf16_t*)o_lo); break;
+    case 192: hipLaunchKernelGGL(merge_latent_kernel<192>, grid, dim3(256), 0, s, a, (bf16_t*)o_hi, (bf16_t*)o_lo); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_attend_bf16(const AttendArgs& a, hipStream_t s) {

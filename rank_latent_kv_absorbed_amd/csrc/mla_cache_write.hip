@@ -2,7 +2,11 @@
 // and 3): one GEMM y = W x over every token of the written frames, 3D-RoPE on
 // the positional columns, round to the storage dtype, scatter each token's row
 // to its ring slot.  The same kernel serves the dense comparison cache (K and
-// V of every head; K rotated per head).
+// V of every head; K rotated per head), and, with other epilogues, the steps
+// on either side of the path (ProjMode in mla_launch.h): the cache write with
+// the latent RMS-normalised, the query projection with W^K_up folded into its
+// weights (each head's [q_lat | q^R] directly from the layer input), and the
+// output projection with W^V_up folded into W^O.
 //
 // 2-byte path (bf16 inputs; bf16 or fp16 ring): a workgroup owns 32 tokens
 // and NT <= 8 32-column tiles of the output, one tile per wave (a d_c = 192
@@ -16,7 +20,10 @@
 // weights as the A operand; the weight rows of a tile are staged in a
 // permuted order so that lane (token lo, hi) ends up holding 16 consecutive
 // output columns of its token, every rotary pair whole, which it rotates,
-// rounds and writes as two 16-byte pieces of the token's ring row.
+// rounds and writes as two 16-byte pieces of the token's ring row.  Weights
+// carried in parts (value and remainder) run the hidden dimension once per
+// part, into the same accumulators.
+
 #include "mla_attn_core.h"
 
 namespace mla {
@@ -25,17 +32,20 @@ namespace {
 
 constexpr int kChunk = 64;  // hidden elements per staged chunk (128-byte rows)
 
-template <typename E, int NT>
+template <typename E, int NT, int MODE = PROJ_CACHE, int NP = 1>
 __global__ __launch_bounds__(NT * 64) void cache_write_bf16_kernel(CacheWriteArgs a) {
   constexpr int RB = kChunk * 2;              // staged bytes per row
   constexpr int ROWS = 32 + 32 * NT;          // token rows, then weight rows
   constexpr int SB = ROWS * RB;               // bytes per stage
   constexpr int SPANS = SB / 1024;            // 1-KiB load spans per stage (8 rows each)
   constexpr int SPW = (SPANS + NT - 1) / NT;  // spans per wave; surplus slots repeat the last span
+  constexpr bool RING = MODE == PROJ_CACHE || MODE == PROJ_CACHE_NORM;
   static_assert(SB % 1024 == 0, "whole spans per stage");
+  static_assert(NP >= 1 && NP <= kProjMaxPasses, "projection passes");
   __shared__ __attribute__((aligned(1024))) char st0[SB], st1[SB], st2[SB];
   __shared__ float2 rcs[32][kMaxRopePairs];  // cos, sin per (token, rotary pair)
-  __shared__ int64_t rowoff[32];             // ring row of each token (elements)
+  __shared__ int64_t rowoff[32];             // output row of each token (elements)
+  __shared__ float nss[MODE == PROJ_CACHE_NORM ? 32 : 1][2 * NT];  // partial sums of squares
   const int tid = threadIdx.x;
   const int w = NT == 1 ? 0 : __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63, lo = l & 31, hi = l >> 5;
@@ -50,12 +60,14 @@ __global__ __launch_bounds__(NT * 64) void cache_write_bf16_kernel(CacheWriteArg
   // Lane l of span sp fills row 8 sp + l / 8, slot l % 8.
   const bf16_t* const xg = (const bf16_t*)a.x;
   const char* src[SPW];
+  bool wrow[SPW];  // the span's rows are weight rows (not token rows)
 #pragma unroll
   for (int j = 0; j < SPW; ++j) {
     const int sp = w + j * NT < SPANS ? w + j * NT : SPANS - 1;
     const int row = 8 * sp + (l >> 3);
     const int q = (l & 7) ^ ((row >> 1) & 7);
     const bf16_t* p;
+    wrow[j] = row >= 32;
     if (row < 32) {
       const int64_t t = tok0 + row < a.M ? tok0 + row : a.M - 1;
       p = xg + t * a.hidden;
@@ -71,15 +83,21 @@ __global__ __launch_bounds__(NT * 64) void cache_write_bf16_kernel(CacheWriteArg
   // Workgroups walk the chunks from different starting points: the rows
   // are hidden * 2 bytes apart, so one chunk of every weight row sits in a
   // few L2 channels, which workgroups in lockstep would all hit at once.
+  // With several passes, chunk c of the walk is chunk c % NC of pass c / NC.
   const int NC = a.hidden / kChunk;
+  const int NCT = NP * NC;
   const int rot = (int)(blockIdx.x % (unsigned)NC);
   auto issue = [&](int c, char* stg) MLA_INLINE {
     lds_char* const ls = (lds_char*)stg;
-    const int cr = c + rot < NC ? c + rot : c + rot - NC;
+    const int pass = NP == 1 ? 0 : c / NC;
+    const int cc = NP == 1 ? c : c - pass * NC;
+    const int cr = cc + rot < NC ? cc + rot : cc + rot - NC;
 #pragma unroll
     for (int j = 0; j < SPW; ++j) {
       const int sp = w + j * NT < SPANS ? w + j * NT : SPANS - 1;
-      global_to_lds16(src[j] + cr * RB, ls + sp * 1024);
+      const char* base = src[j];
+      if constexpr (NP > 1) base += wrow[j] ? a.w_part[pass] : a.x_part[pass];
+      global_to_lds16(base + cr * RB, ls + sp * 1024);
     }
   };
 
@@ -118,24 +136,34 @@ __global__ __launch_bounds__(NT * 64) void cache_write_bf16_kernel(CacheWriteArg
     compute(cur);
     wait_vmem(SPW);
     lds_barrier();
-    issue(c + 3 < NC ? c + 3 : NC - 1, cur);
+    issue(c + 3 < NCT ? c + 3 : NCT - 1, cur);
   };
   issue(0, st0);
-  issue(NC > 1 ? 1 : 0, st1);
-  issue(NC > 2 ? 2 : 0, st2);
-  // While the first chunks load: each token's ring row, and cos / sin of
+  issue(NCT > 1 ? 1 : 0, st1);
+  issue(NCT > 2 ? 2 : 0, st2);
+  // While the first chunks load: each token's output row, and cos / sin of
   // every rotary pair of every token (rotated columns c use pair
-  // ((c - rot_begin) % rot_group) / 2).
-  const int npairs = a.rot_end > a.rot_begin ? a.rot_group / 2 : 0;
+  // ((c - rot_begin) % rot_group - rot_skip) / 2).  Cache writes place token
+  // i of a sequence at its ring slot and position (frame0 + i / T, i % T);
+  // projections write token rows and take positions from q_token0 + i.
+  const int npairs = a.rot_end > a.rot_begin ? (a.rot_group - a.rot_skip) / 2 : 0;
   for (int e = tid; e < 32 * (npairs + 1); e += NT * 64) {
     const int r = e & 31, p = (e >> 5) - 1;
     const int64_t t = tok0 + r < a.M ? tok0 + r : a.M - 1;
     const int64_t b = t / a.tokens_per_batch;
     const int i = (int)(t - b * a.tokens_per_batch);
-    const int64_t frame = a.frame0 + i / a.T;
-    const int tau = i % a.T;
+    int64_t frame;
+    int tau;
+    if constexpr (RING) {
+      frame = a.frame0 + i / a.T;
+      tau = i % a.T;
+    } else {
+      const int64_t g = a.q_token0 + i;
+      frame = g / a.T;
+      tau = (int)(g - frame * a.T);
+    }
     if (p < 0) {
-      rowoff[r] = (b * a.ring_rows + (frame % a.W) * a.T + tau) * a.width;
+      rowoff[r] = RING ? (b * a.ring_rows + (frame % a.W) * a.T + tau) * a.width : t * a.width;
     } else {
       TokPos pos;
       pos.f = frame;
@@ -149,40 +177,78 @@ __global__ __launch_bounds__(NT * 64) void cache_write_bf16_kernel(CacheWriteArg
   wait_vmem(2 * SPW);
   lds_barrier();
   int c = 0;
-  for (; c + 3 <= NC; c += 3) {
+  for (; c + 3 <= NCT; c += 3) {
     step(c, st0);
     step(c + 1, st1);
     step(c + 2, st2);
   }
-  if (c < NC) step(c, st0);
-  if (c + 1 < NC) step(c + 1, st1);
+  if (c < NCT) step(c, st0);
+  if (c + 1 < NCT) step(c + 1, st1);
   // No load into LDS may still be in flight when the workgroup ends.
   __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
 
   // Lane (lo, hi) holds columns cb .. cb + 15 of token tok0 + lo.
-  if (tok0 + lo >= a.M || col0 + 32 * w >= a.width) return;
   const int cb = col0 + 32 * w + 16 * hi;
   float v[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) v[r] = acc[r];
+  if constexpr (MODE == PROJ_CACHE_NORM) {
+    // RMS of the token's first norm_cols columns: this workgroup holds the
+    // token's whole row (one wave per 32-column tile), partial sums of squares
+    // meet in LDS.
+    float ss = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ss += cb + r < a.norm_cols ? v[r] * v[r] : 0.0f;
+    nss[lo][2 * w + hi] = ss;
+    __syncthreads();
+    float tot = 0.0f;
+    for (int k = 0; k < 2 * NT; ++k) tot += nss[lo][k];
+    const float inv = 1.0f / sqrtf(tot / (float)a.norm_cols + a.eps);
+    const bf16_t* gam = (const bf16_t*)a.gamma;
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (cb + r < a.norm_cols) v[r] = v[r] * inv * (float)gam[cb + r];
+  }
+  if (tok0 + lo >= a.M || col0 + 32 * w >= a.width) return;
 #pragma unroll
   for (int p = 0; p < 8; ++p) {
     const int c = cb + 2 * p;
     if (c >= a.rot_begin && c < a.rot_end) {
-      const float2 t = rcs[lo][((c - a.rot_begin) % a.rot_group) >> 1];
-      const float ra = v[2 * p] * t.x - v[2 * p + 1] * t.y;
-      const float rb = v[2 * p] * t.y + v[2 * p + 1] * t.x;
-      v[2 * p] = ra;
-      v[2 * p + 1] = rb;
+      const int k = (c - a.rot_begin) % a.rot_group;
+      if (k >= a.rot_skip) {
+        const float2 t = rcs[lo][(k - a.rot_skip) >> 1];
+        const float ra = v[2 * p] * t.x - v[2 * p + 1] * t.y;
+        const float rb = v[2 * p] * t.y + v[2 * p + 1] * t.x;
+        v[2 * p] = ra;
+        v[2 * p + 1] = rb;
+      }
     }
+  }
+  if constexpr (MODE == PROJ_OUT) {
+    float* dst = (float*)a.ring + rowoff[lo] + cb;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      f32x4 o = {v[4 * u], v[4 * u + 1], v[4 * u + 2], v[4 * u + 3]};
+      *reinterpret_cast<f32x4*>(dst + 4 * u) = o;
+    }
+    return;
+  }
+  if constexpr (MODE == PROJ_QUERY) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) v[r] *= a.scale;
   }
   E* dst = (E*)a.ring + rowoff[lo] + cb;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    typename Elem<E>::v8 o;
+    typename Elem<E>::v8 o, ol;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = Elem<E>::from(v[8 * u + e]);
+    for (int e = 0; e < 8; ++e) {
+      o[e] = Elem<E>::from(v[8 * u + e]);
+      ol[e] = Elem<E>::from(v[8 * u + e] - (float)o[e]);
+    }
     *reinterpret_cast<typename Elem<E>::v8*>(dst + 8 * u) = o;
+    if constexpr (MODE == PROJ_QUERY)
+      if (a.out_lo != nullptr) *reinterpret_cast<typename Elem<E>::v8*>((E*)a.out_lo + rowoff[lo] + cb + 8 * u) = ol;
   }
 }
 
@@ -223,10 +289,10 @@ __global__ __launch_bounds__(256) void cache_write_f32_kernel(CacheWriteArgs a) 
   dst[1] = y1;
 }
 
-template <typename E, int NT>
+template <typename E, int NT, int MODE, int NP>
 hipError_t launch_nt(const CacheWriteArgs& a, hipStream_t s) {
   dim3 grid((unsigned)((a.M + 31) / 32), (unsigned)((a.width / 32 + NT - 1) / NT));
-  hipLaunchKernelGGL((cache_write_bf16_kernel<E, NT>), grid, dim3(NT * 64), 0, s, a);
+  hipLaunchKernelGGL((cache_write_bf16_kernel<E, NT, MODE, NP>), grid, dim3(NT * 64), 0, s, a);
   return hipGetLastError();
 }
 
@@ -234,23 +300,52 @@ hipError_t launch_nt(const CacheWriteArgs& a, hipStream_t s) {
 // workgroups per token tile (at most 8 tiles each) that still give every
 // compute unit a workgroup; the last workgroup of a row may own fewer tiles
 // than waves.
-template <typename E>
-hipError_t launch_typed(const CacheWriteArgs& a, hipStream_t s) {
+int tiles_per_group(const CacheWriteArgs& a) {
   const int tiles = a.width / 32;
   const int64_t token_tiles = (a.M + 31) / 32;
   int groups = (tiles + 7) / 8;
   const int cus = device_cu_count();
   while (groups < tiles && token_tiles * groups < cus) ++groups;
-  const int nt = (tiles + groups - 1) / groups;
+  return (tiles + groups - 1) / groups;
+}
+
+template <typename E>
+hipError_t launch_typed(const CacheWriteArgs& a, hipStream_t s) {
+  switch (tiles_per_group(a)) {
+    case 8: return launch_nt<E, 8, PROJ_CACHE, 1>(a, s);
+    case 7: return launch_nt<E, 7, PROJ_CACHE, 1>(a, s);
+    case 6: return launch_nt<E, 6, PROJ_CACHE, 1>(a, s);
+    case 5: return launch_nt<E, 5, PROJ_CACHE, 1>(a, s);
+    case 4: return launch_nt<E, 4, PROJ_CACHE, 1>(a, s);
+    case 3: return launch_nt<E, 3, PROJ_CACHE, 1>(a, s);
+    case 2: return launch_nt<E, 2, PROJ_CACHE, 1>(a, s);
+    default: return launch_nt<E, 1, PROJ_CACHE, 1>(a, s);
+  }
+}
+
+// The normalised cache write keeps a token's whole row in one workgroup (the
+// row's sum of squares meets in LDS): latent rows of 96, 160 or 224 columns.
+template <typename E>
+hipError_t launch_norm(const CacheWriteArgs& a, hipStream_t s) {
+  switch (a.width / 32) {
+    case 7: return launch_nt<E, 7, PROJ_CACHE_NORM, 1>(a, s);
+    case 5: return launch_nt<E, 5, PROJ_CACHE_NORM, 1>(a, s);
+    case 3: return launch_nt<E, 3, PROJ_CACHE_NORM, 1>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// Projections on two- or three-part operands take 1, 2, 4 or 8 tiles per
+// workgroup (the fewest that fill the device, rounded up to a power of two).
+template <typename E, int MODE, int NP>
+hipError_t launch_parts(const CacheWriteArgs& a, hipStream_t s) {
+  int nt = tiles_per_group(a);
+  nt = nt > 4 ? 8 : (nt > 2 ? 4 : nt);
   switch (nt) {
-    case 8: return launch_nt<E, 8>(a, s);
-    case 7: return launch_nt<E, 7>(a, s);
-    case 6: return launch_nt<E, 6>(a, s);
-    case 5: return launch_nt<E, 5>(a, s);
-    case 4: return launch_nt<E, 4>(a, s);
-    case 3: return launch_nt<E, 3>(a, s);
-    case 2: return launch_nt<E, 2>(a, s);
-    default: return launch_nt<E, 1>(a, s);
+    case 8: return launch_nt<E, 8, MODE, NP>(a, s);
+    case 4: return launch_nt<E, 4, MODE, NP>(a, s);
+    case 2: return launch_nt<E, 2, MODE, NP>(a, s);
+    default: return launch_nt<E, 1, MODE, NP>(a, s);
   }
 }
 
@@ -262,6 +357,16 @@ bool cache_write_bf16_supported(int width, int hidden) {
 
 hipError_t launch_cache_write_bf16(const CacheWriteArgs& a, hipStream_t s) {
   return a.out_type == 2 ? launch_typed<f16_t>(a, s) : launch_typed<bf16_t>(a, s);
+}
+
+hipError_t launch_projection_bf16(const CacheWriteArgs& a, int mode, hipStream_t s) {
+  const bool f16 = a.out_type == 2;
+  if (mode == PROJ_CACHE_NORM && a.passes == 1)
+    return f16 ? launch_norm<f16_t>(a, s) : launch_norm<bf16_t>(a, s);
+  if (mode == PROJ_QUERY && a.passes == 2)
+    return f16 ? launch_parts<f16_t, PROJ_QUERY, 2>(a, s) : launch_parts<bf16_t, PROJ_QUERY, 2>(a, s);
+  if (mode == PROJ_OUT && a.passes == 3) return launch_parts<bf16_t, PROJ_OUT, 3>(a, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_cache_write_f32(const CacheWriteArgs& a, hipStream_t s) {

@@ -262,10 +262,12 @@ bool split_operands(const mla_layer_config& c) { return c.cache_dtype == MLA_BF1
 struct LatentLayout {
   mla::Schedule sched;
   size_t qcat_off, qlo_off, opart_off, ml_off, total;
+  size_t ohi_off, olo_off;  // attention block: latent outputs in two bf16 parts
 };
 
 // Layouts for `Lk` resident keys (default: the handle's current window).
-LatentLayout latent_layout(const mla_cache* h, int32_t Lq, int32_t key_splits, int64_t Lk = -1) {
+LatentLayout latent_layout(const mla_cache* h, int32_t Lq, int32_t key_splits, int64_t Lk = -1,
+                           bool block = false) {
   const mla_layer_config& c = h->cfg;
   const int64_t R = (int64_t)Lq * c.n_heads;
   LatentLayout L;
@@ -281,6 +283,13 @@ LatentLayout latent_layout(const mla_cache* h, int32_t Lq, int32_t key_splits, i
   L.opart_off = split ? 2 * qbytes : qbytes;
   L.ml_off = L.opart_off + round_up(slots * c.batch * R * c.d_c * 4, kAlign);
   L.total = L.ml_off + round_up(slots * c.batch * R * 2 * 4, kAlign);
+  L.ohi_off = L.olo_off = L.total;
+  if (block) {
+    const size_t obytes = round_up((size_t)c.batch * R * c.d_c * 2, kAlign);
+    L.ohi_off = L.total;
+    L.olo_off = L.ohi_off + obytes;
+    L.total = L.olo_off + obytes;
+  }
   return L;
 }
 
@@ -392,6 +401,86 @@ mla::RopeTable expand_rope(const mla_layer_config& c) {
 
 mla_status launch_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
 
+// Projection arguments with every optional part off (one pass, no rotation
+// skip, no normalisation, unit scale).
+mla::CacheWriteArgs projection_defaults() {
+  mla::CacheWriteArgs a;
+  memset(&a, 0, sizeof(a));
+  a.passes = 1;
+  a.scale = 1.0f;
+  a.rot_group = 1;
+  return a;
+}
+
+// Latent attention of Lq queries at q_token0 over the current window.
+mla::AttendArgs latent_attend_args(const mla_cache* h, const void* q, int64_t q_token0, int32_t Lq,
+                                   const void* w_uk, const void* w_uv, float* out) {
+  const mla_layer_config& c = h->cfg;
+  mla::AttendArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.ring = h->storage;
+  a.w_uk = w_uk;
+  a.w_uv = w_uv;
+  a.out = out;
+  a.B = c.batch;
+  a.Lq = Lq;
+  a.n_h = c.n_heads;
+  a.d_nope = c.d_nope;
+  a.d_rope = c.d_rope;
+  a.d_v = c.d_v;
+  a.d_c = c.d_c;
+  a.q_token0 = q_token0;
+  a.T = (int)tokens_per_frame(c);
+  a.grid_w = c.grid_w;
+  a.ring_rows = (int64_t)c.window_frames * a.T;
+  a.key_slot0 = (h->oldest % c.window_frames) * a.T;
+  a.Lk = (int)(n_resident(h) * a.T);
+  a.cache_type = c.cache_dtype;
+  a.qscale = (float)(1.4426950408889634 / sqrt((double)(c.d_nope + c.d_rope)));
+  a.ev_start = h->prof_start;
+  a.ev_stop = h->prof_stop;
+  a.rope = latent_rope(c);
+  return a;
+}
+
+// The attention block's shapes: 2-byte rings of the absorbed core's head
+// shapes, and projection widths the GEMM tiles (32 output columns, 64-element
+// depth chunks).
+bool block_supported(const mla_layer_config& c) {
+  return c.dtype == MLA_BF16 && mla::attend_bf16_supported(c.d_c, c.d_rope, c.d_nope, c.d_v) &&
+         c.hidden % 64 == 0 && (c.n_heads * (c.d_c + c.d_rope)) % 32 == 0 &&
+         (c.n_heads * c.d_c) % 64 == 0;
+}
+
+// The latent cache write of n_frames frames from frame0.
+mla::CacheWriteArgs latent_write_args(const mla_cache* h, const void* x, const void* w_dkr,
+                                      int64_t frame0, int32_t n_frames) {
+  const mla_layer_config& c = h->cfg;
+  const int width = c.d_c + c.d_rope;
+  mla::CacheWriteArgs a = projection_defaults();
+  a.x = x;
+  a.w = w_dkr;
+  a.w2 = w_dkr;
+  a.w_split = width;
+  a.ring = h->storage;
+  a.tokens_per_batch = (int)(n_frames * tokens_per_frame(c));
+  a.M = (int64_t)c.batch * a.tokens_per_batch;
+  a.hidden = c.hidden;
+  a.width = width;
+  a.rot_begin = c.d_c;
+  a.rot_end = width;
+  a.rot_group = c.d_rope > 0 ? c.d_rope : 1;
+  a.T = (int)tokens_per_frame(c);
+  a.grid_w = c.grid_w;
+  a.W = c.window_frames;
+  a.ring_rows = (int64_t)c.window_frames * a.T;
+  a.frame0 = frame0;
+  a.out_type = c.cache_dtype;
+  a.rope = latent_rope(c);
+  return a;
+}
+
 mla_status create(const mla_layer_config* cfg, void* storage, size_t storage_bytes, bool dense,
                   mla_cache** out) {
   if (out == nullptr) return MLA_ERR_INVALID_ARG;
@@ -461,29 +550,32 @@ mla_status mla_cache_write(mla_cache* h, const void* x, const void* w_dkr, int64
   const int width = c.d_c + c.d_rope;
   if (c.dtype == MLA_BF16 && !mla::cache_write_bf16_supported(width, c.hidden))
     return MLA_ERR_UNSUPPORTED;
-  mla::CacheWriteArgs a;
-  a.x = x;
-  a.w = w_dkr;
-  a.w2 = w_dkr;
-  a.w_split = width;
-  a.ring = h->storage;
-  a.tokens_per_batch = (int)(n_frames * tokens_per_frame(c));
-  a.M = (int64_t)c.batch * a.tokens_per_batch;
-  a.hidden = c.hidden;
-  a.width = width;
-  a.rot_begin = c.d_c;
-  a.rot_end = width;
-  a.rot_group = c.d_rope > 0 ? c.d_rope : 1;
-  a.T = (int)tokens_per_frame(c);
-  a.grid_w = c.grid_w;
-  a.W = c.window_frames;
-  a.ring_rows = (int64_t)c.window_frames * a.T;
-  a.frame0 = frame0;
-  a.out_type = c.cache_dtype;
-  a.rope = latent_rope(c);
+  const mla::CacheWriteArgs a = latent_write_args(h, x, w_dkr, frame0, n_frames);
   hipStream_t s = (hipStream_t)stream;
   st = launch_status(c.dtype == MLA_BF16 ? mla::launch_cache_write_bf16(a, s)
                                          : mla::launch_cache_write_f32(a, s));
+  if (st == MLA_OK) commit_write(h, frame0, n_frames);
+  return st;
+}
+
+mla_status mla_cache_write_norm(mla_cache* h, const void* x, const void* w_dkr, const void* gamma,
+                                float eps, int64_t frame0, int32_t n_frames, void* stream) {
+  if (h == nullptr || !aligned16(x) || !aligned16(w_dkr) || !aligned16(gamma) || !(eps >= 0.0f) ||
+      !isfinite(eps))
+    return MLA_ERR_INVALID_ARG;
+  if (h->dense) return MLA_ERR_WRONG_KIND;
+  mla_status st = check_write(h, frame0, n_frames);
+  if (st != MLA_OK) return st;
+  const mla_layer_config& c = h->cfg;
+  const int width = c.d_c + c.d_rope;
+  if (c.dtype != MLA_BF16 || !mla::cache_write_bf16_supported(width, c.hidden) ||
+      (width != 96 && width != 160 && width != 224))
+    return MLA_ERR_UNSUPPORTED;
+  mla::CacheWriteArgs a = latent_write_args(h, x, w_dkr, frame0, n_frames);
+  a.gamma = gamma;
+  a.eps = eps;
+  a.norm_cols = c.d_c;
+  st = launch_status(mla::launch_projection_bf16(a, mla::PROJ_CACHE_NORM, (hipStream_t)stream));
   if (st == MLA_OK) commit_write(h, frame0, n_frames);
   return st;
 }
@@ -500,7 +592,7 @@ mla_status mha_cache_write(mla_cache* h, const void* x, const void* w_k, const v
   const int width = (int)dense_width(c);
   if (c.dtype == MLA_BF16 && !mla::cache_write_bf16_supported(width, c.hidden))
     return MLA_ERR_UNSUPPORTED;
-  mla::CacheWriteArgs a;
+  mla::CacheWriteArgs a = projection_defaults();
   a.x = x;
   a.w = w_k;
   a.w2 = w_v;
@@ -612,31 +704,7 @@ mla_status mla_attend(mla_cache* h, const void* q, int64_t q_token0, int32_t Lq,
   const bool expand = bf16 && attend_path_for(h, Lq, key_splits) == MLA_PATH_EXPAND;
   if (bf16 && !expand && !mla::attend_bf16_supported(c.d_c, c.d_rope, c.d_nope, c.d_v))
     return MLA_ERR_UNSUPPORTED;
-  mla::AttendArgs a;
-  memset(&a, 0, sizeof(a));
-  a.q = q;
-  a.ring = h->storage;
-  a.w_uk = w_uk;
-  a.w_uv = w_uv;
-  a.out = out;
-  a.B = c.batch;
-  a.Lq = Lq;
-  a.n_h = c.n_heads;
-  a.d_nope = c.d_nope;
-  a.d_rope = c.d_rope;
-  a.d_v = c.d_v;
-  a.d_c = c.d_c;
-  a.q_token0 = q_token0;
-  a.T = (int)tokens_per_frame(c);
-  a.grid_w = c.grid_w;
-  a.ring_rows = (int64_t)c.window_frames * a.T;
-  a.key_slot0 = (h->oldest % c.window_frames) * a.T;
-  a.Lk = (int)(n_resident(h) * a.T);
-  a.cache_type = c.cache_dtype;
-  a.qscale = (float)(1.4426950408889634 / sqrt((double)(c.d_nope + c.d_rope)));
-  a.ev_start = h->prof_start;
-  a.ev_stop = h->prof_stop;
-  a.rope = latent_rope(c);
+  mla::AttendArgs a = latent_attend_args(h, q, q_token0, Lq, w_uk, w_uv, out);
   hipStream_t s = (hipStream_t)stream;
   if (!bf16) return launch_status(mla::launch_attend_f32(a, s));
   if (expand) {
@@ -742,6 +810,155 @@ mla_status mla_attend_noalloc(mla_cache* h, const void* q, int64_t q_token0, int
 }
 
 size_t mla_attend_noalloc_max_bytes(void) { return mla::kScratchBytes; }
+
+size_t mla_fold_query_bytes(const mla_cache* h) {
+  if (h == nullptr || h->dense) return 0;
+  const mla_layer_config& c = h->cfg;
+  return (size_t)2 * c.n_heads * (c.d_c + c.d_rope) * c.hidden * 2;
+}
+
+size_t mla_fold_output_bytes(const mla_cache* h) {
+  if (h == nullptr || h->dense) return 0;
+  const mla_layer_config& c = h->cfg;
+  return (size_t)2 * c.hidden * c.n_heads * c.d_c * 2;
+}
+
+mla_status mla_fold_query_weights(const mla_cache* h, const void* w_q, const void* w_uk, void* w_qf,
+                                  size_t w_qf_bytes, void* stream) {
+  if (h == nullptr || !aligned16(w_q) || !aligned16(w_uk) || !aligned16(w_qf)) return MLA_ERR_INVALID_ARG;
+  if (h->dense) return MLA_ERR_WRONG_KIND;
+  if (!block_supported(h->cfg)) return MLA_ERR_UNSUPPORTED;
+  if (w_qf_bytes < mla_fold_query_bytes(h)) return MLA_ERR_INVALID_ARG;
+  const mla_layer_config& c = h->cfg;
+  mla::FoldArgs f;
+  memset(&f, 0, sizeof(f));
+  f.w_q = w_q;
+  f.w_uk = w_uk;
+  f.out = w_qf;
+  f.n_h = c.n_heads;
+  f.d_nope = c.d_nope;
+  f.d_rope = c.d_rope;
+  f.d_v = c.d_v;
+  f.d_c = c.d_c;
+  f.hidden = c.hidden;
+  return launch_status(mla::launch_fold_query(f, (hipStream_t)stream));
+}
+
+mla_status mla_fold_output_weights(const mla_cache* h, const void* w_o, const void* w_uv, void* w_fo,
+                                   size_t w_fo_bytes, void* stream) {
+  if (h == nullptr || !aligned16(w_o) || !aligned16(w_uv) || !aligned16(w_fo)) return MLA_ERR_INVALID_ARG;
+  if (h->dense) return MLA_ERR_WRONG_KIND;
+  if (!block_supported(h->cfg)) return MLA_ERR_UNSUPPORTED;
+  if (w_fo_bytes < mla_fold_output_bytes(h)) return MLA_ERR_INVALID_ARG;
+  const mla_layer_config& c = h->cfg;
+  mla::FoldArgs f;
+  memset(&f, 0, sizeof(f));
+  f.w_o = w_o;
+  f.w_uv = w_uv;
+  f.out = w_fo;
+  f.n_h = c.n_heads;
+  f.d_nope = c.d_nope;
+  f.d_rope = c.d_rope;
+  f.d_v = c.d_v;
+  f.d_c = c.d_c;
+  f.hidden = c.hidden;
+  return launch_status(mla::launch_fold_output(f, (hipStream_t)stream));
+}
+
+size_t mla_attend_block_workspace_bytes(const mla_cache* h, int32_t Lq, int32_t key_splits) {
+  if (h == nullptr || h->dense || Lq <= 0 || key_splits < 0 || !block_supported(h->cfg)) return 0;
+  const int64_t T = tokens_per_frame(h->cfg);
+  size_t need = 0;
+  for (int64_t f = 1; f <= h->cfg.window_frames; ++f) {
+    const size_t t = latent_layout(h, Lq, key_splits, f * T, true).total;
+    need = t > need ? t : need;
+  }
+  return need;
+}
+
+mla_status mla_attend_block(mla_cache* h, const void* x, int64_t q_token0, int32_t Lq, const void* w_qf,
+                            const void* w_fo, float* out, int32_t key_splits, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  if (h == nullptr || !aligned16(x) || !aligned16(w_qf) || !aligned16(w_fo) || !aligned16(out) ||
+      Lq <= 0 || key_splits < 0 || q_token0 < 0)
+    return MLA_ERR_INVALID_ARG;
+  if (h->dense) return MLA_ERR_WRONG_KIND;
+  if (n_resident(h) <= 0) return MLA_ERR_EMPTY;
+  const mla_layer_config& c = h->cfg;
+  if ((int64_t)Lq * c.n_heads >= (1LL << 30)) return MLA_ERR_INVALID_ARG;
+  if (!block_supported(c)) return MLA_ERR_UNSUPPORTED;
+  const LatentLayout L = latent_layout(h, Lq, key_splits, -1, true);
+  if (workspace == nullptr || ((uintptr_t)workspace % kAlign) != 0 || workspace_bytes < L.total)
+    return MLA_ERR_WORKSPACE;
+  h->ex_valid = false;  // overwrites the workspace like an absorbed attend
+  char* ws = (char*)workspace;
+  ws_clobber(ws, L.total);
+  const bool split = split_operands(c);
+  mla::AttendArgs a = latent_attend_args(h, nullptr, q_token0, Lq, nullptr, nullptr, out);
+  a.qcat = ws + L.qcat_off;
+  a.qcat_lo = split ? ws + L.qlo_off : nullptr;
+  a.opart = (float*)(ws + L.opart_off);
+  a.ml = (float*)(ws + L.ml_off);
+  a.sched = L.sched;
+  hipStream_t s = (hipStream_t)stream;
+  // 1. [q_lat | q^R] of every head straight from x with the folded weights
+  //    (two parts), rotated at each query's position and scaled
+  const int qw = c.n_heads * (c.d_c + c.d_rope);
+  mla::CacheWriteArgs p = projection_defaults();
+  p.x = x;
+  p.w = w_qf;
+  p.w2 = w_qf;
+  p.w_split = qw;
+  p.ring = a.qcat;
+  p.M = (int64_t)c.batch * Lq;
+  p.tokens_per_batch = Lq;
+  p.hidden = c.hidden;
+  p.width = qw;
+  p.rot_begin = 0;
+  p.rot_end = qw;
+  p.rot_group = c.d_c + c.d_rope;
+  p.rot_skip = c.d_c;
+  p.T = a.T;
+  p.grid_w = c.grid_w;
+  p.W = c.window_frames;
+  p.q_token0 = q_token0;
+  p.out_type = c.cache_dtype;
+  p.rope = latent_rope(c);
+  p.passes = 2;
+  p.w_part[1] = (int64_t)qw * c.hidden * 2;
+  p.scale = a.qscale;
+  p.out_lo = a.qcat_lo;
+  hipError_t e = mla::launch_projection_bf16(p, mla::PROJ_QUERY, s);
+  if (e != hipSuccess) return MLA_ERR_HIP;
+  // 2. the absorbed core, 3. merged latent outputs in two parts
+  e = mla::launch_attend_core_only(a, s);
+  if (e != hipSuccess) return MLA_ERR_HIP;
+  void* o_hi = ws + L.ohi_off;
+  void* o_lo = ws + L.olo_off;
+  e = mla::launch_merge_latent(a, o_hi, o_lo, s);
+  if (e != hipSuccess) return MLA_ERR_HIP;
+  // 4. model-width output with the folded output weights: three passes of the
+  //    two-part operands (value x value, value x remainder, remainder x value)
+  const int K = c.n_heads * c.d_c;
+  mla::CacheWriteArgs o = projection_defaults();
+  o.x = o_hi;
+  o.w = w_fo;
+  o.w2 = w_fo;
+  o.w_split = c.hidden;
+  o.ring = out;
+  o.M = (int64_t)c.batch * Lq;
+  o.tokens_per_batch = Lq;
+  o.hidden = K;
+  o.width = c.hidden;
+  o.T = a.T;
+  o.grid_w = c.grid_w;
+  o.W = c.window_frames;
+  o.out_type = MLA_BF16;
+  o.passes = 3;
+  o.w_part[1] = (int64_t)c.hidden * K * 2;
+  o.x_part[2] = (int64_t)((char*)o_lo - (char*)o_hi);
+  return launch_status(mla::launch_projection_bf16(o, mla::PROJ_OUT, s));
+}
 
 size_t mha_attend_workspace_bytes(const mla_cache* h, int32_t Lq) {
   if (h == nullptr || !h->dense || Lq <= 0) return 0;

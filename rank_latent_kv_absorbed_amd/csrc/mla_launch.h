@@ -18,26 +18,51 @@ struct RopeTable {
   double inv_freq[kMaxRopePairs];
 };
 
-// Fused cache write: y = W x for every token of n whole frames, RoPE on the
-// rotated columns, round to the storage dtype, scatter rows to ring slots.
+// Projection y = W x for a run of tokens on the LDS-staged MFMA GEMM, with an
+// epilogue per use:
+//  * cache write (PROJ_CACHE): RoPE on the rotated columns, round to the
+//    storage dtype, scatter each token's row to its ring slot;
+//  * cache write with the latent RMS-normalised (PROJ_CACHE_NORM): the first
+//    norm_cols columns scaled by gamma / rms before rounding;
+//  * folded query projection (PROJ_QUERY): rows [q_lat | q^R] per head, RoPE
+//    on the positional columns of every head at the query's position, scaled
+//    by `scale`, written to token rows of the cache type (and the remainders'
+//    rounding to out_lo for split operands);
+//  * output projection (PROJ_OUT): fp32 token rows.
+// The weights (and the inputs) may come in parts whose products are summed:
+// pass p multiplies x part x_part[p] by weight part w_part[p] (byte offsets
+// from x and from w / w2), so a weight carried as two bf16 parts (value and
+// remainder) keeps 16 significant bits.
+enum ProjMode { PROJ_CACHE = 0, PROJ_CACHE_NORM = 1, PROJ_QUERY = 2, PROJ_OUT = 3 };
+constexpr int kProjMaxPasses = 3;
 struct CacheWriteArgs {
   const void* x;          // [M][hidden], M = batch * tokens_per_batch
   const void* w;          // rows [0, w_split) of the [width][hidden] projection
   const void* w2;         // rows [w_split, width) (may alias w + w_split*hidden)
   int w_split;
-  void* ring;             // [batch][ring_rows][width]
+  void* ring;             // cache: [batch][ring_rows][width]; query / out: [M][width]
   int64_t M;
-  int tokens_per_batch;   // n_frames * T
+  int tokens_per_batch;   // cache: n_frames * T; query / out: Lq
   int hidden;
   int width;              // output columns (latent: d_c + d_rope; dense: 2 * n_h * d_h)
   int rot_begin;          // first rotated column
   int rot_end;            // one past the last rotated column
   int rot_group;          // rotated columns restart their pair count every rot_group
+  int rot_skip;           // columns below rot_skip within each group are not rotated
   int T, grid_w, W;
   int64_t ring_rows;      // W * T
-  int64_t frame0;
-  int out_type;           // ring element type: 1 = bf16, 2 = fp16 (2-byte path only)
+  int64_t frame0;         // cache: first frame written
+  int64_t q_token0;       // query: global token of row 0 of every sequence
+  int out_type;           // element type of 2-byte outputs: 1 = bf16, 2 = fp16
   RopeTable rope;
+  int passes;                             // 1 .. kProjMaxPasses
+  int64_t x_part[kProjMaxPasses];         // byte offset of pass p's x part from x
+  int64_t w_part[kProjMaxPasses];         // byte offset of pass p's weight part from w and w2
+  const void* gamma;      // PROJ_CACHE_NORM: [norm_cols] gain, input dtype (bf16)
+  float eps;
+  int norm_cols;
+  float scale;            // PROJ_QUERY: applied to every column
+  void* out_lo;           // PROJ_QUERY with split operands: remainders (null otherwise)
 };
 
 #if defined(__HIPCC__)
@@ -311,6 +336,9 @@ struct ExpandArgs {
 };
 
 hipError_t launch_cache_write_bf16(const CacheWriteArgs& a, hipStream_t s);
+// The other projection modes (PROJ_CACHE_NORM, PROJ_QUERY, PROJ_OUT) on the
+// same GEMM; `mode` selects the epilogue.
+hipError_t launch_projection_bf16(const CacheWriteArgs& a, int mode, hipStream_t s);
 hipError_t launch_cache_write_f32(const CacheWriteArgs& a, hipStream_t s);
 bool cache_write_bf16_supported(int width, int hidden);
 
@@ -323,6 +351,28 @@ bool attend_bf16_supported(int d_c, int d_rope, int d_nope, int d_v);
 // as in the latent path.
 hipError_t launch_mha_attend_bf16_ws(const MhaAttendArgs& a, float* opart, float* ml,
                                      const Schedule& sched, hipStream_t s);
+
+// Weight-level folds around the absorbed path (mla_block.hip), each written as
+// two bf16 parts (value, remainder) of the fp32 product:
+//  query:  w_qf[part][h][i][k] = sum_n w_uk[h][n][i] w_q[h*d_qk + n][k] (i < d_c),
+//          w_q[h*d_qk + d_nope + i - d_c][k] (d_c <= i < d_c + d_rope);
+//  output: w_fo[part][c][h*d_c + i] = sum_v w_o[c][h*d_v + v] w_uv[h][v][i].
+struct FoldArgs {
+  const void* w_q;   // [n_h * (d_nope + d_rope)][hidden] bf16
+  const void* w_uk;  // [n_h][d_nope][d_c] bf16
+  const void* w_o;   // [hidden][n_h * d_v] bf16
+  const void* w_uv;  // [n_h][d_v][d_c] bf16
+  void* out;         // [2][...] bf16
+  int n_h, d_nope, d_rope, d_v, d_c, hidden;
+};
+hipError_t launch_fold_query(const FoldArgs& f, hipStream_t s);
+hipError_t launch_fold_output(const FoldArgs& f, hipStream_t s);
+
+// Attention block (mla_attend_block): the absorbed core's partials merged,
+// normalised and written as the latent outputs o_lat [B*Lq][n_h*d_c] in two
+// bf16 parts (o_hi, o_lo), the operand of the folded output projection.
+hipError_t launch_attend_core_only(const AttendArgs& a, hipStream_t s);
+hipError_t launch_merge_latent(const AttendArgs& a, void* o_hi, void* o_lo, hipStream_t s);
 
 // Static device scratch of mla_attend_noalloc (mla_noalloc.hip): its size, and
 // its address on the calling thread's current device (looked up once per

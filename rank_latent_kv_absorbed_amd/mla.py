@@ -63,6 +63,13 @@ SIGNATURES = {
     "mha_cache_create": (_I32, [_CFGP, _VP, _SZ, ctypes.POINTER(_HANDLE)]),
     "mla_cache_destroy": (None, [_HANDLE]),
     "mla_cache_write": (_I32, [_HANDLE, _VP, _VP, _I64, _I32, _VP]),
+    "mla_cache_write_norm": (_I32, [_HANDLE, _VP, _VP, _VP, ctypes.c_float, _I64, _I32, _VP]),
+    "mla_fold_query_bytes": (_SZ, [_HANDLE]),
+    "mla_fold_output_bytes": (_SZ, [_HANDLE]),
+    "mla_fold_query_weights": (_I32, [_HANDLE, _VP, _VP, _VP, _SZ, _VP]),
+    "mla_fold_output_weights": (_I32, [_HANDLE, _VP, _VP, _VP, _SZ, _VP]),
+    "mla_attend_block_workspace_bytes": (_SZ, [_HANDLE, _I32, _I32]),
+    "mla_attend_block": (_I32, [_HANDLE, _VP, _I64, _I32, _VP, _VP, _VP, _I32, _VP, _SZ, _VP]),
     "mha_cache_write": (_I32, [_HANDLE, _VP, _VP, _VP, _I64, _I32, _VP]),
     "mla_cache_evict": (_I32, [_HANDLE, _I32]),
     "mla_cache_query": (_I32, [_HANDLE, ctypes.POINTER(CacheInfoC)]),
@@ -248,6 +255,62 @@ class LatentCache(_CacheBase):
         _need(w_dkr, "w_dkr", self.tdtype, (self.width, cfg.hidden), self.device)
         _check(lib().mla_cache_write(self._h, _ptr(x), _ptr(w_dkr), int(frame0), int(n_frames),
                                      _stream(stream)), "cache_write")
+
+    def write_norm(self, x, w_dkr, gamma, eps, frame0, n_frames, stream=None):
+        """Cache write with the latent RMS-normalised (mla_cache_write_norm)."""
+        cfg = self.cfg
+        _need(x, "x", self.tdtype, (self.batch, n_frames * self.T, cfg.hidden), self.device)
+        _need(w_dkr, "w_dkr", self.tdtype, (self.width, cfg.hidden), self.device)
+        _need(gamma, "gamma", self.tdtype, (cfg.d_c,), self.device)
+        _check(lib().mla_cache_write_norm(self._h, _ptr(x), _ptr(w_dkr), _ptr(gamma), float(eps),
+                                          int(frame0), int(n_frames), _stream(stream)), "cache_write_norm")
+
+    def fold_query_weights(self, w_q, w_uk, stream=None):
+        """[2, n_h, d_c + d_rope, hidden] bf16: W^K_up folded into the query
+        projection, as value and remainder parts (mla_fold_query_weights)."""
+        cfg = self.cfg
+        _need(w_q, "w_q", self.tdtype, (cfg.n_heads * (cfg.d_nope + cfg.d_rope), cfg.hidden), self.device)
+        _need(w_uk, "w_uk", self.tdtype, (cfg.n_heads, cfg.d_nope, cfg.d_c), self.device)
+        out = _alloc((2, cfg.n_heads, cfg.d_c + cfg.d_rope, cfg.hidden), self.tdtype, self.device, stream)
+        _check(lib().mla_fold_query_weights(self._h, _ptr(w_q), _ptr(w_uk), _ptr(out),
+                                            out.numel() * out.element_size(), _stream(stream)),
+               "fold_query_weights")
+        return out
+
+    def fold_output_weights(self, w_o, w_uv, stream=None):
+        """[2, hidden, n_h * d_c] bf16: W^V_up folded into W^O, as value and
+        remainder parts (mla_fold_output_weights)."""
+        cfg = self.cfg
+        _need(w_o, "w_o", self.tdtype, (cfg.hidden, cfg.n_heads * cfg.d_v), self.device)
+        _need(w_uv, "w_uv", self.tdtype, (cfg.n_heads, cfg.d_v, cfg.d_c), self.device)
+        out = _alloc((2, cfg.hidden, cfg.n_heads * cfg.d_c), self.tdtype, self.device, stream)
+        _check(lib().mla_fold_output_weights(self._h, _ptr(w_o), _ptr(w_uv), _ptr(out),
+                                             out.numel() * out.element_size(), _stream(stream)),
+               "fold_output_weights")
+        return out
+
+    def block_workspace_bytes(self, Lq, key_splits=0):
+        return lib().mla_attend_block_workspace_bytes(self._h, int(Lq), int(key_splits))
+
+    def attend_block(self, x, q_token0, w_qf, w_fo, out=None, key_splits=0, workspace=None, stream=None):
+        """Model-width attention block of the query tokens' layer input x
+        [batch, Lq, hidden] with folded weights (mla_attend_block)."""
+        cfg = self.cfg
+        Lq = x.shape[1]
+        _need(x, "x", self.tdtype, (self.batch, Lq, cfg.hidden), self.device)
+        _need(w_qf, "w_qf", self.tdtype, (2, cfg.n_heads, cfg.d_c + cfg.d_rope, cfg.hidden), self.device)
+        _need(w_fo, "w_fo", self.tdtype, (2, cfg.hidden, cfg.n_heads * cfg.d_c), self.device)
+        if out is None:
+            out = _alloc((self.batch, Lq, cfg.hidden), torch.float32, self.device, stream)
+        _need(out, "out", torch.float32, (self.batch, Lq, cfg.hidden), self.device)
+        need = self.block_workspace_bytes(Lq, key_splits)
+        if workspace is None and need > 0:
+            workspace = _alloc(need, torch.uint8, self.device, stream)
+        wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        _check(lib().mla_attend_block(self._h, _ptr(x), int(q_token0), int(Lq), _ptr(w_qf), _ptr(w_fo),
+                                      _ptr(out), int(key_splits), _ptr(workspace), wbytes,
+                                      _stream(stream)), "attend_block")
+        return out
 
     def workspace_bytes(self, Lq, key_splits=0):
         return lib().mla_attend_workspace_bytes(self._h, int(Lq), int(key_splits))

@@ -57,6 +57,19 @@ bool expand_supported(int d_c, int d_rope, int d_nope, int d_v) {
 }
 hipError_t launch_expand_kv(const ExpandArgs& a, hipStream_t) { g_expand = a; return rec(7); }
 hipError_t launch_mha_attend_f32(const MhaAttendArgs& a, hipStream_t) { g_mha = a; return rec(6); }
+mla::CacheWriteArgs g_proj[2];  // the last query and output projections
+int g_proj_mode = -1;
+hipError_t launch_projection_bf16(const CacheWriteArgs& a, int mode, hipStream_t) {
+  g_proj_mode = mode;
+  if (mode == PROJ_CACHE_NORM) g_write = a;
+  if (mode == PROJ_QUERY) g_proj[0] = a;
+  if (mode == PROJ_OUT) g_proj[1] = a;
+  return rec(10 + mode);
+}
+hipError_t launch_fold_query(const FoldArgs&, hipStream_t) { return rec(20); }
+hipError_t launch_fold_output(const FoldArgs&, hipStream_t) { return rec(21); }
+hipError_t launch_attend_core_only(const AttendArgs& a, hipStream_t) { g_attend = a; return rec(22); }
+hipError_t launch_merge_latent(const AttendArgs&, void*, void*, hipStream_t) { return rec(23); }
 // The static scratch stands at a fixed fake address (never dereferenced).
 hipError_t scratch_for_current_device(void** out) {
   *out = (void*)(uintptr_t)(3ULL << 40);
@@ -66,6 +79,18 @@ hipError_t scratch_for_current_device(void** out) {
 
 extern "C" {
 int fake_kind() { return g_kind; }
+// The last projection of `which` (0 query, 1 output): M, tokens_per_batch,
+// hidden, width, rot_begin, rot_end, rot_group, rot_skip, passes, w_part[1],
+// x_part[2], q_token0, ring pointer, out_lo pointer, x pointer.
+void fake_proj_info(int which, long long* o) {
+  const mla::CacheWriteArgs& a = mla::g_proj[which];
+  long long v[15] = {a.M, a.tokens_per_batch, a.hidden, a.width, a.rot_begin, a.rot_end,
+                     a.rot_group, a.rot_skip, a.passes, a.w_part[1], a.x_part[2], a.q_token0,
+                     (long long)(intptr_t)a.ring, (long long)(intptr_t)a.out_lo, (long long)(intptr_t)a.x};
+  memcpy(o, v, sizeof(v));
+}
+float fake_write_eps() { return g_write.eps; }
+int fake_write_norm_cols() { return g_write.norm_cols; }
 int fake_count() { return g_count; }
 void fake_fail_next() { g_fail = 1; }
 // frame0, M, tokens_per_batch, width, ring_rows, rot_begin, rot_end, rot_group, w_split, hidden

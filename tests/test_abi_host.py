@@ -706,3 +706,77 @@ def test_set_state_and_slot_validation(sim):
     assert sim.mla_cache_slot(h, 22, 1560) == -1
     assert sim.mla_cache_slot(h, -1, 0) == -1
     assert sim.mla_cache_slot(h, 43, 5) == (43 % 21) * 1560 + 5
+
+
+def _proj_info(L, which):
+    a = (ctypes.c_longlong * 15)()
+    L.fake_proj_info(which, a)
+    keys = ["M", "tokens_per_batch", "hidden", "width", "rot_begin", "rot_end", "rot_group", "rot_skip",
+            "passes", "w_part1", "x_part2", "q_token0", "ring", "out_lo", "x"]
+    return dict(zip(keys, list(a)))
+
+
+def test_attend_block_arguments_and_workspace(sim):
+    """mla_attend_block: the folded query projection writes [q_lat | q^R] rows
+    of every head (rotation past d_c in each 224-wide head group, two weight
+    parts) into the workspace's query block, the core and the latent merge
+    follow, and the folded output projection (three passes of two-part
+    operands, K = n_h * d_c) writes model-width rows to `out`."""
+    for cache_dtype in ("f16", "bf16"):
+        c = _cfg(cache_dtype=cache_dtype)
+        st, h = _create(sim, c)
+        assert sim.mla_cache_set_state(h, 3, 23) == 0
+        Lq = 4680
+        need = sim.mla_attend_block_workspace_bytes(h, Lq, 0)
+        ws, out, x = 1 << 40, FAKE_PTR + 4096, FAKE_PTR + 8192
+        assert sim.mla_attend_block(h, P(x), 21 * 1560, Lq, P(FAKE_PTR), P(FAKE_PTR), P(out), 0, P(ws),
+                                    need - 1, None) == 7
+        n = sim.fake_count()
+        assert sim.mla_attend_block(h, P(x), 21 * 1560, Lq, P(FAKE_PTR), P(FAKE_PTR), P(out), 0, P(ws),
+                                    need, None) == 0
+        assert sim.fake_count() == n + 4                  # projection, core, merge, projection
+        qp, op, at = _proj_info(sim, 0), _proj_info(sim, 1), _attend_info(sim)
+        p_ = _attend_ptrs(sim)
+        ptrs = [p_["qcat"], p_["qcat_lo"], p_["opart"], p_["ml"]]
+        assert (qp["M"], qp["tokens_per_batch"], qp["hidden"], qp["width"]) == (Lq, Lq, 1536, 12 * 224)
+        assert (qp["rot_begin"], qp["rot_end"], qp["rot_group"], qp["rot_skip"]) == (0, 12 * 224, 224, 192)
+        assert (qp["passes"], qp["w_part1"], qp["q_token0"], qp["x"]) == (2, 12 * 224 * 1536 * 2, 21 * 1560, x)
+        assert qp["ring"] == ptrs[0] == ws and qp["out_lo"] == ptrs[1]
+        assert (ptrs[1] != 0) == (cache_dtype == "bf16")
+        assert (op["M"], op["hidden"], op["width"], op["passes"]) == (Lq, 12 * 192, 1536, 3)
+        assert op["w_part1"] == 1536 * 12 * 192 * 2 and op["ring"] == out
+        o_bytes = -(-Lq * 12 * 192 * 2 // 256) * 256
+        assert op["x_part2"] == o_bytes and ws < op["x"] and op["x"] + 2 * o_bytes <= ws + need
+        assert op["x"] >= ptrs[3] + at["n_slots"] * Lq * 12 * 8    # after the max/sum block
+        assert (at["block_rows"], at["key_tile"]) == expected_shape(Lq * 12, split=cache_dtype == "bf16")[:2]
+        assert sim.mla_fold_query_bytes(h) == 2 * 12 * 224 * 1536 * 2
+        assert sim.mla_fold_output_bytes(h) == 2 * 1536 * 12 * 192 * 2
+        assert sim.mla_fold_query_weights(h, P(FAKE_PTR), P(FAKE_PTR), P(ws), 1 << 30, None) == 0
+        assert sim.mla_fold_query_weights(h, P(FAKE_PTR), P(FAKE_PTR), P(ws), 1024, None) == 1
+        assert sim.mla_fold_output_weights(h, P(FAKE_PTR), P(FAKE_PTR), P(ws), 1 << 30, None) == 0
+    # fp32 handles and dense handles have no block
+    st, g = _create(sim, _cfg(dtype="f32", cache_dtype="f32"))
+    assert sim.mla_attend_block_workspace_bytes(g, 16, 0) == 0
+    assert sim.mla_attend_block(g, P(FAKE_PTR), 0, 16, P(FAKE_PTR), P(FAKE_PTR), P(FAKE_PTR), 0,
+                                P(1 << 40), 1 << 30, None) in (6, 8)
+    st, d = _create(sim, _cfg(), dense=True)
+    assert sim.mla_attend_block(d, P(FAKE_PTR), 0, 16, P(FAKE_PTR), P(FAKE_PTR), P(FAKE_PTR), 0,
+                                P(1 << 40), 1 << 30, None) == 9
+
+
+def test_cache_write_norm_arguments(sim):
+    c = _cfg()
+    st, h = _create(sim, c)
+    sim.fake_write_eps.restype = ctypes.c_float
+    assert sim.mla_cache_write_norm(h, P(FAKE_PTR), P(FAKE_PTR), P(FAKE_PTR), ctypes.c_float(-1.0), 0, 3,
+                                    None) == 1
+    assert sim.mla_cache_write_norm(h, P(FAKE_PTR), P(FAKE_PTR), P(FAKE_PTR), ctypes.c_float(1e-6), 0, 3,
+                                    None) == 0
+    assert sim.fake_kind() == 10 + 1 and sim.fake_write_norm_cols() == 192
+    assert abs(sim.fake_write_eps() - 1e-6) < 1e-12
+    assert _info(sim, h)[:3] == (0, 2, 3)
+    assert sim.mla_cache_write_norm(h, P(FAKE_PTR), P(FAKE_PTR), P(FAKE_PTR), ctypes.c_float(1e-6), 5, 3,
+                                    None) == 4                       # not contiguous
+    st, g = _create(sim, _cfg(dtype="f32", cache_dtype="f32"))
+    assert sim.mla_cache_write_norm(g, P(FAKE_PTR), P(FAKE_PTR), P(FAKE_PTR), ctypes.c_float(0.0), 0, 1,
+                                    None) == 8
