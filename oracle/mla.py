@@ -82,14 +82,41 @@ def round_to_f16(a):
         return np.asarray(a, dtype=np.float64).astype(np.float16).astype(np.float64)
 
 
+def round_to_e4m3(a):
+    """Round float64 values to the OCP 8-bit float E4M3 ('fn' variant), ties
+    to even, saturating.
+
+    E4M3 keeps 4 significant bits (1 implicit + 3 stored), exponent bias 7,
+    no infinities: the largest finite magnitude is 1.75 * 2^8 = 448, the
+    smallest normal 2^-6, and below it subnormals keep a fixed quantum of
+    2^-9.  Written from the format's definition like round_to_bf16.  Values
+    whose magnitude rounds past 448 saturate to +-448 (the format's saturating
+    conversion; its only other choice is NaN); NaN stays NaN.
+    """
+    a = np.asarray(a, dtype=np.float64)
+    out = np.array(a, copy=True)
+    finite = np.isfinite(a) & (a != 0.0)
+    v = a[finite]
+    _, e = np.frexp(v)                      # v = m * 2^e, 0.5 <= |m| < 1
+    e = np.maximum(e, -5)                   # below 2^-6 the quantum stops shrinking
+    q = np.ldexp(np.rint(np.ldexp(v, 4 - e)), e - 4)
+    out[finite] = np.clip(q, -448.0, 448.0)
+    inf = np.isinf(a)
+    out[inf] = np.copysign(448.0, a[inf])
+    return out
+
+
 def round_storage(a, dtype):
-    """Round to the cache storage dtype: 'bf16', 'f16', 'f32', or None (keep fp64)."""
+    """Round to the cache storage dtype: 'bf16', 'f16', 'e4m3', 'f32', or None
+    (keep fp64)."""
     if dtype is None:
         return np.asarray(a, dtype=np.float64)
     if dtype == "bf16":
         return round_to_bf16(a)
     if dtype == "f16":
         return round_to_f16(a)
+    if dtype == "e4m3":
+        return round_to_e4m3(a)
     if dtype == "f32":
         return round_to_f32(a)
     raise ValueError(f"unknown storage dtype {dtype!r}")

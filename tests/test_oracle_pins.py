@@ -94,6 +94,47 @@ def test_f16_rounding_overflows_to_infinity_past_the_range():
     np.testing.assert_array_equal(got, want)
 
 
+def test_e4m3_rounding_matches_torch():
+    """OCP E4M3 against torch's float8_e4m3fn conversion, inside the range
+    where the two agree (|v| <= 464: torch turns larger values into NaN)."""
+    rng = np.random.default_rng(21)
+    v = (rng.standard_normal(20000) * np.exp2(rng.integers(-14, 8, 20000))).astype(np.float32)
+    v = v[np.abs(v) <= 464.0]
+    # every finite code, and the exact midpoints between neighbouring codes
+    # (both parities of the last stored bit)
+    codes = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    codes = np.unique(codes[np.isfinite(codes)])
+    mids = (codes[:-1] + codes[1:]) / 2.0
+    allv = np.concatenate([v.astype(np.float64), codes, mids, [0.0, -0.0, 464.0, -464.0, 447.9]])
+    want = torch.from_numpy(allv.astype(np.float32)).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    np.testing.assert_array_equal(O.round_to_e4m3(allv), want)
+
+
+def test_e4m3_code_table_closed_forms():
+    """The representable magnitudes are m * 2^-9 (m = 0..7, subnormal) and
+    (1 + k/8) * 2^(e-7) for e = 1..15, k = 0..7 except e = 15, k = 7 (NaN):
+    253 finite non-negative values up to 448; each rounds to itself."""
+    sub = np.arange(8) * 2.0 ** -9
+    norm = np.array([(1 + k / 8) * 2.0 ** (e - 7) for e in range(1, 16) for k in range(8)
+                     if not (e == 15 and k == 7)])
+    table = np.concatenate([sub, norm])
+    assert table.size == 127 and table.max() == 448.0 and norm.min() == 2.0 ** -6
+    both = np.concatenate([table, -table])
+    np.testing.assert_array_equal(O.round_to_e4m3(both), both)
+    # a value between two codes goes to the nearer one
+    np.testing.assert_array_equal(O.round_to_e4m3(table[1:] - 0.3 * np.diff(table)), table[1:])
+    np.testing.assert_array_equal(O.round_to_e4m3(table[:-1] + 0.3 * np.diff(table)), table[:-1])
+
+
+def test_e4m3_saturates_past_the_range():
+    """Magnitudes that round past 448 saturate to +-448 (the format has no
+    infinity); NaN stays NaN."""
+    v = np.array([448.0, 463.99, 464.0, 465.0, 1e6, np.inf, -np.inf, -500.0, np.nan])
+    got = O.round_to_e4m3(v)
+    np.testing.assert_array_equal(got[:-1], [448.0, 448.0, 448.0, 448.0, 448.0, 448.0, -448.0, -448.0])
+    assert np.isnan(got[-1])
+
+
 def test_f32_rounding_matches_torch():
     v = np.random.default_rng(2).standard_normal(1000) * 1e3
     want = torch.from_numpy(v).to(torch.float32).to(torch.float64).numpy()
