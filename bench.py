@@ -479,50 +479,75 @@ def run_extras(args, result, torch, dev, cfg, caches, weights, x_pre, x_chunk, q
 
     # ---- cache-bound small-query shapes: Lq queries per sequence over the full
     # window, latent widths 192 / 128 / 64, batch 8 and 11, 30 layer windows
-    # cycled (1.5-4.8 GB of windows, far above the last-level cache)
+    # cycled (1.5-4.8 GB of windows, far above the last-level cache); the
+    # one-byte E4M3 ring at d_c = 192 (half the window bytes)
+    host_gen = torch.Generator().manual_seed(5)
+
+    def small_queries(sq, d_c, Bs, cache_dtype, suffix=""):
+        scfg = cfg.with_(batch=Bs, d_c=d_c, cache_dtype=cache_dtype)
+        sw = [{k: v.to(dev) for k, v in layer_weights(scfg, layer=l).items()} for l in range(2)]
+        scaches = []
+        staged = None
+        for l in range(L):
+            c = LatentCache(scfg, device=dev)
+            r = c.ring()
+            if r.dtype == torch.float8_e4m3fn:
+                # Gaussian values rounded to E4M3 on the host, staged once
+                if staged is None:
+                    staged = torch.randn(r.shape, generator=host_gen).to(r.dtype).view(torch.uint8).to(dev)
+                r.view(torch.uint8).copy_(staged)
+            else:
+                r.copy_(torch.randn(r.shape, generator=gen, device=dev).to(r.dtype))
+            c.set_state(0, W - 1)
+            scaches.append(c)
+        del staged
+        elem = scaches[0].ring().element_size()
+        for Lqs in (1, 4, 8):
+            qs = torch.randn((Bs, Lqs, cfg.n_heads, cfg.d_qk), generator=gen, device=dev).to(torch.bfloat16)
+            so = torch.empty((Bs, Lqs, cfg.n_heads, cfg.d_v), dtype=torch.float32, device=dev)
+            sws = torch.empty(max(scaches[0].workspace_bytes(Lqs), 1), dtype=torch.uint8, device=dev)
+
+            def call(i):
+                scaches[i % L].attend(qs, Lk - Lqs, sw[i % 2]["w_uk"], sw[i % 2]["w_uv"], out=so,
+                                      workspace=sws)
+
+            for i in range(L):
+                call(i)
+            call_ms = event_ms(call, 2 * L)
+            sev = [(ev.create(), ev.create()) for _ in range(2 * L)]
+            for i, (a_, b_) in enumerate(sev):
+                c = scaches[i % L]
+                c.set_profile_events(a_, b_)
+                call(i)
+                c.set_profile_events(None, None)
+            torch.cuda.synchronize()
+            kms = sum(ev.elapsed_ms(a_, b_) for a_, b_ in sev) / len(sev)
+            win = Bs * Lk * (d_c + cfg.d_rope) * elem
+            nbytes = attend_bytes(cfg.n_heads, Lqs, Lk, d_c, cfg.d_rope, cfg.d_nope, cfg.d_v, Bs,
+                                  cache_elem=elem)
+            sq[f"dc{d_c}_Lq{Lqs}_B{Bs}{suffix}"] = {
+                "attend_ms": round(call_ms, 4), "core_kernel_ms": round(kms, 4),
+                "algorithmic_bytes": nbytes,
+                "core_GBps": round(win / (kms / 1e3) / 1e9, 1),
+                "call_GBps": round(nbytes / (call_ms / 1e3) / 1e9, 1),
+                "hbm_frac_call": round(nbytes / (call_ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+                "query_tokens_per_s": round(Bs * Lqs / (call_ms / 1e3), 1)}
+            del sws, so, qs
+        del scaches, sw
+        torch.cuda.empty_cache()
+
     sq = {}
     for d_c in (192, 128, 64):
         for Bs in (8, 11):
-            scfg = cfg.with_(batch=Bs, d_c=d_c)
-            sw = [{k: v.to(dev) for k, v in layer_weights(scfg, layer=l).items()} for l in range(2)]
-            scaches = []
-            for l in range(L):
-                c = LatentCache(scfg, device=dev)
-                c.ring().copy_(torch.randn(c.ring().shape, generator=gen, device=dev).to(c.ring().dtype))
-                c.set_state(0, W - 1)
-                scaches.append(c)
-            for Lqs in (1, 4, 8):
-                qs = torch.randn((Bs, Lqs, cfg.n_heads, cfg.d_qk), generator=gen, device=dev).to(torch.bfloat16)
-                so = torch.empty((Bs, Lqs, cfg.n_heads, cfg.d_v), dtype=torch.float32, device=dev)
-                sws = torch.empty(max(scaches[0].workspace_bytes(Lqs), 1), dtype=torch.uint8, device=dev)
-
-                def call(i):
-                    scaches[i % L].attend(qs, Lk - Lqs, sw[i % 2]["w_uk"], sw[i % 2]["w_uv"], out=so,
-                                          workspace=sws)
-
-                for i in range(L):
-                    call(i)
-                call_ms = event_ms(call, 2 * L)
-                sev = [(ev.create(), ev.create()) for _ in range(2 * L)]
-                for i, (a_, b_) in enumerate(sev):
-                    c = scaches[i % L]
-                    c.set_profile_events(a_, b_)
-                    call(i)
-                    c.set_profile_events(None, None)
-                torch.cuda.synchronize()
-                kms = sum(ev.elapsed_ms(a_, b_) for a_, b_ in sev) / len(sev)
-                win = Bs * Lk * (d_c + cfg.d_rope) * 2
-                nbytes = attend_bytes(cfg.n_heads, Lqs, Lk, d_c, cfg.d_rope, cfg.d_nope, cfg.d_v, Bs)
-                sq[f"dc{d_c}_Lq{Lqs}_B{Bs}"] = {
-                    "attend_ms": round(call_ms, 4), "core_kernel_ms": round(kms, 4),
-                    "algorithmic_bytes": nbytes,
-                    "core_GBps": round(win / (kms / 1e3) / 1e9, 1),
-                    "call_GBps": round(nbytes / (call_ms / 1e3) / 1e9, 1),
-                    "hbm_frac_call": round(nbytes / (call_ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
-                    "query_tokens_per_s": round(Bs * Lqs / (call_ms / 1e3), 1)}
-                del sws, so, qs
-            del scaches, sw
-            torch.cuda.empty_cache()
+            small_queries(sq, d_c, Bs, cfg.cache_dtype)
+    sq8 = {}
+    for Bs in (8, 11):
+        small_queries(sq8, 192, Bs, "e4m3", "_e4m3")
+    for k, v in sq8.items():
+        base = sq.get(k[:-len("_e4m3")])
+        if base is not None:
+            v["speedup_vs_2byte_ring"] = round(base["attend_ms"] / v["attend_ms"], 3)
+    result["small_query_e4m3"] = sq8
     result["small_query_cache_bound"] = sq
     log("small queries")
 

@@ -51,6 +51,14 @@
  *     value beyond that is stored as +-infinity (IEEE round to nearest),
  *     and attention over such a row returns NaN for its sequence.  bf16 and
  *     fp32 rings have the fp32 exponent range.
+ *   - One-byte latent ring (MLA_E4M3; beyond the pages, which imply two-byte
+ *     scalars): the OCP 8-bit float E4M3 ('fn': 4 significant bits, largest
+ *     magnitude 448, subnormal quantum 2^-9, no infinities), rounded to
+ *     nearest even; magnitudes that round past 448 are stored as +-448
+ *     (saturation, never NaN or infinity).  The attention widens the stored
+ *     values to fp16 (exactly) and computes as for an fp16 ring: the result
+ *     is the attention over the stored E4M3 values.  Absorbed path only (no
+ *     expand-then-attend); no dense (mha_*) caches.
  *
  * Ownership: the caller owns every device buffer (ring storage, weights,
  * activations, outputs, workspace).  The library owns only the small host
@@ -90,7 +98,7 @@ typedef enum {
   MLA_ERR_SCRATCH = 11           /* call needs more than the static scratch        */
 } mla_status;
 
-typedef enum { MLA_F32 = 0, MLA_BF16 = 1, MLA_F16 = 2 } mla_dtype;
+typedef enum { MLA_F32 = 0, MLA_BF16 = 1, MLA_F16 = 2, MLA_E4M3 = 3 } mla_dtype;
 
 typedef struct {
   int32_t hidden;         /* layer input width                                  */
@@ -106,7 +114,9 @@ typedef struct {
   float rope_base;        /* frequency base, e.g. 10000                         */
   int32_t dtype;          /* inputs (x, q, weights): MLA_BF16 or MLA_F32         */
   int32_t cache_dtype;    /* ring storage: MLA_F32 with fp32 inputs; MLA_BF16 or
-                             MLA_F16 with bf16 inputs (2 bytes per scalar)      */
+                             MLA_F16 with bf16 inputs (2 bytes per scalar);
+                             MLA_E4M3 with bf16 inputs, latent caches only
+                             (1 byte per scalar)                                */
 } mla_layer_config;
 
 typedef struct {

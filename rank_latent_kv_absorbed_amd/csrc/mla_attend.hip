@@ -508,16 +508,19 @@ template <typename E>
 constexpr bool kSplitOf = __is_same(E, bf16_t);
 
 // Core launch for the schedule's shape (block rows, key tile, stages).
-template <typename E, int DC>
+// F8: the ring holds one-byte E4M3 rows, widened to fp16 operands (E) in the
+// core; the chunk shape then runs without the ping-pong wave groups.
+template <typename E, int DC, bool F8 = false>
 hipError_t launch_core(const AttnCore& c, hipStream_t s) {
   const Schedule& sc = c.sched;
   const dim3 grid((unsigned)sc.n_blocks);
   constexpr bool SPLIT = kSplitOf<E>;
-#define MLA_SHAPE(NW, KT, NS, ROWS)                                                                    \
-  if (sc.block_rows == ROWS * NW && sc.key_tile == KT && sc.stages == NS) {                           \
-    hipLaunchKernelGGL((attn_core_kernel<E, DC + 32, DC, NW, KT, NS, true, 1, (NW == 8), ROWS, SPLIT>), \
-                       grid, dim3(NW * 64), 0, s, c);                                                 \
-    return hipGetLastError();                                                                         \
+#define MLA_SHAPE(NW, KT, NS, ROWS)                                                                  \
+  if (sc.block_rows == ROWS * NW && sc.key_tile == KT && sc.stages == NS) {                         \
+    hipLaunchKernelGGL(                                                                             \
+        (attn_core_kernel<E, DC + 32, DC, NW, KT, NS, true, 1, (NW == 8 && !F8), ROWS, SPLIT, F8>), \
+        grid, dim3(NW * 64), 0, s, c);                                                              \
+    return hipGetLastError();                                                                       \
   }
   if constexpr (SPLIT) {
     MLA_SHAPE(4, 64, 3, 32)
@@ -533,7 +536,7 @@ hipError_t launch_core(const AttnCore& c, hipStream_t s) {
 }
 
 // The core over the prepared queries in a.qcat (profiling events around it).
-template <typename E, int DC>
+template <typename E, int DC, bool F8 = false>
 hipError_t launch_core_of(const AttendArgs& a, hipStream_t s) {
   AttnCore c;
   c.qrows = a.qcat;
@@ -557,7 +560,7 @@ hipError_t launch_core_of(const AttendArgs& a, hipStream_t s) {
     hipError_t e = hipEventRecord(a.ev_start, s);
     if (e != hipSuccess) return e;
   }
-  hipError_t e = launch_core<E, DC>(c, s);
+  hipError_t e = launch_core<E, DC, F8>(c, s);
   if (e != hipSuccess) return e;
   if (a.ev_stop != nullptr) e = hipEventRecord(a.ev_stop, s);
   return e;
@@ -596,7 +599,7 @@ __global__ __launch_bounds__(256) void merge_latent_kernel(AttendArgs a, bf16_t*
   st_bf16x8(o_lo + off, l8);
 }
 
-template <typename E, int DC>
+template <typename E, int DC, bool F8 = false>
 hipError_t launch_dc(const AttendArgs& a, hipStream_t s) {
   constexpr bool SPLIT = kSplitOf<E>;
   if ((a.qcat_lo != nullptr) != SPLIT) return hipErrorInvalidValue;
@@ -613,7 +616,7 @@ hipError_t launch_dc(const AttendArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   {
-    hipError_t e = launch_core_of<E, DC>(a, s);
+    hipError_t e = launch_core_of<E, DC, F8>(a, s);
     if (e != hipSuccess) return e;
   }
   // Rows with many key-range partials each (narrow blocks on 32-key tiles,
@@ -643,17 +646,26 @@ bool attend_bf16_supported(int d_c, int d_rope, int d_nope, int d_v) {
          d_nope % 16 == 0 && d_v > 0 && d_v % 32 == 0;
 }
 
-template <typename E>
+template <typename E, bool F8 = false>
 hipError_t launch_typed(const AttendArgs& a, hipStream_t s) {
   switch (a.d_c) {
-    case 64: return launch_dc<E, 64>(a, s);
-    case 128: return launch_dc<E, 128>(a, s);
-    case 192: return launch_dc<E, 192>(a, s);
+    case 64: return launch_dc<E, 64, F8>(a, s);
+    case 128: return launch_dc<E, 128, F8>(a, s);
+    case 192: return launch_dc<E, 192, F8>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_attend_core_only(const AttendArgs& a, hipStream_t s) {
+  if (a.cache_type == 3) {
+    if (a.qcat_lo != nullptr) return hipErrorInvalidValue;
+    switch (a.d_c) {
+      case 64: return launch_core_of<f16_t, 64, true>(a, s);
+      case 128: return launch_core_of<f16_t, 128, true>(a, s);
+      case 192: return launch_core_of<f16_t, 192, true>(a, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
   const bool f16 = a.cache_type == 2;
   if ((a.qcat_lo != nullptr) == f16) return hipErrorInvalidValue;
   switch (a.d_c) {
@@ -677,6 +689,7 @@ hipError_t launch_merge_latent(const AttendArgs& a, void* o_hi, void* o_lo, hipS
 }
 
 hipError_t launch_attend_bf16(const AttendArgs& a, hipStream_t s) {
+  if (a.cache_type == 3) return launch_typed<f16_t, true>(a, s);
   return a.cache_type == 2 ? launch_typed<f16_t>(a, s) : launch_typed<bf16_t>(a, s);
 }
 

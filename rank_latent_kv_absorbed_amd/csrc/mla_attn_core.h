@@ -56,6 +56,14 @@
 // issued for both parts with the same cached operand: 16 significant bits,
 // at twice the matrix work.  The extra registers take the whole register
 // file of a SIMD, so split blocks run one wave per SIMD.
+//
+// One-byte latent rows (F8, an E4M3 cache): the direct loads bring the raw
+// tile (KT * DQK bytes, the ring rows as they are) into a staging buffer,
+// half the bytes of a 2-byte tile; at the start of its step every lane widens
+// its share to fp16 (exact) into one decode buffer in the layout above, keys
+// past the window zeroed, and a barrier publishes it.  The staging buffer is
+// refilled right after that barrier, so NS - 1 raw tiles stay in flight while
+// one is consumed.  Products then run on fp16 operands as for an fp16 cache.
 #pragma once
 
 #include "mla_device.h"
@@ -162,7 +170,7 @@ __device__ __forceinline__ void lds_barrier() {
 // narrow blocks can share a compute unit; one wave per SIMD (the whole
 // register file, accumulators in AGPRs) when each wave owns RB > 1 row blocks.
 template <typename E, int DQK, int DV, int NW, int KT, int NS, bool SHARED_KV, int RB = 1,
-          bool PP = false, int ROWS = 32, bool SPLIT = false>
+          bool PP = false, int ROWS = 32, bool SPLIT = false, bool F8 = false>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu((RB == 1 && !SPLIT) ? 2 : 1, (RB == 1 && !SPLIT) ? 2 : 1)))
 void attn_core_kernel(AttnCore a) {
@@ -194,7 +202,12 @@ void attn_core_kernel(AttnCore a) {
   static_assert(!PP || (NS == 3 && NW % 2 == 0 && NW >= 2), "ping-pong: two wave groups, three buffers");
   static_assert(!SPLIT || (NW <= 4 && RB == 1), "split operands: one wave per SIMD");
   constexpr int NQ = SPLIT ? 2 : 1;           // operand parts (leading, remainder)
-  static_assert((SPANS + NW - 1) / NW * (NS - 1) <= 63, "tile loads in flight fit the vmcnt counter");
+  static_assert(!F8 || (SHARED_KV && __is_same(E, f16_t) && !PP && !SPLIT && RB == 1),
+                "one-byte latent rows widen to fp16 operands");
+  constexpr int SPANS8 = KT * DQK / 1024;     // 1-KiB direct-load spans of a raw one-byte tile
+  static_assert(!F8 || (KT * DQK) % 1024 == 0, "raw tiles are whole 1-KiB spans");
+  constexpr int SPL = F8 ? SPANS8 : SPANS;    // spans loaded per tile
+  static_assert((SPL + NW - 1) / NW * (NS - 1) <= 63, "tile loads in flight fit the vmcnt counter");
   // Whole spans with every lane active (exact load counts per wave); the chunk
   // permutation stays inside aligned groups of a row.
   static_assert(CHUNKS % 64 == 0, "tiles are whole 1-KiB spans");
@@ -202,11 +215,15 @@ void attn_core_kernel(AttnCore a) {
                           : (CPK % 16 == 0 && KCH % 16 == 0),
                 "row strides the swizzle was laid out for");
 
-  __shared__ __attribute__((aligned(1024))) E kt0[TILE];
-  __shared__ __attribute__((aligned(1024))) E kt1[TILE];
-  __shared__ __attribute__((aligned(1024))) E kt2[NS > 2 ? TILE : 8];
-  __shared__ __attribute__((aligned(1024))) E kt3[NS > 3 ? TILE : 8];
-  __shared__ __attribute__((aligned(1024))) E kt4[NS > 4 ? TILE : 8];
+  // Tile buffers (raw one-byte tiles for F8: half the size) and, for F8, the
+  // decode buffer the products read.
+  constexpr int TB = F8 ? TILE / 2 : TILE;
+  __shared__ __attribute__((aligned(1024))) E kt0[TB];
+  __shared__ __attribute__((aligned(1024))) E kt1[TB];
+  __shared__ __attribute__((aligned(1024))) E kt2[NS > 2 ? TB : 8];
+  __shared__ __attribute__((aligned(1024))) E kt3[NS > 3 ? TB : 8];
+  __shared__ __attribute__((aligned(1024))) E kt4[NS > 4 ? TB : 8];
+  __shared__ __attribute__((aligned(1024))) E kd[F8 ? TILE : 8];
 
   const Schedule& sc = a.sched;
   const int tid = threadIdx.x;
@@ -217,7 +234,7 @@ void attn_core_kernel(AttnCore a) {
   const int w = NW == 1 ? 0 : tid >> 6, l = tid & 63, lo = l & 31, hi = l >> 5;
   const int g = sched_block_of(sc, blockIdx.x);
   const int n_steps = sched_block_steps(sc, g);
-  const int n_ld = (SPANS - w + NW - 1) / NW;  // direct loads this wave issues per tile
+  const int n_ld = (SPL - w + NW - 1) / NW;  // direct loads this wave issues per tile
 
   // Chunk permutation of key row r (it depends on r mod 16 only).  Latent
   // rows are 4 * CPK dwords long, an odd multiple of 16 dwords (mod 64), so
@@ -242,6 +259,8 @@ void attn_core_kernel(AttnCore a) {
   constexpr int LPW = (SPANS + NW - 1) / NW;  // span slots per wave
   // Lane offset (elements) of span sp relative to the first key row of a
   // tile and the head's K columns (V columns sit at v_off - k_off from K).
+  // For F8 the same offsets (ring_stride = DQK) address the 8 raw bytes of
+  // the chunk a lane decodes in the staging buffer.
   // 16 keys fill CPK / 4 spans exactly and the chunk permutation repeats
   // every 16 keys, so span sp + CPK / 4 is span sp shifted by 16 key rows: a
   // one-wave block keeps the CPK / 4 distinct lane offsets, a wider block the
@@ -262,13 +281,35 @@ void attn_core_kernel(AttnCore a) {
     lane_bytes[j] = (uint32_t)lane_off[j] * (uint32_t)sizeof(E);
   }
   auto load_tile = [&](int b, int head, int kt, E* dst) MLA_INLINE {
-    const E* ring = (const E*)a.ring + (size_t)b * a.ring_rows * a.ring_stride;
     const int rows = (int)a.ring_rows;
     int s0 = (int)a.key_slot0 + kt * KT;
     s0 = s0 >= rows ? s0 - rows : s0;
+    if constexpr (F8) {
+      // The raw tile is KT * DQK contiguous bytes of the ring (rows of DQK
+      // bytes); lane l of span sp copies bytes [1024 sp + 16 l, + 16).  Past
+      // the ring's end the bytes continue at its start.
+      const char* base = (const char*)a.ring + ((size_t)b * rows + s0) * DQK;
+      lds_char* const ldst = (lds_char*)dst;
+      const int split = (rows - s0) * DQK, back = rows * DQK;
+#pragma unroll
+      for (int j = 0; j < (SPANS8 + NW - 1) / NW; ++j) {
+        const int sp = w + j * NW;
+        if (NW == 1 || sp < SPANS8) {
+          int off = sp * 1024 + 16 * l;
+          off = off >= split ? off - back : off;
+          if (rows < KT)  // a ring shorter than the tile: keys past the window wrap again
+            while (off >= split) off -= back;
+          global_to_lds16(base + off, ldst + sp * 1024);
+        }
+      }
+      return;
+    }
+    const E* ring = (const E*)a.ring + (size_t)b * a.ring_rows * a.ring_stride;
     const E* base = ring + ((size_t)s0 * a.ring_stride + a.k_off + head * a.head_stride);
     // Keys of a tile that crosses the ring's end continue at its start: the
-    // lane offsets at or past the crossing move back by the ring size.
+    // lane offsets at or past the crossing move back by the ring size (as
+    // often as needed when the ring holds fewer rows than a tile; such keys
+    // are past the window, so only their addresses matter).
     // (Keys past the window still read ring rows - allocated, possibly stale
     // memory; the step that uses the tile clears them in LDS.)
     const bool wraps = s0 + KT > rows;
@@ -295,6 +336,8 @@ void attn_core_kernel(AttnCore a) {
       if (NW == 1 || sp < SPANS) {
         int off = NW == 1 ? (j / PER) * 16 * a.ring_stride + lane_off[j % PER] : lane_off[j];
         off = off >= split ? off - back : off;
+        if (rows < KT)  // a ring shorter than the tile: keys past the window wrap again
+          while (off >= split) off -= back;
         global_to_lds16(base + off, ldst + sp * 1024);
       }
     }
@@ -307,6 +350,27 @@ void attn_core_kernel(AttnCore a) {
     f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int c = nk * CPK + w * 64 + l; c < KT * CPK; c += NW * 64)
       *reinterpret_cast<f32x4*>(buf + c * 8) = zero;
+  };
+
+  // F8: widen the raw tile in `stage` (key tile kt) into the decode buffer.
+  // Lane l of span sp writes decode chunk c = 64 sp + l (key c / CPK, the
+  // permuted position of the direct loads above) from the 8 raw bytes of the
+  // key's chunk (c % CPK) ^ swz(key); keys past the window become zeros.
+  auto decode = [&](const E* stage, int kt) MLA_INLINE {
+    const char* src = (const char*)stage;
+    const int nk = a.Lk - kt * KT;  // keys of the tile inside the window
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) {
+      const int sp = NW == 1 ? j : w + j * NW;
+      if (NW == 1 || sp < SPANS) {
+        const int off = NW == 1 ? (j / PER) * 16 * DQK + lane_off[j % PER] : lane_off[j];
+        const uint2 raw = *reinterpret_cast<const uint2*>(src + off);
+        f16x8 h = e4m3x8_to_f16(raw.x, raw.y);
+        const int c = sp * 64 + l;
+        if (nk < KT && c / CPK >= nk) h = zero8<f16_t>();
+        *reinterpret_cast<f16x8*>(kd + c * 8) = h;
+      }
+    }
   };
 
   // Lane-constant parts of the LDS read addresses.  Score reads: lane (lo, hi)
@@ -607,6 +671,55 @@ void attn_core_kernel(AttnCore a) {
   wi = wc;
   const StepInfo s0 = wc.c.si;
   const int b0 = wc.b;
+
+  if constexpr (F8) {
+    // A step: widen the raw tile, publish it (the barrier also frees the raw
+    // buffer, refilled at once with tile i + NS), compute on the decode
+    // buffer, then wait for this wave's loads of tile i + 1 and meet the
+    // other waves (nobody reads the decode buffer any more).
+    auto step8 = [&](int i, E* stage) MLA_INLINE {
+      const StepInfo si = wc.c.si;
+      const int b = wc.b;
+      decode(stage, si.kt);
+      lds_barrier();
+      if (i + NS < n_steps) issue(stage);
+      if (si.first && i > 0) {
+        begin_segment(b, si.grp - b * sc.n_rg);
+        asm volatile("" ::: "memory");  // keep the loads above the wait
+        __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
+      }
+      if (live) {
+        AccT sv[RB][NKB];
+        V8 pf[NQ][RB][NPF];
+        scores(kd, sv);
+        softmax(si.kt, sv, pf);
+        values(kd, pf);
+        if (si.last) write_partial(si, b);
+      }
+      walk_next(wc);
+      if (i + 1 < n_steps) {
+        wait_vmem(n_ld * ahead(i));
+        lds_barrier();
+      }
+    };
+    issue(kt0);
+    if (n_steps > 1) issue(kt1);
+    if (NS > 2 && n_steps > 2) issue(kt2);
+    if (NS > 3 && n_steps > 3) issue(kt3);
+    if (NS > 4 && n_steps > 4) issue(kt4);
+    begin_segment(b0, s0.grp - b0 * sc.n_rg);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
+    lds_barrier();
+    for (int i = 0; i < n_steps; i += NS) {
+      step8(i, kt0);
+      if (i + 1 < n_steps) step8(i + 1, kt1);
+      if constexpr (NS > 2) if (i + 2 < n_steps) step8(i + 2, kt2);
+      if constexpr (NS > 3) if (i + 3 < n_steps) step8(i + 3, kt3);
+      if constexpr (NS > 4) if (i + 4 < n_steps) step8(i + 4, kt4);
+    }
+    return;
+  }
 
   if constexpr (PP) {
     // Two wave groups, one wave of each per SIMD, work half a step apart so

@@ -238,6 +238,13 @@ __global__ __launch_bounds__(NT * 64) void cache_write_bf16_kernel(CacheWriteArg
     for (int r = 0; r < 16; ++r) v[r] *= a.scale;
   }
   E* dst = (E*)a.ring + rowoff[lo] + cb;
+  if constexpr (__is_same(E, e4m3_t)) {
+    // 16 one-byte codes: one 16-byte store (rows are multiples of 32 bytes)
+    u32x4 o = {e4m3_pack4(v[0], v[1], v[2], v[3]), e4m3_pack4(v[4], v[5], v[6], v[7]),
+               e4m3_pack4(v[8], v[9], v[10], v[11]), e4m3_pack4(v[12], v[13], v[14], v[15])};
+    *reinterpret_cast<u32x4*>(dst) = o;
+    return;
+  } else {
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     typename Elem<E>::v8 o, ol;
@@ -249,6 +256,7 @@ __global__ __launch_bounds__(NT * 64) void cache_write_bf16_kernel(CacheWriteArg
     *reinterpret_cast<typename Elem<E>::v8*>(dst + 8 * u) = o;
     if constexpr (MODE == PROJ_QUERY)
       if (a.out_lo != nullptr) *reinterpret_cast<typename Elem<E>::v8*>((E*)a.out_lo + rowoff[lo] + cb + 8 * u) = ol;
+  }
   }
 }
 
@@ -356,13 +364,17 @@ bool cache_write_bf16_supported(int width, int hidden) {
 }
 
 hipError_t launch_cache_write_bf16(const CacheWriteArgs& a, hipStream_t s) {
+  if (a.out_type == 3) return launch_typed<e4m3_t>(a, s);
   return a.out_type == 2 ? launch_typed<f16_t>(a, s) : launch_typed<bf16_t>(a, s);
 }
 
 hipError_t launch_projection_bf16(const CacheWriteArgs& a, int mode, hipStream_t s) {
   const bool f16 = a.out_type == 2;
-  if (mode == PROJ_CACHE_NORM && a.passes == 1)
+  if (mode == PROJ_CACHE_NORM && a.passes == 1) {
+    if (a.out_type == 3) return launch_norm<e4m3_t>(a, s);
     return f16 ? launch_norm<f16_t>(a, s) : launch_norm<bf16_t>(a, s);
+  }
+  if (a.out_type == 3) return hipErrorInvalidValue;  // projections write 2-byte operands
   if (mode == PROJ_QUERY && a.passes == 2)
     return f16 ? launch_parts<f16_t, PROJ_QUERY, 2>(a, s) : launch_parts<bf16_t, PROJ_QUERY, 2>(a, s);
   if (mode == PROJ_OUT && a.passes == 3) return launch_parts<bf16_t, PROJ_OUT, 3>(a, s);

@@ -98,6 +98,51 @@ __device__ __forceinline__ typename Elem<E>::v8 zero8() {
   return z;
 }
 
+// OCP 8-bit float E4M3 ('fn' variant: exponent bias 7, no infinities, largest
+// finite magnitude 448, smallest normal 2^-6, subnormal quantum 2^-9): the
+// one-byte cache scalar.  Storage only: the attention core widens it to fp16,
+// which holds every E4M3 value exactly.
+struct e4m3_t {
+  uint8_t bits;
+};
+
+// float -> E4M3 code, round to nearest even, saturating: magnitudes that
+// round past 448 (infinities included) store 448; NaN stores the NaN code.
+// Below 2^-6 a value is a multiple of 2^-9, so the code is rint(|f| * 2^9)
+// (0 .. 8; 8 is the smallest normal's code).  Above, the code is the float's
+// exponent and top three fraction bits, rounded half to even at bit 20 and
+// rebased from exponent bias 127 to 7.
+__device__ __forceinline__ uint32_t e4m3_code(float f) {
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t mag = u & 0x7fffffffu;
+  uint32_t m;
+  if (mag >= 0x43e00000u)                          // 448.0f
+    m = mag > 0x7f800000u ? 0x7fu : 0x7eu;
+  else if (mag < 0x3c800000u)                      // 2^-6
+    m = (uint32_t)__builtin_rintf(__uint_as_float(mag) * 512.0f);
+  else
+    m = ((mag + 0x7ffffu + ((mag >> 20) & 1u)) >> 20) - (120u << 3);
+  return sign | m;
+}
+
+// Four floats -> four E4M3 codes, element i in byte i.
+__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d) {
+  return e4m3_code(a) | (e4m3_code(b) << 8) | (e4m3_code(c) << 16) | (e4m3_code(d) << 24);
+}
+
+// Eight E4M3 codes (byte i of w0 = element i, byte i of w1 = element 4 + i) ->
+// fp16, with gfx950's conversion instruction (unit scale: exact).
+__device__ __forceinline__ f16x8 e4m3x8_to_f16(uint32_t w0, uint32_t w1) {
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false);
+  const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true);
+  const f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false);
+  const f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true);
+  f16x8 r = {a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+  return r;
+}
+
 // 2^x on the hardware exponential unit (v_exp_f32) without the library's
 // denormal-range fix-up: results below 2^-126 flush to zero, which softmax
 // weights tolerate (they are summed against a maximum weight of at least 1).

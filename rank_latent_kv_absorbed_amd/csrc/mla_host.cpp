@@ -47,14 +47,18 @@ namespace {
 constexpr size_t kAlign = 256;
 
 size_t elem_size(int32_t dtype) {
+  if (dtype == MLA_E4M3) return 1;
   return (dtype == MLA_BF16 || dtype == MLA_F16) ? 2 : (dtype == MLA_F32 ? 4 : 0);
 }
 
 // Input / storage combinations with kernels: fp32 everywhere, or bf16 inputs
-// with a 2-byte (bf16 or fp16) ring.
-bool valid_types(const mla_layer_config* c) {
+// with a 2-byte (bf16 or fp16) ring, or (latent caches only) a one-byte E4M3
+// ring.
+bool valid_types(const mla_layer_config* c, bool dense) {
   if (c->dtype == MLA_F32) return c->cache_dtype == MLA_F32;
-  if (c->dtype == MLA_BF16) return c->cache_dtype == MLA_BF16 || c->cache_dtype == MLA_F16;
+  if (c->dtype == MLA_BF16)
+    return c->cache_dtype == MLA_BF16 || c->cache_dtype == MLA_F16 ||
+           (!dense && c->cache_dtype == MLA_E4M3);
   return false;
 }
 
@@ -127,7 +131,7 @@ bool valid_config(const mla_layer_config* c, bool dense) {
   if (!dense && c->rope_pairs_t + c->rope_pairs_h + c->rope_pairs_w != c->d_rope / 2) return false;
   if (dense && (c->d_nope + c->d_rope) % 2 != 0) return false;
   if (!(c->rope_base > 0.0f) || !isfinite(c->rope_base)) return false;
-  if (!valid_types(c)) return false;
+  if (!valid_types(c, dense)) return false;
   if (c->d_rope / 2 > mla::kMaxRopePairs) return false;
   if (dense && (c->d_nope + c->d_rope) / 2 > mla::kMaxRopePairs) return false;
   // ring rows, key counts and element offsets inside one sequence's ring are
@@ -193,8 +197,11 @@ constexpr int64_t kMinStepsPerBlock = 8;
 constexpr int64_t kSegmentCostLatent = 3;
 constexpr int64_t kSegmentCostDense = 6;
 
+// chunks_per_key: 16-byte chunks of a cached key row; decode_chunks_per_key:
+// those of the fp16 decode tile of a one-byte ring (0 otherwise).
 mla::Schedule make_schedule(int64_t B, int64_t R, int64_t Lk, int32_t key_splits, int64_t cus,
-                            mla::CoreShape sh, int chunks_per_key, int64_t seg_cost, bool split) {
+                            mla::CoreShape sh, int chunks_per_key, int64_t seg_cost, bool split,
+                            int decode_chunks_per_key = 0) {
   mla::Schedule s;
   sh = mla::core_shape_for_keys(sh, chunks_per_key);
   const int64_t br = (int64_t)sh.rows * sh.waves;
@@ -207,7 +214,7 @@ mla::Schedule make_schedule(int64_t B, int64_t R, int64_t Lk, int32_t key_splits
     nb = groups * key_splits;
   } else {
     const int64_t by_work = (total + kMinStepsPerBlock - 1) / kMinStepsPerBlock;
-    const int64_t resident = cus * mla::core_blocks_per_cu(sh, chunks_per_key, split);
+    const int64_t resident = cus * mla::core_blocks_per_cu(sh, chunks_per_key, split, decode_chunks_per_key);
     nb = resident < by_work ? resident : by_work;
   }
   if (nb < 1) nb = 1;
@@ -272,9 +279,11 @@ LatentLayout latent_layout(const mla_cache* h, int32_t Lq, int32_t key_splits, i
   const int64_t R = (int64_t)Lq * c.n_heads;
   LatentLayout L;
   const bool split = split_operands(c);
+  const bool f8 = c.cache_dtype == MLA_E4M3;  // one-byte rows, widened in the core
+  const int row_chunks = (c.d_c + c.d_rope) / (f8 ? 16 : 8);
   L.sched = make_schedule(c.batch, R, Lk < 0 ? window_keys(h) : Lk, key_splits, mla::device_cu_count(),
-                          mla::core_shape_for_rows(R, split), (c.d_c + c.d_rope) / 8, kSegmentCostLatent,
-                          split);
+                          mla::core_shape_for_rows(R, split), row_chunks, kSegmentCostLatent, split,
+                          f8 ? (c.d_c + c.d_rope) / 8 : 0);
   const size_t width = (size_t)(c.d_c + c.d_rope);
   const size_t slots = (size_t)L.sched.n_slots;
   const size_t qbytes = round_up((size_t)c.batch * R * width * 2, kAlign);
@@ -922,7 +931,7 @@ mla_status mla_attend_block(mla_cache* h, const void* x, int64_t q_token0, int32
   p.grid_w = c.grid_w;
   p.W = c.window_frames;
   p.q_token0 = q_token0;
-  p.out_type = c.cache_dtype;
+  p.out_type = c.cache_dtype == MLA_E4M3 ? MLA_F16 : c.cache_dtype;  // the core's operand type
   p.rope = latent_rope(c);
   p.passes = 2;
   p.w_part[1] = (int64_t)qw * c.hidden * 2;

@@ -53,7 +53,7 @@ struct CacheWriteArgs {
   int64_t ring_rows;      // W * T
   int64_t frame0;         // cache: first frame written
   int64_t q_token0;       // query: global token of row 0 of every sequence
-  int out_type;           // element type of 2-byte outputs: 1 = bf16, 2 = fp16
+  int out_type;           // output element type: 1 = bf16, 2 = fp16, 3 = E4M3 (cache writes)
   RopeTable rope;
   int passes;                             // 1 .. kProjMaxPasses
   int64_t x_part[kProjMaxPasses];         // byte offset of pass p's x part from x
@@ -114,11 +114,13 @@ inline CoreShape core_shape_for_keys(CoreShape sh, int chunks_per_key) {
 }
 
 // Blocks of a shape that fit one compute unit at once: LDS (160 KiB per CU)
-// holds `stages` key tiles of `chunks_per_key` 16-byte chunks per key, and
-// the core's register use allows two waves per SIMD (eight per CU), or one
-// (four per CU) for split operands.
-inline int core_blocks_per_cu(CoreShape sh, int chunks_per_key, bool split = false) {
-  const int lds = sh.stages * sh.key_tile * chunks_per_key * 16;
+// holds `stages` key tiles of `chunks_per_key` 16-byte chunks per key (plus,
+// for one-byte rows, one decode tile of `decode_chunks_per_key`), and the
+// core's register use allows two waves per SIMD (eight per CU), or one (four
+// per CU) for split operands.
+inline int core_blocks_per_cu(CoreShape sh, int chunks_per_key, bool split = false,
+                              int decode_chunks_per_key = 0) {
+  const int lds = (sh.stages * chunks_per_key + decode_chunks_per_key) * sh.key_tile * 16;
   const int by_lds = (160 * 1024) / lds;
   const int by_waves = (split ? 4 : 8) / sh.waves;
   return by_lds < by_waves ? by_lds : by_waves;
@@ -294,7 +296,7 @@ struct AttendArgs {
   int64_t key_slot0;      // ring slot of resident key 0
   int Lk;                 // resident keys
   Schedule sched;
-  int cache_type;         // 1 = bf16, 2 = fp16 (2-byte path); inputs are bf16
+  int cache_type;         // 1 = bf16, 2 = fp16, 3 = E4M3 (widened to fp16); inputs are bf16
   float qscale;           // log2(e) / sqrt(d_nope + d_rope)
   hipEvent_t ev_start;    // optional: recorded right before / after the core kernel
   hipEvent_t ev_stop;

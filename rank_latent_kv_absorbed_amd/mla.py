@@ -31,8 +31,9 @@ class MlaError(RuntimeError):
 # status codes (include/mla.h)
 OK, ERR_INVALID_ARG, ERR_STORAGE_TOO_SMALL, ERR_FULL, ERR_NOT_CONTIGUOUS, ERR_EVICT_RANGE, \
     ERR_EMPTY, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_WRONG_KIND, ERR_HIP, ERR_SCRATCH = range(12)
-F32, BF16, F16 = 0, 1, 2
-_DTYPES = {"f32": (F32, torch.float32), "bf16": (BF16, torch.bfloat16), "f16": (F16, torch.float16)}
+F32, BF16, F16, E4M3 = 0, 1, 2, 3
+_DTYPES = {"f32": (F32, torch.float32), "bf16": (BF16, torch.bfloat16), "f16": (F16, torch.float16),
+           "e4m3": (E4M3, torch.float8_e4m3fn)}
 
 
 class LayerConfigC(ctypes.Structure):
@@ -125,7 +126,7 @@ def default_rope_split(d_rope):
 def make_config(cfg, batch=None):
     """ctypes config from any object with the layer attributes (hidden, n_heads,
     d_nope, d_rope, d_v, d_c, grid_h, grid_w, window_frames, batch, rope_split,
-    rope_base, dtype in {'bf16', 'f32'}, cache_dtype in {'bf16', 'f16', 'f32'}; a
+    rope_base, dtype in {'bf16', 'f32'}, cache_dtype in {'bf16', 'f16', 'e4m3', 'f32'}; a
     missing cache_dtype means fp16 storage for bf16 inputs, fp32 for fp32)."""
     split = getattr(cfg, "rope_split", None) or default_rope_split(cfg.d_rope)
     c = LayerConfigC()
@@ -416,10 +417,12 @@ def attend_flops(n_heads, Lq, Lk, d_c, d_rope, d_nope, d_v, batch=1):
     return R * Lk * (2 * (d_c + d_rope) + 2 * d_c) + R * (2 * d_nope * d_c + 2 * d_c * d_v)
 
 
-def attend_bytes(n_heads, Lq, Lk, d_c, d_rope, d_nope, d_v, batch=1, elem=2):
-    """Algorithmic HBM bytes of one attend call: the window read once, queries
-    in, fp32 output out, and the up-projection weights."""
-    return batch * (Lk * (d_c + d_rope) * elem + Lq * n_heads * (d_nope + d_rope) * elem
+def attend_bytes(n_heads, Lq, Lk, d_c, d_rope, d_nope, d_v, batch=1, elem=2, cache_elem=None):
+    """Algorithmic HBM bytes of one attend call: the window read once (at
+    cache_elem bytes per scalar, default elem), queries in, fp32 output out,
+    and the up-projection weights."""
+    ce = elem if cache_elem is None else cache_elem
+    return batch * (Lk * (d_c + d_rope) * ce + Lq * n_heads * (d_nope + d_rope) * elem
                     + Lq * n_heads * d_v * 4) + n_heads * (d_nope + d_v) * d_c * elem
 
 

@@ -89,6 +89,12 @@ void fake_proj_info(int which, long long* o) {
                      (long long)(intptr_t)a.ring, (long long)(intptr_t)a.out_lo, (long long)(intptr_t)a.x};
   memcpy(o, v, sizeof(v));
 }
+// Element types of the last cache write, latent attend and query projection.
+void fake_type_info(int* o) {
+  o[0] = g_write.out_type;
+  o[1] = g_attend.cache_type;
+  o[2] = mla::g_proj[0].out_type;
+}
 float fake_write_eps() { return g_write.eps; }
 int fake_write_norm_cols() { return g_write.norm_cols; }
 int fake_count() { return g_count; }

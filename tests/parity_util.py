@@ -47,11 +47,14 @@ def dev(t):
 
 
 NAN_BITS = {"bf16": 0x7FC0, "f16": 0x7E00}
+E4M3_NAN = 0x7F
 
 
 def nan_fill_(storage, dtype):
     """Fill ring storage with NaN in the storage dtype."""
-    if dtype in NAN_BITS:
+    if dtype == "e4m3":
+        storage.view(torch.uint8).fill_(E4M3_NAN)
+    elif dtype in NAN_BITS:
         storage.view(torch.int16).fill_(NAN_BITS[dtype])
     else:
         storage.view(torch.float32).fill_(float("nan"))
@@ -102,6 +105,8 @@ class LatentRun:
         self.store[:, slots, :] = rows
         ring = self.gpu.ring()
         t = torch.from_numpy(np.ascontiguousarray(rows)).to(ring.dtype)
+        if ring.dtype == torch.float8_e4m3fn:   # one-byte codes, copied as bytes
+            ring, t = ring.view(torch.uint8), t.view(torch.uint8)
         ring[:, torch.from_numpy(slots)] = t.to(ring.device)
         torch.cuda.synchronize()
 

@@ -780,3 +780,52 @@ def test_cache_write_norm_arguments(sim):
     st, g = _create(sim, _cfg(dtype="f32", cache_dtype="f32"))
     assert sim.mla_cache_write_norm(g, P(FAKE_PTR), P(FAKE_PTR), P(FAKE_PTR), ctypes.c_float(0.0), 0, 1,
                                     None) == 8
+
+
+def test_e4m3_ring_rules(sim):
+    """A one-byte (E4M3) ring: latent caches with bf16 inputs only, one byte
+    per stored scalar; writes and attends carry the type; no expansion; the
+    core's LDS holds the raw tiles plus one fp16 decode tile, which sets the
+    blocks per compute unit; the attention block's query projection writes
+    fp16 operands."""
+    E4M3 = 3
+    c = _cfg(cache_dtype="e4m3")
+    assert sim.mla_cache_bytes(ctypes.byref(c)) == 21 * 1560 * 224
+    assert sim.mha_cache_bytes(ctypes.byref(c)) == 0
+    assert _create(sim, c, dense=True)[0] == 1
+    f32 = _cfg(cache_dtype="e4m3")
+    f32.dtype = 0
+    assert sim.mla_cache_bytes(ctypes.byref(f32)) == 0
+    st, h = _create(sim, c)
+    assert st == 0
+    assert sim.mla_cache_write(h, P(FAKE_PTR), P(FAKE_PTR), 0, 3, None) == 0
+    t = (ctypes.c_int * 3)()
+    sim.fake_type_info(t)
+    assert t[0] == E4M3
+    assert sim.mla_cache_set_attend_path(h, 2) == 8
+    assert sim.mla_attend_path(h, 4680, 0) == 1
+    assert sim.mla_cache_set_state(h, 3, 23) == 0
+    ws = 1 << 40
+    for Lq in (1, 4, 8, 11, 100, 4680):
+        R = Lq * 12
+        need = sim.mla_attend_workspace_bytes(h, Lq, 0)
+        assert sim.mla_attend(h, P(FAKE_PTR), 21 * 1560, Lq, P(FAKE_PTR), P(FAKE_PTR),
+                              P(FAKE_PTR), 0, P(ws), need, None) == 0
+        sim.fake_type_info(t)
+        assert t[1] == E4M3
+        a = _attend_info(sim)
+        shape = expected_shape(R, chunks_per_key=14)      # raw rows: 224 bytes
+        assert (a["block_rows"], a["key_tile"], a["stages"]) == shape, Lq
+        check_schedule(sim, a, R)
+        br, kt, ns = shape
+        waves = 1 if br <= 32 else (4 if br == 64 else br // 32)
+        per_cu = min(160 * 1024 // ((ns * 14 + 28) * kt * 16), 8 // waves)
+        assert a["n_blocks"] == min(256 * per_cu, -(-a["n_groups"] * a["n_kt"] // 8))
+        p = _attend_ptrs(sim)
+        qbytes = -(-R * 224 * 2 // 256) * 256
+        assert p["qcat_lo"] == 0 and p["opart"] == ws + qbytes
+    bw = sim.mla_attend_block_workspace_bytes(h, 40, 0)
+    assert sim.mla_attend_block(h, P(FAKE_PTR), 21 * 1560 - 40, 40, P(FAKE_PTR), P(FAKE_PTR),
+                                P(FAKE_PTR), 0, P(ws), bw, None) == 0
+    sim.fake_type_info(t)
+    assert t[2] == 2 and t[1] == E4M3

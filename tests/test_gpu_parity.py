@@ -211,6 +211,23 @@ def test_attend_narrow_blocks_ragged_with_wrap(Lq, key_splits):
     assert_parity(got, ref, "bf16", f"narrow blocks Lq={Lq} splits={key_splits}")
 
 
+@pytest.mark.parametrize("cache_dtype", ["f16", "bf16", "e4m3"])
+@pytest.mark.parametrize("window_frames,n_frames", [(3, 3), (40, 37)])
+def test_ring_shorter_than_a_key_tile(cache_dtype, window_frames, n_frames):
+    """One token per frame: a 3-row ring is shorter than every key tile, so a
+    tile's keys past the window wrap around it more than once (their scores
+    are masked); a 40-row ring is shorter than the 64-key tiles of the chunk
+    shape.  Every element, 1 and 130 queries."""
+    cfg = mid_cfg(grid_h=1, grid_w=1, window_frames=window_frames, batch=3, cache_dtype=cache_dtype)
+    run = LatentRun(cfg)
+    run.write(0, n_frames)
+    for Lq in (1, 130):
+        q = run.query(Lq, chunk=Lq)
+        got, ref, _ = run.attend(q, n_frames - 1)
+        assert_parity(got, ref, "bf16", f"{window_frames}-row ring {cache_dtype} Lq={Lq}",
+                      mean_lim=ring_lim(cfg))
+
+
 @pytest.mark.parametrize("d_c", [64, 128, 192])
 def test_attend_wan_heads_latent_widths(d_c):
     cfg = wan_small(d_c=d_c)
