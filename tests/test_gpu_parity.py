@@ -710,7 +710,8 @@ def _climbing_window(cfg, step_log2, seed=0):
     return rows, col - cfg.d_c, A
 
 
-@pytest.mark.parametrize("cache_dtype,path", [("f16", "absorbed"), ("f16", "expand"), ("bf16", "absorbed")])
+@pytest.mark.parametrize("cache_dtype,path", [("f16", "absorbed"), ("f16", "expand"), ("bf16", "absorbed"),
+                                              ("e4m3", "absorbed")])
 def test_sharp_attention_running_max_climbs(cache_dtype, path):
     """Every frame's keys score about 9 log2 units above the previous frame's,
     so each row's running maximum jumps by more than the lazy-rescale
@@ -720,8 +721,7 @@ def test_sharp_attention_running_max_climbs(cache_dtype, path):
     cfg = config("wan_window").with_(cache_dtype=cache_dtype)
     run = LatentRun(cfg, path=path)
     stored, qcol, A = _climbing_window(cfg, 9.0)
-    conv = {"f16": torch.float16, "bf16": torch.bfloat16}[cache_dtype]
-    stored = torch.from_numpy(stored).to(conv).double().numpy()
+    stored = O.round_storage(stored, cache_dtype)
     oldest = 10                                     # frames 10..30: slots wrap after frame 20
     # resident order is oldest first: frame oldest + i holds the i-th climb step
     order = np.concatenate([np.arange(i * cfg.T, (i + 1) * cfg.T) for i in range(cfg.window_frames)])
