@@ -8,7 +8,7 @@ the fp64 oracle on the same seeded inputs:
     the two bf16 parts sum to the fp64 products within 2^-15 of each value;
   * the attention block (mla_attend_block) from the query tokens' layer input
     to model width, every element on mid sizes and sampled rows at the Wan
-    shape, both ring types.
+    shape, every ring type.
 
 Bars as in the other parity tests: max|err| <= 1e-2 max|ref| and
 sum|err| <= 2e-3 sum|ref| (1.5e-3 for a bf16 ring).
@@ -25,7 +25,7 @@ from tests.parity_util import (BF16_RING_MEAN_REL, LatentRun, assert_parity, dev
 
 pytestmark = pytest.mark.gpu
 
-SIG_BITS = {"bf16": 8, "f16": 11}
+SIG_BITS = {"bf16": 8, "f16": 11, "e4m3": 4}
 EPS = 1e-6
 
 
@@ -88,16 +88,18 @@ class BlockRun(LatentRun):
 # cache write with the latent normalised
 # --------------------------------------------------------------------------
 
-@pytest.mark.parametrize("cache_dtype,d_c", [("f16", 64), ("bf16", 128), ("f16", 192)])
+@pytest.mark.parametrize("cache_dtype,d_c", [("f16", 64), ("bf16", 128), ("f16", 192), ("e4m3", 192)])
 def test_cache_write_norm_values(cache_dtype, d_c):
     cfg = mid_cfg(cache_dtype=cache_dtype, d_c=d_c, batch=2) if d_c < 192 else \
         config("wan_layer").with_(grid_h=5, grid_w=13, window_frames=6, batch=2, cache_dtype=cache_dtype)
     run = BlockRun(cfg, norm=True)
     x = run.write(0, 3)
     torch.cuda.synchronize()
-    got = run.gpu.ring().double().cpu().numpy()[:, :3 * cfg.T]
+    got = run.gpu.ring().cpu().double().numpy()[:, :3 * cfg.T]
     ref = run.store[:, :3 * cfg.T]
     ulp = np.ldexp(1.0, np.frexp(np.abs(ref))[1] - SIG_BITS[cache_dtype])
+    if cache_dtype == "e4m3":
+        ulp = np.maximum(ulp, 2.0 ** -9)          # the subnormal quantum
     # fp32 summation of the hidden-wide products (scaled like the stored value)
     # and of the row's sum of squares
     raw = np.abs(x.double().numpy()) @ np.abs(run.w["w_dkr"].double().numpy()).T
@@ -159,7 +161,7 @@ def test_folded_weights_match_fp64_products():
 
 # Mid sizes through a ring wrap (300 keys, ragged tiles); query counts reach
 # the narrow and chunk core shapes; forced key splits merge partials.
-@pytest.mark.parametrize("cache_dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("cache_dtype", ["f16", "bf16", "e4m3"])
 @pytest.mark.parametrize("Lq,key_splits", [(3, 0), (20, 0), (33, 3), (130, 0)])
 def test_attend_block_every_element(cache_dtype, Lq, key_splits):
     cfg = mid_cfg(d_nope=96, d_rope=32, d_v=128, d_c=64, cache_dtype=cache_dtype)
@@ -174,7 +176,7 @@ def test_attend_block_every_element(cache_dtype, Lq, key_splits):
     assert_parity(got, ref, "bf16", f"block {cache_dtype} Lq={Lq} splits={key_splits}", mean_lim=ring_lim(cfg))
 
 
-@pytest.mark.parametrize("cache_dtype,norm", [("f16", False), ("bf16", False), ("f16", True)])
+@pytest.mark.parametrize("cache_dtype,norm", [("f16", False), ("bf16", False), ("f16", True), ("e4m3", True)])
 def test_attend_block_wan_layer_sampled_rows(cache_dtype, norm):
     cfg = config("wan_layer").with_(cache_dtype=cache_dtype)
     run = BlockRun(cfg, norm=norm)

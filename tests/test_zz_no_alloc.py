@@ -95,7 +95,7 @@ def test_noalloc_uses_the_scratch_and_refuses_oversized_calls(sim):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("cache_dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("cache_dtype", ["f16", "bf16", "e4m3"])
 def test_noalloc_matches_mla_attend_twice(cache_dtype):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
