@@ -269,6 +269,40 @@ def test_attend_small_queries_latent_widths(Lq, d_c):
     assert_parity(got, ref, "bf16", f"small query Lq={Lq} d_c={d_c}")
 
 
+@pytest.mark.parametrize("cache_dtype,path", [("f16", "absorbed"), ("f16", "expand"), ("bf16", "absorbed"),
+                                              ("e4m3", "absorbed")])
+def test_degenerate_softmax_closed_forms(cache_dtype, path):
+    """Two windows whose attention has a closed form, 300 keys through a wrap:
+    zero queries weight every key equally, so each head's output is W^V_up,h
+    applied to the mean stored latent; a window of identical rows gives
+    W^V_up,h c for any query.  Checked against the closed forms (fp64, from
+    the stored values) and the oracle."""
+    cfg = mid_cfg(d_nope=96, d_rope=32, d_v=128, d_c=192, cache_dtype=cache_dtype)
+    run = LatentRun(cfg, path=path)
+    run.write(0, 4)
+    run.evict(2)
+    run.write(4, 2)
+    run.evict(1)
+    run.write(6, 2)
+    slots = run.ring.resident_slots()
+    w_uv = run.w["w_uv"].double().numpy()
+    for Lq in (20, 130):
+        q = torch.zeros((cfg.batch, Lq, cfg.n_heads, cfg.d_qk), dtype=torch.bfloat16)
+        got, ref, _ = run.attend(q, 8 * cfg.T - Lq)
+        cbar = run.store[:, slots, :cfg.d_c].mean(axis=1)                 # [B, d_c]
+        want = np.einsum("hvc,bc->bhv", w_uv, cbar)[:, None].repeat(Lq, axis=1)
+        assert_parity(got, want, "bf16", f"zero queries {cache_dtype} {path} Lq={Lq}", mean_lim=ring_lim(cfg))
+        assert_parity(ref, want, "f32", "oracle, zero queries")
+    # every resident row equal to one stored row
+    row = run.store[:, slots[:1]]
+    run.fill(run.ring.oldest, run.ring.newest, np.repeat(row, len(slots), axis=1))
+    q = run.query(40)
+    got, ref, _ = run.attend(q, 8 * cfg.T - 40)
+    want = np.einsum("hvc,bc->bhv", w_uv, row[:, 0, :cfg.d_c])[:, None].repeat(40, axis=1)
+    assert_parity(got, want, "bf16", f"identical keys {cache_dtype} {path}", mean_lim=ring_lim(cfg))
+    assert_parity(ref, want, "f32", "oracle, identical keys")
+
+
 def test_nan_poison_determinism_and_split_agreement():
     cfg = wan_small()
     runs = [LatentRun(cfg, poison=p) for p in (False, True)]
