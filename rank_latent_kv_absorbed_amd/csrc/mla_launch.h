@@ -183,15 +183,26 @@ MLA_HD inline int sched_block_steps(const Schedule& s, int g) {
 }
 
 // Logical block of hardware workgroup hw.  Workgroups are dealt round-robin
-// to the kDies accelerator dies (die hw % kDies), each with its own L2; die x
-// runs the contiguous logical blocks [O_x, O_x + c_x), so consecutive row
-// groups - the same head on the per-head path, whose blocks read the same key
-// and value tiles in lockstep - share one L2 instead of spreading over all.
+// to the kDies accelerator dies (die hw % kDies), each with its own L2, so
+// die x runs hardware workgroups P_x .. P_x + c_x - 1 in this count.  With no
+// balanced tail, die x runs the contiguous logical blocks [P_x, P_x + c_x):
+// consecutive row groups - the same head on the per-head path, whose blocks
+// read the same key and value tiles in lockstep - share one L2 instead of
+// spreading over all.  With a tail, the main blocks 0 .. rem - 1 and the tail
+// blocks rem .. n_blocks - 1 are spread over the dies in proportion
+// (die x: main blocks [P_x rem / n_blocks, P_{x+1} rem / n_blocks), and the
+// tail blocks in the same proportion), so that a die's tail blocks finish the
+// row groups its own main blocks started and their short tail key ranges are
+// read through the L2 that already holds that head's tiles.
 constexpr int kDies = 8;
 MLA_HD inline int sched_block_of(const Schedule& s, int hw) {
   const int nb = s.n_blocks, q = nb / kDies, r = nb % kDies;
   const int x = hw % kDies, k = hw / kDies;
-  return x * q + (x < r ? x : r) + k;
+  const int start = x * q + (x < r ? x : r), cnt = q + (x < r ? 1 : 0);
+  if (s.rem <= 0 || s.main_len >= s.n_kt) return start + k;
+  const int m0 = (int)((int64_t)start * s.rem / nb);
+  const int mc = (int)((int64_t)(start + cnt) * s.rem / nb) - m0;
+  return k < mc ? m0 + k : s.rem + (start - m0) + (k - mc);
 }
 
 // Step i (0 <= i < sched_block_steps(s, g)) of block g.

@@ -119,6 +119,7 @@ void fake_attend_info(long long* o) {
 }
 // The last (which = 0: latent, 1: dense) attend's schedule as the kernels decode it.
 static const mla::Schedule& sched_of(int which) { return which ? g_mha_sched : g_attend.sched; }
+int fake_sched_block_of(int which, int hw) { return mla::sched_block_of(sched_of(which), hw); }
 int fake_sched_steps(int which, int g) { return mla::sched_block_steps(sched_of(which), g); }
 void fake_sched_decode(int which, int g, int i, int* o) {
   const mla::StepInfo si = mla::sched_decode(sched_of(which), g, i);

@@ -829,3 +829,40 @@ def test_e4m3_ring_rules(sim):
                                 P(FAKE_PTR), 0, P(ws), bw, None) == 0
     sim.fake_type_info(t)
     assert t[2] == 2 and t[1] == E4M3
+
+
+def test_block_placement_is_a_permutation_with_tails_beside_their_groups(sim):
+    """Hardware workgroup -> logical block (dealt round-robin over 8 dies) is a
+    permutation of the blocks; with a balanced tail, each die runs a
+    proportional share of the main blocks and of the tail blocks, and the
+    groups its tail blocks finish are within a die's worth of the groups its
+    main blocks start."""
+    ws = 1 << 40
+    for name, kw, Lq in (("wan_window", {}, 4680), ("wan_window", {"batch": 11}, 1),
+                         ("wan_window", {"batch": 3}, 8), ("wan_layer", {}, 4680)):
+        for path in (1, 2):
+            st, h = _create(sim, _cfg(name, **kw))
+            assert st == 0
+            c = _cfg(name, **kw)
+            assert sim.mla_cache_set_state(h, 0, c.window_frames - 1) == 0
+            if sim.mla_cache_set_attend_path(h, path) != 0:
+                continue
+            need = sim.mla_attend_workspace_bytes(h, Lq, 0)
+            assert sim.mla_attend(h, P(FAKE_PTR), c.window_frames * 1560 - Lq, Lq, P(FAKE_PTR),
+                                  P(FAKE_PTR), P(FAKE_PTR), 0, P(ws), need, None) == 0
+            which = 1 if path == 2 else 0
+            a = _mha_info(sim) if which else _attend_info(sim)
+            nb, rem = a["n_blocks"], a["rem"]
+            g = [sim.fake_sched_block_of(which, hw) for hw in range(nb)]
+            assert sorted(g) == list(range(nb)), (name, kw, Lq, path)
+            if rem == 0 or a["main_len"] >= a["n_kt"]:
+                continue
+            tl = a["n_kt"] - a["main_len"]
+            for x in range(8):
+                mine = [g[hw] for hw in range(x, nb, 8)]
+                mains = [b for b in mine if b < rem]
+                tails = [b - rem for b in mine if b >= rem]
+                assert abs(len(mains) - len(mine) * rem / nb) <= 1.0
+                if mains and tails:
+                    first_grp = min(tails) * a["tpb"] // tl
+                    assert abs(first_grp - min(mains)) <= -(-rem // 8) + 1, (name, kw, Lq, path, x)
