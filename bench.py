@@ -51,11 +51,13 @@ TRAFFIC_FILES = {"absorbed": os.path.join(ROOT, "profiles", "attend_core_wan_win
 CORE_SOURCES = {
     "absorbed": ["rank_latent_kv_absorbed_amd/csrc/mla_attn_core.h",
                  "rank_latent_kv_absorbed_amd/csrc/mla_attend.hip",
-                 "rank_latent_kv_absorbed_amd/csrc/mla_device.h"],
+                 "rank_latent_kv_absorbed_amd/csrc/mla_device.h",
+                 "rank_latent_kv_absorbed_amd/csrc/mla_launch.h"],
     "expand": ["rank_latent_kv_absorbed_amd/csrc/mla_attn_core.h",
                "rank_latent_kv_absorbed_amd/csrc/mha_attend.hip",
                "rank_latent_kv_absorbed_amd/csrc/mla_expand.hip",
-               "rank_latent_kv_absorbed_amd/csrc/mla_device.h"],
+               "rank_latent_kv_absorbed_amd/csrc/mla_device.h",
+               "rank_latent_kv_absorbed_amd/csrc/mla_launch.h"],
 }
 CORE_KERNELS = {"absorbed": "attn_core_kernel<E, 224, 192, ...> (latent scores and value sums)",
                 "expand": "attn_core_kernel<E, 128, 128, ...> (per-head attention over the "
