@@ -219,6 +219,7 @@ hipError_t launch_mha_typed(const MhaAttendArgs& a, float* opart, float* ml, con
   c.qrows = a.qrot;
   c.qrows_lo = a.qrot_lo;
   c.ring = a.ring;
+  c.part16 = 0;
   c.opart = opart;
   c.ml = ml;
   c.ring_rows = a.ring_rows;

@@ -240,16 +240,18 @@ __global__ __launch_bounds__(64) void epilogue_bf16_kernel(AttendArgs a) {
   for (int k = 0; k < n_part; ++k) {
     const size_t prow = ((size_t)k * a.B + b) * R + row;
     const float wgt = exp2_fast(a.ml[prow * 2] - M);
-    L += wgt * a.ml[prow * 2 + 1];
-    const float* op = a.opart + prow * DC + 8 * hi;
+    const float lk = a.ml[prow * 2 + 1];
+    L += wgt * lk;
+    const float wv = wgt;  // fp32 partials (fp16 ones are merged by the per-row epilogue)
+    const size_t e0 = prow * DC + 8 * hi;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      const f32x4 x0 = *reinterpret_cast<const f32x4*>(op + 16 * ks);
-      const f32x4 x1 = *reinterpret_cast<const f32x4*>(op + 16 * ks + 4);
+      const f32x4 x0 = load_part4<false>(a.opart, e0 + 16 * ks);
+      const f32x4 x1 = load_part4<false>(a.opart, e0 + 16 * ks + 4);
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        v[ks][t] += wgt * x0[t];
-        v[ks][4 + t] += wgt * x1[t];
+        v[ks][t] += wv * x0[t];
+        v[ks][4 + t] += wv * x1[t];
       }
     }
   }
@@ -305,7 +307,7 @@ constexpr int kEpiWeights = 1024;    // slot weights kept in LDS
 constexpr int kEpiMaxDv = 256;       // output dimensions (one per thread)
 constexpr int kEpiLeanRows = 256;    // rows (blocks) from which the lean form runs
 
-template <int DC, bool LEAN>
+template <int DC, bool LEAN, bool P16>
 __global__ __launch_bounds__(256) void epilogue_rows_kernel(AttendArgs a) {
   constexpr int kEpiRun = LEAN ? 8 : 26;  // partial loads in flight per thread
   constexpr int C4 = DC / 4;       // 4-column chunks of a partial row
@@ -321,6 +323,7 @@ __global__ __launch_bounds__(256) void epilogue_rows_kernel(AttendArgs a) {
   const int tok = row / a.n_h, h = row - tok * a.n_h;
   const int n_part = sched_group_slots(a.sched, b * a.sched.n_rg + row / a.sched.block_rows);
   auto prow_of = [&](int k) { return ((size_t)k * a.B + b) * R + row; };
+  constexpr bool p16 = P16;
   const int c4 = tid % C4, j = tid / C4;
   const bool lane_ok = j < LANES;
 
@@ -339,9 +342,10 @@ __global__ __launch_bounds__(256) void epilogue_rows_kernel(AttendArgs a) {
 #pragma unroll
   for (int u = 0; u < kEpiRun; ++u) {
     const int k = min(j + LANES * u, n_part - 1);
-    x[u] = *reinterpret_cast<const f32x4*>(a.opart + prow_of(k) * DC + 4 * c4);
+    x[u] = load_part4<P16>(a.opart, prow_of(k) * DC + 4 * c4);
   }
   const float m0 = tid < n_part ? ml2.x : -INFINITY, l0 = ml2.y;
+  // normalised fp16 partials: each slot's values also weighted by its sum
 
   // block maximum of the slot maxima (slots past the first 256 by a loop)
   float mx = m0;
@@ -360,7 +364,7 @@ __global__ __launch_bounds__(256) void epilogue_rows_kernel(AttendArgs a) {
       lk = a.ml[prow_of(k) * 2 + 1];
     }
     const float wk = exp2_fast(mk - M);
-    if (k < kEpiWeights) wts[k] = wk;
+    if (k < kEpiWeights) wts[k] = p16 ? wk * lk : wk;
     ls += wk * lk;
   }
 #pragma unroll
@@ -368,7 +372,11 @@ __global__ __launch_bounds__(256) void epilogue_rows_kernel(AttendArgs a) {
   if (lane == 0) red[1][wave] = ls;
   __syncthreads();
   const float inv = 1.0f / (red[1][0] + red[1][1] + red[1][2] + red[1][3]);
-  auto weight = [&](int k) { return k < kEpiWeights ? wts[k] : exp2_fast(a.ml[prow_of(k) * 2] - M); };
+  auto weight = [&](int k) {
+    if (k < kEpiWeights) return wts[k];
+    const float wk = exp2_fast(a.ml[prow_of(k) * 2] - M);
+    return p16 ? wk * a.ml[prow_of(k) * 2 + 1] : wk;
+  };
 
   f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
   if (lane_ok) {
@@ -383,8 +391,7 @@ __global__ __launch_bounds__(256) void epilogue_rows_kernel(AttendArgs a) {
     for (int k0 = j + LANES * kEpiRun; k0 < n_part; k0 += LANES * kEpiRun) {
 #pragma unroll
       for (int u = 0; u < kEpiRun; ++u)
-        x[u] = *reinterpret_cast<const f32x4*>(a.opart + prow_of(min(k0 + LANES * u, n_part - 1)) * DC +
-                                               4 * c4);
+        x[u] = load_part4<P16>(a.opart, prow_of(min(k0 + LANES * u, n_part - 1)) * DC + 4 * c4);
 #pragma unroll
       for (int u = 0; u < kEpiRun; ++u) {
         const int k = k0 + LANES * u;
@@ -542,6 +549,7 @@ hipError_t launch_core_of(const AttendArgs& a, hipStream_t s) {
   c.qrows = a.qcat;
   c.qrows_lo = a.qcat_lo;
   c.ring = a.ring;
+  c.part16 = a.part16;
   c.opart = a.opart;
   c.ml = a.ml;
   c.ring_rows = a.ring_rows;
@@ -570,7 +578,7 @@ hipError_t launch_core_of(const AttendArgs& a, hipStream_t s) {
 // merges the row's partials by log-sum-exp, normalises, and writes the 8
 // values as two bf16 parts (value, remainder) into token rows
 // [B * Lq][n_h * DC] (row tok * n_h + h of sequence b is that token's head h).
-template <int DC>
+template <int DC, bool P16>
 __global__ __launch_bounds__(256) void merge_latent_kernel(AttendArgs a, bf16_t* o_hi, bf16_t* o_lo) {
   constexpr int C8 = DC / 8;
   const int R = a.Lq * a.n_h;
@@ -583,11 +591,12 @@ __global__ __launch_bounds__(256) void merge_latent_kernel(AttendArgs a, bf16_t*
   AttnCore c;
   c.opart = a.opart;
   c.ml = a.ml;
+  c.part16 = a.part16;
   c.R = R;
   c.B = a.B;
   c.sched = a.sched;
   float acc[8];
-  merge_row_partials(c, DC, b, row, 8 * c8, 8, acc);
+  merge_row_partials<P16>(c, DC, b, row, 8 * c8, 8, acc);
   bf16x8 h8, l8;
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
@@ -626,12 +635,21 @@ hipError_t launch_dc(const AttendArgs& a, hipStream_t s) {
   if ((a.sched.key_tile < 64 || a.sched.n_slots > kLaneMergeMaxSlots) &&
       a.d_v <= kEpiMaxDv) {
     const dim3 grid((unsigned)(a.Lq * a.n_h), (unsigned)a.B);
-    if (grid.x * grid.y >= (unsigned)kEpiLeanRows)
-      hipLaunchKernelGGL((epilogue_rows_kernel<DC, true>), grid, dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL((epilogue_rows_kernel<DC, false>), grid, dim3(256), 0, s, a);
+    const bool lean = grid.x * grid.y >= (unsigned)kEpiLeanRows;
+    if (a.part16) {
+      if (lean)
+        hipLaunchKernelGGL((epilogue_rows_kernel<DC, true, true>), grid, dim3(256), 0, s, a);
+      else
+        hipLaunchKernelGGL((epilogue_rows_kernel<DC, false, true>), grid, dim3(256), 0, s, a);
+    } else {
+      if (lean)
+        hipLaunchKernelGGL((epilogue_rows_kernel<DC, true, false>), grid, dim3(256), 0, s, a);
+      else
+        hipLaunchKernelGGL((epilogue_rows_kernel<DC, false, false>), grid, dim3(256), 0, s, a);
+    }
     return hipGetLastError();
   }
+  if (a.part16) return hipErrorInvalidValue;  // fp16 partials only reach the per-row epilogue
   {
     dim3 grid((unsigned)((a.Lq + 31) / 32), (unsigned)a.n_h, (unsigned)a.B);
     hipLaunchKernelGGL(epilogue_bf16_kernel<DC>, grid, dim3(64), 0, s, a);
@@ -679,12 +697,20 @@ hipError_t launch_attend_core_only(const AttendArgs& a, hipStream_t s) {
 hipError_t launch_merge_latent(const AttendArgs& a, void* o_hi, void* o_lo, hipStream_t s) {
   const int64_t n = (int64_t)a.B * a.Lq * a.n_h * (a.d_c / 8);
   const dim3 grid((unsigned)((n + 255) / 256));
+#define MLA_MERGE(DC)                                                                                  \
+  if (a.part16)                                                                                        \
+    hipLaunchKernelGGL((merge_latent_kernel<DC, true>), grid, dim3(256), 0, s, a, (bf16_t*)o_hi,       \
+                       (bf16_t*)o_lo);                                                                 \
+  else                                                                                                 \
+    hipLaunchKernelGGL((merge_latent_kernel<DC, false>), grid, dim3(256), 0, s, a, (bf16_t*)o_hi,      \
+                       (bf16_t*)o_lo);
   switch (a.d_c) {
-    case 64: hipLaunchKernelGGL(merge_latent_kernel<64>, grid, dim3(256), 0, s, a, (bf16_t*)o_hi, (bf16_t*)o_lo); break;
-    case 128: hipLaunchKernelGGL(merge_latent_kernel<128>, grid, dim3(256), 0, s, a, (bf16_t*)o_hi, (bf16_t*)o_lo); break;
-    case 192: hipLaunchKernelGGL(merge_latent_kernel<192>, grid, dim3(256), 0, s, a, (bf16_t*)o_hi, (bf16_t*)o_lo); break;
+    case 64: MLA_MERGE(64) break;
+    case 128: MLA_MERGE(128) break;
+    case 192: MLA_MERGE(192) break;
     default: return hipErrorInvalidValue;
   }
+#undef MLA_MERGE
   return hipGetLastError();
 }
 

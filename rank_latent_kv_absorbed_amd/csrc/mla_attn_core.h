@@ -76,6 +76,7 @@ struct AttnCore {
   const void* ring;      // [B][ring_rows][ring_stride]
   float* opart;          // [n_slots][B][R][DV]  un-normalised value sums
   float* ml;             // [n_slots][B][R][2]   running max (log2 units), sum
+  int part16;            // partials stored normalised (O / l) as fp16 (see load_part4)
   int64_t ring_rows;
   int ring_stride;       // elements per cached token row
   int k_off, v_off;      // offsets of K and V of head 0 inside a cached row
@@ -88,6 +89,20 @@ struct AttnCore {
   Schedule sched;
   int64_t key_slot0;     // ring slot of resident key 0
 };
+
+// Four values of a partial row at element `elem` as fp32.  Partials of the
+// few-row shapes are stored normalised (O / l: a convex combination of cached
+// values, so within the cache type's range) as fp16, half the bytes of the
+// fp32 sums; readers then weight them by l as well.
+template <bool P16>
+__device__ __forceinline__ f32x4 load_part4(const float* opart, size_t elem) {
+  if constexpr (P16) {
+    const f16x4 h = *reinterpret_cast<const f16x4*>((const f16_t*)opart + elem);
+    f32x4 r = {(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+    return r;
+  }
+  return *reinterpret_cast<const f32x4*>(opart + elem);
+}
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -619,8 +634,19 @@ void attn_core_kernel(AttnCore a) {
       if (row[0] < a.R) {
         const size_t prow = ((size_t)si.slot * a.B + b) * a.R + row[0];
         float* op = a.opart + prow * DV;
+        if (a.part16) {
+          const float inv = 1.0f / ltot;
+          f16_t* oh = (f16_t*)a.opart + prow * DV;
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4*>(op + 16 * dt + 4 * g16) = o[0][dt];
+          for (int dt = 0; dt < NDT; ++dt) {
+            f16x4 hv = {(f16_t)(o[0][dt][0] * inv), (f16_t)(o[0][dt][1] * inv), (f16_t)(o[0][dt][2] * inv),
+                        (f16_t)(o[0][dt][3] * inv)};
+            *reinterpret_cast<f16x4*>(oh + 16 * dt + 4 * g16) = hv;
+          }
+        } else {
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4*>(op + 16 * dt + 4 * g16) = o[0][dt];
+        }
         if (g16 == 0) {
           a.ml[prow * 2] = m[0];
           a.ml[prow * 2 + 1] = ltot;
@@ -633,13 +659,20 @@ void attn_core_kernel(AttnCore a) {
         if (row[rb] < a.R) {
           const size_t prow = ((size_t)si.slot * a.B + b) * a.R + row[rb];
           float* op = a.opart + prow * DV;
+          const float inv = 1.0f / ltot;
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
             for (int gg = 0; gg < 4; ++gg) {
-              f32x4 v = {o[rb][dt][4 * gg], o[rb][dt][4 * gg + 1], o[rb][dt][4 * gg + 2],
-                         o[rb][dt][4 * gg + 3]};
-              *reinterpret_cast<f32x4*>(op + dt * 32 + 8 * gg + 4 * hi) = v;
+              if (a.part16) {
+                f16x4 hv = {(f16_t)(o[rb][dt][4 * gg] * inv), (f16_t)(o[rb][dt][4 * gg + 1] * inv),
+                            (f16_t)(o[rb][dt][4 * gg + 2] * inv), (f16_t)(o[rb][dt][4 * gg + 3] * inv)};
+                *reinterpret_cast<f16x4*>((f16_t*)a.opart + prow * DV + dt * 32 + 8 * gg + 4 * hi) = hv;
+              } else {
+                f32x4 v = {o[rb][dt][4 * gg], o[rb][dt][4 * gg + 1], o[rb][dt][4 * gg + 2],
+                           o[rb][dt][4 * gg + 3]};
+                *reinterpret_cast<f32x4*>(op + dt * 32 + 8 * gg + 4 * hi) = v;
+              }
             }
           if (hi == 0) {
             a.ml[prow * 2] = m[rb];
@@ -855,6 +888,7 @@ void attn_core_kernel(AttnCore a) {
 // Log-sum-exp merge of one row's partials into `acc` (n values from column
 // c0, n a multiple of 4): acc = sum_k w_k O_k / sum_k w_k l_k with
 // w_k = 2^(m_k - max_k m_k).
+template <bool P16 = false>
 __device__ __forceinline__ void merge_row_partials(const AttnCore& a, int DV, int b, int row,
                                                    int c0, int n, float* acc) {
   const Schedule& sc = a.sched;
@@ -866,14 +900,15 @@ __device__ __forceinline__ void merge_row_partials(const AttnCore& a, int DV, in
   for (int k = 0; k < n_part; ++k) {
     const size_t prow = ((size_t)k * a.B + b) * a.R + row;
     const float wgt = exp2_fast(a.ml[prow * 2] - M);
-    L += wgt * a.ml[prow * 2 + 1];
-    const float* op = a.opart + prow * DV + c0;
+    const float lk = a.ml[prow * 2 + 1];
+    L += wgt * lk;
+    const float wv = P16 ? wgt * lk : wgt;
     for (int i = 0; i < n; i += 4) {
-      const f32x4 x = *reinterpret_cast<const f32x4*>(op + i);
-      acc[i] += wgt * x[0];
-      acc[i + 1] += wgt * x[1];
-      acc[i + 2] += wgt * x[2];
-      acc[i + 3] += wgt * x[3];
+      const f32x4 x = load_part4<P16>(a.opart, prow * DV + c0 + i);
+      acc[i] += wv * x[0];
+      acc[i + 1] += wv * x[1];
+      acc[i + 2] += wv * x[2];
+      acc[i + 3] += wv * x[3];
     }
   }
   const float inv = 1.0f / L;

@@ -266,6 +266,15 @@ int64_t window_keys(const mla_cache* h) {
 // bits for them on their own.  fp16 rings and fp32 handles do not split.
 bool split_operands(const mla_layer_config& c) { return c.cache_dtype == MLA_BF16; }
 
+// The few-row core shapes (32-key tiles: up to 128 query rows per sequence)
+// split each row's keys into many ranges, and their partial value sums are a
+// large share of the call's memory traffic; with a 2-byte operand ring they
+// are stored normalised as fp16 (half the bytes; values within the cache
+// type's range).  Split-operand (bf16) rings keep fp32 partials.
+bool fp16_partials(const mla_layer_config& c, const mla::Schedule& s) {
+  return !split_operands(c) && c.dtype == MLA_BF16 && s.key_tile == 32 && c.d_v <= 256;
+}
+
 struct LatentLayout {
   mla::Schedule sched;
   size_t qcat_off, qlo_off, opart_off, ml_off, total;
@@ -797,6 +806,7 @@ mla_status mla_attend(mla_cache* h, const void* q, int64_t q_token0, int32_t Lq,
   a.opart = (float*)(ws + L.opart_off);
   a.ml = (float*)(ws + L.ml_off);
   a.sched = L.sched;
+  a.part16 = fp16_partials(c, L.sched);
   return launch_status(mla::launch_attend_bf16(a, s));
 }
 
@@ -909,6 +919,7 @@ mla_status mla_attend_block(mla_cache* h, const void* x, int64_t q_token0, int32
   a.opart = (float*)(ws + L.opart_off);
   a.ml = (float*)(ws + L.ml_off);
   a.sched = L.sched;
+  a.part16 = fp16_partials(c, L.sched);
   hipStream_t s = (hipStream_t)stream;
   // 1. [q_lat | q^R] of every head straight from x with the folded weights
   //    (two parts), rotated at each query's position and scaled

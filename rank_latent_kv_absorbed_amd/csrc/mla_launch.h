@@ -300,6 +300,7 @@ struct AttendArgs {
   void* qcat_lo;          // bf16 cache: the remainders of qcat (same layout); else null
   float* opart;           // workspace [n_split][B][R][d_c]
   float* ml;              // workspace [n_split][B][R][2]  (running max (log2 units), sum)
+  int part16;             // partials stored normalised as fp16 (few-row core shapes)
   int B, Lq, n_h, d_nope, d_rope, d_v, d_c;
   int64_t q_token0;
   int T, grid_w;
