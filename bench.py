@@ -423,6 +423,27 @@ def run_extras(args, result, torch, dev, cfg, caches, weights, x_pre, x_chunk, q
     torch.cuda.empty_cache()
     log("bf16 ring")
 
+    # ---- the same step with a one-byte E4M3 ring (half the cache bytes),
+    # on the handle's automatic path (the rebuild widens the rows)
+    ecfg = cfg.with_(cache_dtype="e4m3")
+    ecaches = make_caches(ecfg, "auto")
+    ews = torch.empty(max(ecaches[0].workspace_bytes(Lq), 1), dtype=torch.uint8, device=dev)
+    st = Stepper(ecaches, ews)
+    for _ in range(5):
+        st.step()
+    e_step, e_core = st.timed(min(args.steps, 20))
+    e_path = ecaches[0].attend_path(Lq)
+    e_flop = core_flop(ecfg, e_path, B, Lq, Lk)
+    result["e4m3_ring"] = {
+        "path": e_path, "ms_per_step": round(e_step, 4), "value": round(B * Lq / (e_step / 1e3), 1),
+        "attend_core_ms": round(e_core, 4),
+        "core_frac": round(e_flop / (e_core / 1e3) / (PEAK_BF16_TFLOPS * 1e12), 4),
+        "cache_bytes_per_layer": ecaches[0].nbytes,
+        "note": "E4M3 storage (1 byte per scalar), widened to fp16 for the arithmetic"}
+    del ecaches, ews, st
+    torch.cuda.empty_cache()
+    log("e4m3 ring")
+
     # ---- several attends per written chunk (denoising steps): with reuse on,
     # the expand path rebuilds the window once per chunk
     if path == "expand":

@@ -57,8 +57,10 @@
  *     nearest even; magnitudes that round past 448 are stored as +-448
  *     (saturation, never NaN or infinity).  The attention widens the stored
  *     values to fp16 (exactly) and computes as for an fp16 ring: the result
- *     is the attention over the stored E4M3 values.  Absorbed path only (no
- *     expand-then-attend); no dense (mha_*) caches.
+ *     is the attention over the stored E4M3 values.  Both attention paths:
+ *     the expand-then-attend path widens the rows as it rebuilds the per-head
+ *     keys and values, which it rounds to fp16 as for an fp16 ring.  No dense
+ *     (mha_*) caches.
  *
  * Ownership: the caller owns every device buffer (ring storage, weights,
  * activations, outputs, workspace).  The library owns only the small host
@@ -288,12 +290,12 @@ mla_status mla_attend_block(mla_cache* cache, const void* x, int64_t q_token0, i
  *   2 (d_nope + d_rope) + 2 d_v (d_c = 192 for the Wan head shape; not 128 or
  *   64, where the latent form is as fast or faster).  Both paths compute the
  * same function; they differ in rounding (the expanded keys and values are
- * rounded to the cache's element type, fp16: only fp16 rings expand). */
+ * rounded to fp16: fp16 and E4M3 rings expand, bf16 rings do not). */
 typedef enum { MLA_PATH_AUTO = 0, MLA_PATH_ABSORBED = 1, MLA_PATH_EXPAND = 2 } mla_attend_path_kind;
 
 /* Selects the path of later mla_attend calls on this latent handle.
  * MLA_ERR_UNSUPPORTED for MLA_PATH_EXPAND unless the handle has bf16 inputs,
- * an fp16 ring, d_nope = 96, d_rope = 32, d_v = 128 and d_c in {64, 128, 192}
+ * an fp16 or E4M3 ring, d_nope = 96, d_rope = 32, d_v = 128 and d_c in {64, 128, 192}
  * (a bf16 ring is refused: its expanded keys and values, rounded to bf16,
  * would each move the output by about 1e-3 of its size); MLA_ERR_WRONG_KIND
  * on a dense handle. */

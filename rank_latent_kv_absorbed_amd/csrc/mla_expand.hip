@@ -9,12 +9,13 @@
 // One kernel, then the per-head attention path of the dense cache:
 //  expand_kv_kernel: for every resident key j and head h,
 //       K[j][h] = [ W^K_up,h c_j | k^R_j ],   V[j][h] = W^V_up,h c_j,
-//     written as [B][Lk][2][n_h][d_h] in the ring's element type - the layout
-//     of the dense cache, so the same attention core reads it.  A workgroup
-//     owns one head and a range of keys of one sequence: the head's whole
-//     [d_nope + d_v][d_c] matrix is loaded into LDS once (converted from bf16
-//     to fp16 on the way; only fp16 rings expand), then each wave
-//     independently walks 32-key blocks:
+//     written as [B][Lk][2][n_h][d_h] in fp16 - the layout of the dense
+//     cache, so the same attention core reads it.  A workgroup owns one head
+//     and a range of keys of one sequence: the head's whole [d_nope + d_v][d_c]
+//     matrix is loaded into LDS once (converted from bf16 to fp16 on the way;
+//     fp16 and one-byte E4M3 rings expand, the latter widening each latent row
+//     to fp16 exactly as it is loaded), then each wave independently walks
+//     32-key blocks:
 //     latent rows into registers (MFMA A operand), D[key][col] =
 //     c[key][:] . W[col][:] on 32x32x16 MFMA per 32-row weight tile (B
 //     operand from LDS), the head's key and value blocks staged in the wave's
@@ -34,9 +35,9 @@ constexpr int kExpandKTiles = kExpandNope / 32, kExpandTiles = kExpandKTiles + k
 
 // DC: latent width.  Workgroup (x, h, b): head h of sequence b, keys
 // [x * keys_per_block, (x + 1) * keys_per_block).
-template <typename E, int DC>
+template <typename E, int DC, bool F8 = false>
 __global__ __launch_bounds__(kExpandWaves * 64) void expand_kv_kernel(ExpandArgs a, int keys_per_block) {
-  static_assert(__is_same(E, f16_t), "only fp16 rings expand");
+  static_assert(__is_same(E, f16_t), "the rebuilt keys and values are fp16");
   typedef typename Elem<E>::v8 V8;
   constexpr int NKS = DC / 16;         // MFMA depth steps
   constexpr int CPR = DC / 8;          // 16-byte chunks per weight row
@@ -163,12 +164,28 @@ __global__ __launch_bounds__(kExpandWaves * 64) void expand_kv_kernel(ExpandArgs
   // of one sequence fit 32 bits (checked when the cache is created).
   constexpr int NR = kExpandRope / 16;  // k^R pieces per lane
   constexpr int RW = DC + kExpandRope;  // elements per cached row
-  const char* const ring_b = (const char*)a.ring + (size_t)b * a.ring_rows * RW * sizeof(E);
+  constexpr int EB = F8 ? 1 : (int)sizeof(E);  // bytes per cached scalar
+  const char* const ring_b = (const char*)a.ring + (size_t)b * a.ring_rows * RW * EB;
   const int rows = (int)a.ring_rows;
   auto load_row = [&](int k0, V8 (&c)[NKS], V8 (&r)[NR]) MLA_INLINE {
     const int key = k0 + lo < kend ? k0 + lo : k0;
     int slot = (int)a.key_slot0 + key;
     slot = slot >= rows ? slot - rows : slot;
+    if constexpr (F8) {
+      // one-byte row: 8 codes per operand piece, widened to fp16
+      const char* p8 = ring_b + ((uint32_t)slot * (uint32_t)RW + 8 * hi);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const uint2 raw = *reinterpret_cast<const uint2*>(p8 + 16 * ks);
+        c[ks] = e4m3x8_to_f16(raw.x, raw.y);
+      }
+#pragma unroll
+      for (int j = 0; j < NR; ++j) {
+        const uint2 raw = *reinterpret_cast<const uint2*>(p8 + DC + 16 * j);
+        r[j] = e4m3x8_to_f16(raw.x, raw.y);
+      }
+      return;
+    }
     const char* p = ring_b + ((uint32_t)slot * (uint32_t)(RW * sizeof(E)) + 16 * hi);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) c[ks] = *reinterpret_cast<const V8*>(p + 32 * ks);
@@ -244,21 +261,21 @@ int expand_splits(int n_h, int B, int Lk) {
   return best;
 }
 
-template <typename E, int DC>
+template <typename E, int DC, bool F8>
 hipError_t launch_expand_dc(const ExpandArgs& a, hipStream_t s) {
   const int splits = expand_splits(a.n_h, a.B, a.Lk);
   const int kpb = ((a.Lk + splits - 1) / splits + 31) / 32 * 32;
   dim3 grid((unsigned)((a.Lk + kpb - 1) / kpb), (unsigned)a.n_h, (unsigned)a.B);
-  hipLaunchKernelGGL((expand_kv_kernel<E, DC>), grid, dim3(kExpandWaves * 64), 0, s, a, kpb);
+  hipLaunchKernelGGL((expand_kv_kernel<E, DC, F8>), grid, dim3(kExpandWaves * 64), 0, s, a, kpb);
   return hipGetLastError();
 }
 
-template <typename E>
+template <typename E, bool F8>
 hipError_t launch_expand_typed(const ExpandArgs& a, hipStream_t s) {
   switch (a.d_c) {
-    case 64: return launch_expand_dc<E, 64>(a, s);
-    case 128: return launch_expand_dc<E, 128>(a, s);
-    case 192: return launch_expand_dc<E, 192>(a, s);
+    case 64: return launch_expand_dc<E, 64, F8>(a, s);
+    case 128: return launch_expand_dc<E, 128, F8>(a, s);
+    case 192: return launch_expand_dc<E, 192, F8>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -270,9 +287,10 @@ bool expand_supported(int d_c, int d_rope, int d_nope, int d_v) {
          d_v == kExpandDv;
 }
 
-// Only fp16 rings expand (the host refuses the expansion for a bf16 ring).
+// fp16 and E4M3 rings expand (the host refuses the expansion for a bf16 ring).
 hipError_t launch_expand_kv(const ExpandArgs& a, hipStream_t s) {
-  return a.cache_type == 2 ? launch_expand_typed<f16_t>(a, s) : hipErrorInvalidValue;
+  if (a.cache_type == 3) return launch_expand_typed<f16_t, true>(a, s);
+  return a.cache_type == 2 ? launch_expand_typed<f16_t, false>(a, s) : hipErrorInvalidValue;
 }
 
 }  // namespace mla

@@ -375,13 +375,14 @@ constexpr double kExpandFlopRatio = 1.5;
 // expanded full window (every key, every head) keeps one sequence's offsets
 // below 2^31 elements, like a dense cache.  The expanded window is sized for
 // the full window so the workspace size does not change as frames arrive.
-// A bf16 ring has no expansion: the rebuilt per-head keys and values would be
+// fp16 and E4M3 rings expand into an fp16 window (an E4M3 value widens to
+// fp16 exactly).  A bf16 ring has no expansion: the rebuilt per-head keys and values would be
 // rounded to bf16, and those roundings (like the query's and the
 // probabilities') each move the attention output by about 1e-3 of its size
 // on Gaussian inputs, independent of the window length.
 bool expand_possible(const mla_cache* h) {
   const mla_layer_config& c = h->cfg;
-  return c.dtype == MLA_BF16 && c.cache_dtype == MLA_F16 &&
+  return c.dtype == MLA_BF16 && (c.cache_dtype == MLA_F16 || c.cache_dtype == MLA_E4M3) &&
          mla::expand_supported(c.d_c, c.d_rope, c.d_nope, c.d_v) &&
          (int64_t)c.window_frames * tokens_per_frame(c) * 2 * c.n_heads * (c.d_nope + c.d_rope) <
              (1LL << 31);
@@ -763,7 +764,7 @@ mla_status mla_attend(mla_cache* h, const void* q, int64_t q_token0, int32_t Lq,
     m.ring_rows = a.Lk;
     m.key_slot0 = 0;
     m.Lk = a.Lk;
-    m.cache_type = c.cache_dtype;
+    m.cache_type = MLA_F16;  // the rebuilt window is fp16 for either ring
     m.qscale = a.qscale;
     m.ev_start = h->prof_start;
     m.ev_stop = h->prof_stop;

@@ -341,12 +341,12 @@ struct ExpandArgs {
   const void* ring;       // [B][ring_rows][d_c + d_rope] cache type
   const void* w_uk;       // [n_h][d_nope][d_c] bf16
   const void* w_uv;       // [n_h][d_v][d_c] bf16
-  void* kv;               // workspace [B][Lk][2][n_h][d_nope + d_rope] cache type
+  void* kv;               // workspace [B][Lk][2][n_h][d_nope + d_rope] fp16
   int B, n_h, d_nope, d_rope, d_c, d_v;
   int64_t ring_rows;
   int64_t key_slot0;      // ring slot of resident key 0
   int Lk;
-  int cache_type;         // 1 = bf16, 2 = fp16
+  int cache_type;         // ring: 2 = fp16, 3 = E4M3 (either way the rebuilt window is fp16)
 };
 
 hipError_t launch_cache_write_bf16(const CacheWriteArgs& a, hipStream_t s);

@@ -94,6 +94,8 @@ void fake_type_info(int* o) {
   o[0] = g_write.out_type;
   o[1] = g_attend.cache_type;
   o[2] = mla::g_proj[0].out_type;
+  o[3] = g_expand.cache_type;
+  o[4] = g_mha.cache_type;
 }
 float fake_write_eps() { return g_write.eps; }
 int fake_write_norm_cols() { return g_write.norm_cols; }

@@ -784,7 +784,8 @@ def test_cache_write_norm_arguments(sim):
 
 def test_e4m3_ring_rules(sim):
     """A one-byte (E4M3) ring: latent caches with bf16 inputs only, one byte
-    per stored scalar; writes and attends carry the type; no expansion; the
+    per stored scalar; writes and attends carry the type; the expansion reads
+    the one-byte rows and hands an fp16 window to the per-head attention; the
     core's LDS holds the raw tiles plus one fp16 decode tile, which sets the
     blocks per compute unit; the attention block's query projection writes
     fp16 operands."""
@@ -799,13 +800,19 @@ def test_e4m3_ring_rules(sim):
     st, h = _create(sim, c)
     assert st == 0
     assert sim.mla_cache_write(h, P(FAKE_PTR), P(FAKE_PTR), 0, 3, None) == 0
-    t = (ctypes.c_int * 3)()
+    t = (ctypes.c_int * 5)()
     sim.fake_type_info(t)
     assert t[0] == E4M3
-    assert sim.mla_cache_set_attend_path(h, 2) == 8
-    assert sim.mla_attend_path(h, 4680, 0) == 1
     assert sim.mla_cache_set_state(h, 3, 23) == 0
     ws = 1 << 40
+    assert sim.mla_attend_path(h, 4680, 0) == 2 and sim.mla_attend_path(h, 8, 0) == 1
+    need = sim.mla_attend_workspace_bytes(h, 4680, 0)
+    assert sim.mla_attend(h, P(FAKE_PTR), 21 * 1560 - 4680, 4680, P(FAKE_PTR), P(FAKE_PTR),
+                          P(FAKE_PTR), 0, P(ws), need, None) == 0
+    sim.fake_type_info(t)
+    assert t[3] == E4M3 and t[4] == 2        # one-byte rows in, fp16 window to the per-head core
+    assert sim.mla_cache_set_attend_path(h, 2) == 0
+    assert sim.mla_cache_set_attend_path(h, 1) == 0
     for Lq in (1, 4, 8, 11, 100, 4680):
         R = Lq * 12
         need = sim.mla_attend_workspace_bytes(h, Lq, 0)

@@ -15,7 +15,9 @@ fp16 query and probability operands, as for an fp16 ring.
   * attention: every element at mid sizes through ring wraps (all core shapes,
     key splits, d_c in {64, 128, 192}); sampled rows of the Wan layer, of the
     21-frame window at batch 1, 2, 4, 8 and 11, of small queries over the full
-    window, and of an 80-chunk rollout for each latent width.
+    window, and of an 80-chunk rollout for each latent width; the
+    expand-then-attend path (rows widened as the per-head keys and values are
+    rebuilt) every element at mid sizes and sampled at the Wan shapes.
 
 Bars as for the fp16 ring: max|err| <= 1e-2 max|ref|, sum|err| <= 2e-3 sum|ref|.
 """
@@ -26,7 +28,7 @@ import torch
 
 from oracle import mla as O
 from synthetic import chunk_x, config
-from rank_latent_kv_absorbed_amd.mla import ERR_INVALID_ARG, ERR_UNSUPPORTED, MlaError
+from rank_latent_kv_absorbed_amd.mla import ERR_INVALID_ARG, MlaError
 from tests.parity_util import E4M3_NAN, LatentRun, assert_parity, dev, sample_rows
 
 pytestmark = pytest.mark.gpu
@@ -180,6 +182,17 @@ def test_every_code_widens_exactly_in_a_tiny_ring():
 # reach every core shape: 3 (16-row waves), 8 and 20 (one 32-row wave), 33
 # (four-wave blocks), 130 and 300 (the eight-wave chunk blocks).
 @pytest.mark.parametrize("d_c", [64, 128, 192])
+@pytest.mark.parametrize("Lq", [3, 33, 130, 300])
+def test_expand_every_element_ragged_with_wrap(d_c, Lq):
+    cfg = mid_cfg(d_nope=96, d_v=128, d_c=d_c)
+    run = LatentRun(cfg, path="expand")
+    wrapped_window(run)
+    q = run.query(Lq)
+    got, ref, _ = run.attend(q, 8 * cfg.T - Lq)
+    assert_parity(got, ref, "bf16", f"e4m3 expand d_c={d_c} Lq={Lq}")
+
+
+@pytest.mark.parametrize("d_c", [64, 128, 192])
 @pytest.mark.parametrize("Lq,key_splits", [(3, 0), (8, 0), (20, 2), (33, 3), (130, 0), (300, 0)])
 def test_attend_every_element_ragged_with_wrap(d_c, Lq, key_splits):
     cfg = mid_cfg(d_nope=96, d_v=128, d_c=d_c)
@@ -206,16 +219,17 @@ def test_attend_tiny_bf16_inputs():
 # Wan shapes, sampled rows
 # --------------------------------------------------------------------------
 
-def test_wan_layer_sampled_rows():
+@pytest.mark.parametrize("path", ["absorbed", "auto"])
+def test_wan_layer_sampled_rows(path):
     cfg = config("wan_layer").with_(cache_dtype="e4m3")
-    run = LatentRun(cfg)
+    run = LatentRun(cfg, path=path)
     run.write(0, cfg.prefill_frames)
     run.write(cfg.chunk_frame0, cfg.chunk_frames)
-    assert run.gpu.attend_path(cfg.Lq) == "absorbed"
+    assert run.gpu.attend_path(cfg.Lq) == ("absorbed" if path == "absorbed" else "expand")
     q = run.query(cfg.Lq)
     rows = sample_rows(cfg.Lq, 64)
     got, ref, _ = run.attend(q, cfg.chunk_frame0 * cfg.T, rows=rows)
-    assert_parity(got, ref, "bf16", "e4m3 wan layer sampled")
+    assert_parity(got, ref, "bf16", f"e4m3 wan layer sampled {path}")
 
 
 def _full_window(run, cfg):
@@ -226,28 +240,30 @@ def _full_window(run, cfg):
     assert run.gpu.info()["n_resident_frames"] == 21
 
 
-@pytest.mark.parametrize("batch", [1, 2, 4, 8, 11])
-def test_full_window_sampled_rows(batch):
+@pytest.mark.parametrize("batch,path", [(1, "auto"), (2, "auto"), (4, "auto"), (8, "auto"), (11, "auto"),
+                                        (1, "absorbed"), (4, "absorbed")])
+def test_full_window_sampled_rows(batch, path):
     cfg = config("wan_window").with_(batch=batch, cache_dtype="e4m3")
-    run = LatentRun(cfg)
+    run = LatentRun(cfg, path=path)
     _full_window(run, cfg)
     q = run.query(cfg.Lq)
     rows = sample_rows(cfg.Lq, 32 if batch <= 2 else 8)
     got, ref, _ = run.attend(q, cfg.chunk_frame0 * cfg.T, rows=rows)
     for b in (0, batch - 1):
-        assert_parity(got[b], ref[b], "bf16", f"e4m3 B={batch} sequence {b}")
-    assert_parity(got, ref, "bf16", f"e4m3 21-frame window B={batch}")
+        assert_parity(got[b], ref[b], "bf16", f"e4m3 B={batch} sequence {b} {path}")
+    assert_parity(got, ref, "bf16", f"e4m3 21-frame window B={batch} {run.gpu.attend_path(cfg.Lq)}")
 
 
-@pytest.mark.parametrize("d_c", [64, 128, 192])
-@pytest.mark.parametrize("Lq", [1, 8])
-def test_small_queries_full_window_batch11(d_c, Lq):
+@pytest.mark.parametrize("d_c,Lq,path", [(64, 1, "auto"), (128, 1, "auto"), (192, 1, "auto"),
+                                         (64, 8, "auto"), (128, 8, "auto"), (192, 8, "auto"),
+                                         (192, 1, "expand")])
+def test_small_queries_full_window_batch11(d_c, Lq, path):
     cfg = config("wan_window").with_(batch=11, d_c=d_c, cache_dtype="e4m3")
-    run = LatentRun(cfg)
+    run = LatentRun(cfg, path=path)
     _full_window(run, cfg)
     q = run.query(Lq)
     got, ref, _ = run.attend(q, (cfg.chunk_frame0 + cfg.chunk_frames) * cfg.T - Lq)
-    assert_parity(got, ref, "bf16", f"e4m3 B=11 d_c={d_c} small query Lq={Lq}")
+    assert_parity(got, ref, "bf16", f"e4m3 B=11 d_c={d_c} small query Lq={Lq} {path}")
 
 
 @pytest.mark.parametrize("d_c", [64, 128, 192])
@@ -269,14 +285,13 @@ def test_rollout_80_chunks_gaussian_sampled_rows(d_c):
 # what the one-byte ring refuses
 # --------------------------------------------------------------------------
 
-def test_no_expand_path_and_no_dense_cache():
+def test_path_choice_and_no_dense_cache():
     from rank_latent_kv_absorbed_amd import DenseCache
     cfg = config("wan_layer").with_(cache_dtype="e4m3")
     run = LatentRun(cfg)
-    with pytest.raises(MlaError) as e:
-        run.gpu.set_attend_path("expand")
-    assert e.value.status == ERR_UNSUPPORTED
-    assert run.gpu.attend_path(4680) == "absorbed"
+    assert run.gpu.attend_path(4680) == "expand" and run.gpu.attend_path(8) == "absorbed"
+    run.gpu.set_attend_path("expand")
+    assert run.gpu.attend_path(8) == "expand"
     with pytest.raises(MlaError) as e:
         DenseCache(cfg)
     assert e.value.status == ERR_INVALID_ARG

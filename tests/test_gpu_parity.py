@@ -270,7 +270,7 @@ def test_attend_small_queries_latent_widths(Lq, d_c):
 
 
 @pytest.mark.parametrize("cache_dtype,path", [("f16", "absorbed"), ("f16", "expand"), ("bf16", "absorbed"),
-                                              ("e4m3", "absorbed")])
+                                              ("e4m3", "absorbed"), ("e4m3", "expand")])
 def test_degenerate_softmax_closed_forms(cache_dtype, path):
     """Two windows whose attention has a closed form, 300 keys through a wrap:
     zero queries weight every key equally, so each head's output is W^V_up,h
@@ -745,7 +745,7 @@ def _climbing_window(cfg, step_log2, seed=0):
 
 
 @pytest.mark.parametrize("cache_dtype,path", [("f16", "absorbed"), ("f16", "expand"), ("bf16", "absorbed"),
-                                              ("e4m3", "absorbed")])
+                                              ("e4m3", "absorbed"), ("e4m3", "expand")])
 def test_sharp_attention_running_max_climbs(cache_dtype, path):
     """Every frame's keys score about 9 log2 units above the previous frame's,
     so each row's running maximum jumps by more than the lazy-rescale
