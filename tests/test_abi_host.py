@@ -66,6 +66,12 @@ def sim(tmp_path_factory):
            "-I", "/opt/rocm/include", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
            os.path.join(CSRC, "mla_host.cpp"), os.path.join(ROOT, "tests", "hostsim", "fake_launch.cpp"),
            "-o", out]
+    # MLA_HOSTSIM_SANITIZE=1 builds the host library with AddressSanitizer and
+    # UBSan (run with the sanitizer runtimes in LD_PRELOAD, e.g.
+    # LD_PRELOAD=$(gcc -print-file-name=libasan.so):$(gcc -print-file-name=libubsan.so)
+    # ASAN_OPTIONS=detect_leaks=0 UBSAN_OPTIONS=halt_on_error=1).
+    if os.environ.get("MLA_HOSTSIM_SANITIZE"):
+        cmd[1:1] = ["-g", "-fsanitize=address,undefined", "-fno-omit-frame-pointer"]
     subprocess.run(cmd, check=True, capture_output=True)
     L = ctypes.CDLL(out)
     from rank_latent_kv_absorbed_amd.mla import SIGNATURES
