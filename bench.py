@@ -13,7 +13,7 @@ layer = batch * 4680 / step time, plus MFMA utilisation.
 
 Also reported on the same JSON line: the main attention kernel alone (HIP
 events recorded by the library on its stream) against the MFMA roofline; the
-other path's step time; the same step with a bf16 ring (split operands); the
+other path's step time; the same step with a bf16 ring (both paths); the
 dense per-head MHA comparison (same shape, and at the largest batch whose
 30-layer dense cache fits the GPU, with the measured batch capacity of both
 caches); cache-bound small-query cases against HBM bandwidth; batch scaling;
@@ -401,25 +401,39 @@ def run_extras(args, result, torch, dev, cfg, caches, weights, x_pre, x_chunk, q
         del ws2, st
     log("other path")
 
-    # ---- the same step with a bf16 ring: the attention core runs on split
-    # operands (query and probabilities as two bf16 parts, twice the products),
-    # absorbed path (a bf16 ring has no expansion)
+    # ---- the same step with a bf16 ring, on its automatic path (the rebuild
+    # multiplies the bf16 rows on bf16 matrix units into fp16 keys and values)
+    # and on the absorbed path (split operands: query and probabilities as two
+    # bf16 parts, twice the products)
     bcfg = cfg.with_(cache_dtype="bf16")
-    bcaches = make_caches(bcfg, "auto")
-    bws = torch.empty(max(bcaches[0].workspace_bytes(Lq), 1), dtype=torch.uint8, device=dev)
-    st = Stepper(bcaches, bws)
-    for _ in range(5):
-        st.step()
-    b_step, b_core = st.timed(min(args.steps, 20))
-    b_flop = core_flop(bcfg, "absorbed", B, Lq, Lk)
-    result["bf16_ring"] = {
-        "path": bcaches[0].attend_path(Lq), "ms_per_step": round(b_step, 4),
-        "value": round(B * Lq / (b_step / 1e3), 1), "attend_core_ms": round(b_core, 4),
-        "core_frac_algorithmic": round(b_flop / (b_core / 1e3) / (PEAK_BF16_TFLOPS * 1e12), 4),
-        "core_frac_executed": round(2 * b_flop / (b_core / 1e3) / (PEAK_BF16_TFLOPS * 1e12), 4),
-        "note": "bf16 MFMA on split operands: every score and value product is issued twice "
-                "(leading part and remainder), so executed matrix work is twice the algorithmic"}
-    del bcaches, bws, st
+    bcaches = make_caches(bcfg, "absorbed")
+    b_need = bcaches[0].workspace_bytes(Lq)
+    bcaches[0].set_attend_path("auto")
+    bws = torch.empty(max(b_need, bcaches[0].workspace_bytes(Lq), 1), dtype=torch.uint8, device=dev)
+    bres = {}
+    for bpath in ("auto", "absorbed"):
+        for c in bcaches:
+            c.set_attend_path(bpath)
+        st = Stepper(bcaches, bws)
+        for _ in range(5):
+            st.step()
+        b_step, b_core = st.timed(min(args.steps, 20))
+        taken = bcaches[0].attend_path(Lq)
+        b_flop = core_flop(bcfg, taken, B, Lq, Lk)
+        r = {"path": taken, "ms_per_step": round(b_step, 4), "value": round(B * Lq / (b_step / 1e3), 1),
+             "attend_core_ms": round(b_core, 4),
+             "core_frac_algorithmic": round(b_flop / (b_core / 1e3) / (PEAK_BF16_TFLOPS * 1e12), 4)}
+        if taken == "absorbed":
+            r["core_frac_executed"] = round(2 * b_flop / (b_core / 1e3) / (PEAK_BF16_TFLOPS * 1e12), 4)
+            r["note"] = ("bf16 MFMA on split operands: every score and value product is issued twice "
+                         "(leading part and remainder), so executed matrix work is twice the algorithmic")
+        else:
+            r["note"] = "rebuild on bf16 MFMA into fp16 keys and values, then the fp16 per-head core"
+        bres[bpath] = r
+        del st
+    result["bf16_ring"] = dict(bres["auto"], absorbed=bres["absorbed"]) if bres["auto"]["path"] != "absorbed" \
+        else bres["absorbed"]
+    del bcaches, bws
     torch.cuda.empty_cache()
     log("bf16 ring")
 

@@ -288,17 +288,24 @@ mla_status mla_attend_block(mla_cache* cache, const void* x, int64_t q_token0, i
  *   supports it, key_splits is 0 and the latent products per (query, key,
  *   head), 2 (d_c + d_rope) + 2 d_c, are at least 1.5 times the per-head ones,
  *   2 (d_nope + d_rope) + 2 d_v (d_c = 192 for the Wan head shape; not 128 or
- *   64, where the latent form is as fast or faster).  Both paths compute the
- * same function; they differ in rounding (the expanded keys and values are
- * rounded to fp16: fp16 and E4M3 rings expand, bf16 rings do not). */
+ *   64, where the latent form is as fast or faster).  A bf16 ring, whose
+ *   absorbed core issues every product twice, expands sooner: from 128
+ *   queries when twice the latent products are at least 3 times the per-head
+ *   ones (d_c = 192), from 256 when at least 2 times (d_c = 128), else from
+ *   384 (d_c = 64).  Both paths compute the
+ * same function; they differ in rounding.  Every ring type expands into
+ * fp16 keys and values: a bf16 ring's rebuild multiplies its stored values on
+ * bf16 matrix units (exact products, fp32 sums) and rounds the results to
+ * fp16, so the expanded attention is as accurate as an fp16 ring's (the
+ * split operands of the bf16 absorbed core are not needed) and has fp16's
+ * range: a rebuilt key or value beyond 65504 in magnitude becomes
+ * +-infinity and the sequence's output NaN. */
 typedef enum { MLA_PATH_AUTO = 0, MLA_PATH_ABSORBED = 1, MLA_PATH_EXPAND = 2 } mla_attend_path_kind;
 
 /* Selects the path of later mla_attend calls on this latent handle.
- * MLA_ERR_UNSUPPORTED for MLA_PATH_EXPAND unless the handle has bf16 inputs,
- * an fp16 or E4M3 ring, d_nope = 96, d_rope = 32, d_v = 128 and d_c in {64, 128, 192}
- * (a bf16 ring is refused: its expanded keys and values, rounded to bf16,
- * would each move the output by about 1e-3 of its size); MLA_ERR_WRONG_KIND
- * on a dense handle. */
+ * MLA_ERR_UNSUPPORTED for MLA_PATH_EXPAND unless the handle has bf16 inputs
+ * (any two-byte or E4M3 ring), d_nope = 96, d_rope = 32, d_v = 128 and d_c in
+ * {64, 128, 192}; MLA_ERR_WRONG_KIND on a dense handle. */
 mla_status mla_cache_set_attend_path(mla_cache* cache, int32_t path);
 
 /* Reuse of the expanded window across attends (enable = 1; 0 switches it off;

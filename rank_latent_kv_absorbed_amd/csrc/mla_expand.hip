@@ -12,10 +12,12 @@
 //     written as [B][Lk][2][n_h][d_h] in fp16 - the layout of the dense
 //     cache, so the same attention core reads it.  A workgroup owns one head
 //     and a range of keys of one sequence: the head's whole [d_nope + d_v][d_c]
-//     matrix is loaded into LDS once (converted from bf16 to fp16 on the way;
-//     fp16 and one-byte E4M3 rings expand, the latter widening each latent row
-//     to fp16 exactly as it is loaded), then each wave independently walks
-//     32-key blocks:
+//     matrix is loaded into LDS once (converted from bf16 to fp16 on the way
+//     for fp16 and one-byte E4M3 rings, the latter widening each latent row to
+//     fp16 exactly as it is loaded; kept in bf16 for a bf16 ring, whose
+//     products then run on bf16 MFMA - exact products of the stored values -
+//     into the same fp16 window), then each wave independently walks 32-key
+//     blocks:
 //     latent rows into registers (MFMA A operand), D[key][col] =
 //     c[key][:] . W[col][:] on 32x32x16 MFMA per 32-row weight tile (B
 //     operand from LDS), the head's key and value blocks staged in the wave's
@@ -33,12 +35,26 @@ constexpr int kExpandWaves = 8;       // waves per workgroup (two per SIMD)
 constexpr int kExpandNope = 96, kExpandRope = 32, kExpandDv = 128;
 constexpr int kExpandKTiles = kExpandNope / 32, kExpandTiles = kExpandKTiles + kExpandDv / 32;
 
+template <bool B, typename T, typename F>
+struct Pick {
+  typedef T type;
+};
+template <typename T, typename F>
+struct Pick<false, T, F> {
+  typedef F type;
+};
+
 // DC: latent width.  Workgroup (x, h, b): head h of sequence b, keys
 // [x * keys_per_block, (x + 1) * keys_per_block).
-template <typename E, int DC, bool F8 = false>
+// E: the rebuilt window's type (fp16).  F8: one-byte E4M3 ring.  BF: bf16
+// ring (weights and latent rows stay bf16 as MFMA operands).
+template <typename E, int DC, bool F8 = false, bool BF = false>
 __global__ __launch_bounds__(kExpandWaves * 64) void expand_kv_kernel(ExpandArgs a, int keys_per_block) {
   static_assert(__is_same(E, f16_t), "the rebuilt keys and values are fp16");
+  static_assert(!(F8 && BF), "one ring type");
   typedef typename Elem<E>::v8 V8;
+  typedef typename Pick<BF, bf16_t, E>::type OP;  // operand type of the products
+  typedef typename Elem<OP>::v8 OV8;
   constexpr int NKS = DC / 16;         // MFMA depth steps
   constexpr int CPR = DC / 8;          // 16-byte chunks per weight row
   constexpr int TILE = 32 * DC;        // elements per weight tile (32 rows)
@@ -47,7 +63,7 @@ __global__ __launch_bounds__(kExpandWaves * 64) void expand_kv_kernel(ExpandArgs
   static_assert(DC % 64 == 0 && (TILE * 2) % 1024 == 0, "whole 1-KiB spans per tile");
   static_assert(CPR % 8 == 0, "the chunk permutation stays inside groups of 8");
   static_assert(kExpandNope + kExpandRope == DH && kExpandDv == DH, "128-wide heads");
-  __shared__ __attribute__((aligned(1024))) E wts[kExpandTiles * TILE];
+  __shared__ __attribute__((aligned(1024))) OP wts[kExpandTiles * TILE];
   __shared__ __attribute__((aligned(16))) E stg[kExpandWaves][32 * DH];
 
   const int tid = threadIdx.x;
@@ -65,8 +81,9 @@ __global__ __launch_bounds__(kExpandWaves * 64) void expand_kv_kernel(ExpandArgs
   // distinct banks.  Lane l of span sp fills LDS chunk c = 64 sp + l: row
   // c / CPR, position c % CPR of the rows of all tiles.
   // The rows come straight from W^K_up,h and W^V_up,h (bf16), converted to
-  // fp16 on the way (exact for magnitudes in [6.1e-5, 65504]; smaller weights
-  // land in fp16's subnormal range with an absolute quantum of 2^-24).
+  // fp16 on the way unless the products run in bf16 (exact for magnitudes in
+  // [6.1e-5, 65504]; smaller weights land in fp16's subnormal range with an
+  // absolute quantum of 2^-24).
   {
     const bf16_t* src_k = (const bf16_t*)a.w_uk + (size_t)h * kExpandNope * DC;
     const bf16_t* src_v = (const bf16_t*)a.w_uv + (size_t)h * kExpandDv * DC;
@@ -91,10 +108,10 @@ __global__ __launch_bounds__(kExpandWaves * 64) void expand_kv_kernel(ExpandArgs
       for (int j = 0; j < SPW; ++j) {
         const int sp = w + j * kExpandWaves;
         if (sp < WSPANS) {
-          V8 o;
+          OV8 o;
 #pragma unroll
-          for (int t = 0; t < 8; ++t) o[t] = Elem<E>::from((float)v[j][t]);
-          *reinterpret_cast<V8*>(wts + (size_t)(sp * 64 + l) * 8) = o;
+          for (int t = 0; t < 8; ++t) o[t] = Elem<OP>::from((float)v[j][t]);
+          *reinterpret_cast<OV8*>(wts + (size_t)(sp * 64 + l) * 8) = o;
         }
       }
     }
@@ -116,16 +133,16 @@ __global__ __launch_bounds__(kExpandWaves * 64) void expand_kv_kernel(ExpandArgs
   auto stage_at = [&](int kk, int col) MLA_INLINE {
     return kk * DH + ((((col >> 3) ^ kk) & 15) << 3) + (col & 7);
   };
-  auto mma = [&](int t, const V8 (&c)[NKS]) MLA_INLINE {
-    const E* wrow = wts + t * TILE + lo * DC;
-    V8 wf[NKS];
+  auto mma = [&](int t, const OV8 (&c)[NKS]) MLA_INLINE {
+    const OP* wrow = wts + t * TILE + lo * DC;
+    OV8 wf[NKS];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) wf[ks] = ld8<E>(wrow + 8 * ((2 * ks + hi) ^ rsw));
+    for (int ks = 0; ks < NKS; ++ks) wf[ks] = ld8<OP>(wrow + 8 * ((2 * ks + hi) ^ rsw));
     f32x16 acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) acc = Elem<E>::mfma(wf[ks], c[ks], acc);
+    for (int ks = 0; ks < NKS; ++ks) acc = Elem<OP>::mfma(wf[ks], c[ks], acc);
     return acc;
   };
   // Tile t's columns: key columns 32 t for t < 3, value columns 32 (t - 3).
@@ -167,7 +184,7 @@ __global__ __launch_bounds__(kExpandWaves * 64) void expand_kv_kernel(ExpandArgs
   constexpr int EB = F8 ? 1 : (int)sizeof(E);  // bytes per cached scalar
   const char* const ring_b = (const char*)a.ring + (size_t)b * a.ring_rows * RW * EB;
   const int rows = (int)a.ring_rows;
-  auto load_row = [&](int k0, V8 (&c)[NKS], V8 (&r)[NR]) MLA_INLINE {
+  auto load_row = [&](int k0, OV8 (&c)[NKS], V8 (&r)[NR]) MLA_INLINE {
     const int key = k0 + lo < kend ? k0 + lo : k0;
     int slot = (int)a.key_slot0 + key;
     slot = slot >= rows ? slot - rows : slot;
@@ -188,19 +205,30 @@ __global__ __launch_bounds__(kExpandWaves * 64) void expand_kv_kernel(ExpandArgs
     }
     const char* p = ring_b + ((uint32_t)slot * (uint32_t)(RW * sizeof(E)) + 16 * hi);
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) c[ks] = *reinterpret_cast<const V8*>(p + 32 * ks);
+    for (int ks = 0; ks < NKS; ++ks) c[ks] = *reinterpret_cast<const OV8*>(p + 32 * ks);
 #pragma unroll
-    for (int j = 0; j < NR; ++j) r[j] = *reinterpret_cast<const V8*>(p + 2 * DC + 32 * j);
+    for (int j = 0; j < NR; ++j) {
+      if constexpr (BF) {
+        // k^R of a bf16 ring into the fp16 key rows
+        const bf16x8 x = *reinterpret_cast<const bf16x8*>(p + 2 * DC + 32 * j);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) r[j][t] = (f16_t)(float)x[t];
+      } else {
+        r[j] = *reinterpret_cast<const V8*>(p + 2 * DC + 32 * j);
+      }
+    }
   };
 
   // Each wave walks its 32-key blocks with the next block's rows in flight.
   // The seven weight tiles run as a two-deep pipeline: tile t + 1's products
   // are issued before tile t's results are converted and staged.
   int k0 = kbeg + 32 * w;
-  V8 cf[NKS], rf[NR];
+  OV8 cf[NKS];
+  V8 rf[NR];
   if (k0 < kend) load_row(k0, cf, rf);
   for (; k0 < kend; k0 += 32 * kExpandWaves) {
-    V8 cn[NKS], rn[NR];
+    OV8 cn[NKS];
+    V8 rn[NR];
     const int k1 = k0 + 32 * kExpandWaves;
     if (k1 < kend) load_row(k1, cn, rn);
     // k^R into columns d_nope .. 127 of the staged key block
@@ -261,21 +289,21 @@ int expand_splits(int n_h, int B, int Lk) {
   return best;
 }
 
-template <typename E, int DC, bool F8>
+template <typename E, int DC, bool F8, bool BF>
 hipError_t launch_expand_dc(const ExpandArgs& a, hipStream_t s) {
   const int splits = expand_splits(a.n_h, a.B, a.Lk);
   const int kpb = ((a.Lk + splits - 1) / splits + 31) / 32 * 32;
   dim3 grid((unsigned)((a.Lk + kpb - 1) / kpb), (unsigned)a.n_h, (unsigned)a.B);
-  hipLaunchKernelGGL((expand_kv_kernel<E, DC, F8>), grid, dim3(kExpandWaves * 64), 0, s, a, kpb);
+  hipLaunchKernelGGL((expand_kv_kernel<E, DC, F8, BF>), grid, dim3(kExpandWaves * 64), 0, s, a, kpb);
   return hipGetLastError();
 }
 
-template <typename E, bool F8>
+template <typename E, bool F8, bool BF>
 hipError_t launch_expand_typed(const ExpandArgs& a, hipStream_t s) {
   switch (a.d_c) {
-    case 64: return launch_expand_dc<E, 64, F8>(a, s);
-    case 128: return launch_expand_dc<E, 128, F8>(a, s);
-    case 192: return launch_expand_dc<E, 192, F8>(a, s);
+    case 64: return launch_expand_dc<E, 64, F8, BF>(a, s);
+    case 128: return launch_expand_dc<E, 128, F8, BF>(a, s);
+    case 192: return launch_expand_dc<E, 192, F8, BF>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -287,10 +315,11 @@ bool expand_supported(int d_c, int d_rope, int d_nope, int d_v) {
          d_v == kExpandDv;
 }
 
-// fp16 and E4M3 rings expand (the host refuses the expansion for a bf16 ring).
+// Every 2-byte and one-byte ring expands into an fp16 window.
 hipError_t launch_expand_kv(const ExpandArgs& a, hipStream_t s) {
-  if (a.cache_type == 3) return launch_expand_typed<f16_t, true>(a, s);
-  return a.cache_type == 2 ? launch_expand_typed<f16_t, false>(a, s) : hipErrorInvalidValue;
+  if (a.cache_type == 3) return launch_expand_typed<f16_t, true, false>(a, s);
+  if (a.cache_type == 1) return launch_expand_typed<f16_t, false, true>(a, s);
+  return a.cache_type == 2 ? launch_expand_typed<f16_t, false, false>(a, s) : hipErrorInvalidValue;
 }
 
 }  // namespace mla

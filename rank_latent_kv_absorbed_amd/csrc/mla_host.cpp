@@ -317,11 +317,13 @@ struct DenseLayout {
   size_t qrot_off, qlo_off, opart_off, ml_off, total;
 };
 
-DenseLayout dense_layout(const mla_cache* h, int32_t Lq, int64_t Lk = -1) {
+// rebuilt: the per-head attention over an expanded (fp16) window, never on
+// split operands whatever the ring type.
+DenseLayout dense_layout(const mla_cache* h, int32_t Lq, int64_t Lk = -1, bool rebuilt = false) {
   const mla_layer_config& c = h->cfg;
   const int d_h = c.d_nope + c.d_rope;
   DenseLayout L;
-  const bool split = split_operands(c);
+  const bool split = !rebuilt && split_operands(c);
   const mla::CoreShape sh = mla::core_shape_for_rows(Lq, split);
   const int br = sh.rows * sh.waves;
   L.lq_pad = (Lq + br - 1) / br * br;
@@ -348,7 +350,7 @@ struct ExpandLayout {
 ExpandLayout expand_layout(const mla_cache* h, int32_t Lq, int64_t Lk = -1) {
   const mla_layer_config& c = h->cfg;
   ExpandLayout L;
-  L.dense = dense_layout(h, Lq, Lk);
+  L.dense = dense_layout(h, Lq, Lk, true);
   L.kv_off = 0;
   L.base = L.kv_off + round_up((size_t)c.batch * c.window_frames * tokens_per_frame(c) * 2 *
                                     c.n_heads * (c.d_nope + c.d_rope) * 2,
@@ -368,21 +370,33 @@ ExpandLayout expand_layout(const mla_cache* h, int32_t Lq, int64_t Lk = -1) {
 // expand faster from 1024 (0.32 vs 0.44 ms) up to 4680 (1.18 vs 1.47 ms);
 // d_c 128 (576 vs 512): even or absorbed faster at every chunk length;
 // d_c 64: absorbed faster throughout.
+// A bf16 ring's absorbed core issues every product twice (split operands)
+// while its expansion runs the plain fp16 per-head core, so the rebuild pays
+// back much sooner; measured on the same window (whole calls, batch 1):
+// d_c 192: absorbed 0.096 / expand 0.125 ms at 64 queries, 0.156 / 0.136 at
+// 128; d_c 128: 0.109 / 0.134 at 128, 0.182 / 0.141 at 256; d_c 64: 0.133 /
+// 0.131 at 256, 0.188 / 0.164 at 384 (batch 4: even near 350).  Split rings
+// expand from 128 queries when the issued latent products are at least 3
+// times the per-head ones, from 256 when at least 2 times, else from 384.
 constexpr int32_t kExpandMinQueries = 512;
 constexpr double kExpandFlopRatio = 1.5;
+constexpr int32_t kSplitExpandMinQueries[3] = {128, 256, 384};
 
 // The expansion serves fp16-ring handles of the dense core's head width whose
 // expanded full window (every key, every head) keeps one sequence's offsets
 // below 2^31 elements, like a dense cache.  The expanded window is sized for
 // the full window so the workspace size does not change as frames arrive.
-// fp16 and E4M3 rings expand into an fp16 window (an E4M3 value widens to
-// fp16 exactly).  A bf16 ring has no expansion: the rebuilt per-head keys and values would be
-// rounded to bf16, and those roundings (like the query's and the
-// probabilities') each move the attention output by about 1e-3 of its size
-// on Gaussian inputs, independent of the window length.
+// Every ring with bf16 inputs expands into an fp16 window: an E4M3 value
+// widens to fp16 exactly, a bf16 ring's products run on bf16 MFMA (exact
+// products of the stored values).  Rounded to bf16 instead, the rebuilt keys
+// and values (like the query and the probabilities) would each move the
+// attention output by about 1e-3 of its size on Gaussian inputs; in fp16 the
+// expansion is as accurate as an fp16 ring's, with fp16's range (the rebuilt
+// values must stay below 65504 in magnitude).
 bool expand_possible(const mla_cache* h) {
   const mla_layer_config& c = h->cfg;
-  return c.dtype == MLA_BF16 && (c.cache_dtype == MLA_F16 || c.cache_dtype == MLA_E4M3) &&
+  return c.dtype == MLA_BF16 &&
+         (c.cache_dtype == MLA_F16 || c.cache_dtype == MLA_E4M3 || c.cache_dtype == MLA_BF16) &&
          mla::expand_supported(c.d_c, c.d_rope, c.d_nope, c.d_v) &&
          (int64_t)c.window_frames * tokens_per_frame(c) * 2 * c.n_heads * (c.d_nope + c.d_rope) <
              (1LL << 31);
@@ -395,6 +409,13 @@ int32_t attend_path_for(const mla_cache* h, int32_t Lq, int32_t key_splits) {
   if (h->attend_path == MLA_PATH_EXPAND) return MLA_PATH_EXPAND;
   const double latent = 2.0 * (c.d_c + c.d_rope) + 2.0 * c.d_c;
   const double per_head = 2.0 * (c.d_nope + c.d_rope) + 2.0 * c.d_v;
+  if (split_operands(c)) {
+    const double issued = 2.0 * latent;
+    const int32_t min_q = issued >= 3.0 * per_head   ? kSplitExpandMinQueries[0]
+                          : issued >= 2.0 * per_head ? kSplitExpandMinQueries[1]
+                                                     : kSplitExpandMinQueries[2];
+    return Lq >= min_q ? MLA_PATH_EXPAND : MLA_PATH_ABSORBED;
+  }
   return Lq >= kExpandMinQueries && latent >= kExpandFlopRatio * per_head ? MLA_PATH_EXPAND
                                                                           : MLA_PATH_ABSORBED;
 }
@@ -753,7 +774,7 @@ mla_status mla_attend(mla_cache* h, const void* q, int64_t q_token0, int32_t Lq,
     m.ring = e.kv;
     m.out = out;
     m.qrot = ws + X.base + X.dense.qrot_off;
-    m.qrot_lo = nullptr;  // fp16 ring only
+    m.qrot_lo = nullptr;  // fp16 window: plain operands
     m.B = c.batch;
     m.Lq = Lq;
     m.n_h = c.n_heads;

@@ -378,18 +378,29 @@ def _attend_ptrs(L):
     return dict(zip(["qcat", "qcat_lo", "opart", "ml"], list(a)))
 
 
-def test_bf16_ring_split_operands_and_no_expansion(sim):
-    """A bf16 ring runs the attention core on split operands: the workspace
-    carries the query remainders after the queries, the chunk shape has four
-    waves (one per SIMD), and there is no expand path (MLA_ERR_UNSUPPORTED
-    when asked for, the absorbed form on automatic).  fp16 rings do not split."""
+def test_bf16_ring_split_operands_and_fp16_expansion(sim):
+    """A bf16 ring runs the absorbed core on split operands: the workspace
+    carries the query remainders after the queries and the chunk shape has
+    four waves (one per SIMD).  Its expansion rebuilds into the same fp16
+    window as an fp16 ring's, so the per-head attention behind it takes plain
+    operands (no remainders, the 8-wave chunk shape).  fp16 rings do not
+    split."""
     ws = 1 << 40
     for cache_dtype in ("bf16", "f16"):
         split = cache_dtype == "bf16"
         st, h = _create(sim, _cfg(cache_dtype=cache_dtype))
         assert st == 0 and sim.mla_cache_set_state(h, 3, 23) == 0
-        assert sim.mla_cache_set_attend_path(h, 2) == (8 if split else 0)
-        assert sim.mla_attend_path(h, 4680, 0) == (1 if split else 2)
+        assert sim.mla_attend_path(h, 4680, 0) == 2
+        need = sim.mla_attend_workspace_bytes(h, 4680, 0)
+        assert sim.mla_attend(h, P(FAKE_PTR), 21 * 1560 - 4680, 4680, P(FAKE_PTR), P(FAKE_PTR),
+                              P(FAKE_PTR), 0, P(ws), need, None) == 0
+        a, p = _mha_info(sim), _mha_ptrs(sim)
+        assert (a["block_rows"], a["key_tile"], a["stages"]) == expected_shape(4680, 32, False)
+        assert p["qrot_lo"] == 0
+        t = (ctypes.c_int * 5)()
+        sim.fake_type_info(t)
+        assert t[3] == (1 if split else 2) and t[4] == 2
+        assert sim.mla_cache_set_attend_path(h, 2) == 0
         assert sim.mla_cache_set_attend_path(h, 1) == 0
         for Lq in (1, 4, 8, 11, 100, 4680):
             R = Lq * 12
@@ -459,6 +470,14 @@ def test_attend_path_choice(sim):
         st, g = _create(sim, _cfg(d_c=d_c))
         assert st == 0 and sim.mla_attend_path(g, 4680, 0) == 1, d_c
         assert sim.mla_cache_set_attend_path(g, 2) == 0 and sim.mla_attend_path(g, 4680, 0) == 2
+    # bf16 rings (the absorbed core issues every product twice): expand from
+    # 128 / 256 / 384 queries at d_c 192 / 128 / 64
+    for d_c, first in ((192, 128), (128, 256), (64, 384)):
+        st, g = _create(sim, _cfg(d_c=d_c, cache_dtype="bf16"))
+        assert st == 0 and sim.mla_cache_set_state(g, 0, 20) == 0
+        assert sim.mla_attend_path(g, first - 1, 0) == 1, d_c
+        assert sim.mla_attend_path(g, first, 0) == 2 and sim.mla_attend_path(g, 4680, 0) == 2, d_c
+        assert sim.mla_attend_path(g, 4680, 2) == 1, d_c
     st, d = _create(sim, c, dense=True)
     assert sim.mla_cache_set_attend_path(d, 1) == 9 and sim.mla_attend_path(d, 16, 0) == -1
 

@@ -17,7 +17,6 @@ import torch
 
 from oracle import mla as O
 from synthetic import config, chunk_q, chunk_x
-from rank_latent_kv_absorbed_amd.mla import ERR_UNSUPPORTED, MlaError
 from tests.parity_util import (BF16_RING_MEAN_REL, NAN_BITS, DenseRun, LatentRun, assert_parity, dev,
                                nan_fill_, parity_stats, sample_rows)
 
@@ -270,7 +269,7 @@ def test_attend_small_queries_latent_widths(Lq, d_c):
 
 
 @pytest.mark.parametrize("cache_dtype,path", [("f16", "absorbed"), ("f16", "expand"), ("bf16", "absorbed"),
-                                              ("e4m3", "absorbed"), ("e4m3", "expand")])
+                                              ("bf16", "expand"), ("e4m3", "absorbed"), ("e4m3", "expand")])
 def test_degenerate_softmax_closed_forms(cache_dtype, path):
     """Two windows whose attention has a closed form, 300 keys through a wrap:
     zero queries weight every key equally, so each head's output is W^V_up,h
@@ -341,7 +340,8 @@ def test_frame_shift_changes_nothing_beyond_rounding():
 # attention at Wan sizes, sampled rows
 # --------------------------------------------------------------------------
 
-@pytest.mark.parametrize("cache_dtype,path", [("f16", "absorbed"), ("f16", "expand"), ("bf16", "auto")])
+@pytest.mark.parametrize("cache_dtype,path", [("f16", "absorbed"), ("f16", "expand"), ("bf16", "absorbed"),
+                                              ("bf16", "auto")])
 def test_wan_layer_sampled_rows(cache_dtype, path):
     cfg = config("wan_layer").with_(cache_dtype=cache_dtype)
     run = LatentRun(cfg, path=path)
@@ -350,26 +350,35 @@ def test_wan_layer_sampled_rows(cache_dtype, path):
     q = run.query(cfg.Lq)
     rows = sample_rows(cfg.Lq, 96)
     taken = run.gpu.attend_path(cfg.Lq)
-    assert taken == (path if path != "auto" else ("absorbed" if cache_dtype == "bf16" else "expand"))
+    assert taken == (path if path != "auto" else "expand")
     got, ref, _ = run.attend(q, cfg.chunk_frame0 * cfg.T, rows=rows)
     assert_parity(got, ref, "bf16", f"wan layer (6+3 frames) sampled {cache_dtype} {taken}",
                   mean_lim=ring_lim(cfg))
 
 
-def test_bf16_ring_has_no_expand_path():
-    """A bf16 ring refuses the expansion (its rebuilt keys and values would be
-    rounded to bf16): MLA_ERR_UNSUPPORTED, and automatic stays absorbed."""
-    cfg = config("wan_layer").with_(cache_dtype="bf16")
-    run = LatentRun(cfg)
-    with pytest.raises(MlaError) as e:
-        run.gpu.set_attend_path("expand")
-    assert e.value.status == ERR_UNSUPPORTED
-    assert run.gpu.attend_path(4680) == "absorbed"
+# A bf16 ring's expansion: bf16 products of the stored values, the rebuilt
+# keys and values in fp16 like an fp16 ring's, mid sizes through a wrap with
+# the shapes of the fp16 expand cases, every element.
+@pytest.mark.parametrize("Lq,d_c,n_heads", [(3, 192, 4), (33, 64, 4), (120, 128, 6), (300, 192, 4)])
+def test_bf16_ring_expand_mid_ragged_with_wrap(Lq, d_c, n_heads):
+    cfg = mid_cfg(d_nope=96, d_rope=32, d_v=128, d_c=d_c, n_heads=n_heads, cache_dtype="bf16")
+    run = LatentRun(cfg, path="expand")
+    run.write(0, 4)
+    run.evict(2)
+    run.write(4, 2)
+    run.evict(1)
+    run.write(6, 2)       # frames 3..7 resident, Lk = 300
+    assert run.gpu.attend_path(Lq) == "expand"
+    q = run.query(Lq)
+    got, ref, _ = run.attend(q, 8 * cfg.T - Lq)
+    assert_parity(got, ref, "bf16", f"bf16 ring expand Lq={Lq} d_c={d_c} n_h={n_heads}", mean_lim=ring_lim(cfg))
+    mx, mean = parity_stats(got, ref)
+    assert mean < 1e-3, mean      # fp16 rebuilt keys and values: an fp16 ring's error, not bf16's
 
 
 @pytest.mark.parametrize("batch,cache_dtype,path",
                          [(1, "f16", "absorbed"), (2, "f16", "absorbed"), (1, "bf16", "absorbed"),
-                          (1, "f16", "expand"), (2, "bf16", "auto"), (1, "f16", "auto")])
+                          (1, "f16", "expand"), (2, "bf16", "auto"), (1, "bf16", "expand"), (1, "f16", "auto")])
 def test_full_window_sampled_rows(batch, cache_dtype, path):
     cfg = config("wan_window").with_(batch=batch, cache_dtype=cache_dtype)
     run = LatentRun(cfg, path=path)
@@ -431,18 +440,20 @@ def test_expand_poisoned_free_slots_and_agreement():
     assert mx < 1e-2 and mean < 2e-3, (mx, mean)
 
 
-@pytest.mark.parametrize("Lq,path", [(1, "absorbed"), (8, "absorbed"), (1, "expand")])
-def test_small_queries_full_window(Lq, path):
+@pytest.mark.parametrize("Lq,path,cache_dtype", [(1, "absorbed", "f16"), (8, "absorbed", "f16"), (1, "expand", "f16"),
+                                                (8, "expand", "bf16")])
+def test_small_queries_full_window(Lq, path, cache_dtype):
     """Decode-like shapes on the full 21-frame window: each sequence's few rows
     spread over many key ranges (about a hundred partials per row)."""
-    cfg = config("wan_window").with_(batch=2)
+    cfg = config("wan_window").with_(batch=2, cache_dtype=cache_dtype)
     run = LatentRun(cfg, path=path)
     run.write(0, cfg.prefill_frames)
     run.evict(cfg.evict_frames)
     run.write(cfg.chunk_frame0, cfg.chunk_frames)
     q = run.query(Lq)
     got, ref, _ = run.attend(q, (cfg.chunk_frame0 + cfg.chunk_frames) * cfg.T - Lq)
-    assert_parity(got, ref, "bf16", f"21-frame window small query Lq={Lq} {path}")
+    assert_parity(got, ref, "bf16", f"21-frame window small query Lq={Lq} {path} {cache_dtype}",
+                  mean_lim=ring_lim(cfg))
 
 
 # --------------------------------------------------------------------------
@@ -512,22 +523,24 @@ def test_dense_mha_ring_wrap():
 # expand-then-attend: path choice, batches, workspace reuse
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("Lq", [511, 512])
-def test_auto_path_threshold_batch3_wrap(Lq):
-    """Three sequences through a ring wrap; 511 queries take the absorbed path
-    and 512 the expand path on automatic, both against the oracle."""
-    cfg = mid_cfg(d_nope=96, d_rope=32, d_v=128, d_c=192, n_heads=6, batch=3)
+@pytest.mark.parametrize("cache_dtype,Lq,first", [("f16", 511, 512), ("f16", 512, 512), ("bf16", 127, 128),
+                                                 ("bf16", 128, 128)])
+def test_auto_path_threshold_batch3_wrap(cache_dtype, Lq, first):
+    """Three sequences through a ring wrap; on automatic an fp16 ring expands
+    from 512 queries and a bf16 ring (split-operand absorbed core) from 128,
+    both sides of each threshold against the oracle."""
+    cfg = mid_cfg(d_nope=96, d_rope=32, d_v=128, d_c=192, n_heads=6, batch=3, cache_dtype=cache_dtype)
     run = LatentRun(cfg)
     run.write(0, 4)
     run.evict(2)
     run.write(4, 2)
     run.evict(1)
     run.write(6, 2)       # frames 3..7 resident through a wrap, Lk = 300
-    assert run.gpu.attend_path(Lq) == ("expand" if Lq >= 512 else "absorbed")
+    assert run.gpu.attend_path(Lq) == ("expand" if Lq >= first else "absorbed")
     q = run.query(Lq)
     rows = sample_rows(Lq, 64)
     got, ref, _ = run.attend(q, 8 * cfg.T, rows=rows)
-    assert_parity(got, ref, "bf16", f"auto path Lq={Lq} B=3")
+    assert_parity(got, ref, "bf16", f"auto path {cache_dtype} Lq={Lq} B=3", mean_lim=ring_lim(cfg))
 
 
 def test_expand_workspace_reused_as_window_fills():
@@ -745,7 +758,7 @@ def _climbing_window(cfg, step_log2, seed=0):
 
 
 @pytest.mark.parametrize("cache_dtype,path", [("f16", "absorbed"), ("f16", "expand"), ("bf16", "absorbed"),
-                                              ("e4m3", "absorbed"), ("e4m3", "expand")])
+                                              ("bf16", "expand"), ("e4m3", "absorbed"), ("e4m3", "expand")])
 def test_sharp_attention_running_max_climbs(cache_dtype, path):
     """Every frame's keys score about 9 log2 units above the previous frame's,
     so each row's running maximum jumps by more than the lazy-rescale
