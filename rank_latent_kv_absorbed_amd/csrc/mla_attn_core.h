@@ -414,6 +414,31 @@ void attn_core_kernel(AttnCore a) {
   const int t16 = r16 >> 2, c16 = r16 & 3;
   const int tsw16 = swz(4 * g16 + t16);
 
+  // F8, one-wave 16-row blocks: each lane widens exactly the key fragments
+  // its score products take (chunk 4 ks + g16 of key kb * 16 + r16, read from
+  // the raw tile at its place in the ring row) and keeps them in registers;
+  // only the value columns (the first DV of a row) go to the decode buffer,
+  // at the permuted positions the transpose reads expect.  The wave's lanes
+  // cover every chunk of the tile once, so nothing is read back for the
+  // scores.  Keys past the window become zeros.
+  auto decode_frags = [&](const E* stage, int kt, auto& kf) MLA_INLINE {
+    const char* src = (const char*)stage;
+    const int nk = a.Lk - kt * KT;  // keys of the tile inside the window
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const int key = kb * 16 + r16;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const int q = 4 * ks + g16;
+        const uint2 raw = *reinterpret_cast<const uint2*>(src + key * DQK + 8 * q);
+        f16x8 h = e4m3x8_to_f16(raw.x, raw.y);
+        if (key >= nk) h = zero8<f16_t>();
+        kf[kb][ks] = h;
+        if (ks < DV / 32) *reinterpret_cast<f16x8*>(kd + (key * CPK + (q ^ k_sw16)) * 8) = h;
+      }
+    }
+  };
+
   // Per row block rb of the wave: query fragments, value sums, running max
   // and sum, the lane's row.  Each key fragment read from LDS feeds RB
   // products, so LDS traffic per product falls as 1 / RB.
@@ -483,6 +508,21 @@ void attn_core_kernel(AttnCore a) {
   };
 
   // The three phases of a step on one key tile, for this wave's rows.
+  // 16-row waves: the score products from the tile's key fragments (lane
+  // (r16, g16) holds chunk 4 ks + g16 of key kb * 16 + r16), the two key
+  // blocks' chains interleaved.
+  auto score_products16 = [&](const auto& kf, auto& sv) MLA_INLINE {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < AV; ++r) sv[0][kb][r] = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int u = 0; u < NQ; ++u) sv[0][kb] = Elem<E>::mfma16(kf[kb][ks], qf[u][0][ks], sv[0][kb]);
+  };
   // Scores S^T = K Q^T of the tile in `cur`.
   auto scores = [&](const E* cur, AccT (&sv)[RB][NKB]) MLA_INLINE {
     if constexpr (R16) {
@@ -497,16 +537,7 @@ void attn_core_kernel(AttnCore a) {
         for (int ks = 0; ks < NKS; ++ks) kf[kb][ks] = ld8<E>(krow + 8 * ((4 * ks + g16) ^ k_sw16));
       }
       __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < AV; ++r) sv[0][kb][r] = 0.0f;
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int u = 0; u < NQ; ++u) sv[0][kb] = Elem<E>::mfma16(kf[kb][ks], qf[u][0][ks], sv[0][kb]);
+      score_products16(kf, sv);
     } else {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
@@ -710,10 +741,16 @@ void attn_core_kernel(AttnCore a) {
     // buffer, refilled at once with tile i + NS), compute on the decode
     // buffer, then wait for this wave's loads of tile i + 1 and meet the
     // other waves (nobody reads the decode buffer any more).
+    constexpr bool DIRECT = NW == 1 && R16;
+    static_assert(!DIRECT || DV % 32 == 0, "value columns are whole 32-column score steps");
     auto step8 = [&](int i, E* stage) MLA_INLINE {
       const StepInfo si = wc.c.si;
       const int b = wc.b;
-      decode(stage, si.kt);
+      V8 kf[DIRECT ? NKB : 1][DIRECT ? NKS : 1];
+      if constexpr (DIRECT)
+        decode_frags(stage, si.kt, kf);
+      else
+        decode(stage, si.kt);
       lds_barrier();
       if (i + NS < n_steps) issue(stage);
       if (si.first && i > 0) {
@@ -724,7 +761,10 @@ void attn_core_kernel(AttnCore a) {
       if (live) {
         AccT sv[RB][NKB];
         V8 pf[NQ][RB][NPF];
-        scores(kd, sv);
+        if constexpr (DIRECT)
+          score_products16(kf, sv);
+        else
+          scores(kd, sv);
         softmax(si.kt, sv, pf);
         values(kd, pf);
         if (si.last) write_partial(si, b);
