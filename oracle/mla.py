@@ -30,7 +30,9 @@ Readings the pages leave open (each one listed with its reason in the design
 notes): score scale 1/sqrt(d_nope + d_rope); RoPE pairs are adjacent
 elements, grouped t then h then w, frequencies base^(-i/P_axis); positions are
 (absolute latent-frame index, row, column); k^R comes from the layer input x;
-no norms or biases; the stored cache is rounded to the storage dtype (RNE).
+no biases, and norms only where asked for (an RMS norm of the latent c in the
+cache write; an RMS norm of each head's query row [q^nope | q^R] before its
+rotation); the stored cache is rounded to the storage dtype (RNE).
 
 Everything is float64 NumPy; a matmul is the only library primitive used as a
 step.  Plain loops are used where they make the definition clearer.
@@ -304,17 +306,22 @@ def cache_evict(ring, n_frames):
 # ----------------------------------------------------------------------------
 
 
-def attend(store, ring, q, q_token0, w_uk, w_uv, cfg, rows=None, block=512):
+def attend(store, ring, q, q_token0, w_uk, w_uv, cfg, rows=None, block=512, q_norm=None):
     """Attention of query chunk q over every resident token, per head.
 
     Keys are all tokens of all resident frames (no mask inside the window).
     Query i sits at global token q_token0 + i; its q^R is rotated there.
     rows: optional array of query indices to evaluate (default: all).
+    q_norm: optional (gamma [d_nope + d_rope], eps): each head's query row
+    [q^nope | q^R] is RMS-normalised (rms_norm over its d_nope + d_rope values,
+    the same gain for every head) before anything else, the rotation included.
     Returns float64 [B, len(rows), n_h, d_v].
     """
     q = np.asarray(q, dtype=np.float64)
     B, Lq, n_h, dq = q.shape
     assert n_h == cfg.n_heads and dq == cfg.d_nope + cfg.d_rope
+    if q_norm is not None:
+        q = rms_norm(q, q_norm[0], q_norm[1])
     if ring.n_resident <= 0:
         raise RingError("attend on an empty window")
     rows = np.arange(Lq) if rows is None else np.asarray(rows, dtype=np.int64)

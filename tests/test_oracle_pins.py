@@ -527,6 +527,62 @@ def test_cache_write_with_latent_norm_normalises_only_c():
     assert (ratio > 0).all()
 
 
+def _qnorm_case(seed):
+    cfg = config("tiny").with_(batch=2)
+    rng = np.random.default_rng(seed)
+    store = O.round_storage(rng.standard_normal((2, cfg.window_frames * cfg.T, cfg.width)), "f32")
+    ring = O.RingModel(cfg.window_frames, cfg.T)
+    ring.write(0, 3)
+    w_uk = rng.standard_normal((cfg.n_heads, cfg.d_nope, cfg.d_c)) / math.sqrt(cfg.d_c)
+    w_uv = rng.standard_normal((cfg.n_heads, cfg.d_v, cfg.d_c)) / math.sqrt(cfg.d_c)
+    # rows of very different sizes, so that the norm changes the attention
+    q = rng.standard_normal((2, 5, cfg.n_heads, cfg.d_qk)) * np.exp(rng.standard_normal((2, 5, cfg.n_heads, 1)))
+    return cfg, rng, store, ring, w_uk, w_uv, q
+
+
+def test_query_norm_is_identity_on_rows_of_unit_rms():
+    """gamma = 1, eps = 0: rows already of mean square 1 over d_nope + d_rope
+    come out unchanged, so the attention equals the plain one; rows normalised
+    over the content part only, or over all heads, do not (the axis is pinned)."""
+    cfg, rng, store, ring, w_uk, w_uv, q = _qnorm_case(41)
+    unit = q / np.sqrt(np.mean(q * q, axis=-1, keepdims=True))
+    ones = (np.ones(cfg.d_qk), 0.0)
+    plain = O.attend(store, ring, unit, 2 * cfg.T, w_uk, w_uv, cfg)
+    np.testing.assert_allclose(O.attend(store, ring, unit, 2 * cfg.T, w_uk, w_uv, cfg, q_norm=ones), plain,
+                               rtol=1e-12, atol=1e-13)
+    for other in (q / np.sqrt(np.mean(q[..., :cfg.d_nope] ** 2, axis=-1, keepdims=True)),
+                  q / np.sqrt(np.mean(q * q, axis=(-2, -1), keepdims=True))):
+        a = O.attend(store, ring, other, 2 * cfg.T, w_uk, w_uv, cfg, q_norm=ones)
+        b = O.attend(store, ring, other, 2 * cfg.T, w_uk, w_uv, cfg)
+        assert np.abs(a - b).max() > 1e-3
+
+
+def test_query_norm_removes_each_rows_scale():
+    """eps = 0: multiplying each (token, head) row by its own positive factor
+    changes nothing; without the norm it does."""
+    cfg, rng, store, ring, w_uk, w_uv, q = _qnorm_case(42)
+    gamma = 1.0 + 0.3 * rng.standard_normal(cfg.d_qk)
+    f = np.exp(2.0 * rng.standard_normal(q.shape[:-1] + (1,)))
+    a = O.attend(store, ring, q, 2 * cfg.T, w_uk, w_uv, cfg, q_norm=(gamma, 0.0))
+    b = O.attend(store, ring, f * q, 2 * cfg.T, w_uk, w_uv, cfg, q_norm=(gamma, 0.0))
+    np.testing.assert_allclose(a, b, rtol=1e-10, atol=1e-12)
+    assert np.abs(O.attend(store, ring, f * q, 2 * cfg.T, w_uk, w_uv, cfg) - a).max() > 1e-3
+
+
+def test_query_norm_acts_on_the_unrotated_query():
+    """The gain meets q^R before its rotation: the normalised attention is the
+    plain attention of torch's rms_norm(q, gamma, eps).  The gain differs
+    inside every rotary pair, where scaling and rotating do not commute, so an
+    oracle that applied it after the rotation would fail this."""
+    cfg, rng, store, ring, w_uk, w_uv, q = _qnorm_case(43)
+    gamma = 1.0 + 0.5 * rng.standard_normal(cfg.d_qk)
+    assert np.abs(gamma[cfg.d_nope::2] - gamma[cfg.d_nope + 1::2]).min() > 1e-3
+    eps = 1e-3
+    pre = torch.nn.functional.rms_norm(torch.from_numpy(q), (cfg.d_qk,), torch.from_numpy(gamma), eps).numpy()
+    got = O.attend(store, ring, q, 2 * cfg.T, w_uk, w_uv, cfg, q_norm=(gamma, eps))
+    np.testing.assert_allclose(got, O.attend(store, ring, pre, 2 * cfg.T, w_uk, w_uv, cfg), rtol=1e-11, atol=1e-13)
+
+
 def test_attention_block_with_identity_projections_is_the_attention():
     """hidden = n_h * d_qk = n_h * d_v and identity W_q, W_O: the block is the
     per-head attention of x read as queries, the heads concatenated."""
