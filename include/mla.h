@@ -219,6 +219,23 @@ mla_status mla_attend(mla_cache* cache, const void* q, int64_t q_token0, int32_t
                       const void* w_uk, const void* w_uv, float* out, int32_t key_splits,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* Query-side RMS norm for later mla_attend calls on this latent handle (and
+ * mla_attend_noalloc): each head's query row [q^nope | q^R] is replaced by
+ *   gamma * q_h / sqrt(mean(q_h^2) + eps)   (mean over its d_nope + d_rope values)
+ * before its rotation and the folding of W^K_up, the same gain for every head.
+ * The pages print no normalisation (technical summary, method items 2-3); a
+ * query norm leaves the absorption intact, while a norm of the per-head keys
+ * would not (it acts on W^K_up,h c, after the up-projection), so the key-side
+ * counterpart is the latent norm of mla_cache_write_norm.  gamma: device
+ * pointer to [d_nope + d_rope] gains in the input dtype (bf16), 16-byte
+ * aligned, owned by the caller and read by every attend while set; NULL
+ * switches the norm off.  eps >= 0 and finite.  Errors: MLA_ERR_INVALID_ARG
+ * (null handle, misaligned gamma, bad eps), MLA_ERR_WRONG_KIND (dense
+ * handle), MLA_ERR_UNSUPPORTED (fp32 handles).  While it is set,
+ * mla_attend_block returns MLA_ERR_UNSUPPORTED (its folded projection never
+ * forms the per-head queries). */
+mla_status mla_cache_set_query_norm(mla_cache* cache, const void* gamma, float eps);
+
 /* Allocation-free mla_attend, for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid
  * allocation): the same computation on the same path as mla_attend (the
@@ -270,7 +287,8 @@ size_t mla_attend_block_workspace_bytes(const mla_cache* cache, int32_t Lq, int3
  * (rotated and scaled in its epilogue), the latent core, the merged latent
  * outputs, then out [batch][Lq][hidden] fp32 = w_fo o_lat in one product.
  * MLA_ERR_UNSUPPORTED unless bf16 inputs, the absorbed core's head shapes,
- * hidden % 64 == 0 and n_h * d_c % 64 == 0.  Other errors as mla_attend. */
+ * hidden % 64 == 0 and n_h * d_c % 64 == 0, and while a query norm is set
+ * (mla_cache_set_query_norm).  Other errors as mla_attend. */
 mla_status mla_attend_block(mla_cache* cache, const void* x, int64_t q_token0, int32_t Lq,
                             const void* w_qf, const void* w_fo, float* out, int32_t key_splits,
                             void* workspace, size_t workspace_bytes, void* stream);

@@ -19,7 +19,11 @@ namespace {
 constexpr int kQprepTokens = 4;
 constexpr int kQprepRun = 4;
 
-template <typename E, bool SPLIT>
+// NORM (a query norm is set; d_h = 128): the 16 lanes that hold a row's 16
+// chunks (a row starts at a multiple of 16 chunks, and every thread's chunks
+// sit 256 apart) sum its squares by shuffles; each value is gained before
+// the rotation and scaled by the row's 1 / rms with the score scale, in fp32.
+template <typename E, bool SPLIT, bool NORM = false>
 __global__ __launch_bounds__(256) void mha_qprep_bf16_kernel(MhaAttendArgs a, int lq_pad) {
   typedef typename Elem<E>::v8 V8;
   __shared__ float cs[kQprepTokens][kMaxRopePairs][2];
@@ -52,6 +56,18 @@ __global__ __launch_bounds__(256) void mha_qprep_bf16_kernel(MhaAttendArgs a, in
       const int tok = tok0 + tt < a.Lq ? tok0 + tt : a.Lq - 1;
       v[u] = ld_bf16x8((const bf16_t*)a.q + (((size_t)b * a.Lq + tok) * a.n_h + h) * a.d_h + 8 * ch);
     }
+    float rs[kQprepRun];  // NORM: each chunk's row 1 / rms (every lane takes part)
+    if constexpr (NORM) {
+#pragma unroll
+      for (int u = 0; u < kQprepRun; ++u) {
+        float ss = 0.0f;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) ss = fmaf((float)v[u][t], (float)v[u][t], ss);
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) ss += __shfl_xor(ss, o);
+        rs[u] = 1.0f / sqrtf(ss / (float)a.d_h + a.qn_eps);
+      }
+    }
 #pragma unroll
     for (int u = 0; u < kQprepRun; ++u) {
       const int i = i0 + u * blockDim.x;
@@ -59,12 +75,22 @@ __global__ __launch_bounds__(256) void mha_qprep_bf16_kernel(MhaAttendArgs a, in
       const int h = rem / C, ch = rem - h * C;
       const int tok = tok0 + tt;
       if (i >= total || tok >= a.Lq) continue;
+      float sc = a.qscale;
+      bf16x8 g8;
+      if constexpr (NORM) {
+        g8 = ld_bf16x8((const bf16_t*)a.qn_gamma + 8 * ch);
+        sc *= rs[u];
+      }
       V8 o, ol;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float c = cs[tt][4 * ch + j][0], s = cs[tt][4 * ch + j][1];
-        const float x0 = (float)v[u][2 * j], x1 = (float)v[u][2 * j + 1];
-        const float y0 = (x0 * c - x1 * s) * a.qscale, y1 = (x0 * s + x1 * c) * a.qscale;
+        float x0 = (float)v[u][2 * j], x1 = (float)v[u][2 * j + 1];
+        if constexpr (NORM) {
+          x0 *= (float)g8[2 * j];
+          x1 *= (float)g8[2 * j + 1];
+        }
+        const float y0 = (x0 * c - x1 * s) * sc, y1 = (x0 * s + x1 * c) * sc;
         o[2 * j] = Elem<E>::from(y0);
         o[2 * j + 1] = Elem<E>::from(y1);
         ol[2 * j] = Elem<E>::from(y0 - (float)o[2 * j]);
@@ -209,9 +235,14 @@ hipError_t launch_mha_typed(const MhaAttendArgs& a, float* opart, float* ml, con
   constexpr bool SPLIT = __is_same(E, bf16_t);
   if ((a.qrot_lo != nullptr) != SPLIT) return hipErrorInvalidValue;
   {
-    hipLaunchKernelGGL((mha_qprep_bf16_kernel<E, SPLIT>),
-                       dim3((unsigned)((a.Lq + kQprepTokens - 1) / kQprepTokens), (unsigned)a.B),
-                       dim3(256), 0, s, a, lq_pad);
+    const dim3 grid((unsigned)((a.Lq + kQprepTokens - 1) / kQprepTokens), (unsigned)a.B);
+    if (a.qn_gamma != nullptr) {
+      // the norm's 16-lane row reduction needs 16 chunks per row
+      if (a.d_h != 128) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((mha_qprep_bf16_kernel<E, SPLIT, true>), grid, dim3(256), 0, s, a, lq_pad);
+    } else {
+      hipLaunchKernelGGL((mha_qprep_bf16_kernel<E, SPLIT>), grid, dim3(256), 0, s, a, lq_pad);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

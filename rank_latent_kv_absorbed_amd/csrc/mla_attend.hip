@@ -40,11 +40,16 @@ __device__ __forceinline__ void store_q(E* hi, E* lo, float v) {
   if constexpr (SPLIT) *lo = Elem<E>::from(v - (float)h);
 }
 
-template <typename E, int DC, bool SPLIT>
+// NORM (a query norm is set): the gained query g q^nope (exact in fp32) enters
+// the products as two bf16 parts, its leading part and the bf16 rounding of
+// the remainder, against the same weights; the row's 1 / rms, a scalar that
+// commutes with the fold, scales the result with the score scale.
+template <typename E, int DC, bool SPLIT, bool NORM = false>
 __global__ __launch_bounds__(256) void qprep_bf16_kernel(AttendArgs a) {
   constexpr int NT = DC / 32;
   constexpr int WSTR = DC + 8;                 // padded LDS row (elements)
   extern __shared__ bf16_t wlds[];             // [d_nope][WSTR]
+  __shared__ float inv_s[NORM ? 128 : 1];      // 1 / rms of the block's 128 tokens
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63, lo = l & 31, hi = l >> 5;
   const int h = blockIdx.y, b = blockIdx.z;
@@ -70,12 +75,27 @@ __global__ __launch_bounds__(256) void qprep_bf16_kernel(AttendArgs a) {
   for (int it = 0; it < NT; ++it)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[it][r] = 0.0f;
+  const bf16_t* gam = (const bf16_t*)a.qn_gamma;
+  float ss = 0.0f;  // NORM: the lane's share of the row's sum of squares
   for (int k0 = 0; k0 < a.d_nope; k0 += 16) {
     bf16x8 bq = zero_bf16x8();
     if (valid) {
       const bf16x4 q0 = *reinterpret_cast<const bf16x4*>(qrow + k0);
       const bf16x4 q1 = *reinterpret_cast<const bf16x4*>(qrow + k0 + 8);
       bq = __builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    bf16x8 bq_lo = zero_bf16x8();
+    if constexpr (NORM) {
+      const bf16x4 g0 = *reinterpret_cast<const bf16x4*>(gam + k0 + 4 * hi);
+      const bf16x4 g1 = *reinterpret_cast<const bf16x4*>(gam + k0 + 8 + 4 * hi);
+      const bf16x8 g8 = __builtin_shufflevector(g0, g1, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const float x = (float)bq[t], p = x * (float)g8[t];
+        ss = fmaf(x, x, ss);
+        bq[t] = to_bf16(p);
+        bq_lo[t] = to_bf16(p - (float)bq[t]);
+      }
     }
     const bf16_t* wrow = wlds + (k0 + tr_key) * WSTR + tr_col;
 #pragma unroll
@@ -84,11 +104,27 @@ __global__ __launch_bounds__(256) void qprep_bf16_kernel(AttendArgs a) {
       const i16x4 hi4 = lds_read_tr16(wrow + 8 * WSTR + it * 32);
       const bf16x8 wa = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
       acc[it] = mfma32(wa, bq, acc[it]);
+      if constexpr (NORM) acc[it] = mfma32(wa, bq_lo, acc[it]);
     }
+  }
+  float inv = 1.0f;
+  if constexpr (NORM) {
+    // the rotary part's squares (this lane's half of the row), then the row
+    if (valid) {
+      const bf16_t* qr = (const bf16_t*)a.q + (((size_t)b * a.Lq + tok) * a.n_h + h) * d_qk + a.d_nope;
+      for (int d = hi; d < a.d_rope; d += 2) {
+        const float x = (float)qr[d];
+        ss = fmaf(x, x, ss);
+      }
+    }
+    ss += __shfl_xor(ss, 32);
+    inv = 1.0f / sqrtf(ss / (float)d_qk + a.qn_eps);
+    if (hi == 0) inv_s[w * 32 + lo] = inv;
   }
   const size_t orow = ((size_t)b * R + (size_t)tok * a.n_h + h) * width;
   E* out = (E*)a.qcat + orow;
   if (valid) {
+    const float sc = a.qscale * inv;
 #pragma unroll
     for (int it = 0; it < NT; ++it)
 #pragma unroll
@@ -96,7 +132,7 @@ __global__ __launch_bounds__(256) void qprep_bf16_kernel(AttendArgs a) {
         typename Elem<E>::v4 o, ol;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float v = acc[it][4 * g + j] * a.qscale;
+          const float v = acc[it][4 * g + j] * sc;
           o[j] = Elem<E>::from(v);
           ol[j] = Elem<E>::from(v - (float)o[j]);
         }
@@ -106,6 +142,8 @@ __global__ __launch_bounds__(256) void qprep_bf16_kernel(AttendArgs a) {
       }
   }
   // rotary part: lanes walk (token, pair) of this wave's 32 tokens
+  // (NORM: the gain before the rotation, the row's 1 / rms after it)
+  if constexpr (NORM) __syncthreads();
   const int P = a.d_rope / 2;
   for (int e = l; e < 32 * P; e += 64) {
     const int tt = blockIdx.x * 128 + w * 32 + e / P;
@@ -114,11 +152,17 @@ __global__ __launch_bounds__(256) void qprep_bf16_kernel(AttendArgs a) {
     const bf16_t* qr =
         (const bf16_t*)a.q + (((size_t)b * a.Lq + tt) * a.n_h + h) * d_qk + a.d_nope + 2 * p;
     float x0 = (float)qr[0], x1 = (float)qr[1];
+    float sc = a.qscale;
+    if constexpr (NORM) {
+      x0 *= (float)gam[a.d_nope + 2 * p];
+      x1 *= (float)gam[a.d_nope + 2 * p + 1];
+      sc *= inv_s[w * 32 + e / P];
+    }
     rope_pair(a.rope, p, token_pos(a.q_token0 + tt, a.T, a.grid_w), x0, x1);
     const size_t off = ((size_t)b * R + (size_t)tt * a.n_h + h) * width + DC + 2 * p;
     E* lo = SPLIT ? (E*)a.qcat_lo + off : nullptr;
-    store_q<E, SPLIT>((E*)a.qcat + off, lo, x0 * a.qscale);
-    store_q<E, SPLIT>((E*)a.qcat + off + 1, lo + 1, x1 * a.qscale);
+    store_q<E, SPLIT>((E*)a.qcat + off, lo, x0 * sc);
+    store_q<E, SPLIT>((E*)a.qcat + off + 1, lo + 1, x1 * sc);
   }
 }
 
@@ -136,7 +180,9 @@ constexpr int qprep_rows_max_nope() {
   return (256 / (DC / 8)) * kQprepRowsMaxK;
 }
 
-template <typename E, int DC, bool SPLIT>
+// NORM: the queries are gained and scaled by their row's 1 / rms in fp32 as
+// they are staged; the rotary pairs likewise, the gain before the rotation.
+template <typename E, int DC, bool SPLIT, bool NORM = false>
 __global__ __launch_bounds__(256) void qprep_rows_kernel(AttendArgs a) {
   constexpr int CH = DC / 8;                      // 8-column chunks of a W row
   constexpr int NG = 256 / CH;                    // row groups
@@ -144,6 +190,7 @@ __global__ __launch_bounds__(256) void qprep_rows_kernel(AttendArgs a) {
   constexpr int QPT = (kQprepRowsMaxLq * NMAX + 255) / 256;  // query elements per thread
   __shared__ float qs[kQprepRowsMaxLq * NMAX];    // [tok][n] fp32 queries
   __shared__ float red[NG][DC];                   // one token's row-group sums
+  __shared__ float inv_s[NORM ? kQprepRowsMaxLq : 1];  // 1 / rms of each token's row
   const int tid = threadIdx.x;
   const int j = tid % CH, g = tid / CH;
   const bool active = g < NG;
@@ -170,9 +217,36 @@ __global__ __launch_bounds__(256) void qprep_rows_kernel(AttendArgs a) {
     const int tok = e / d_nope, n = e - tok * d_nope;
     qv[i] = (float)q[(((size_t)b * a.Lq + tok) * a.n_h + h) * d_qk + n];
   }
+  const bf16_t* gam = (const bf16_t*)a.qn_gamma;
+  if constexpr (NORM) {
+    // wave 0: each token's sum of squares over its d_nope + d_rope values
+    if (tid < 64) {
+      for (int tok = 0; tok < a.Lq; ++tok) {
+        const bf16_t* qr = q + (((size_t)b * a.Lq + tok) * a.n_h + h) * d_qk;
+        float ss = 0.0f;
+        for (int d = tid; d < d_qk; d += 64) {
+          const float x = (float)qr[d];
+          ss = fmaf(x, x, ss);
+        }
 #pragma unroll
-  for (int i = 0; i < QPT; ++i)
-    if (tid + 256 * i < nq) qs[tid + 256 * i] = qv[i];
+        for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+        if (tid == 0) inv_s[tok] = 1.0f / sqrtf(ss / (float)d_qk + a.qn_eps);
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < QPT; ++i) {
+    const int e = tid + 256 * i;
+    if (e < nq) {
+      if constexpr (NORM) {
+        const int tok = e / d_nope, n = e - tok * d_nope;
+        qs[e] = qv[i] * (float)gam[n] * inv_s[tok];
+      } else {
+        qs[e] = qv[i];
+      }
+    }
+  }
   __syncthreads();
 
   for (int tok = 0; tok < a.Lq; ++tok) {
@@ -206,11 +280,17 @@ __global__ __launch_bounds__(256) void qprep_rows_kernel(AttendArgs a) {
     const int tok = e / P, p = e - tok * P;
     const bf16_t* qr = q + (((size_t)b * a.Lq + tok) * a.n_h + h) * d_qk + d_nope + 2 * p;
     float x0 = (float)qr[0], x1 = (float)qr[1];
+    float sc = a.qscale;
+    if constexpr (NORM) {
+      x0 *= (float)gam[d_nope + 2 * p];
+      x1 *= (float)gam[d_nope + 2 * p + 1];
+      sc *= inv_s[tok];
+    }
     rope_pair(a.rope, p, token_pos(a.q_token0 + tok, a.T, a.grid_w), x0, x1);
     const size_t off = ((size_t)b * R + (size_t)tok * a.n_h + h) * width + DC + 2 * p;
     E* lo = SPLIT ? (E*)a.qcat_lo + off : nullptr;
-    store_q<E, SPLIT>((E*)a.qcat + off, lo, x0 * a.qscale);
-    store_q<E, SPLIT>((E*)a.qcat + off + 1, lo + 1, x1 * a.qscale);
+    store_q<E, SPLIT>((E*)a.qcat + off, lo, x0 * sc);
+    store_q<E, SPLIT>((E*)a.qcat + off + 1, lo + 1, x1 * sc);
   }
 }
 
@@ -612,15 +692,22 @@ template <typename E, int DC, bool F8 = false>
 hipError_t launch_dc(const AttendArgs& a, hipStream_t s) {
   constexpr bool SPLIT = kSplitOf<E>;
   if ((a.qcat_lo != nullptr) != SPLIT) return hipErrorInvalidValue;
+  const bool norm = a.qn_gamma != nullptr;
   if (a.Lq <= kQprepRowsMaxLq && a.d_nope <= qprep_rows_max_nope<DC>()) {
-    hipLaunchKernelGGL((qprep_rows_kernel<E, DC, SPLIT>), dim3((unsigned)a.n_h, (unsigned)a.B), dim3(256), 0,
-                       s, a);
+    const dim3 grid((unsigned)a.n_h, (unsigned)a.B);
+    if (norm)
+      hipLaunchKernelGGL((qprep_rows_kernel<E, DC, SPLIT, true>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((qprep_rows_kernel<E, DC, SPLIT>), grid, dim3(256), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   } else {
     const size_t lds = (size_t)a.d_nope * (DC + 8) * sizeof(bf16_t);
     dim3 grid((unsigned)((a.Lq + 127) / 128), (unsigned)a.n_h, (unsigned)a.B);
-    hipLaunchKernelGGL((qprep_bf16_kernel<E, DC, SPLIT>), grid, dim3(256), lds, s, a);
+    if (norm)
+      hipLaunchKernelGGL((qprep_bf16_kernel<E, DC, SPLIT, true>), grid, dim3(256), lds, s, a);
+    else
+      hipLaunchKernelGGL((qprep_bf16_kernel<E, DC, SPLIT>), grid, dim3(256), lds, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -40,6 +40,10 @@ struct mla_cache {
   const void* ex_wuv;
   uint64_t ex_gen;
   uint64_t ex_token;  // the expansion's entry in the workspace record below
+  // mla_cache_set_query_norm: gain (caller's device memory) and epsilon of the
+  // RMS norm of each head's query row; null when off.
+  const void* qn_gamma;
+  float qn_eps;
 };
 
 namespace {
@@ -478,6 +482,8 @@ mla::AttendArgs latent_attend_args(const mla_cache* h, const void* q, int64_t q_
   a.Lk = (int)(n_resident(h) * a.T);
   a.cache_type = c.cache_dtype;
   a.qscale = (float)(1.4426950408889634 / sqrt((double)(c.d_nope + c.d_rope)));
+  a.qn_gamma = h->qn_gamma;
+  a.qn_eps = h->qn_eps;
   a.ev_start = h->prof_start;
   a.ev_stop = h->prof_stop;
   a.rope = latent_rope(c);
@@ -542,6 +548,8 @@ mla_status create(const mla_layer_config* cfg, void* storage, size_t storage_byt
   h->gen = 0;
   h->expand_reuse = 0;
   h->ex_valid = false;
+  h->qn_gamma = nullptr;
+  h->qn_eps = 0.0f;
   h->ex_ws = h->ex_wuk = h->ex_wuv = nullptr;
   h->ex_gen = 0;
   h->ex_token = 0;
@@ -730,6 +738,21 @@ mla_status mla_cache_set_attend_path(mla_cache* h, int32_t path) {
   return MLA_OK;
 }
 
+mla_status mla_cache_set_query_norm(mla_cache* h, const void* gamma, float eps) {
+  if (h == nullptr) return MLA_ERR_INVALID_ARG;
+  if (h->dense) return MLA_ERR_WRONG_KIND;
+  if (gamma == nullptr) {
+    h->qn_gamma = nullptr;
+    h->qn_eps = 0.0f;
+    return MLA_OK;
+  }
+  if (!aligned16(gamma) || !(eps >= 0.0f) || !isfinite(eps)) return MLA_ERR_INVALID_ARG;
+  if (h->cfg.dtype != MLA_BF16) return MLA_ERR_UNSUPPORTED;
+  h->qn_gamma = gamma;
+  h->qn_eps = eps;
+  return MLA_OK;
+}
+
 mla_status mla_attend(mla_cache* h, const void* q, int64_t q_token0, int32_t Lq, const void* w_uk,
                       const void* w_uv, float* out, int32_t key_splits, void* workspace,
                       size_t workspace_bytes, void* stream) {
@@ -787,6 +810,8 @@ mla_status mla_attend(mla_cache* h, const void* q, int64_t q_token0, int32_t Lq,
     m.Lk = a.Lk;
     m.cache_type = MLA_F16;  // the rebuilt window is fp16 for either ring
     m.qscale = a.qscale;
+    m.qn_gamma = a.qn_gamma;
+    m.qn_eps = a.qn_eps;
     m.ev_start = h->prof_start;
     m.ev_stop = h->prof_stop;
     m.rope = expand_rope(c);
@@ -928,6 +953,9 @@ mla_status mla_attend_block(mla_cache* h, const void* x, int64_t q_token0, int32
   const mla_layer_config& c = h->cfg;
   if ((int64_t)Lq * c.n_heads >= (1LL << 30)) return MLA_ERR_INVALID_ARG;
   if (!block_supported(c)) return MLA_ERR_UNSUPPORTED;
+  // The block never forms the per-head queries the norm would act on (they
+  // come out of the folded projection already absorbed).
+  if (h->qn_gamma != nullptr) return MLA_ERR_UNSUPPORTED;
   const LatentLayout L = latent_layout(h, Lq, key_splits, -1, true);
   if (workspace == nullptr || ((uintptr_t)workspace % kAlign) != 0 || workspace_bytes < L.total)
     return MLA_ERR_WORKSPACE;

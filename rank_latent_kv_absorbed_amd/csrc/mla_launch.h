@@ -310,6 +310,8 @@ struct AttendArgs {
   Schedule sched;
   int cache_type;         // 1 = bf16, 2 = fp16, 3 = E4M3 (widened to fp16); inputs are bf16
   float qscale;           // log2(e) / sqrt(d_nope + d_rope)
+  const void* qn_gamma;   // optional RMS norm of each head's query row: gain [d_nope + d_rope] bf16; null = none
+  float qn_eps;
   hipEvent_t ev_start;    // optional: recorded right before / after the core kernel
   hipEvent_t ev_stop;
   RopeTable rope;
@@ -330,6 +332,8 @@ struct MhaAttendArgs {
   int Lk;
   int cache_type;
   float qscale;
+  const void* qn_gamma;   // optional RMS norm of each query row over d_h: gain [d_h] bf16; null = none
+  float qn_eps;
   hipEvent_t ev_start;
   hipEvent_t ev_stop;
   RopeTable rope;

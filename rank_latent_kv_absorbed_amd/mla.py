@@ -86,6 +86,7 @@ SIGNATURES = {
     "mla_cache_set_attend_path": (_I32, [_HANDLE, _I32]),
     "mla_attend_path": (_I32, [_HANDLE, _I32, _I32]),
     "mla_cache_set_expand_reuse": (_I32, [_HANDLE, _I32]),
+    "mla_cache_set_query_norm": (_I32, [_HANDLE, _VP, ctypes.c_float]),
     "mla_status_str": (ctypes.c_char_p, [_I32]),
     "mla_version": (ctypes.c_char_p, []),
 }
@@ -324,6 +325,20 @@ class LatentCache(_CacheBase):
         """Let expand-path attends reuse the rebuilt window while it is unchanged
         (same workspace and weights; see mla_cache_set_expand_reuse)."""
         _check(lib().mla_cache_set_expand_reuse(self._h, 1 if enable else 0), "set_expand_reuse")
+
+    def set_query_norm(self, gamma, eps=1e-6):
+        """RMS-normalise each head's query row with gain `gamma` [d_nope + d_rope]
+        (input dtype, on this device) in later attends; None switches it off
+        (see mla_cache_set_query_norm).  The handle keeps a reference to gamma
+        while the norm is set."""
+        if gamma is None:
+            _check(lib().mla_cache_set_query_norm(self._h, None, 0.0), "set_query_norm")
+            self._qn_gamma = None
+            return
+        cfg = self.cfg
+        _need(gamma, "gamma", self.tdtype, (cfg.d_nope + cfg.d_rope,), self.device)
+        _check(lib().mla_cache_set_query_norm(self._h, _ptr(gamma), float(eps)), "set_query_norm")
+        self._qn_gamma = gamma
 
     def attend_path(self, Lq, key_splits=0):
         """Name of the path an attend of Lq queries takes on this handle."""

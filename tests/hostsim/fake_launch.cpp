@@ -156,6 +156,12 @@ int fake_sched_group_slots(int which, int grp) {
   return mla::sched_group_slots(sched_of(which), grp);
 }
 float fake_attend_qscale() { return g_attend.qscale; }
+// Query norm the last latent (which = 0) or per-head (which = 1) attend
+// carried: the gain pointer, and its epsilon through fake_qnorm_eps.
+long long fake_qnorm_gamma(int which) {
+  return (long long)(intptr_t)(which ? g_mha.qn_gamma : g_attend.qn_gamma);
+}
+float fake_qnorm_eps(int which) { return which ? g_mha.qn_eps : g_attend.qn_eps; }
 // The last latent attend's workspace pointers: qcat, qcat_lo, opart, ml.
 void fake_attend_ptrs(long long* o) {
   long long v[4] = {(long long)(intptr_t)g_attend.qcat, (long long)(intptr_t)g_attend.qcat_lo,

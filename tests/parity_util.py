@@ -80,6 +80,7 @@ class LatentRun:
         self.rnd = storage_round or cfg.cache_dtype
         self.n_ops = 0
         self.last_frame0 = None
+        self.q_norm = None
 
     def write(self, frame0, n_frames, x=None):
         if x is None:
@@ -113,13 +114,23 @@ class LatentRun:
     def query(self, Lq, chunk=1000):
         return chunk_q(self.cfg, Lq, layer=self.layer, chunk=chunk)
 
+    def set_query_norm(self, gamma, eps):
+        """Query RMS norm on the GPU handle and in the oracle (gamma: CPU tensor
+        in the input dtype, or None to switch it off)."""
+        if gamma is None:
+            self.gpu.set_query_norm(None)
+            self.q_norm = None
+            return
+        self.gpu.set_query_norm(dev(gamma), eps)
+        self.q_norm = (gamma.double().numpy(), eps)
+
     def attend(self, q, q_token0, key_splits=0, rows=None, workspace=None):
         out = self.gpu.attend(dev(q), q_token0, self.wd["w_uk"], self.wd["w_uv"],
                               key_splits=key_splits, workspace=workspace)
         torch.cuda.synchronize()
         ref = O.attend(self.store, self.ring, q.double().numpy(), q_token0,
                        self.w["w_uk"].double().numpy(), self.w["w_uv"].double().numpy(), self.cfg,
-                       rows=rows)
+                       rows=rows, q_norm=self.q_norm)
         got = out.cpu().numpy()
         if rows is not None:
             got = got[:, rows]

@@ -79,6 +79,8 @@ def sim(tmp_path_factory):
         f = getattr(L, name)
         f.restype, f.argtypes = res, args
     L.fake_attend_qscale.restype = ctypes.c_float
+    L.fake_qnorm_gamma.restype = ctypes.c_longlong
+    L.fake_qnorm_eps.restype = ctypes.c_float
     return L
 
 
@@ -898,3 +900,48 @@ def test_block_placement_is_a_permutation_with_tails_beside_their_groups(sim):
                 if mains and tails:
                     first_grp = min(tails) * a["tpb"] // tl
                     assert abs(first_grp - min(mains)) <= -(-rem // 8) + 1, (name, kw, Lq, path, x)
+
+
+def test_query_norm_state_reaches_both_paths_and_the_block_refuses(sim):
+    """mla_cache_set_query_norm: argument checks, the gain and epsilon carried
+    by the latent (absorbed) and per-head (expand) attends, switched off by
+    NULL, refused on dense and fp32 handles, and mla_attend_block refuses
+    while it is set (nothing launched)."""
+    gam = FAKE_PTR + 4096
+    st, h = _create(sim, _cfg())
+    assert st == 0 and sim.mla_cache_set_state(h, 0, 20) == 0
+    f32 = ctypes.c_float
+    assert sim.mla_cache_set_query_norm(None, P(gam), f32(1e-6)) == 1
+    assert sim.mla_cache_set_query_norm(h, P(gam + 8), f32(1e-6)) == 1      # misaligned
+    assert sim.mla_cache_set_query_norm(h, P(gam), f32(-1.0)) == 1
+    assert sim.mla_cache_set_query_norm(h, P(gam), f32(float("inf"))) == 1
+    assert sim.mla_cache_set_query_norm(h, P(gam), f32(float("nan"))) == 1
+    assert sim.mla_cache_set_query_norm(h, P(gam), f32(1e-5)) == 0
+    ws = 1 << 40
+    for path, which in ((1, 0), (2, 1)):
+        assert sim.mla_cache_set_attend_path(h, path) == 0
+        need = sim.mla_attend_workspace_bytes(h, 4680, 0)
+        assert sim.mla_attend(h, P(FAKE_PTR), 21 * 1560 - 4680, 4680, P(FAKE_PTR), P(FAKE_PTR),
+                              P(FAKE_PTR), 0, P(ws), need, None) == 0
+        assert sim.fake_qnorm_gamma(which) == gam
+        assert sim.fake_qnorm_eps(which) == np.float32(1e-5)
+    # the attention block never forms per-head queries: refused, nothing launched
+    assert sim.mla_cache_set_attend_path(h, 0) == 0
+    n0 = sim.fake_count()
+    need = sim.mla_attend_block_workspace_bytes(h, 64, 0)
+    assert sim.mla_attend_block(h, P(FAKE_PTR), 0, 64, P(FAKE_PTR), P(FAKE_PTR), P(FAKE_PTR), 0,
+                                P(ws), need, None) == 8
+    assert sim.fake_count() == n0
+    # off again: attends carry no gain, the block runs
+    assert sim.mla_cache_set_query_norm(h, None, f32(0.0)) == 0
+    assert sim.mla_attend(h, P(FAKE_PTR), 0, 64, P(FAKE_PTR), P(FAKE_PTR), P(FAKE_PTR), 0, P(ws),
+                          sim.mla_attend_workspace_bytes(h, 64, 0), None) == 0
+    assert sim.fake_qnorm_gamma(0) == 0
+    assert sim.mla_attend_block(h, P(FAKE_PTR), 0, 64, P(FAKE_PTR), P(FAKE_PTR), P(FAKE_PTR), 0,
+                                P(ws), need, None) == 0
+    # dense and fp32 handles
+    st, d = _create(sim, _cfg(), dense=True)
+    assert st == 0 and sim.mla_cache_set_query_norm(d, P(gam), f32(1e-6)) == 9
+    st, g = _create(sim, _cfg(dtype="f32", cache_dtype="f32"))
+    assert st == 0 and sim.mla_cache_set_query_norm(g, P(gam), f32(1e-6)) == 8
+    assert sim.mla_cache_set_query_norm(g, None, f32(0.0)) == 0
