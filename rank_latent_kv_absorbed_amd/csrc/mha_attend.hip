@@ -1,8 +1,10 @@
-// Dense per-head attention over a dense K/V window (the comparison path: in
+// Dense per-head attention over a dense K/V window: the comparison path (in
 // the VideoMLA problem definition every cached token stores full keys and
-// values for every head).  Queries are rotated over the whole head width and
-// pre-scaled, then the shared flash-style core runs per head with K and V as
-// separate slices of the cached row, and a merge kernel normalises into fp32.
+// values for every head), and the second half of expand-then-attend, over
+// the window rebuilt from the latent.  Queries are rotated over the whole head
+// width (optionally RMS-normalised first) and pre-scaled, then the shared
+// flash-style core runs per head with K and V as separate slices of the
+// cached row, and a merge kernel normalises into fp32.
 #include "mla_attn_core.h"
 
 namespace mla {

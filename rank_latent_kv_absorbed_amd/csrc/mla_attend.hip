@@ -6,7 +6,9 @@
 //               position, both scaled by log2(e)/sqrt(d_nope + d_rope), written
 //               as one row [q_lat | q^R_rot] of the cache type per (token, head)
 //               pair (a bf16 cache also gets the row of remainders, the bf16
-//               rounding of q - bf16(q), for the split-operand core).
+//               rounding of q - bf16(q), for the split-operand core).  With a
+//               query norm set, each head's query row is RMS-normalised with
+//               its gain first (before the rotation and the fold).
 //  2. attend:   the shared flash-style core (mla_attn_core.h).  Rows are
 //               (token, head) pairs; every row scores against the same cached
 //               rows [c | k^R], so a key tile staged once in LDS serves all heads

@@ -62,8 +62,12 @@
 // half the bytes of a 2-byte tile; at the start of its step every lane widens
 // its share to fp16 (exact) into one decode buffer in the layout above, keys
 // past the window zeroed, and a barrier publishes it.  The staging buffer is
-// refilled right after that barrier, so NS - 1 raw tiles stay in flight while
-// one is consumed.  Products then run on fp16 operands as for an fp16 cache.
+// refilled right after that barrier, so the next NS raw tiles stream in while
+// the widened one is consumed.  Products then run on fp16 operands as for an
+// fp16 cache.
+// One-wave 16-row blocks widen differently: each lane widens the key
+// fragments of its own score products into registers and writes only the
+// value columns to the decode buffer (nothing is read back for the scores).
 #pragma once
 
 #include "mla_device.h"

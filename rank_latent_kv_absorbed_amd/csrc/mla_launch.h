@@ -350,7 +350,7 @@ struct ExpandArgs {
   int64_t ring_rows;
   int64_t key_slot0;      // ring slot of resident key 0
   int Lk;
-  int cache_type;         // ring: 2 = fp16, 3 = E4M3 (either way the rebuilt window is fp16)
+  int cache_type;         // ring: 1 = bf16, 2 = fp16, 3 = E4M3 (the rebuilt window is fp16 for each)
 };
 
 hipError_t launch_cache_write_bf16(const CacheWriteArgs& a, hipStream_t s);
