@@ -214,7 +214,13 @@ size_t mla_attend_workspace_bytes(const mla_cache* cache, int32_t Lq, int32_t ke
  * key_splits = 0 lets the library choose; > 0 cuts every row group's key
  * range into about that many pieces.  workspace: device memory of at least
  * mla_attend_workspace_bytes(cache, Lq, key_splits).  MLA_ERR_EMPTY if no frame
- * is resident. */
+ * is resident.
+ * Graph capture: the call enqueues only kernels on `stream` (no memset, no
+ * allocation, no host synchronisation), so it can be captured into a HIP
+ * graph.  A captured call keeps its arguments and the window state of the
+ * capture (resident key count, first slot, attend path): replay it for new
+ * contents of the same buffers, and capture again after a write, an
+ * eviction or a state change. */
 mla_status mla_attend(mla_cache* cache, const void* q, int64_t q_token0, int32_t Lq,
                       const void* w_uk, const void* w_uv, float* out, int32_t key_splits,
                       void* workspace, size_t workspace_bytes, void* stream);
