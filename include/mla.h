@@ -13,9 +13,12 @@
  *     (problem definition: a 21-latent-frame window);
  *   - attention rebuilds each head's content key and value from the latent
  *     with per-head up-projections W^K_up, W^V_up            (method item 2).
- *     This library computes that result in absorbed form: W^K_up is folded into
- *     each head's query, softmax(.)·C is accumulated in latent space, and
- *     W^V_up is applied afterwards (equal by associativity).
+ *     This library computes that result in two ways (see mla_attend_path):
+ *     in absorbed form - W^K_up folded into each head's query, softmax(.)·C
+ *     accumulated in latent space, W^V_up applied afterwards (equal by
+ *     associativity) - or, for long query chunks where it needs fewer
+ *     products, by rebuilding every resident key's per-head key and value
+ *     once per call and running per-head attention over them.
  * A dense per-head K/V cache (problem definition: every cached token stores
  * full keys and values for every head) is provided with the same conventions
  * as the in-run comparison.
@@ -42,11 +45,14 @@
  *     cache_dtype (fp32 with fp32 inputs; bf16 or fp16 with bf16 inputs: two
  *     bytes per stored scalar either way, the per-token count of method
  *     item 4 at the 2-byte width the problem definition's ~6.0 GB implies).
- *     Prepared queries and softmax weights enter the matrix units in the
- *     cache type; with a bf16 ring each of them is carried as two bf16 parts
- *     (the value and the bf16 rounding of its remainder; twice the matrix
- *     work), since bf16's 8 significant bits alone move the output by about
- *     1e-3 of its size.  Every sum is fp32 and the attention output is fp32.
+ *     On the absorbed path prepared queries and softmax weights enter the
+ *     matrix units in the cache type; with a bf16 ring each of them is
+ *     carried as two bf16 parts (the value and the bf16 rounding of its
+ *     remainder; twice the matrix work), since bf16's 8 significant bits
+ *     alone move the output by about 1e-3 of its size.  The expand path
+ *     rebuilds fp16 per-head keys and values for every ring type and runs
+ *     its attention on fp16 operands.  Every sum is fp32 and the attention
+ *     output is fp32.
  *   - Range: an fp16 ring holds magnitudes up to 65504; a computed c or k^R
  *     value beyond that is stored as +-infinity (IEEE round to nearest),
  *     and attention over such a row returns NaN for its sequence.  bf16 and
