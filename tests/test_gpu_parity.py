@@ -716,11 +716,12 @@ def test_rollout_80_chunks_ring_bit_exact(d_c):
             assert_parity(got, ref, "bf16", f"exact rollout d_c={d_c} chunk {k}")
 
 
-@pytest.mark.parametrize("d_c", [64, 128, 192])
-def test_rollout_80_chunks_gaussian_sampled_rows(d_c):
+@pytest.mark.parametrize("d_c,cache_dtype", [(64, "f16"), (128, "f16"), (192, "f16"), (192, "bf16")])
+def test_rollout_80_chunks_gaussian_sampled_rows(d_c, cache_dtype):
     """The same rollout on Gaussian inputs (seeded per chunk), attention on the
-    library's automatic path, sampled rows checked at chunks 0, 6, 7, 79."""
-    cfg = config("wan_window").with_(d_c=d_c)
+    library's automatic path, sampled rows checked at chunks 0, 6, 7, 79 (a
+    bf16 ring expands into fp16 keys and values there)."""
+    cfg = config("wan_window").with_(d_c=d_c, cache_dtype=cache_dtype)
     run = LatentRun(cfg)
     rows = sample_rows(cfg.Lq, 16)
     ws = torch.empty(run.gpu.workspace_bytes(cfg.Lq), dtype=torch.uint8, device="cuda")
@@ -731,7 +732,8 @@ def test_rollout_80_chunks_gaussian_sampled_rows(d_c):
             q = run.query(cfg.Lq, chunk=k)
             got, ref, _ = run.attend(q, 3 * k * cfg.T, rows=rows, workspace=ws)
             assert_parity(got, ref, "bf16",
-                          f"gaussian rollout d_c={d_c} chunk {k} {run.gpu.attend_path(cfg.Lq)}")
+                          f"gaussian rollout d_c={d_c} {cache_dtype} chunk {k} {run.gpu.attend_path(cfg.Lq)}",
+                          mean_lim=ring_lim(cfg))
 
 
 # ---------------------------------------------------------------------------
