@@ -129,3 +129,19 @@ def test_query_norm_off_again_and_block_refusal():
     assert np.abs(ref_p - ref_n).max() > 1e-2 * np.abs(ref_p).max()   # the norm mattered
     run.gpu.attend_block(xq, 8 * cfg.T - 16, w_qf, w_fo)
     torch.cuda.synchronize()
+
+
+def test_query_norm_key_splits_and_noalloc():
+    """With the norm set: forced key splits against the oracle, and the
+    allocation-free entry bit for bit against mla_attend (same path and
+    schedule)."""
+    cfg, run = wrapped_mid_run("f16", "absorbed")
+    run.set_query_norm(gain(cfg), EPS)
+    q = uneven_query(run, 40)
+    got, ref, _ = run.attend(q, 8 * cfg.T - 40, key_splits=3)
+    assert_parity(got, ref, "bf16", "query norm, 3 key ranges")
+    _, _, out = run.attend(q, 8 * cfg.T - 40)
+    o2 = torch.empty_like(out)
+    run.gpu.attend_noalloc(dev(q), 8 * cfg.T - 40, run.wd["w_uk"], run.wd["w_uv"], o2)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, out)
