@@ -241,7 +241,8 @@ mla_status mla_attend(mla_cache* cache, const void* q, int64_t q_token0, int32_t
  * counterpart is the latent norm of mla_cache_write_norm.  gamma: device
  * pointer to [d_nope + d_rope] gains in the input dtype (bf16), 16-byte
  * aligned, owned by the caller and read by every attend while set; NULL
- * switches the norm off.  eps >= 0 and finite.  Errors: MLA_ERR_INVALID_ARG
+ * switches the norm off.  eps >= 0 and finite (with eps = 0 an all-zero query
+ * row has no scale and its output is NaN).  Errors: MLA_ERR_INVALID_ARG
  * (null handle, misaligned gamma, bad eps), MLA_ERR_WRONG_KIND (dense
  * handle), MLA_ERR_UNSUPPORTED (fp32 handles).  While it is set,
  * mla_attend_block returns MLA_ERR_UNSUPPORTED (its folded projection never
