@@ -145,3 +145,21 @@ def test_query_norm_key_splits_and_noalloc():
     run.gpu.attend_noalloc(dev(q), 8 * cfg.T - 40, run.wd["w_uk"], run.wd["w_uv"], o2)
     torch.cuda.synchronize()
     assert torch.equal(o2, out)
+
+
+@pytest.mark.parametrize("path", ["absorbed", "expand"])
+def test_query_norm_zero_row_with_zero_eps_stays_in_its_row(path):
+    """eps = 0 and one all-zero query row: that (token, head) row has no scale
+    and comes out NaN, as in the oracle (0 / 0); every other row is untouched
+    and matches the oracle."""
+    cfg, run = wrapped_mid_run("f16", path)
+    run.set_query_norm(gain(cfg), 0.0)
+    q = uneven_query(run, 130)
+    q[1, 17, 2] = 0.0
+    with np.errstate(invalid="ignore", divide="ignore"):      # the oracle's 0 / 0
+        got, ref, _ = run.attend(q, 8 * cfg.T - 130)
+    assert np.isnan(ref[1, 17, 2]).all() and np.isnan(got[1, 17, 2]).all()
+    keep = np.ones(got.shape[:3], dtype=bool)
+    keep[1, 17, 2] = False
+    assert np.isfinite(got[keep]).all()
+    assert_parity(got[keep], ref[keep], "bf16", f"query norm, zero row elsewhere, {path}")
