@@ -13,7 +13,8 @@ layer = batch * 4680 / step time, plus MFMA utilisation.
 
 Also reported on the same JSON line: the main attention kernel alone (HIP
 events recorded by the library on its stream) against the MFMA roofline; the
-other path's step time; the same step with a bf16 ring (both paths); the
+other path's step time; the same step with a bf16 ring (both paths) and with
+the query norm set; the
 dense per-head MHA comparison (same shape, and at the largest batch whose
 30-layer dense cache fits the GPU, with the measured batch capacity of both
 caches); cache-bound small-query cases against HBM bandwidth; batch scaling;
@@ -457,6 +458,31 @@ def run_extras(args, result, torch, dev, cfg, caches, weights, x_pre, x_chunk, q
     del ecaches, ews, st
     torch.cuda.empty_cache()
     log("e4m3 ring")
+
+    # ---- the same step with the query RMS norm set on every layer window
+    # (gain 1 + 0.25 N(0, 1)): its cost over the plain step
+    # Plain and normed steps alternate (three rounds each), so that clock
+    # drift over the run does not enter the comparison.
+    qn_gain = (1.0 + 0.25 * torch.randn(cfg.d_qk, generator=gen, device=dev)).to(torch.bfloat16)
+    st = Stepper(caches, ws)
+    timing = {False: [], True: []}
+    for _ in range(3):
+        for norm in (False, True):
+            for c in caches:
+                c.set_query_norm(qn_gain if norm else None, 1e-6)
+            for _ in range(3):
+                st.step()
+            timing[norm].append(st.timed(min(args.steps, 10))[0])
+    for c in caches:
+        c.set_query_norm(None)
+    qn_step, plain_step = min(timing[True]), min(timing[False])
+    result["query_norm"] = {"ms_per_step": round(qn_step, 4), "value": round(B * Lq / (qn_step / 1e3), 1),
+                            "plain_ms_per_step_alternating": round(plain_step, 4),
+                            "overhead_pct": round(100.0 * (qn_step / plain_step - 1.0), 2), "path": path,
+                            "note": "each head's query row RMS-normalised before the rotation and the fold; "
+                                    "best of three rounds, alternating with plain steps"}
+    del st
+    log("query norm")
 
     # ---- several attends per written chunk (denoising steps): with reuse on,
     # the expand path rebuilds the window once per chunk
