@@ -146,13 +146,29 @@ def cpu_baseline(cfg, x_chunk, w, q, repeats=3):
         O.attend(store, ring, qs, cfg.window_frames * T, wd["w_uk"], wd["w_uv"], cfg)
         times.append(time.perf_counter() - t0)
     t_step = sorted(times)[len(times) // 2]
+    # the cache-bound case beside it: one query token of 8 sequences over the
+    # full window (the oracle's explicit per-head rebuild of every key)
+    sq_cfg = cfg.with_(batch=8)
+    sq_store = O.round_storage(rng.standard_normal((8, cfg.window_frames * T, cfg.width)), cfg.cache_dtype)
+    sq_ring = O.RingModel(cfg.window_frames, T)
+    sq_ring.write(0, cfg.window_frames)
+    sq_q = rng.standard_normal((8, 1, cfg.n_heads, cfg.d_qk))
+    sq_times = []
+    for _ in range(repeats):
+        t0 = time.perf_counter()
+        O.attend(sq_store, sq_ring, sq_q, cfg.window_frames * T - 1, wd["w_uk"], wd["w_uv"], sq_cfg)
+        sq_times.append(time.perf_counter() - t0)
+    t_sq = sorted(sq_times)[len(sq_times) // 2]
     return {
         "value": cfg.Lq / t_step, "unit": "query tokens/s per layer", "cores": int(threads),
         "kind": "oracle",
         "sample": (f"one full step at batch 1 (evict {cfg.chunk_frames} frames, cache write of "
                    f"{cfg.Lq} tokens, attention of {cfg.Lq} queries x {cfg.n_heads} heads over "
                    f"{cfg.window_frames * T} keys), fp64 NumPy oracle, median of {repeats} runs"),
-        "seconds_measured": round(sum(times), 2),
+        "seconds_measured": round(sum(times) + sum(sq_times), 2),
+        "small_query": {"value": 8 / t_sq, "unit": "query tokens/s per layer",
+                        "sample": (f"attention of 1 query x {cfg.n_heads} heads in each of 8 sequences over "
+                                   f"{cfg.window_frames * T} keys, fp64 NumPy oracle, median of {repeats} runs")},
         "cpu_model": cpu_model(), "host_cores": HOST_CORES,
         "openblas_num_threads": os.environ.get("OPENBLAS_NUM_THREADS"),
     }
@@ -254,24 +270,31 @@ def main():
                 c.set_profile_events(None, None)
 
         def timed(self, n_steps):
-            """(ms per step, mean core-kernel ms) over n_steps steps."""
+            """(ms per step, mean core-kernel ms) over n_steps steps; the
+            per-step and per-launch times are kept in self.last."""
             core_ev = [(ev.create(), ev.create()) for _ in range(n_steps)]
-            t_start = torch.cuda.Event(enable_timing=True)
-            t_stop = torch.cuda.Event(enable_timing=True)
+            marks = [torch.cuda.Event(enable_timing=True) for _ in range(n_steps + 1)]
             torch.cuda.synchronize()
-            t_start.record()
+            marks[0].record()
             for k in range(n_steps):
                 self.step(core_ev[k])
-            t_stop.record()
+                marks[k + 1].record()
             torch.cuda.synchronize()
             core_ms = [ev.elapsed_ms(a, b) for a, b in core_ev]
-            return t_start.elapsed_time(t_stop) / n_steps, sum(core_ms) / len(core_ms)
+            self.last = {"step_ms": [marks[k].elapsed_time(marks[k + 1]) for k in range(n_steps)],
+                         "core_ms": core_ms}
+            return marks[0].elapsed_time(marks[n_steps]) / n_steps, sum(core_ms) / len(core_ms)
 
     main_steps = Stepper(caches, ws)
     for _ in range(args.warmup):
         main_steps.step()
     torch.cuda.synchronize()
     ms_step, core_avg = main_steps.timed(args.steps)
+
+    def pct(v, p):
+        v = sorted(v)
+        return v[min(len(v) - 1, int(round(p / 100.0 * (len(v) - 1))))]
+    spread = {k: [round(pct(v, p), 4) for p in (10, 50, 90)] for k, v in main_steps.last.items()}
 
     # algorithmic work of the path that ran
     c_flop = core_flop(cfg, path, B, Lq, Lk)
@@ -322,6 +345,7 @@ def main():
                                                  if clock else None)},
         "step_flop": step_flop,
         "breakdown_ms": {"step": round(ms_step, 4), "attend_core": round(core_avg, 4)},
+        "p10_p50_p90_ms": {"step": spread["step_ms"], "attend_core": spread["core_ms"]},
         "cache_bytes": {"latent_per_layer": caches[0].nbytes, "latent_30_layers": caches[0].nbytes * 30,
                         "dense_per_layer": None},
     }
@@ -401,6 +425,43 @@ def run_extras(args, result, torch, dev, cfg, caches, weights, x_pre, x_chunk, q
             c.set_attend_path(args.path)
         del ws2, st
     log("other path")
+
+    # ---- the Wan-layer configuration: the chunk's queries over 9 resident
+    # frames (6 earlier + the 3 of the chunk, 14 040 keys), attention only,
+    # 30 layer windows cycled (each window narrowed to its newest 9 frames and
+    # restored afterwards)
+    saved = [c.info() for c in caches]
+    for c, inf in zip(caches, saved):
+        c.set_state(inf["newest_frame"] - 8, inf["newest_frame"])
+    Lk9 = 9 * T
+    p9 = caches[0].attend_path(Lq)
+
+    def call9(i):
+        l = i % L
+        caches[l].attend(q, (saved[l]["newest_frame"] - 2) * T, weights[l]["w_uk"], weights[l]["w_uv"],
+                         out=out, workspace=ws)
+
+    for i in range(L):
+        call9(i)
+    ms9 = event_ms(call9, 2 * L)
+    ev9 = [(ev.create(), ev.create()) for _ in range(2 * L)]
+    for i, (a_, b_) in enumerate(ev9):
+        caches[i % L].set_profile_events(a_, b_)
+        call9(i)
+        caches[i % L].set_profile_events(None, None)
+    torch.cuda.synchronize()
+    core9 = sum(ev.elapsed_ms(a_, b_) for a_, b_ in ev9) / len(ev9)
+    for c, inf in zip(caches, saved):
+        c.set_state(inf["oldest_frame"], inf["newest_frame"])
+    f9 = core_flop(cfg, p9, B, Lq, Lk9)
+    result["wan_layer_9_frames"] = {
+        "path": p9, "resident_keys": Lk9, "attend_ms": round(ms9, 4), "attend_core_ms": round(core9, 4),
+        "query_tokens_per_s": round(B * Lq / (ms9 / 1e3), 1),
+        "core_frac": round(f9 / (core9 / 1e3) / (PEAK_BF16_TFLOPS * 1e12), 4),
+        "mfma_util_pct_absorbed_form": round(100.0 * attend_flops(cfg.n_heads, Lq, Lk9, cfg.d_c, cfg.d_rope,
+                                                                  cfg.d_nope, cfg.d_v, B)
+                                             / (ms9 / 1e3) / (PEAK_BF16_TFLOPS * 1e12), 2)}
+    log("wan layer, 9 frames")
 
     # ---- the same step with a bf16 ring, on its automatic path (the rebuild
     # multiplies the bf16 rows on bf16 matrix units into fp16 keys and values)
