@@ -670,6 +670,36 @@ def test_batches_full_window_sampled_rows(batch, cache_dtype, path):
                   mean_lim=ring_lim(cfg))
 
 
+@pytest.mark.parametrize("path", ["auto", "absorbed"])
+def test_batch64_full_window_sampled_sequences(path):
+    """64 sequences over the full window (the expanded window alone holds
+    6.4e9 elements, past 2^32): random stored rows placed straight into the
+    ring (frames 10..30 resident, so it wraps), the whole chunk attended,
+    sampled rows of the first, a middle and the last sequence against the
+    oracle on those sequences."""
+    cfg = config("wan_window").with_(batch=64)
+    run = LatentRun(cfg, path=path)
+    rng = np.random.default_rng(64)
+    rows = O.round_storage(rng.standard_normal((cfg.batch, cfg.window_frames * cfg.T, cfg.width)),
+                           cfg.cache_dtype)
+    run.fill(10, 30, rows)
+    del rows
+    q = run.query(cfg.Lq)
+    q_token0 = 28 * cfg.T
+    out = run.gpu.attend(dev(q), q_token0, run.wd["w_uk"], run.wd["w_uv"])
+    torch.cuda.synchronize()
+    taken = run.gpu.attend_path(cfg.Lq)
+    assert taken == ("expand" if path == "auto" else "absorbed")
+    one = cfg.with_(batch=1)
+    sel = sample_rows(cfg.Lq, 8)
+    for b in (0, 31, 63):
+        ref = O.attend(run.store[b:b + 1], run.ring, q[b:b + 1].double().numpy(), q_token0,
+                       run.w["w_uk"].double().numpy(), run.w["w_uv"].double().numpy(), one, rows=sel)
+        got = out[b:b + 1, torch.from_numpy(sel)].cpu().numpy()
+        assert_parity(got, ref, "bf16", f"B=64 sequence {b} {taken}")
+    del out
+
+
 @pytest.mark.parametrize("Lq", [1, 8])
 def test_batch11_small_queries_full_window(Lq):
     cfg = config("wan_window").with_(batch=11)
